@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the SkipLayerNormalization row kernel on one MI355X.
+
+One step = one ``skipln_forward`` over one batch of the workload (the whole
+operator: sum, optional residual store, row statistics, normalization).
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+Steps rotate over enough copies of the buffers that a workload smaller than
+the 256 MiB last-level cache is still read from HBM.  The timed steps are
+captured once into a HIP graph and replayed, so the GPU runs them back to
+back; HIP events on the launch stream give the average launch duration.
+
+Prints one JSON line: rows/s of the headline workload (BERT-base shaped,
+8x128x768 fp32) with its HBM roofline, the same figures for the larger
+workloads (``sweep``), and the CPU oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SkipLayerNorm rows/s and achieved HBM GB/s (% of MI355X peak) at H=768..8192"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
+CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+HEADLINE = "bert_base_8x128x768_f32"
+SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_mean100"]
+KERNEL_SRC = os.path.join(ROOT, "transformer_residual_add_amd", "csrc", "skipln_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--no-sweep", action="store_true", help="only the headline workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle baseline")
+    p.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    p.add_argument("--variant", type=int, default=0, help="kernel family (SKIPLN_VARIANT_*), 0 = auto")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="instead of the operator, time the streaming copy of this many bytes")
+    return p.parse_args(argv)
+
+
+def source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none for this kernel/workload or the kernel source
+    changed since the counters were taken."""
+    try:
+        with open(COUNTERS) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    for e in data.get("entries", []):
+        if e.get("kernel") == kernel and e.get("workload") == workload:
+            if e.get("source_sha256") != source_sha():
+                return None
+            return int(e["fetch_bytes"] + e["write_bytes"])
+    return None
+
+
+class DeviceSets:
+    """``n`` copies of one workload's tensors on the GPU."""
+
+    def __init__(self, w, inputs, n: int):
+        import torch
+
+        dt = {"f32": torch.float32, "f16": torch.float16}[w.dtype]
+        first = {k: (None if v is None else torch.from_numpy(v).to("cuda")) for k, v in inputs.items()}
+        self.sets = []
+        for i in range(n):
+            d = {k: (None if v is None else (v if i == 0 else v.clone())) for k, v in first.items()}
+            d["out"] = torch.empty(w.rows, w.hidden, dtype=dt, device="cuda")
+            d["res"] = torch.empty(w.rows, w.hidden, dtype=dt, device="cuda") if w.residual else None
+            self.sets.append(d)
+
+
+def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
+    import torch
+
+    import transformer_residual_add_amd as T
+    from transformer_residual_add_amd import _lib as L
+    from transformer_residual_add_amd import workloads as W
+
+    code = L.F32 if w.dtype == "f32" else L.F16
+    kernel = T.select_kernel(w.hidden, code, True, variant)
+    alg = w.algorithmic_bytes()
+    # Per-step bytes actually touched (the broadcast skip counted once) decide
+    # how many buffer copies keep the working set above the cache.
+    n_sets = max(1, min(64, -(-3 * CACHE_BYTES // alg)))
+    log(f"{w.name}: generating inputs (rows={w.rows} H={w.hidden} {w.dtype}), {n_sets} buffer set(s)")
+    t0 = time.perf_counter()
+    inputs = W.make_inputs(w)
+    dev = DeviceSets(w, inputs, n_sets)
+    del inputs
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs ready in {time.perf_counter() - t0:.1f}s; kernel {kernel}")
+
+    mode = L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT
+    srows = w.skip_rows if w.broadcast else 0
+    eps = float(w.eps)
+    ptr = lambda t: None if t is None else t.data_ptr()
+
+    def step(i: int, stream: int):
+        d = dev.sets[i % n_sets]
+        T.forward_raw(ptr(d["input"]), ptr(d["skip"]), mode, srows, ptr(d["gamma"]), ptr(d["beta"]),
+                      ptr(d["bias"]), ptr(d["out"]), ptr(d["res"]), w.rows, w.hidden, eps, code, stream, variant)
+
+    main = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i, main.cuda_stream)
+    torch.cuda.synchronize()
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if launch == "graph":
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(steps):
+                step(i, cap)
+        g.replay()  # first replay uploads the graph; not timed
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(main)
+        g.replay()
+        ev1.record(main)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(main)
+        for i in range(steps):
+            step(i, main.cuda_stream)
+        ev1.record(main)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+    wall = t1 - t0
+    launch_s = ev0.elapsed_time(ev1) * 1e-3 / steps
+    achieved = alg / launch_s / 1e9
+    traffic = counter_traffic(kernel, w.name)
+    res = {
+        "workload": w.name,
+        "rows": w.rows,
+        "hidden": w.hidden,
+        "dtype": w.dtype,
+        "kernel": kernel,
+        "ms_per_step": wall / steps * 1e3,
+        "rows_per_s": w.rows * steps / wall,
+        "launch_us": launch_s * 1e6,
+        "algorithmic_bytes": alg,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "buffer_sets": n_sets,
+    }
+    del dev
+    torch.cuda.empty_cache()
+    log(f"{w.name}: {res['launch_us']:.2f} us/launch, {achieved:.0f} GB/s algorithmic "
+        f"({achieved / HBM_PEAK_GBS:.1%} of peak), {res['rows_per_s']:.3e} rows/s")
+    return res
+
+
+def time_copy(nbytes: int, steps: int, warmup: int):
+    import torch
+
+    from transformer_residual_add_amd import _lib as L
+
+    nbytes -= nbytes % 16
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    lib = L.load()
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        L.check(lib.skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_copy")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        L.check(lib.skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_copy")
+    ev1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst), "copy mismatch"
+    dt = ev0.elapsed_time(ev1) * 1e-3 / steps
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "launch_us": dt * 1e6, "gb_per_s": 2 * nbytes / dt / 1e9}
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle (as it stands) on this host's cores, on repeated full
+    batches of the workload until about ``seconds`` of wall time."""
+    from oracle import oracle as O
+    from transformer_residual_add_amd import workloads as W
+
+    threads = max(1, os.cpu_count() or 1)
+    inputs = W.make_inputs(w)
+    reps, rows = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"], w.eps,
+                          broadcast=w.broadcast, residual=w.residual, threads=threads)
+        reps += 1
+        rows += w.rows
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": rows / el,
+        "unit": "rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{reps} passes over the full {w.rows}x{w.hidden} {w.dtype} batch of {w.name} "
+                  f"({el:.1f} s, binary64 statistics, {threads} threads)",
+        "gb_per_s": w.algorithmic_bytes() * reps / el / 1e9,
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the operator has no multi-GPU path to time "
+              f"(rows shard across GPUs with no communication); got --gpus {args.gpus}", file=sys.stderr)
+        return 2
+    import torch
+
+    from transformer_residual_add_amd import _lib as L
+    from transformer_residual_add_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP GPU", file=sys.stderr)
+        return 1
+    L.load()
+    torch.cuda.set_device(0)
+
+    if args.copy_bytes:
+        print(json.dumps({"copy": time_copy(args.copy_bytes, args.steps, args.warmup)}), flush=True)
+        return 0
+
+    w = W.WORKLOADS[args.workload]
+    head = time_workload(w, args.steps, args.warmup, args.launch, args.variant)
+    sweep = []
+    if not args.no_sweep:
+        for name in SWEEP:
+            if name == w.name:
+                continue
+            big = W.WORKLOADS[name]
+            steps = max(5, min(args.steps, int(2.0 / max(big.algorithmic_bytes() / 5e12, 1e-9))))
+            sweep.append(time_workload(big, steps, min(args.warmup, 10), args.launch, args.variant))
+    base = None
+    if not args.no_cpu_baseline:
+        log(f"CPU baseline: oracle on {w.name} for ~{args.cpu_seconds:.0f}s")
+        base = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": head["rows_per_s"],
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(mu,sigma)/U(0.5,1.5) tensors of the workload's shape",
+        "config": {
+            "workload": w.name,
+            "rows": w.rows,
+            "hidden": w.hidden,
+            "shape": list(w.shape),
+            "skip_shape": list(w.skip_shape),
+            "bias": w.bias_dist is not None,
+            "beta": w.beta_dist is not None,
+            "residual_out": w.residual,
+            "eps": w.eps,
+            "kernel": head["kernel"],
+            "launch": args.launch,
+            "buffer_sets": head["buffer_sets"],
+            "launch_us": round(head["launch_us"], 3),
+            "gb_per_s": head["roofline"]["achieved"],
+        },
+        "roofline": head["roofline"],
+        "cpu_baseline": base,
+        "sweep": [
+            {k: r[k] for k in ("workload", "rows", "hidden", "dtype", "kernel", "rows_per_s", "launch_us",
+                               "roofline", "buffer_sets")}
+            for r in sweep
+        ],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,166 @@
+/*
+ * libskipln -- SkipLayerNormalization row kernels for AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * The operator (com.microsoft SkipLayerNormalization WebGPU manifest):
+ *   - `description`, `inputs[input]`: skip addition fused with a layer
+ *     normalization over the last (hidden) axis;
+ *   - `inputs[skip]`: skip has the input's shape, or for rank-3 input
+ *     (N, S, H) the shapes (1, S, H) and (S, H), broadcast over the batch;
+ *   - `inputs[bias]`: an optional length-H bias joins input + skip before the
+ *     normalization;
+ *   - `inputs[gamma]`, `inputs[beta]`: length-H scale (required) and shift
+ *     (optional, absent = 0);
+ *   - `outputs[output]`: normalized tensor, shape of input;
+ *     `outputs[input_skip_bias_sum]`: optional pre-normalization sum;
+ *   - `attributes.epsilon` / `attributeDescriptions.epsilon`: non-negative
+ *     epsilon added to the variance under the square root, carried as a
+ *     binary32 value by the manifest's `Params` structs;
+ *   - `typeConstraints.T`: every tensor is float32 or float16.
+ *
+ * For row r (0 <= r < rows) and column c (0 <= c < hidden), with j = r for an
+ * exact skip and j = r mod skip_rows for a broadcast skip:
+ *   s[r,c]    = fl32(fl32(input[r,c] + skip[j,c]) + bias[c])   (IEEE binary32)
+ *   residual  = s rounded once to T (round to nearest even)
+ *   mean      = sum_c s[r,c] / hidden
+ *   var       = sum_c (s[r,c] - mean)^2 / hidden               (population)
+ *   out[r,c]  = (s[r,c] - mean) / sqrt(var + eps) * gamma[c] + beta[c], to T
+ * Arithmetic is binary32 for both I/O types; float16 is converted exactly on
+ * load and rounded to nearest even on store.
+ *
+ * Memory and ownership (every entry point):
+ *   - Every tensor pointer is device memory owned by the caller; tensors are
+ *     dense and row-major: input/out/residual_out are rows x hidden, skip is
+ *     rows x hidden (exact) or skip_rows x hidden (broadcast), gamma/beta/bias
+ *     have hidden elements.  All tensors share one element type `dtype`.
+ *   - The library allocates nothing, frees nothing and never synchronizes:
+ *     work is enqueued on `stream` (NULL = the null stream) and the call
+ *     returns at once.  It keeps no mutable state besides a cache of device
+ *     attributes, and is safe to call from several host threads.
+ *   - Outputs may alias inputs only exactly: out or residual_out may equal
+ *     input, or skip when the skip is exact; every other overlap is an error.
+ *   - On an error nothing is enqueued (except SKIPLN_ERR_LAUNCH, which reports
+ *     a launch the runtime refused).
+ */
+#ifndef SKIPLN_H
+#define SKIPLN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP stream type (hipStream_t), declared without the HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t* skipln_stream_t;
+
+/* Element types (`typeConstraints.T`). */
+enum { SKIPLN_F32 = 0, SKIPLN_F16 = 1 };
+
+/* Skip forms (`inputs[skip]`): exact shape, or S rows broadcast over the
+ * batch, where row r of the input reads skip row r mod S. */
+enum { SKIPLN_SKIP_EXACT = 0, SKIPLN_SKIP_BROADCAST = 1 };
+
+/* Status codes. */
+enum {
+    SKIPLN_OK = 0,
+    SKIPLN_ERR_NULL = 1,        /* a required pointer is NULL while rows > 0 */
+    SKIPLN_ERR_SHAPE = 2,       /* rows < 0, hidden <= 0 or > 2^31-1, size
+                                   overflow, bad skip_rows for a broadcast */
+    SKIPLN_ERR_DTYPE = 3,       /* dtype is neither SKIPLN_F32 nor SKIPLN_F16 */
+    SKIPLN_ERR_MODE = 4,        /* unknown skip_mode */
+    SKIPLN_ERR_EPS = 5,         /* eps < 0 or NaN */
+    SKIPLN_ERR_ALIAS = 6,       /* outputs overlap inputs or each other */
+    SKIPLN_ERR_UNSUPPORTED = 7, /* a forced variant cannot run this shape */
+    SKIPLN_ERR_LAUNCH = 8,      /* the HIP runtime refused the launch */
+    SKIPLN_ERR_DEVICE = 9,      /* querying the current device failed */
+    SKIPLN_ERR_VARIANT = 10     /* unknown variant id */
+};
+
+/* Kernel families, for skipln_forward_variant / skipln_select. */
+enum {
+    SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
+    SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
+                                     alignment, three passes over the row */
+    SKIPLN_VARIANT_ROWTILE = 2,   /* row held in registers, 16-byte accesses:
+                                     needs hidden*sizeof(T) % 16 == 0, 16-byte
+                                     aligned pointers, hidden <= 4096*16/sizeof(T) */
+    SKIPLN_VARIANT_MULTIWAVE = 3, /* ROWTILE with at least two wavefronts per
+                                     row (exercises the cross-wave combine) */
+    SKIPLN_VARIANT_GEOMETRY = 64  /* + g: ROWTILE with row-tile geometry g,
+                                     0 <= g < skipln_rowtile_geometries(), for
+                                     tests and tuning */
+};
+
+/*
+ * Fused skip addition + layer normalization (SkipLayerNormalization manifest,
+ * `description`, `inputs`, `outputs`, `attributes.epsilon`).
+ *
+ * input         rows x hidden, T
+ * skip          rows x hidden (SKIPLN_SKIP_EXACT; skip_rows ignored) or
+ *               skip_rows x hidden (SKIPLN_SKIP_BROADCAST; rows must be a
+ *               multiple of skip_rows, the manifest's `Params.skipRows`)
+ * gamma         hidden, T, required
+ * beta, bias    hidden, T, or NULL (absent)
+ * out           rows x hidden, T
+ * residual_out  rows x hidden, T, or NULL (input_skip_bias_sum not written)
+ * rows          >= 0 (0 is a valid no-op); rank-3 (N, S, H) input is passed
+ *               as rows = N*S
+ * hidden        1 .. 2^31-1
+ * eps           >= 0
+ * dtype         SKIPLN_F32 or SKIPLN_F16
+ * Returns SKIPLN_OK or an error code above.
+ */
+int skipln_forward(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                   const void* gamma, const void* beta, const void* bias,
+                   void* out, void* residual_out, int64_t rows, int64_t hidden,
+                   float eps, int dtype, skipln_stream_t stream);
+
+/* skipln_forward with the kernel family forced (SKIPLN_VARIANT_*); the result
+ * is the same operator.  Returns SKIPLN_ERR_UNSUPPORTED when the family cannot
+ * run the shape or alignment. */
+int skipln_forward_variant(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                           const void* gamma, const void* beta, const void* bias,
+                           void* out, void* residual_out, int64_t rows, int64_t hidden,
+                           float eps, int dtype, int variant, skipln_stream_t stream);
+
+/* The argument checks of skipln_forward alone: host code only, no HIP call,
+ * no pointer is dereferenced. */
+int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                    const void* gamma, const void* beta, const void* bias,
+                    const void* out, const void* residual_out, int64_t rows, int64_t hidden,
+                    float eps, int dtype);
+
+/* Kernel that skipln_forward_variant would launch for this shape: returns a
+ * kernel id >= 0 (name via skipln_kernel_name) or a negative status code.
+ * `aligned16` says whether every tensor pointer is 16-byte aligned. */
+int skipln_select(int64_t hidden, int dtype, int aligned16, int variant);
+
+/* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte
+ * aligned, bytes % 16 == 0, no overlap), with the access pattern of the
+ * row-tile kernel (16-byte non-temporal loads and stores, persistent grid).
+ * It is the reference for the bandwidth one kernel can reach on the device
+ * and for calibrating hardware byte counters against a known byte count.
+ * Returns SKIPLN_OK, SKIPLN_ERR_NULL, SKIPLN_ERR_SHAPE (bytes < 0 or not a
+ * multiple of 16, misaligned pointers), SKIPLN_ERR_ALIAS or SKIPLN_ERR_LAUNCH. */
+int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t stream);
+
+/* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
+int skipln_rowtile_geometries(void);
+
+/* Stable name of a kernel id ("generic_f32", "rowtile_f16_g256_c4", ...);
+ * "unknown" for an invalid id. */
+const char* skipln_kernel_name(int kernel_id);
+
+/* Static description of a status code. */
+const char* skipln_status_string(int status);
+
+/* ABI version of this header: 1. */
+int skipln_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKIPLN_H */

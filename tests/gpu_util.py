@@ -1,0 +1,133 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, run the HIP path
+through the C ABI, compare with the oracle.
+
+Tolerances: the normalized output is compared with the oracle's unrounded
+binary64 value, |out - y| <= atol + rtol * |y| with (1e-5, 1e-5) for float32
+and (2e-3, 2e-3) for float16; the residual (input_skip_bias_sum) must match
+bit for bit.
+"""
+from __future__ import annotations
+
+import sys
+from typing import Optional
+
+import numpy as np
+
+import transformer_residual_add_amd as T
+from transformer_residual_add_amd import _lib as L
+from oracle import oracle as O
+
+TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 2e-3)}
+TORCH_DT = None
+
+
+def torch_dtype(dt: str):
+    import torch
+
+    return {"f32": torch.float32, "f16": torch.float16}[dt]
+
+
+def note(msg: str) -> None:
+    """Name the case on stdout before a GPU step (flushed)."""
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DeviceCase:
+    """Device copies of one workload's inputs and its output buffers.
+
+    ``offset_elems`` shifts every tensor by that many elements inside a
+    larger allocation (misaligned pointers)."""
+
+    def __init__(self, w, inputs, residual: bool, offset_elems: int = 0, device: str = "cuda"):
+        import torch
+
+        self.w = w
+        self.inputs = inputs
+        dt = torch_dtype(w.dtype)
+        self._keep = []
+
+        def up(a: Optional[np.ndarray]):
+            if a is None:
+                return None
+            t = torch.from_numpy(np.ascontiguousarray(a).reshape(-1))
+            if offset_elems:
+                buf = torch.empty(t.numel() + offset_elems, dtype=dt, device=device)
+                buf[offset_elems:].copy_(t.to(device))
+                self._keep.append(buf)
+                return buf[offset_elems:]
+            return t.to(device)
+
+        def empty(n):
+            buf = torch.full((n + offset_elems,), float("nan"), dtype=dt, device=device)
+            self._keep.append(buf)
+            return buf[offset_elems:]
+
+        n = w.rows * w.hidden
+        self.x = up(inputs["input"])
+        self.skip = up(inputs["skip"])
+        self.gamma = up(inputs["gamma"])
+        self.beta = up(inputs["beta"])
+        self.bias = up(inputs["bias"])
+        self.out = empty(n)
+        self.res = empty(n) if residual else None
+
+    def run(self, variant: int = L.VARIANT_AUTO, stream: int = 0, out=None, res="default"):
+        w = self.w
+        p = lambda t: None if t is None else t.data_ptr()
+        o = self.out if out is None else out
+        r = self.res if res == "default" else res
+        T.forward_raw(p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
+                      w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
+                      w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
+                      stream, variant)
+
+    def host(self, t):
+        import torch
+
+        torch.cuda.synchronize()
+        return t.cpu().numpy().reshape(self.w.rows, self.w.hidden)
+
+
+def oracle_rows(w, inputs, row_offset: int = 0, threads: int = 8):
+    return O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"],
+                             w.eps, broadcast=w.broadcast, row_offset=row_offset, residual=True, threads=threads)
+
+
+def assert_out_close(got: np.ndarray, want: np.ndarray, dt: str, what: str = "out"):
+    atol, rtol = TOL[dt]
+    g = got.astype(np.float64)
+    nan_w = np.isnan(want)
+    assert np.array_equal(np.isnan(g), nan_w), f"{what}: NaN pattern differs ({int(np.isnan(g).sum())} vs " \
+                                               f"{int(nan_w.sum())})"
+    err = np.abs(g[~nan_w] - want[~nan_w])
+    lim = atol + rtol * np.abs(want[~nan_w])
+    bad = err > lim
+    if bad.any():
+        i = int(np.argmax(err - lim))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements outside {atol}+{rtol}|y|; "
+                             f"worst err {err[i]:.3e} at y={want[~nan_w][i]:.6g}")
+
+
+def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str = "residual"):
+    gb = np.ascontiguousarray(got).view(np.uint16 if got.dtype == np.float16 else np.uint32)
+    wb = np.ascontiguousarray(want).view(np.uint16 if want.dtype == np.float16 else np.uint32)
+    if not np.array_equal(gb, wb):
+        diff = gb != wb
+        idx = np.argwhere(diff)[0]
+        raise AssertionError(f"{what}: {int(diff.sum())} elements differ bitwise; first at {tuple(idx)}: "
+                             f"{got[tuple(idx)]!r} vs {want[tuple(idx)]!r}")
+
+
+def check_case(w, variant: int = L.VARIANT_AUTO, offset_elems: int = 0, inputs=None):
+    """Run one workload through the C ABI and compare all rows with the oracle."""
+    from transformer_residual_add_amd import workloads as W
+
+    inputs = W.make_inputs(w) if inputs is None else inputs
+    dc = DeviceCase(w, inputs, residual=w.residual, offset_elems=offset_elems)
+    dc.run(variant)
+    ref = oracle_rows(w, inputs)
+    assert_out_close(dc.host(dc.out), ref["y"], w.dtype)
+    if w.residual:
+        assert_bits_equal(dc.host(dc.res), ref["residual"])
+    return dc, ref

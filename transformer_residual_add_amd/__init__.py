@@ -1,0 +1,107 @@
+"""MI355X-native SkipLayerNormalization (com.microsoft contrib operator).
+
+``skip_layer_norm`` computes, row by row over the hidden axis,
+``s = input + skip (+ bias)`` and ``(s - mean) / sqrt(var + epsilon) * gamma
+(+ beta)``, optionally returning ``s`` as ``input_skip_bias_sum``
+(com.microsoft SkipLayerNormalization WebGPU manifest: `description`,
+`inputs`, `outputs`, `attributes.epsilon`).  The computation runs in the HIP
+kernels of ``libskipln.so``; PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import SkiplnError  # noqa: F401
+
+# The manifest's default epsilon: 1e-12 rounded to binary32
+# (SkipLayerNormalization manifest, `attributes.epsilon`).
+DEFAULT_EPSILON = 9.999999960041972e-13
+
+__all__ = ["skip_layer_norm", "forward_raw", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
+
+
+def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: int,
+                beta_ptr: Optional[int], bias_ptr: Optional[int], out_ptr: int, residual_ptr: Optional[int],
+                rows: int, hidden: int, eps: float, dtype: int, stream: int = 0,
+                variant: int = _lib.VARIANT_AUTO) -> None:
+    """``skipln_forward_variant`` on raw device pointers; raises SkiplnError."""
+    st = _lib.load().skipln_forward_variant(
+        input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr, beta_ptr or None, bias_ptr or None, out_ptr,
+        residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
+    _lib.check(st, "skipln_forward")
+
+
+def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO) -> str:
+    """Name of the kernel a call with this hidden size would launch."""
+    kid = _lib.load().skipln_select(hidden, dtype, 1 if aligned16 else 0, variant)
+    if kid < 0:
+        raise SkiplnError(-kid, "skipln_select")
+    return _lib.kernel_name(kid)
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return _lib.F32
+    if t.dtype == torch.float16:
+        return _lib.F16
+    raise TypeError(f"SkipLayerNormalization supports float32 and float16, got {t.dtype}")
+
+
+def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = DEFAULT_EPSILON, *,
+                    return_residual: bool = False, out=None, residual_out=None, stream=None,
+                    variant: int = _lib.VARIANT_AUTO):
+    """SkipLayerNormalization on CUDA (HIP) tensors.
+
+    input: (N, S, H) or (rows, H).  skip: the input's shape, or for rank-3
+    input (1, S, H) or (S, H), broadcast over the batch.  gamma (H), optional
+    beta (H) and bias (H).  All tensors contiguous, of one dtype (float32 or
+    float16), on one device.  Returns ``out``, or ``(out, residual)`` with
+    ``return_residual=True`` (the input_skip_bias_sum output).
+    """
+    import torch
+
+    tensors = [t for t in (input, skip, gamma, beta, bias, out, residual_out) if t is not None]
+    code = _dtype_code(input)
+    for t in tensors:
+        if t.dtype != input.dtype:
+            raise TypeError("all tensors must share one dtype")
+        if t.device != input.device or t.device.type != "cuda":
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if input.dim() not in (2, 3):
+        raise ValueError("input must have rank 2 or 3")
+    h = input.shape[-1]
+    rows = input.numel() // h if h else 0
+    if tuple(skip.shape) == tuple(input.shape):
+        mode, skip_rows = _lib.SKIP_EXACT, 0
+    elif input.dim() == 3 and tuple(skip.shape) in ((1,) + tuple(input.shape[1:]), tuple(input.shape[1:])):
+        mode, skip_rows = _lib.SKIP_BROADCAST, input.shape[1]
+    else:
+        raise ValueError(f"skip shape {tuple(skip.shape)} does not fit input {tuple(input.shape)}")
+    for name, t in (("gamma", gamma), ("beta", beta), ("bias", bias)):
+        if t is not None and tuple(t.shape) != (h,):
+            raise ValueError(f"{name} must have shape ({h},)")
+    if out is None:
+        out = torch.empty_like(input)
+    elif out.shape != input.shape:
+        raise ValueError("out must have the input's shape")
+    if return_residual and residual_out is None:
+        residual_out = torch.empty_like(input)
+    if residual_out is not None and residual_out.shape != input.shape:
+        raise ValueError("residual_out must have the input's shape")
+    if stream is None:
+        stream = torch.cuda.current_stream(input.device)
+    s = stream if isinstance(stream, int) else stream.cuda_stream
+    with torch.cuda.device(input.device):
+        forward_raw(input.data_ptr(), skip.data_ptr(), mode, skip_rows, gamma.data_ptr(),
+                    beta.data_ptr() if beta is not None else None,
+                    bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                    residual_out.data_ptr() if residual_out is not None else None,
+                    rows, h, float(epsilon), code, s, variant)
+    if return_residual:
+        return out, residual_out
+    return out

@@ -1,0 +1,57 @@
+"""Build libskipln.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Usage: ``python -m transformer_residual_add_amd.build`` (always recompiles).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libskipln.so")
+SOURCES = [os.path.join(CSRC, "skipln_kernels.hip"), os.path.join(CSRC, "skipln_api.cpp")]
+ARCH = "gfx950"
+
+FLAGS = [
+    "-O3",
+    "-std=c++17",
+    f"--offload-arch={ARCH}",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # No packed fp32 instructions anywhere in device code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build libskipln")
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc()] + FLAGS + SOURCES + ["-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
+    if verbose:
+        noise = "packed-fp32-ops"  # the host pass does not know this feature
+        for line in (res.stdout + res.stderr).splitlines():
+            if noise not in line:
+                print(line)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

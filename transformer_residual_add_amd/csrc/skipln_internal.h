@@ -1,0 +1,44 @@
+// Internal interface between the C-ABI layer (skipln_api.cpp) and the HIP
+// kernels (skipln_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace skipln {
+
+// Arguments of one SkipLayerNormalization launch, already validated.
+struct Args {
+    const void* input;
+    const void* skip;
+    const void* gamma;
+    const void* beta;  // nullptr: no shift
+    const void* bias;  // nullptr: no bias
+    void* out;
+    void* residual;    // nullptr: residual not written
+    int64_t rows;
+    int64_t skip_rows; // 0: exact skip; > 0: row r reads skip row r % skip_rows
+    int32_t hidden;
+    float eps;
+};
+
+// Kernel ids: dtype * kIdsPerType + index, index 0 = generic, 1.. = row tiles.
+constexpr int kIdsPerType = 32;
+constexpr int kGenericIndex = 0;
+constexpr int kRowtileFirst = 1;
+
+// Number of row-tile geometries and the one chosen for `hidden` (elements),
+// or -1 when none holds the row.  multiwave_only: only geometries whose row
+// group spans two or more wavefronts.
+int rowtile_count();
+int rowtile_pick(int64_t hidden, int dtype, bool multiwave_only);
+// Whether geometry g holds a row of `hidden` elements (16-byte chunks).
+bool rowtile_holds(int geometry, int64_t hidden, int dtype);
+const char* kernel_name(int kernel_id);
+
+// Enqueue one kernel; return 0 or a hipError_t value.
+hipError_t launch_generic(const Args& a, int dtype, hipStream_t stream);
+hipError_t launch_rowtile(const Args& a, int dtype, int geometry, hipStream_t stream);
+hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
+
+}  // namespace skipln

@@ -1,0 +1,626 @@
+// SkipLayerNormalization row kernels for gfx950 (CDNA4, wave64).
+//
+// Operator: com.microsoft SkipLayerNormalization WebGPU manifest --
+// `description` (skip addition fused with a layer normalization over the
+// hidden axis), `inputs[skip]` (exact, or broadcast over the batch with
+// numel(skip)/H rows, the `Params.skipRows` of the broadcast binding set),
+// `inputs[bias]` (joins input + skip before the normalization),
+// `inputs[gamma]` / `inputs[beta]`, `outputs[input_skip_bias_sum]`,
+// `attributes.epsilon`.  Statistics are the population mean and variance of
+// the binary32 sum; all arithmetic is binary32, float16 only at load/store.
+//
+// The work is bound by HBM bandwidth (about 1 flop per byte moved), so the
+// kernels are organised around moving each byte once:
+//   * rowtile_kernel: a group of G lanes owns one row at a time and keeps the
+//     whole row in VGPRs between the statistics and the normalization, so x
+//     and skip are read from HBM exactly once.  Every access is a 16-byte
+//     vector load/store (4 fp32 or 8 fp16), coalesced across the group.  G is
+//     16/32 (several rows per wavefront, small H), 64 (one wavefront per row)
+//     or 128..1024 (several wavefronts per row, partial statistics combined
+//     through LDS with one barrier per row).  The grid is persistent: each
+//     block walks row tiles with a stride of gridDim.x, loads gamma/beta/bias
+//     into registers once, and issues the loads of its next tile before it
+//     reduces and stores the current one, keeping HBM requests in flight
+//     across the reduction.  Streaming tensors use non-temporal accesses so
+//     they do not displace the broadcast skip and the parameters in L2.
+//   * generic_kernel: any H and any alignment, one 256-lane block per row,
+//     three passes over the row (sum, squared deviations, output).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstdio>
+#include <utility>
+
+#include "skipln_internal.h"
+
+namespace skipln {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------
+// Element types: a 16-byte chunk holds kPerChunk elements.
+// ------------------------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static constexpr int kPerChunk = 4;
+    __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
+        f[0] = __builtin_bit_cast(float, r.x);
+        f[1] = __builtin_bit_cast(float, r.y);
+        f[2] = __builtin_bit_cast(float, r.z);
+        f[3] = __builtin_bit_cast(float, r.w);
+    }
+    __device__ __forceinline__ static u32x4 narrow(const float* f) {
+        u32x4 r;
+        r.x = __builtin_bit_cast(unsigned, f[0]);
+        r.y = __builtin_bit_cast(unsigned, f[1]);
+        r.z = __builtin_bit_cast(unsigned, f[2]);
+        r.w = __builtin_bit_cast(unsigned, f[3]);
+        return r;
+    }
+    __device__ __forceinline__ static float load1(const void* p, int64_t i) {
+        return static_cast<const float*>(p)[i];
+    }
+    __device__ __forceinline__ static void store1(void* p, int64_t i, float v) {
+        static_cast<float*>(p)[i] = v;
+    }
+};
+
+template <>
+struct Elem<_Float16> {
+    static constexpr int kPerChunk = 8;
+    __device__ __forceinline__ static float lo(unsigned w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xFFFFu)));
+    }
+    __device__ __forceinline__ static float hi(unsigned w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
+    }
+    // Round to nearest even (the default rounding mode of the conversion).
+    __device__ __forceinline__ static unsigned pack(float a, float b) {
+        unsigned short ha = __builtin_bit_cast(unsigned short, static_cast<_Float16>(a));
+        unsigned short hb = __builtin_bit_cast(unsigned short, static_cast<_Float16>(b));
+        return static_cast<unsigned>(ha) | (static_cast<unsigned>(hb) << 16);
+    }
+    __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
+        f[0] = lo(r.x); f[1] = hi(r.x);
+        f[2] = lo(r.y); f[3] = hi(r.y);
+        f[4] = lo(r.z); f[5] = hi(r.z);
+        f[6] = lo(r.w); f[7] = hi(r.w);
+    }
+    __device__ __forceinline__ static u32x4 narrow(const float* f) {
+        u32x4 r;
+        r.x = pack(f[0], f[1]);
+        r.y = pack(f[2], f[3]);
+        r.z = pack(f[4], f[5]);
+        r.w = pack(f[6], f[7]);
+        return r;
+    }
+    __device__ __forceinline__ static float load1(const void* p, int64_t i) {
+        return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+    }
+    __device__ __forceinline__ static void store1(void* p, int64_t i, float v) {
+        static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+    }
+};
+
+// ------------------------------------------------------------------------
+// Cross-lane sums with DPP (data-parallel primitives: a VALU operand read
+// from another lane of the same row of 16 lanes, no LDS traffic).
+// ------------------------------------------------------------------------
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, RowMask, 0xF, false));
+}
+
+constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+// Sum over aligned groups of 16 lanes; every lane of a group gets the same
+// bits (each step adds a commutative pair).
+__device__ __forceinline__ float sum16(float v) {
+    v += dpp<kQuadSwap1>(v);
+    v += dpp<kQuadSwap2>(v);
+    v += dpp<kRowHalfMirror>(v);  // lane i <-> 7-i within 8: other quad
+    v += dpp<kRowMirror>(v);      // lane i <-> 15-i within 16: other half
+    return v;
+}
+
+// Sum over the whole wavefront, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = sum16(v);
+    v += dpp<kRowBcast15, 0xA>(v);  // rows 1, 3 += rows 0, 2
+    v += dpp<kRowBcast31, 0xC>(v);  // rows 2, 3 += rows 0+1
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over an aligned group of G lanes (G = 16, 32 or 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 16 || G == 32 || G == 64, "group of 16, 32 or 64 lanes");
+    if constexpr (G == 64) {
+        return wave_sum(v);
+    } else {
+        v = sum16(v);
+        if constexpr (G == 32) {
+            // lane ^ 16 within each half-wave (swizzle bit mode: and 0x1F, xor 0x10)
+            v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+        }
+        return v;
+    }
+}
+
+// ------------------------------------------------------------------------
+// Row-tile kernel.
+// ------------------------------------------------------------------------
+// Thread t of a row group owns chunks k*G + t (k < CH) of the row; a chunk
+// past the row end (ragged hidden size) is skipped.  Number of elements of
+// wavefront w of the group, for the cross-wave combine.
+template <int G, int CH, int V>
+__device__ __forceinline__ float wave_elems(int hv, int w) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        int left = hv - (k * G + 64 * w);
+        n += left <= 0 ? 0 : (left >= 64 ? 64 : left);
+    }
+    return static_cast<float>(n * V);
+}
+
+template <typename T, int G, int CH, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
+    using E = Elem<T>;
+    constexpr int V = E::kPerChunk;
+    constexpr int RPB = BLOCK / G;                  // rows per block per tile
+    constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
+    static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
+    __shared__ float2 partial[2][RPB][WPR];
+
+    const int tid = threadIdx.x;
+    // Row of the tile handled by this group; wave-uniform when G >= 64, and
+    // said so, so that row addresses live in scalar registers.
+    const int slot = G >= 64 ? __builtin_amdgcn_readfirstlane(tid / G) : tid / G;
+    const int lt = tid - slot * G; // lane within the group
+    const int hv = a.hidden / V;   // chunks per row
+    const float h = static_cast<float>(a.hidden);
+
+    const u32x4* __restrict__ X = static_cast<const u32x4*>(a.input);
+    const u32x4* __restrict__ S = static_cast<const u32x4*>(a.skip);
+    u32x4* __restrict__ R = static_cast<u32x4*>(a.residual);
+    u32x4* __restrict__ O = static_cast<u32x4*>(a.out);
+    const bool has_bias = a.bias != nullptr;
+    const bool has_beta = a.beta != nullptr;
+    const bool bcast = a.skip_rows > 0;
+
+    bool ok[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) ok[k] = k * G + lt < hv;
+
+    // Parameters: loaded once per block, kept in registers (raw T bits).
+    u32x4 gam[CH], bet[CH], bia[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int c = k * G + lt;
+        gam[k] = u32x4{0, 0, 0, 0};
+        bet[k] = u32x4{0, 0, 0, 0};
+        bia[k] = u32x4{0, 0, 0, 0};
+        if (ok[k]) {
+            gam[k] = static_cast<const u32x4*>(a.gamma)[c];
+            if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
+            if (has_bias) bia[k] = static_cast<const u32x4*>(a.bias)[c];
+        }
+    }
+
+    float nw[WPR];
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
+    const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
+
+    const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
+    const int64_t stride = gridDim.x;
+
+    u32x4 xr[CH], sr[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        xr[k] = u32x4{0, 0, 0, 0};
+        sr[k] = u32x4{0, 0, 0, 0};
+    }
+    auto issue_loads = [&](int64_t tile) {
+        const int64_t row = tile * RPB + slot;
+        if (row < a.rows) {
+            const int64_t srow = bcast ? row % a.skip_rows : row;
+            const u32x4* xp = X + row * hv + lt;
+            const u32x4* sp = S + srow * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+                    xr[k] = __builtin_nontemporal_load(xp + k * G);
+                    // The broadcast skip is re-read by every batch: keep it cached.
+                    sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
+                }
+            }
+        }
+    };
+
+    int64_t tile = blockIdx.x;
+    if (tile < n_tiles) issue_loads(tile);
+    int parity = 0;
+
+    for (; tile < n_tiles; tile += stride) {
+        const int64_t row = tile * RPB + slot;
+        const bool live = row < a.rows;
+        if constexpr (V == 8) {
+            // Keep gamma/beta/bias packed (2 fp16 per VGPR): without this the
+            // compiler hoists their widening out of the loop and triples
+            // their register footprint, which costs occupancy.
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                asm volatile("" : "+v"(gam[k]), "+v"(bet[k]), "+v"(bia[k]));
+            }
+        }
+
+        // s = (x + skip) + bias in binary32, and this lane's partial sum.
+        float s[CH][V];
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            float xf[V], sf[V], bf[V];
+            E::widen(xr[k], xf);
+            E::widen(sr[k], sf);
+            E::widen(bia[k], bf);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float v = xf[e] + sf[e];
+                if (has_bias) v = v + bf[e];
+                s[k][e] = v;
+            }
+            if (ok[k]) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) part += s[k][e];
+            }
+        }
+
+        // Registers of x/skip are free again: start the next tile's loads.
+        if (tile + stride < n_tiles) issue_loads(tile + stride);
+
+        if (R != nullptr && live) {
+            u32x4* rp = R + row * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), rp + k * G);
+        }
+
+        float mean, var;
+        if constexpr (WPR == 1) {
+            mean = group_sum<G>(part) / h;
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = s[k][e] - mean;
+                        q += d * d;
+                    }
+                }
+            }
+            var = group_sum<G>(q) / h;
+        } else {
+            // Per-wavefront count, sum and squared deviations from the
+            // wavefront mean, merged across wavefronts (Chan et al.'s
+            // pairwise update: M2 = sum_w M2_w + n_w (mean_w - mean)^2).
+            const float wsum = wave_sum(part);
+            const float wmean = own_n > 0.0f ? wsum / own_n : 0.0f;
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = s[k][e] - wmean;
+                        q += d * d;
+                    }
+                }
+            }
+            const float wm2 = wave_sum(q);
+            if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float2(wsum, wm2);
+            __syncthreads();
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
+            mean = tot / h;
+            float m2 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                if (nw[w] > 0.0f) {
+                    const float2 p = partial[parity][slot][w];
+                    const float dm = p.x / nw[w] - mean;
+                    m2 += p.y + nw[w] * dm * dm;
+                }
+            }
+            var = m2 / h;
+            parity ^= 1;
+        }
+        const float rstd = rsqrtf(var + a.eps);
+
+        if (live) {
+            u32x4* op = O + row * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+                    float gf[V], bf[V], y[V];
+                    E::widen(gam[k], gf);
+                    E::widen(bet[k], bf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - mean) * rstd * gf[e] + bf[e];
+                    __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Generic kernel: any hidden size and alignment.
+// ------------------------------------------------------------------------
+constexpr int kGenericBlock = 256;
+
+template <typename T>
+__global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
+    using E = Elem<T>;
+    constexpr int W = kGenericBlock / 64;
+    __shared__ float red[2][W];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int64_t H = a.hidden;
+    const float h = static_cast<float>(a.hidden);
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t srow = a.skip_rows > 0 ? row % a.skip_rows : row;
+        const int64_t xo = row * H, so = srow * H;
+        // The same binary32 operations in every pass, hence the same bits.
+        auto sum_at = [&](int64_t c) {
+            float v = E::load1(a.input, xo + c) + E::load1(a.skip, so + c);
+            if (a.bias != nullptr) v = v + E::load1(a.bias, c);
+            return v;
+        };
+
+        float part = 0.0f;
+        for (int64_t c = tid; c < H; c += kGenericBlock) part += sum_at(c);
+        float ws = wave_sum(part);
+        if ((tid & 63) == 0) red[0][wave] = ws;
+        __syncthreads();
+        float tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += red[0][w];
+        const float mean = tot / h;
+
+        float q = 0.0f;
+        for (int64_t c = tid; c < H; c += kGenericBlock) {
+            const float d = sum_at(c) - mean;
+            q += d * d;
+        }
+        ws = wave_sum(q);
+        if ((tid & 63) == 0) red[1][wave] = ws;
+        __syncthreads();
+        tot = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) tot += red[1][w];
+        const float rstd = rsqrtf(tot / h + a.eps);
+
+        // Each element is read and then written by the same lane, so exact
+        // aliasing of an output with input or skip is safe.
+        for (int64_t c = tid; c < H; c += kGenericBlock) {
+            const float v = sum_at(c);
+            if (a.residual != nullptr) E::store1(a.residual, xo + c, v);
+            const float g = E::load1(a.gamma, c);
+            const float b = a.beta != nullptr ? E::load1(a.beta, c) : 0.0f;
+            E::store1(a.out, xo + c, (v - mean) * rstd * g + b);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Streaming copy (bandwidth reference): 16-byte chunks, persistent grid.
+// ------------------------------------------------------------------------
+constexpr int kCopyBlock = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ void __launch_bounds__(kCopyBlock) copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                          int64_t chunks) {
+    const int64_t step = static_cast<int64_t>(gridDim.x) * kCopyBlock;
+    int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyBlock + threadIdx.x;
+    for (; i + (kCopyUnroll - 1) * step < chunks; i += kCopyUnroll * step) {
+        u32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * step);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * step);
+    }
+    for (; i < chunks; i += step) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+// ------------------------------------------------------------------------
+// Host side: geometry table, occupancy-sized persistent grids.
+// ------------------------------------------------------------------------
+struct Geom {
+    int g, ch, block;
+};
+
+// Auto order (increasing capacity G*CH chunks) first, then geometries only
+// reachable through the multi-wavefront variant.
+constexpr Geom kGeoms[] = {
+    {16, 1, 256},  {32, 1, 256},  {64, 1, 256},   {64, 2, 256},   {64, 3, 256},
+    {64, 4, 256},  {128, 4, 256}, {256, 3, 256},  {256, 4, 256},  {512, 3, 512},
+    {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
+};
+constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
+constexpr int kNumAutoGeoms = 13;
+
+hipError_t cu_count(int* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::atomic<int> cache[64];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
+}
+
+template <typename K>
+hipError_t launch_persistent(K kernel, int block, int64_t work_items, const Args& a, hipStream_t st,
+                             int* occupancy_cache) {
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    int occ = __atomic_load_n(occupancy_cache, __ATOMIC_RELAXED);
+    if (occ <= 0) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+        __atomic_store_n(occupancy_cache, occ, __ATOMIC_RELAXED);
+    }
+    int64_t blocks = static_cast<int64_t>(cus) * occ;
+    if (work_items < blocks) blocks = work_items;
+    if (blocks < 1) blocks = 1;
+    Args arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
+                           dim3(block), params, 0, st);
+}
+
+template <typename T, int I>
+hipError_t launch_geom(const Args& a, hipStream_t st) {
+    constexpr Geom g = kGeoms[I];
+    static int occ = 0;
+    const int64_t rpb = g.block / g.g;
+    return launch_persistent(rowtile_kernel<T, g.g, g.ch, g.block>, g.block, (a.rows + rpb - 1) / rpb, a, st,
+                             &occ);
+}
+
+template <typename T, int... I>
+hipError_t launch_geom_dispatch(int idx, const Args& a, hipStream_t st, std::integer_sequence<int, I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((idx == I ? (r = launch_geom<T, I>(a, st), 0) : 0), ...);
+    return r;
+}
+
+template <typename T>
+hipError_t launch_generic_t(const Args& a, hipStream_t st) {
+    static int occ = 0;
+    return launch_persistent(generic_kernel<T>, kGenericBlock, a.rows, a, st, &occ);
+}
+
+// Names: "generic_<t>" and "rowtile_<t>_g<G>_c<CH>".
+char g_names[2][kIdsPerType][32];
+std::atomic<int> g_names_ready{0};
+
+void build_names() {
+    const char* tn[2] = {"f32", "f16"};
+    for (int t = 0; t < 2; ++t) {
+        for (int i = 0; i < kIdsPerType; ++i) {
+            char* dst = g_names[t][i];
+            if (i == kGenericIndex)
+                snprintf(dst, 32, "generic_%s", tn[t]);
+            else if (i - kRowtileFirst < kNumGeoms)
+                snprintf(dst, 32, "rowtile_%s_g%d_c%d", tn[t], kGeoms[i - kRowtileFirst].g,
+                         kGeoms[i - kRowtileFirst].ch);
+            else
+                snprintf(dst, 32, "unknown");
+        }
+    }
+}
+
+}  // namespace
+
+int rowtile_count() { return kNumGeoms; }
+
+int rowtile_pick(int64_t hidden, int dtype, bool multiwave_only) {
+    const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
+    if (hidden <= 0 || hidden % v != 0) return -1;
+    const int64_t hv = hidden / v;
+    int best = -1;
+    for (int i = 0; i < kNumGeoms; ++i) {
+        if (multiwave_only ? kGeoms[i].g < 128 : i >= kNumAutoGeoms) continue;
+        const int64_t cap = static_cast<int64_t>(kGeoms[i].g) * kGeoms[i].ch;
+        if (cap < hv) continue;
+        if (best < 0 || cap < static_cast<int64_t>(kGeoms[best].g) * kGeoms[best].ch) best = i;
+    }
+    return best;
+}
+
+bool rowtile_holds(int geometry, int64_t hidden, int dtype) {
+    const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
+    if (geometry < 0 || geometry >= kNumGeoms || hidden <= 0 || hidden % v != 0) return false;
+    return hidden / v <= static_cast<int64_t>(kGeoms[geometry].g) * kGeoms[geometry].ch;
+}
+
+const char* kernel_name(int kernel_id) {
+    static std::atomic<int> once{0};
+    if (g_names_ready.load(std::memory_order_acquire) == 0) {
+        int expected = 0;
+        if (once.compare_exchange_strong(expected, 1)) {
+            build_names();
+            g_names_ready.store(1, std::memory_order_release);
+        }
+        while (g_names_ready.load(std::memory_order_acquire) == 0) {
+        }
+    }
+    if (kernel_id < 0 || kernel_id >= 2 * kIdsPerType) return "unknown";
+    return g_names[kernel_id / kIdsPerType][kernel_id % kIdsPerType];
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t st) {
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    static int occ = 0;
+    int o = __atomic_load_n(&occ, __ATOMIC_RELAXED);
+    if (o <= 0) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, copy_kernel, kCopyBlock, 0);
+        if (e != hipSuccess) return e;
+        if (o < 1) o = 1;
+        __atomic_store_n(&occ, o, __ATOMIC_RELAXED);
+    }
+    int64_t blocks = static_cast<int64_t>(cus) * o;
+    const int64_t need = (chunks + kCopyBlock - 1) / kCopyBlock;
+    if (need < blocks) blocks = need;
+    if (blocks < 1) blocks = 1;
+    u32x4* d = static_cast<u32x4*>(dst);
+    const u32x4* s = static_cast<const u32x4*>(src);
+    void* params[] = {&d, &s, &chunks};
+    return hipLaunchKernel(reinterpret_cast<const void*>(copy_kernel), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kCopyBlock), params, 0, st);
+}
+
+hipError_t launch_generic(const Args& a, int dtype, hipStream_t st) {
+    return dtype == 0 ? launch_generic_t<float>(a, st) : launch_generic_t<_Float16>(a, st);
+}
+
+hipError_t launch_rowtile(const Args& a, int dtype, int geometry, hipStream_t st) {
+    if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
+    auto seq = std::make_integer_sequence<int, kNumGeoms>{};
+    return dtype == 0 ? launch_geom_dispatch<float>(geometry, a, st, seq)
+                      : launch_geom_dispatch<_Float16>(geometry, a, st, seq);
+}
+
+}  // namespace skipln
