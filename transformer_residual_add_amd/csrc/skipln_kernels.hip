@@ -48,18 +48,20 @@ struct Elem;
 template <>
 struct Elem<float> {
     static constexpr int kPerChunk = 4;
+    // Components are passed by value: __builtin_bit_cast applied directly to
+    // a vector component (r.y) reads component 0 with this compiler.
     __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
-        f[0] = __builtin_bit_cast(float, r.x);
-        f[1] = __builtin_bit_cast(float, r.y);
-        f[2] = __builtin_bit_cast(float, r.z);
-        f[3] = __builtin_bit_cast(float, r.w);
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
     }
     __device__ __forceinline__ static u32x4 narrow(const float* f) {
         u32x4 r;
-        r.x = __builtin_bit_cast(unsigned, f[0]);
-        r.y = __builtin_bit_cast(unsigned, f[1]);
-        r.z = __builtin_bit_cast(unsigned, f[2]);
-        r.w = __builtin_bit_cast(unsigned, f[3]);
+        r.x = __float_as_uint(f[0]);
+        r.y = __float_as_uint(f[1]);
+        r.z = __float_as_uint(f[2]);
+        r.w = __float_as_uint(f[3]);
         return r;
     }
     __device__ __forceinline__ static float load1(const void* p, int64_t i) {
