@@ -100,7 +100,7 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     from transformer_residual_add_amd import workloads as W
 
     code = L.F32 if w.dtype == "f32" else L.F16
-    kernel = T.select_kernel(w.hidden, code, True, variant)
+    kernel = T.select_kernel(w.hidden, code, True, variant, L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.

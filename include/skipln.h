@@ -125,6 +125,21 @@ int skipln_forward_variant(const void* input, const void* skip, int skip_mode, i
                            void* out, void* residual_out, int64_t rows, int64_t hidden,
                            float eps, int dtype, int variant, skipln_stream_t stream);
 
+/* skipln_forward with an explicit launch configuration, for tuning; the
+ * result is the same operator.  geometry: row-tile geometry
+ * (0 <= geometry < skipln_rowtile_geometries()), or -1 for the automatic
+ * choice.  tiles_per_block > 0: each block takes that many row tiles,
+ * contiguous (strided = 0) or strided by the grid size (strided = 1);
+ * tiles_per_block = 0: a persistent grid of as many blocks as the device
+ * holds at once.  Returns SKIPLN_ERR_UNSUPPORTED when the geometry cannot
+ * hold the row or the tensors are not 16-byte aligned, SKIPLN_ERR_SHAPE for
+ * tiles_per_block < 0. */
+int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                          const void* gamma, const void* beta, const void* bias,
+                          void* out, void* residual_out, int64_t rows, int64_t hidden,
+                          float eps, int dtype, int geometry, int64_t tiles_per_block, int strided,
+                          skipln_stream_t stream);
+
 /* The argument checks of skipln_forward alone: host code only, no HIP call,
  * no pointer is dereferenced. */
 int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
@@ -132,10 +147,11 @@ int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t 
                     const void* out, const void* residual_out, int64_t rows, int64_t hidden,
                     float eps, int dtype);
 
-/* Kernel that skipln_forward_variant would launch for this shape: returns a
- * kernel id >= 0 (name via skipln_kernel_name) or a negative status code.
- * `aligned16` says whether every tensor pointer is 16-byte aligned. */
-int skipln_select(int64_t hidden, int dtype, int aligned16, int variant);
+/* Kernel that skipln_forward_variant would launch for this hidden size and
+ * skip form: returns a kernel id >= 0 (name via skipln_kernel_name) or a
+ * negative status code.  `aligned16` says whether every tensor pointer is
+ * 16-byte aligned. */
+int skipln_select(int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
 
 /* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte
  * aligned, bytes % 16 == 0, no overlap), with the access pattern of the

@@ -18,7 +18,6 @@ from transformer_residual_add_amd import _lib as L
 from oracle import oracle as O
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 2e-3)}
-TORCH_DT = None
 
 
 def torch_dtype(dt: str):
@@ -81,6 +80,16 @@ class DeviceCase:
                       w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
                       w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
                       stream, variant)
+
+    def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0):
+        w = self.w
+        p = lambda t: None if t is None else t.data_ptr()
+        st = L.load().skipln_forward_config(
+            p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
+            w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(self.out), p(self.res),
+            w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16, geometry,
+            tiles_per_block, strided, stream or None)
+        L.check(st, "skipln_forward_config")
 
     def host(self, t):
         import torch

@@ -115,30 +115,49 @@ def test_validate_allows_exact_aliasing():
 
 def test_select_kernels():
     lib = L.load()
+    sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT: lib.skipln_select(h, dt, mode, al, v)
     name = lambda kid: L.kernel_name(kid)
-    assert name(lib.skipln_select(768, 0, 1, 0)) == "rowtile_f32_g64_c3"
-    assert name(lib.skipln_select(1024, 1, 1, 0)) == "rowtile_f16_g64_c2"
-    assert name(lib.skipln_select(4096, 0, 1, 0)) == "rowtile_f32_g256_c4"
-    assert name(lib.skipln_select(8192, 1, 1, 0)) == "rowtile_f16_g256_c4"
-    assert name(lib.skipln_select(64, 0, 1, 0)) == "rowtile_f32_g16_c1"
+    assert name(sel(768, 0)) == "rowtile_f32_g192_c1_b192"
+    assert name(sel(1024, 1)) == "rowtile_f16_g128_c1"
+    assert name(sel(4096, 0)) == "rowtile_f32_g256_c4"
+    assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4_b512"
+    assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
+    assert name(sel(64, 0)) == "rowtile_f32_g16_c1"
     # not a multiple of a 16-byte chunk, or misaligned, or too long: generic
-    assert name(lib.skipln_select(1001, 0, 1, 0)) == "generic_f32"
-    assert name(lib.skipln_select(1024, 0, 0, 0)) == "generic_f32"
-    assert name(lib.skipln_select(20000, 0, 1, 0)) == "generic_f32"
-    assert name(lib.skipln_select(8, 1, 1, 1)) == "generic_f16"
-    assert lib.skipln_select(1001, 0, 1, L.VARIANT_ROWTILE) == -L.ERR_UNSUPPORTED
-    assert name(lib.skipln_select(64, 0, 1, L.VARIANT_MULTIWAVE)).startswith("rowtile_f32_g128")
+    assert name(sel(1001, 0)) == "generic_f32"
+    assert name(sel(1024, 0, al=0)) == "generic_f32"
+    assert name(sel(20000, 0)) == "generic_f32"
+    assert name(sel(8, 1, v=1)) == "generic_f16"
+    assert sel(1001, 0, v=L.VARIANT_ROWTILE) == -L.ERR_UNSUPPORTED
+    assert name(sel(64, 0, v=L.VARIANT_MULTIWAVE)).startswith("rowtile_f32_g128")
     ng = lib.skipln_rowtile_geometries()
     assert ng >= 13
     for g in range(ng):
-        kid = lib.skipln_select(64, 0, 1, L.VARIANT_GEOMETRY + g)
+        kid = sel(64, 0, v=L.VARIANT_GEOMETRY + g)
         assert kid >= 0 and name(kid).startswith("rowtile_f32_g")
-    assert lib.skipln_select(16384, 0, 1, L.VARIANT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED
-    assert lib.skipln_select(64, 0, 1, L.VARIANT_GEOMETRY + ng) == -L.ERR_VARIANT
-    assert lib.skipln_select(64, 0, 1, 17) == -L.ERR_VARIANT
-    assert lib.skipln_select(64, 5, 1, 0) == -L.ERR_DTYPE
-    assert lib.skipln_select(0, 0, 1, 0) == -L.ERR_SHAPE
+    assert sel(16384, 0, v=L.VARIANT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED
+    assert sel(64, 0, v=L.VARIANT_GEOMETRY + ng) == -L.ERR_VARIANT
+    assert sel(64, 0, v=17) == -L.ERR_VARIANT
+    assert sel(64, 5) == -L.ERR_DTYPE
+    assert sel(0, 0) == -L.ERR_SHAPE
+    assert sel(64, 0, mode=3) == -L.ERR_MODE
     assert L.kernel_name(-1) == "unknown" and L.kernel_name(10 ** 6) == "unknown"
+
+
+def test_auto_choice_holds_every_hidden_size():
+    """The automatic choice exists for every chunked hidden size up to the
+    row-tile limit, holds the row, and is monotone in capacity."""
+    lib = L.load()
+    for dt, v in ((0, 4), (1, 8)):
+        for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST):
+            for hv in range(1, 4097):
+                kid = lib.skipln_select(hv * v, dt, mode, 1, 0)
+                assert kid >= 0 and L.kernel_name(kid).startswith("rowtile_"), (dt, mode, hv)
+                n = L.kernel_name(kid)
+                g = int(n.split("_g")[1].split("_")[0])
+                c = int(n.split("_c")[1].split("_")[0])
+                assert g * c >= hv
+            assert L.kernel_name(lib.skipln_select(4097 * v, dt, mode, 1, 0)).startswith("generic_")
 
 
 def test_no_cpu_fallback_in_product_path():

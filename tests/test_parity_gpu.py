@@ -51,7 +51,8 @@ def test_workload_full_size_sampled(name):
     U.note(f"workload {name}: generating rows={w.rows} H={w.hidden} {w.dtype}")
     inputs = W.make_inputs(w)
     dc = U.DeviceCase(w, inputs, residual=w.residual)
-    U.note(f"workload {name}: launching {T.select_kernel(w.hidden, L.F32 if w.dtype == 'f32' else L.F16)}")
+    mode = L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT
+    U.note(f"workload {name}: launching {T.select_kernel(w.hidden, L.F32 if w.dtype == 'f32' else L.F16, skip_mode=mode)}")
     dc.run()
     torch.cuda.synchronize()
     U.note(f"workload {name}: comparing sampled rows")
@@ -127,13 +128,8 @@ def test_hidden_sizes(dt, hidden):
     U.check_case(w)
 
 
-def _geometries():
-    lib = L.load()
-    return range(lib.skipln_rowtile_geometries())
-
-
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("geom", list(range(15)))
+@pytest.mark.parametrize("geom", list(range(32)))
 @pytest.mark.parametrize("ragged", [False, True])
 def test_every_geometry(dt, geom, ragged):
     """Each row-tile geometry at its full capacity and one chunk short of it,
@@ -146,13 +142,14 @@ def test_every_geometry(dt, geom, ragged):
     # capacity in chunks: the largest hidden size the geometry accepts
     cap = 0
     for hv in range(1, 4097):
-        if lib.skipln_select(hv * v, code, 1, L.VARIANT_GEOMETRY + geom) < 0:
+        if lib.skipln_select(hv * v, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom) < 0:
             break
         cap = hv
     hidden = (cap - 1 if ragged and cap > 1 else cap) * v
-    name = L.kernel_name(lib.skipln_select(hidden, code, 1, L.VARIANT_GEOMETRY + geom))
+    name = L.kernel_name(lib.skipln_select(hidden, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom))
     g = int(name.split("_g")[1].split("_")[0])
-    rpb = max(1, 256 // g) if g <= 256 else 1
+    block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
+    rpb = block // g
     rows = 3 * rpb + 1
     w = W.small_case(rows, hidden, dt, beta=True, bias=ragged, residual=True, eps=1e-5, seed=geom * 7 + ragged)
     U.note(f"geometry {geom} ({name}) H={hidden} rows={rows}")
@@ -182,6 +179,54 @@ def test_many_rows_small_hidden(dt):
     w = W.small_case(100003, 64, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=5)
     U.note(f"many rows {dt}")
     U.check_case(w)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (1, 1), (3, 0), (3, 1), (7, 0), (1000, 1)],
+                         ids=lambda t: f"tpb{t[0]}_s{t[1]}")
+@pytest.mark.parametrize("geom_hidden", [(-1, 1024), (0, 48), (8, 4000), (14, 768)],
+                         ids=lambda g: f"g{g[0]}_h{g[1]}")
+def test_launch_configs(dt, tiling, geom_hidden):
+    """Every tiling (persistent, contiguous, strided, more tiles per block
+    than exist) gives the same, correct result."""
+    geom, hidden = geom_hidden
+    if dt == "f16" and hidden % 8:
+        hidden += 8 - hidden % 8
+    w = W.small_case(203, hidden, dt, skip_rows=7, beta=True, bias=True, residual=True, eps=1e-5, seed=13)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=True)
+    U.note(f"config {dt} geometry={geom} H={hidden} tiling={tiling}")
+    dc.run_config(geom, *tiling)
+    ref = U.oracle_rows(w, inputs)
+    U.assert_out_close(dc.host(dc.out), ref["y"], dt)
+    U.assert_bits_equal(dc.host(dc.res), ref["residual"])
+
+
+def test_launch_config_errors():
+    w = W.small_case(8, 64, "f32", residual=True)
+    dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run_config(0, -1, 0)
+    assert e.value.status == L.ERR_SHAPE
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run_config(L.load().skipln_rowtile_geometries(), 1, 0)
+    assert e.value.status == L.ERR_VARIANT
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run_config(-2, 1, 0)
+    assert e.value.status == L.ERR_VARIANT
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 1 << 20, (64 << 20) + 48])
+def test_streaming_copy(nbytes):
+    import torch
+
+    src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    L.check(L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, None), "skipln_copy")
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+    assert L.load().skipln_copy(dst.data_ptr() + 8, src.data_ptr(), 16, None) == L.ERR_SHAPE
+    assert L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), 24, None) == L.ERR_SHAPE
 
 
 # ------------------------------------------------------------ edge cases --
@@ -265,6 +310,34 @@ def test_non_default_stream():
     ref = U.oracle_rows(w, inputs)
     U.assert_out_close(dc.host(dc.out), ref["y"], "f32")
     U.assert_bits_equal(dc.host(dc.res), ref["residual"])
+
+
+@pytest.mark.parametrize("name", ["bert_base_8x128x768_f32", "bcast_64x512x4096_f32"])
+def test_graph_replay_matches_eager(name):
+    """Captured into a HIP graph, every replay (with eager work and
+    synchronizations in between) equals the eager launch on the same input."""
+    import torch
+
+    w = W.WORKLOADS[name]
+    if w.rows > 4096:
+        w = w.with_(shape=(8,) + w.shape[1:])
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=True)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        dc.run(stream=torch.cuda.current_stream().cuda_stream)
+    for rep in range(4):
+        dc.x.mul_(0.5).add_(float(rep))  # eager work between replays: new input
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_out, got_res = dc.out.clone(), dc.res.clone()
+        dc.out.fill_(float("nan"))
+        dc.res.fill_(float("nan"))
+        dc.run()
+        torch.cuda.synchronize()
+        assert torch.equal(got_out, dc.out) and torch.equal(got_res, dc.res), f"replay {rep} differs"
 
 
 def test_error_enqueues_nothing():

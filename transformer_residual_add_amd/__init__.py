@@ -32,9 +32,10 @@ def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, g
     _lib.check(st, "skipln_forward")
 
 
-def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO) -> str:
-    """Name of the kernel a call with this hidden size would launch."""
-    kid = _lib.load().skipln_select(hidden, dtype, 1 if aligned16 else 0, variant)
+def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO,
+                  skip_mode: int = _lib.SKIP_EXACT) -> str:
+    """Name of the kernel a call with this hidden size and skip form would launch."""
+    kid = _lib.load().skipln_select(hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
     if kid < 0:
         raise SkiplnError(-kid, "skipln_select")
     return _lib.kernel_name(kid)

@@ -74,14 +74,15 @@ int validate(const void* input, const void* skip, int skip_mode, int64_t skip_ro
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Kernel id (>= 0) for this variant, or -status.
-int select(int64_t hidden, int dtype, bool vec_ok, int variant) {
+int select(int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant) {
     const int base = dtype * skipln::kIdsPerType;
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
     if (variant == SKIPLN_VARIANT_GENERIC) return base + skipln::kGenericIndex;
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
         variant == SKIPLN_VARIANT_MULTIWAVE) {
-        const int g = chunked ? skipln::rowtile_pick(hidden, dtype, variant == SKIPLN_VARIANT_MULTIWAVE) : -1;
+        const int g =
+            chunked ? skipln::rowtile_pick(hidden, dtype, broadcast, variant == SKIPLN_VARIANT_MULTIWAVE) : -1;
         if (g >= 0) return base + skipln::kRowtileFirst + g;
         if (variant == SKIPLN_VARIANT_AUTO) return base + skipln::kGenericIndex;
         return -SKIPLN_ERR_UNSUPPORTED;
@@ -95,36 +96,27 @@ int select(int64_t hidden, int dtype, bool vec_ok, int variant) {
     return -SKIPLN_ERR_VARIANT;
 }
 
-}  // namespace
-
-extern "C" {
-
-int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
-                    const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
-                    int64_t hidden, float eps, int dtype) {
-    return validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
-                    dtype);
+bool all_aligned16(const void* input, const void* skip, const void* gamma, const void* beta, const void* bias,
+                   const void* out, const void* residual_out) {
+    return aligned16(input) && aligned16(skip) && aligned16(gamma) && aligned16(beta) && aligned16(bias) &&
+           aligned16(out) && aligned16(residual_out);
 }
 
-int skipln_select(int64_t hidden, int dtype, int aligned, int variant) {
-    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
-    if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(hidden, dtype, aligned != 0, variant);
+// Tiling of the automatic launch.  Streaming rows (exact skip): one tile per
+// block, so blocks are dispatched in address order and the set of rows in
+// flight stays compact; this reached the 2-read/2-write streaming rate on
+// MI355X.  A broadcast skip is re-read by every batch from L2: a persistent
+// grid keeps gamma/beta in registers and each XCD on the same skip rows.
+skipln::Tiling auto_tiling(bool broadcast) {
+    skipln::Tiling t;
+    t.tiles_per_block = broadcast ? 0 : 1;
+    t.strided = 1;
+    return t;
 }
 
-int skipln_forward_variant(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
-                           const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
-                           int64_t rows, int64_t hidden, float eps, int dtype, int variant,
-                           skipln_stream_t stream) {
-    int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
-                      dtype);
-    if (st != SKIPLN_OK) return st;
-    const bool vec_ok = aligned16(input) && aligned16(skip) && aligned16(gamma) && aligned16(beta) &&
-                        aligned16(bias) && aligned16(out) && aligned16(residual_out);
-    const int id = skipln_select(hidden, dtype, vec_ok ? 1 : 0, variant);
-    if (id < 0) return -id;
-    if (rows == 0) return SKIPLN_OK;
-
+skipln::Args make_args(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
+                       const void* beta, const void* bias, void* out, void* residual_out, int64_t rows,
+                       int64_t hidden, float eps) {
     skipln::Args a;
     a.input = input;
     a.skip = skip;
@@ -137,16 +129,77 @@ int skipln_forward_variant(const void* input, const void* skip, int skip_mode, i
     a.skip_rows = skip_mode == SKIPLN_SKIP_BROADCAST ? skip_rows : 0;
     a.hidden = static_cast<int32_t>(hidden);
     a.eps = eps;
+    a.tiles_per_block = 1;
+    a.strided = 0;
+    return a;
+}
 
+int status_of(hipError_t e) {
+    if (e == hipSuccess) return SKIPLN_OK;
+    if (e == hipErrorInvalidDevice || e == hipErrorNoDevice) return SKIPLN_ERR_DEVICE;
+    return SKIPLN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
+                    const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
+                    int64_t hidden, float eps, int dtype) {
+    return validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                    dtype);
+}
+
+int skipln_select(int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
+    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
+    if (skip_mode != SKIPLN_SKIP_EXACT && skip_mode != SKIPLN_SKIP_BROADCAST) return -SKIPLN_ERR_MODE;
+    if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
+    return select(hidden, dtype, skip_mode == SKIPLN_SKIP_BROADCAST, aligned != 0, variant);
+}
+
+int skipln_forward_variant(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                           const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
+                           int64_t rows, int64_t hidden, float eps, int dtype, int variant,
+                           skipln_stream_t stream) {
+    int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                      dtype);
+    if (st != SKIPLN_OK) return st;
+    const bool vec_ok = all_aligned16(input, skip, gamma, beta, bias, out, residual_out);
+    const int id = skipln_select(hidden, dtype, skip_mode, vec_ok ? 1 : 0, variant);
+    if (id < 0) return -id;
+    if (rows == 0) return SKIPLN_OK;
+
+    const skipln::Args a = make_args(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows,
+                                     hidden, eps);
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int index = id % skipln::kIdsPerType;
-    hipError_t e;
-    if (index == skipln::kGenericIndex)
-        e = skipln::launch_generic(a, dtype, s);
-    else
-        e = skipln::launch_rowtile(a, dtype, index - skipln::kRowtileFirst, s);
-    if (e == hipErrorInvalidDevice || e == hipErrorNoDevice) return SKIPLN_ERR_DEVICE;
-    return e == hipSuccess ? SKIPLN_OK : SKIPLN_ERR_LAUNCH;
+    if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, dtype, s));
+    return status_of(skipln::launch_rowtile(a, dtype, index - skipln::kRowtileFirst,
+                                            auto_tiling(skip_mode == SKIPLN_SKIP_BROADCAST), s));
+}
+
+int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                          const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
+                          int64_t rows, int64_t hidden, float eps, int dtype, int geometry, int64_t tiles_per_block,
+                          int strided, skipln_stream_t stream) {
+    int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                      dtype);
+    if (st != SKIPLN_OK) return st;
+    if (tiles_per_block < 0) return SKIPLN_ERR_SHAPE;
+    const bool vec_ok = all_aligned16(input, skip, gamma, beta, bias, out, residual_out);
+    if (geometry < -1 || geometry >= skipln::rowtile_count()) return SKIPLN_ERR_VARIANT;
+    const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
+    const int id = skipln_select(hidden, dtype, skip_mode, vec_ok ? 1 : 0, variant);
+    if (id < 0) return -id;
+    if (rows == 0) return SKIPLN_OK;
+    const skipln::Args a = make_args(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows,
+                                     hidden, eps);
+    skipln::Tiling t;
+    t.tiles_per_block = tiles_per_block;
+    t.strided = strided ? 1 : 0;
+    return status_of(skipln::launch_rowtile(a, dtype, id % skipln::kIdsPerType - skipln::kRowtileFirst, t,
+                                            reinterpret_cast<hipStream_t>(stream)));
 }
 
 int skipln_forward(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
@@ -162,9 +215,7 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
     if (!dst || !src) return SKIPLN_ERR_NULL;
     if (!aligned16(dst) || !aligned16(src)) return SKIPLN_ERR_SHAPE;
     if (overlap(span(dst, bytes), span(src, bytes))) return SKIPLN_ERR_ALIAS;
-    const hipError_t e = skipln::launch_copy(dst, src, bytes / 16, reinterpret_cast<hipStream_t>(stream));
-    if (e == hipErrorInvalidDevice || e == hipErrorNoDevice) return SKIPLN_ERR_DEVICE;
-    return e == hipSuccess ? SKIPLN_OK : SKIPLN_ERR_LAUNCH;
+    return status_of(skipln::launch_copy(dst, src, bytes / 16, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int skipln_rowtile_geometries(void) { return skipln::rowtile_count(); }

@@ -20,6 +20,17 @@ struct Args {
     int64_t skip_rows; // 0: exact skip; > 0: row r reads skip row r % skip_rows
     int32_t hidden;
     float eps;
+    // Row-tile kernels: tiles (RPB rows each) per block, and whether a block
+    // takes them strided by the grid size (1) or contiguous (0).  Set by the
+    // launcher.
+    int64_t tiles_per_block;
+    int32_t strided;
+};
+
+// How a row-tile launch distributes tiles over blocks.
+struct Tiling {
+    int64_t tiles_per_block;  // 0: persistent, grid sized to the occupancy limit
+    int strided;              // 1: block b takes tiles b, b + grid, ...
 };
 
 // Kernel ids: dtype * kIdsPerType + index, index 0 = generic, 1.. = row tiles.
@@ -27,18 +38,18 @@ constexpr int kIdsPerType = 32;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
 
-// Number of row-tile geometries and the one chosen for `hidden` (elements),
-// or -1 when none holds the row.  multiwave_only: only geometries whose row
-// group spans two or more wavefronts.
+// Number of row-tile geometries and the one chosen for `hidden` (elements)
+// and the skip form, or -1 when none holds the row.  multiwave_only: the
+// smallest geometry whose row group spans two or more wavefronts.
 int rowtile_count();
-int rowtile_pick(int64_t hidden, int dtype, bool multiwave_only);
+int rowtile_pick(int64_t hidden, int dtype, bool broadcast, bool multiwave_only);
 // Whether geometry g holds a row of `hidden` elements (16-byte chunks).
 bool rowtile_holds(int geometry, int64_t hidden, int dtype);
 const char* kernel_name(int kernel_id);
 
 // Enqueue one kernel; return 0 or a hipError_t value.
 hipError_t launch_generic(const Args& a, int dtype, hipStream_t stream);
-hipError_t launch_rowtile(const Args& a, int dtype, int geometry, hipStream_t stream);
+hipError_t launch_rowtile(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln

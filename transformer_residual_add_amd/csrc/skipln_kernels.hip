@@ -226,8 +226,13 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
     const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
 
+    // Tiles of this block: contiguous [b*T, b*T + T), or strided b, b + grid,
+    // ... (T = tiles_per_block); one tile per block when T == 1.
     const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
-    const int64_t stride = gridDim.x;
+    const int64_t t_first = a.strided ? blockIdx.x : blockIdx.x * a.tiles_per_block;
+    const int64_t stride = a.strided ? gridDim.x : 1;
+    const int64_t t_end = a.strided ? n_tiles
+                                    : (t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles);
 
     u32x4 xr[CH], sr[CH];
 #pragma unroll
@@ -252,11 +257,11 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
     };
 
-    int64_t tile = blockIdx.x;
-    if (tile < n_tiles) issue_loads(tile);
+    int64_t tile = t_first;
+    if (tile < t_end) issue_loads(tile);
     int parity = 0;
 
-    for (; tile < n_tiles; tile += stride) {
+    for (; tile < t_end; tile += stride) {
         const int64_t row = tile * RPB + slot;
         const bool live = row < a.rows;
         if constexpr (V == 8) {
@@ -291,7 +296,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
 
         // Registers of x/skip are free again: start the next tile's loads.
-        if (tile + stride < n_tiles) issue_loads(tile + stride);
+        if (tile + stride < t_end) issue_loads(tile + stride);
 
         if (R != nullptr && live) {
             u32x4* rp = R + row * hv + lt;
@@ -463,9 +468,29 @@ constexpr Geom kGeoms[] = {
     {16, 1, 256},  {32, 1, 256},  {64, 1, 256},   {64, 2, 256},   {64, 3, 256},
     {64, 4, 256},  {128, 4, 256}, {256, 3, 256},  {256, 4, 256},  {512, 3, 512},
     {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
+    {512, 2, 512}, {128, 8, 256},  {256, 2, 512},  {256, 4, 512},  {64, 2, 64},
+    {64, 3, 64},   {32, 6, 256},  {192, 1, 192},  {192, 2, 192},  {512, 1, 512},
+    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256},
 };
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
-constexpr int kNumAutoGeoms = 13;
+
+// Automatic choice: the first entry whose capacity holds the row's chunks.
+// Short rows are latency bound: one chunk per lane spreads a row over more
+// lanes and shortens the per-lane load/reduce chain.  Long rows use 256-lane
+// groups (4 wavefronts; 1024-lane groups pay for 16-wavefront barriers).
+// With a broadcast skip, two rows per block share one block's registers of
+// gamma/beta on a persistent grid.
+struct AutoEntry {
+    int max_chunks, geom;
+};
+constexpr AutoEntry kAutoExact[] = {
+    {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
+    {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+};
+constexpr AutoEntry kAutoBroadcast[] = {
+    {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
+    {768, 7}, {1024, 18}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+};
 
 hipError_t cu_count(int* out) {
     int dev = 0;
@@ -488,9 +513,10 @@ hipError_t cu_count(int* out) {
     return hipSuccess;
 }
 
+// Blocks of `kernel` the device holds at once (occupancy limit x CUs); the
+// per-kernel occupancy is cached after the first query.
 template <typename K>
-hipError_t launch_persistent(K kernel, int block, int64_t work_items, const Args& a, hipStream_t st,
-                             int* occupancy_cache) {
+hipError_t resident_blocks(K kernel, int block, int* occupancy_cache, int64_t* out) {
     int cus = 0;
     hipError_t e = cu_count(&cus);
     if (e != hipSuccess) return e;
@@ -501,38 +527,64 @@ hipError_t launch_persistent(K kernel, int block, int64_t work_items, const Args
         if (occ < 1) occ = 1;
         __atomic_store_n(occupancy_cache, occ, __ATOMIC_RELAXED);
     }
-    int64_t blocks = static_cast<int64_t>(cus) * occ;
-    if (work_items < blocks) blocks = work_items;
-    if (blocks < 1) blocks = 1;
+    *out = static_cast<int64_t>(cus) * occ;
+    return hipSuccess;
+}
+
+template <typename K>
+hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipStream_t st) {
     Args arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
                            dim3(block), params, 0, st);
 }
 
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
 template <typename T, int I>
-hipError_t launch_geom(const Args& a, hipStream_t st) {
+hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     constexpr Geom g = kGeoms[I];
     static int occ = 0;
+    auto kernel = rowtile_kernel<T, g.g, g.ch, g.block>;
     const int64_t rpb = g.block / g.g;
-    return launch_persistent(rowtile_kernel<T, g.g, g.ch, g.block>, g.block, (a.rows + rpb - 1) / rpb, a, st,
-                             &occ);
+    const int64_t tiles = (a0.rows + rpb - 1) / rpb;
+    Args a = a0;
+    int64_t per = tiling.tiles_per_block;
+    a.strided = tiling.strided ? 1 : 0;
+    if (per <= 0) {
+        // Persistent: one wave of resident blocks walks all tiles, strided.
+        int64_t resident = 0;
+        const hipError_t e = resident_blocks(kernel, g.block, &occ, &resident);
+        if (e != hipSuccess) return e;
+        per = (tiles + resident - 1) / resident;
+        a.strided = 1;
+    }
+    if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
+    a.tiles_per_block = per;
+    int64_t blocks = (tiles + per - 1) / per;
+    if (blocks < 1) blocks = 1;
+    return launch_grid(kernel, g.block, blocks, a, st);
 }
 
 template <typename T, int... I>
-hipError_t launch_geom_dispatch(int idx, const Args& a, hipStream_t st, std::integer_sequence<int, I...>) {
+hipError_t launch_geom_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
     hipError_t r = hipErrorInvalidValue;
-    ((idx == I ? (r = launch_geom<T, I>(a, st), 0) : 0), ...);
+    ((idx == I ? (r = launch_geom<T, I>(a, t, st), 0) : 0), ...);
     return r;
 }
 
 template <typename T>
 hipError_t launch_generic_t(const Args& a, hipStream_t st) {
     static int occ = 0;
-    return launch_persistent(generic_kernel<T>, kGenericBlock, a.rows, a, st, &occ);
+    int64_t resident = 0;
+    const hipError_t e = resident_blocks(generic_kernel<T>, kGenericBlock, &occ, &resident);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = a.rows < resident ? a.rows : resident;
+    return launch_grid(generic_kernel<T>, kGenericBlock, blocks < 1 ? 1 : blocks, a, st);
 }
 
-// Names: "generic_<t>" and "rowtile_<t>_g<G>_c<CH>".
+// Names: "generic_<t>" and "rowtile_<t>_g<G>_c<CH>", with "_b<block>" when the
+// block is not the default max(256, G).
 char g_names[2][kIdsPerType][32];
 std::atomic<int> g_names_ready{0};
 
@@ -543,9 +595,14 @@ void build_names() {
             char* dst = g_names[t][i];
             if (i == kGenericIndex)
                 snprintf(dst, 32, "generic_%s", tn[t]);
-            else if (i - kRowtileFirst < kNumGeoms)
-                snprintf(dst, 32, "rowtile_%s_g%d_c%d", tn[t], kGeoms[i - kRowtileFirst].g,
-                         kGeoms[i - kRowtileFirst].ch);
+            else if (i - kRowtileFirst < kNumGeoms) {
+                const Geom& g = kGeoms[i - kRowtileFirst];
+                const int default_block = g.g > 256 ? g.g : 256;
+                if (g.block == default_block)
+                    snprintf(dst, 32, "rowtile_%s_g%d_c%d", tn[t], g.g, g.ch);
+                else
+                    snprintf(dst, 32, "rowtile_%s_g%d_c%d_b%d", tn[t], g.g, g.ch, g.block);
+            }
             else
                 snprintf(dst, 32, "unknown");
         }
@@ -556,13 +613,18 @@ void build_names() {
 
 int rowtile_count() { return kNumGeoms; }
 
-int rowtile_pick(int64_t hidden, int dtype, bool multiwave_only) {
+int rowtile_pick(int64_t hidden, int dtype, bool broadcast, bool multiwave_only) {
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     if (hidden <= 0 || hidden % v != 0) return -1;
     const int64_t hv = hidden / v;
-    int best = -1;
+    if (!multiwave_only) {
+        for (const AutoEntry& e : (broadcast ? kAutoBroadcast : kAutoExact))
+            if (hv <= e.max_chunks) return e.geom;
+        return -1;
+    }
+    int best = -1;  // smallest capacity among groups of two or more wavefronts
     for (int i = 0; i < kNumGeoms; ++i) {
-        if (multiwave_only ? kGeoms[i].g < 128 : i >= kNumAutoGeoms) continue;
+        if (kGeoms[i].g < 128) continue;
         const int64_t cap = static_cast<int64_t>(kGeoms[i].g) * kGeoms[i].ch;
         if (cap < hv) continue;
         if (best < 0 || cap < static_cast<int64_t>(kGeoms[best].g) * kGeoms[best].ch) best = i;
@@ -592,18 +654,10 @@ const char* kernel_name(int kernel_id) {
 }
 
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t st) {
-    int cus = 0;
-    hipError_t e = cu_count(&cus);
-    if (e != hipSuccess) return e;
     static int occ = 0;
-    int o = __atomic_load_n(&occ, __ATOMIC_RELAXED);
-    if (o <= 0) {
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, copy_kernel, kCopyBlock, 0);
-        if (e != hipSuccess) return e;
-        if (o < 1) o = 1;
-        __atomic_store_n(&occ, o, __ATOMIC_RELAXED);
-    }
-    int64_t blocks = static_cast<int64_t>(cus) * o;
+    int64_t blocks = 0;
+    const hipError_t e = resident_blocks(copy_kernel, kCopyBlock, &occ, &blocks);
+    if (e != hipSuccess) return e;
     const int64_t need = (chunks + kCopyBlock - 1) / kCopyBlock;
     if (need < blocks) blocks = need;
     if (blocks < 1) blocks = 1;
@@ -618,11 +672,11 @@ hipError_t launch_generic(const Args& a, int dtype, hipStream_t st) {
     return dtype == 0 ? launch_generic_t<float>(a, st) : launch_generic_t<_Float16>(a, st);
 }
 
-hipError_t launch_rowtile(const Args& a, int dtype, int geometry, hipStream_t st) {
+hipError_t launch_rowtile(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t st) {
     if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
     auto seq = std::make_integer_sequence<int, kNumGeoms>{};
-    return dtype == 0 ? launch_geom_dispatch<float>(geometry, a, st, seq)
-                      : launch_geom_dispatch<_Float16>(geometry, a, st, seq);
+    return dtype == 0 ? launch_geom_dispatch<float>(geometry, a, tiling, st, seq)
+                      : launch_geom_dispatch<_Float16>(geometry, a, tiling, st, seq);
 }
 
 }  // namespace skipln
