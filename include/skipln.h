@@ -125,19 +125,30 @@ int skipln_forward_variant(const void* input, const void* skip, int skip_mode, i
                            void* out, void* residual_out, int64_t rows, int64_t hidden,
                            float eps, int dtype, int variant, skipln_stream_t stream);
 
+/* How the row-tile kernel distributes row tiles over workgroups (see
+ * skipln_forward_config). */
+enum {
+    SKIPLN_TILE_CONTIGUOUS = 0,     /* block b: tiles b*T .. b*T + T - 1 */
+    SKIPLN_TILE_STRIDED = 1,        /* block b: tiles b, b + grid, b + 2*grid, ... */
+    SKIPLN_TILE_SKIP_STATIONARY = 2 /* broadcast skip: block b keeps its skip rows
+                                       in registers and walks T batches;
+                                       otherwise as SKIPLN_TILE_STRIDED */
+};
+
 /* skipln_forward with an explicit launch configuration, for tuning; the
  * result is the same operator.  geometry: row-tile geometry
  * (0 <= geometry < skipln_rowtile_geometries()), or -1 for the automatic
- * choice.  tiles_per_block > 0: each block takes that many row tiles,
- * contiguous (strided = 0) or strided by the grid size (strided = 1);
- * tiles_per_block = 0: a persistent grid of as many blocks as the device
- * holds at once.  Returns SKIPLN_ERR_UNSUPPORTED when the geometry cannot
- * hold the row or the tensors are not 16-byte aligned, SKIPLN_ERR_SHAPE for
- * tiles_per_block < 0. */
+ * choice.  tiles_per_block (T) > 0: row tiles (batches, for
+ * SKIPLN_TILE_SKIP_STATIONARY) per block; 0: sized so the grid matches the
+ * blocks the device holds at once (SKIPLN_TILE_CONTIGUOUS then behaves as
+ * SKIPLN_TILE_STRIDED).  tiling: SKIPLN_TILE_*.  Returns
+ * SKIPLN_ERR_UNSUPPORTED when the geometry cannot hold the row or the tensors
+ * are not 16-byte aligned, SKIPLN_ERR_SHAPE for tiles_per_block < 0,
+ * SKIPLN_ERR_VARIANT for an unknown geometry or tiling. */
 int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                           const void* gamma, const void* beta, const void* bias,
                           void* out, void* residual_out, int64_t rows, int64_t hidden,
-                          float eps, int dtype, int geometry, int64_t tiles_per_block, int strided,
+                          float eps, int dtype, int geometry, int64_t tiles_per_block, int tiling,
                           skipln_stream_t stream);
 
 /* The argument checks of skipln_forward alone: host code only, no HIP call,

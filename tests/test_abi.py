@@ -43,6 +43,8 @@ def test_header_enums_match_binding():
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
+        "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
+        "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
     }
     assert vals == expect
 
@@ -120,7 +122,7 @@ def test_select_kernels():
     assert name(sel(768, 0)) == "rowtile_f32_g192_c1_b192"
     assert name(sel(1024, 1)) == "rowtile_f16_g128_c1"
     assert name(sel(4096, 0)) == "rowtile_f32_g256_c4"
-    assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4_b512"
+    assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4"
     assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
     assert name(sel(64, 0)) == "rowtile_f32_g16_c1"
     # not a multiple of a 16-byte chunk, or misaligned, or too long: generic

@@ -182,8 +182,9 @@ def test_many_rows_small_hidden(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (1, 1), (3, 0), (3, 1), (7, 0), (1000, 1)],
-                         ids=lambda t: f"tpb{t[0]}_s{t[1]}")
+@pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (1, 1), (3, 0), (3, 1), (7, 0), (1000, 1), (0, 0), (0, 2),
+                                    (1, 2), (2, 2), (5, 2), (1000, 2)],
+                         ids=lambda t: f"tpb{t[0]}_m{t[1]}")
 @pytest.mark.parametrize("geom_hidden", [(-1, 1024), (0, 48), (8, 4000), (14, 768)],
                          ids=lambda g: f"g{g[0]}_h{g[1]}")
 def test_launch_configs(dt, tiling, geom_hidden):
@@ -202,6 +203,25 @@ def test_launch_configs(dt, tiling, geom_hidden):
     U.assert_bits_equal(dc.host(dc.res), ref["residual"])
 
 
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("geom,hidden,S,batches", [(18, 4096, 8, 13), (13, 512, 6, 5), (0, 64, 32, 5), (0, 64, 24, 3),
+                                                    (8, 2048, 1, 9), (22, 768, 5, 4)])
+@pytest.mark.parametrize("tpb", [0, 1, 3])
+def test_skip_stationary_tiles(dt, geom, hidden, S, batches, tpb):
+    """Broadcast skip with blocks that keep their skip rows across batches,
+    including multi-row tiles and a skip row count that does not split into
+    whole tiles (falls back to strided)."""
+    w = W.small_case(S * batches, hidden, dt, skip_rows=S if S * batches != S else None, beta=True, bias=True,
+                     residual=True, eps=1e-5, seed=S + batches)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=True)
+    U.note(f"stationary {dt} geometry={geom} H={hidden} S={S} N={batches} tpb={tpb}")
+    dc.run_config(geom, tpb, L.TILE_SKIP_STATIONARY)
+    ref = U.oracle_rows(w, inputs)
+    U.assert_out_close(dc.host(dc.out), ref["y"], dt)
+    U.assert_bits_equal(dc.host(dc.res), ref["residual"])
+
+
 def test_launch_config_errors():
     w = W.small_case(8, 64, "f32", residual=True)
     dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
@@ -213,6 +233,9 @@ def test_launch_config_errors():
     assert e.value.status == L.ERR_VARIANT
     with pytest.raises(T.SkiplnError) as e:
         dc.run_config(-2, 1, 0)
+    assert e.value.status == L.ERR_VARIANT
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run_config(0, 1, 3)
     assert e.value.status == L.ERR_VARIANT
 
 

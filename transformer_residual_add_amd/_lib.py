@@ -20,6 +20,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS = 0, 1, 2, 3, 4
 ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT = 7, 8, 9, 10
 VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE = 0, 1, 2, 3
 VARIANT_GEOMETRY = 64
+TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
 
 # Every function the header declares: name -> (restype, argtypes).
 _vp, _i64, _i32, _f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float

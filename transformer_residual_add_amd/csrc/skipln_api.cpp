@@ -16,6 +16,10 @@
 #include "../../include/skipln.h"
 #include "skipln_internal.h"
 
+static_assert(SKIPLN_TILE_CONTIGUOUS == skipln::kTileContiguous && SKIPLN_TILE_STRIDED == skipln::kTileStrided &&
+                  SKIPLN_TILE_SKIP_STATIONARY == skipln::kTileSkipStationary,
+              "tiling modes of the ABI and the kernels agree");
+
 namespace {
 
 struct Range {
@@ -105,12 +109,12 @@ bool all_aligned16(const void* input, const void* skip, const void* gamma, const
 // Tiling of the automatic launch.  Streaming rows (exact skip): one tile per
 // block, so blocks are dispatched in address order and the set of rows in
 // flight stays compact; this reached the 2-read/2-write streaming rate on
-// MI355X.  A broadcast skip is re-read by every batch from L2: a persistent
-// grid keeps gamma/beta in registers and each XCD on the same skip rows.
+// MI355X.  A broadcast skip is shared by every batch: each block keeps its
+// skip rows (and gamma/beta) in registers and walks the batches.
 skipln::Tiling auto_tiling(bool broadcast) {
     skipln::Tiling t;
     t.tiles_per_block = broadcast ? 0 : 1;
-    t.strided = 1;
+    t.mode = broadcast ? skipln::kTileSkipStationary : skipln::kTileStrided;
     return t;
 }
 
@@ -130,7 +134,7 @@ skipln::Args make_args(const void* input, const void* skip, int skip_mode, int64
     a.hidden = static_cast<int32_t>(hidden);
     a.eps = eps;
     a.tiles_per_block = 1;
-    a.strided = 0;
+    a.tiling = skipln::kTileStrided;
     return a;
 }
 
@@ -182,11 +186,13 @@ int skipln_forward_variant(const void* input, const void* skip, int skip_mode, i
 int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                           const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
                           int64_t rows, int64_t hidden, float eps, int dtype, int geometry, int64_t tiles_per_block,
-                          int strided, skipln_stream_t stream) {
+                          int tiling, skipln_stream_t stream) {
     int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
                       dtype);
     if (st != SKIPLN_OK) return st;
     if (tiles_per_block < 0) return SKIPLN_ERR_SHAPE;
+    if (tiling != SKIPLN_TILE_CONTIGUOUS && tiling != SKIPLN_TILE_STRIDED && tiling != SKIPLN_TILE_SKIP_STATIONARY)
+        return SKIPLN_ERR_VARIANT;
     const bool vec_ok = all_aligned16(input, skip, gamma, beta, bias, out, residual_out);
     if (geometry < -1 || geometry >= skipln::rowtile_count()) return SKIPLN_ERR_VARIANT;
     const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
@@ -197,7 +203,7 @@ int skipln_forward_config(const void* input, const void* skip, int skip_mode, in
                                      hidden, eps);
     skipln::Tiling t;
     t.tiles_per_block = tiles_per_block;
-    t.strided = strided ? 1 : 0;
+    t.mode = tiling;
     return status_of(skipln::launch_rowtile(a, dtype, id % skipln::kIdsPerType - skipln::kRowtileFirst, t,
                                             reinterpret_cast<hipStream_t>(stream)));
 }

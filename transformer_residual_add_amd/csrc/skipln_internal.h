@@ -20,17 +20,22 @@ struct Args {
     int64_t skip_rows; // 0: exact skip; > 0: row r reads skip row r % skip_rows
     int32_t hidden;
     float eps;
-    // Row-tile kernels: tiles (RPB rows each) per block, and whether a block
-    // takes them strided by the grid size (1) or contiguous (0).  Set by the
-    // launcher.
+    // Row-tile kernels: tiles (RPB rows each) per block and how a block
+    // walks them (kTile*).  Set by the launcher.
     int64_t tiles_per_block;
-    int32_t strided;
+    int32_t tiling;
 };
+
+// Tiling modes of the row-tile kernel (values of Args::tiling and of the
+// C ABI's tiling argument).
+constexpr int kTileContiguous = 0;      // block b: tiles b*T .. b*T + T - 1
+constexpr int kTileStrided = 1;         // block b: tiles b, b + grid, ...
+constexpr int kTileSkipStationary = 2;  // broadcast skip: fixed skip rows per block
 
 // How a row-tile launch distributes tiles over blocks.
 struct Tiling {
-    int64_t tiles_per_block;  // 0: persistent, grid sized to the occupancy limit
-    int strided;              // 1: block b takes tiles b, b + grid, ...
+    int64_t tiles_per_block;  // 0: sized so the grid matches the resident blocks
+    int mode;                 // kTile*
 };
 
 // Kernel ids: dtype * kIdsPerType + index, index 0 = generic, 1.. = row tiles.

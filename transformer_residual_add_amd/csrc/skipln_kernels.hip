@@ -201,6 +201,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     const bool has_bias = a.bias != nullptr;
     const bool has_beta = a.beta != nullptr;
     const bool bcast = a.skip_rows > 0;
+    const bool small_rows = a.rows <= 0xFFFFFFFFll;
 
     bool ok[CH];
 #pragma unroll
@@ -210,29 +211,54 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     u32x4 gam[CH], bet[CH], bia[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
-        const int c = k * G + lt;
         gam[k] = u32x4{0, 0, 0, 0};
         bet[k] = u32x4{0, 0, 0, 0};
         bia[k] = u32x4{0, 0, 0, 0};
-        if (ok[k]) {
-            gam[k] = static_cast<const u32x4*>(a.gamma)[c];
-            if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
-            if (has_bias) bia[k] = static_cast<const u32x4*>(a.bias)[c];
-        }
     }
+    auto load_params = [&]() {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int c = k * G + lt;
+            if (ok[k]) {
+                gam[k] = static_cast<const u32x4*>(a.gamma)[c];
+                if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
+                if (has_bias) bia[k] = static_cast<const u32x4*>(a.bias)[c];
+            }
+        }
+    };
 
     float nw[WPR];
 #pragma unroll
     for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
     const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
 
-    // Tiles of this block: contiguous [b*T, b*T + T), or strided b, b + grid,
-    // ... (T = tiles_per_block); one tile per block when T == 1.
+    // Tiles (RPB consecutive rows each) of this block, T = tiles_per_block:
+    //   contiguous:      b*T, b*T + 1, ..., b*T + T - 1
+    //   strided:         b, b + grid, b + 2*grid, ...
+    //   skip-stationary: with P = skip_rows / RPB tiles per batch, block b
+    //                    owns tile column p = b mod P (the same skip rows in
+    //                    every batch) and batches [c*T, c*T + T), c = b div P:
+    //                    tiles p + n*P.  Its skip rows are loaded once.
     const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
-    const int64_t t_first = a.strided ? blockIdx.x : blockIdx.x * a.tiles_per_block;
-    const int64_t stride = a.strided ? gridDim.x : 1;
-    const int64_t t_end = a.strided ? n_tiles
-                                    : (t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles);
+    int64_t t_first, stride, t_end;
+    const bool stationary = a.tiling == kTileSkipStationary;
+    if (a.tiling == kTileContiguous) {
+        t_first = blockIdx.x * a.tiles_per_block;
+        stride = 1;
+        t_end = t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles;
+    } else if (a.tiling == kTileStrided) {
+        t_first = blockIdx.x;
+        stride = gridDim.x;
+        t_end = n_tiles;
+    } else {
+        const int64_t P = a.skip_rows / RPB;
+        const int64_t batches = a.rows / a.skip_rows;
+        const int64_t n0 = (blockIdx.x / P) * a.tiles_per_block;
+        const int64_t n1 = n0 + a.tiles_per_block < batches ? n0 + a.tiles_per_block : batches;
+        t_first = n0 * P + blockIdx.x % P;
+        stride = P;
+        t_end = n1 * P;
+    }
 
     u32x4 xr[CH], sr[CH];
 #pragma unroll
@@ -240,10 +266,14 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         xr[k] = u32x4{0, 0, 0, 0};
         sr[k] = u32x4{0, 0, 0, 0};
     }
-    auto issue_loads = [&](int64_t tile) {
+    auto issue_loads = [&](int64_t tile, bool with_skip) {
         const int64_t row = tile * RPB + slot;
         if (row < a.rows) {
-            const int64_t srow = bcast ? row % a.skip_rows : row;
+            // 32-bit remainder whenever the row count fits (always, in practice).
+            const int64_t srow = !bcast ? row
+                                 : (small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) %
+                                                                      static_cast<uint32_t>(a.skip_rows))
+                                               : row % a.skip_rows);
             const u32x4* xp = X + row * hv + lt;
             const u32x4* sp = S + srow * hv + lt;
 #pragma unroll
@@ -251,14 +281,24 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                 if (ok[k]) {
                     xr[k] = __builtin_nontemporal_load(xp + k * G);
                     // The broadcast skip is re-read by every batch: keep it cached.
-                    sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
+                    if (with_skip) sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
                 }
             }
         }
     };
 
+    // Order of the first loads (measured): a block that handles one tile
+    // needs bias as soon as x and skip arrive, so parameters go first; a
+    // long-lived skip-stationary block gets its first tile moving first.
     int64_t tile = t_first;
-    if (tile < t_end) issue_loads(tile);
+    if (stationary) {
+        if (tile < t_end) issue_loads(tile, true);
+        load_params();
+    } else {
+        load_params();
+        if (tile < t_end) issue_loads(tile, true);
+    }
+
     int parity = 0;
 
     for (; tile < t_end; tile += stride) {
@@ -296,7 +336,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
 
         // Registers of x/skip are free again: start the next tile's loads.
-        if (tile + stride < t_end) issue_loads(tile + stride);
+        if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
 
         if (R != nullptr && live) {
             u32x4* rp = R + row * hv + lt;
@@ -478,8 +518,7 @@ constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 // Short rows are latency bound: one chunk per lane spreads a row over more
 // lanes and shortens the per-lane load/reduce chain.  Long rows use 256-lane
 // groups (4 wavefronts; 1024-lane groups pay for 16-wavefront barriers).
-// With a broadcast skip, two rows per block share one block's registers of
-// gamma/beta on a persistent grid.
+// A broadcast skip uses the same geometries with skip-stationary tiling.
 struct AutoEntry {
     int max_chunks, geom;
 };
@@ -489,7 +528,7 @@ constexpr AutoEntry kAutoExact[] = {
 };
 constexpr AutoEntry kAutoBroadcast[] = {
     {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
-    {768, 7}, {1024, 18}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+    {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
 };
 
 hipError_t cu_count(int* out) {
@@ -549,21 +588,39 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     const int64_t rpb = g.block / g.g;
     const int64_t tiles = (a0.rows + rpb - 1) / rpb;
     Args a = a0;
+    int mode = tiling.mode;
     int64_t per = tiling.tiles_per_block;
-    a.strided = tiling.strided ? 1 : 0;
+    // Skip-stationary needs a broadcast skip whose rows split into whole tiles.
+    if (mode == kTileSkipStationary && (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > kMaxGrid))
+        mode = kTileStrided;
+    int64_t resident = 0;
     if (per <= 0) {
-        // Persistent: one wave of resident blocks walks all tiles, strided.
-        int64_t resident = 0;
         const hipError_t e = resident_blocks(kernel, g.block, &occ, &resident);
         if (e != hipSuccess) return e;
-        per = (tiles + resident - 1) / resident;
-        a.strided = 1;
     }
-    if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
+    int64_t blocks = 1;
+    if (mode == kTileSkipStationary) {
+        const int64_t P = a.skip_rows / rpb;
+        const int64_t batches = a.rows / a.skip_rows;
+        if (per <= 0) {
+            // Enough batch chunks per tile column to fill the resident grid.
+            const int64_t chunks = resident > P ? resident / P : 1;
+            per = (batches + chunks - 1) / chunks;
+        }
+        if (P * ((batches + per - 1) / per) > kMaxGrid) per = (batches * P + kMaxGrid - 1) / kMaxGrid;
+        blocks = P * ((batches + per - 1) / per);
+    } else {
+        if (per <= 0) {
+            // Persistent: one wave of resident blocks walks all tiles, strided.
+            per = (tiles + resident - 1) / resident;
+            mode = kTileStrided;
+        }
+        if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
+        blocks = (tiles + per - 1) / per;
+    }
     a.tiles_per_block = per;
-    int64_t blocks = (tiles + per - 1) / per;
-    if (blocks < 1) blocks = 1;
-    return launch_grid(kernel, g.block, blocks, a, st);
+    a.tiling = mode;
+    return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);
 }
 
 template <typename T, int... I>
