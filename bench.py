@@ -29,7 +29,9 @@ METRIC = "SkipLayerNorm rows/s and achieved HBM GB/s (% of MI355X peak) at H=768
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 HEADLINE = "bert_base_8x128x768_f32"
-SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_mean100"]
+SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_mean100",
+         "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16"]
+OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2}  # SKIPLN_OP_*
 KERNEL_SRC = os.path.join(ROOT, "transformer_residual_add_amd", "csrc", "skipln_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -100,7 +102,8 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     from transformer_residual_add_amd import workloads as W
 
     code = L.F32 if w.dtype == "f32" else L.F16
-    kernel = T.select_kernel(w.hidden, code, True, variant, L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT)
+    op = OPS[w.op]
+    kernel = T.select_kernel(w.hidden, code, True, variant, L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT, op)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.
@@ -121,7 +124,8 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     def step(i: int, stream: int):
         d = dev.sets[i % n_sets]
         T.forward_raw(ptr(d["input"]), ptr(d["skip"]), mode, srows, ptr(d["gamma"]), ptr(d["beta"]),
-                      ptr(d["bias"]), ptr(d["out"]), ptr(d["res"]), w.rows, w.hidden, eps, code, stream, variant)
+                      ptr(d["bias"]), ptr(d["out"]), ptr(d["res"]), w.rows, w.hidden, eps, code, stream, variant,
+                      op)
 
     main = torch.cuda.current_stream()
     for i in range(warmup):
@@ -159,6 +163,7 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     traffic = counter_traffic(kernel, w.name)
     res = {
         "workload": w.name,
+        "op": w.op,
         "rows": w.rows,
         "hidden": w.hidden,
         "dtype": w.dtype,
@@ -219,8 +224,13 @@ def cpu_baseline(w, seconds: float):
     reps, rows = 0, 0
     t0 = time.perf_counter()
     while True:
-        O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"], w.eps,
-                          broadcast=w.broadcast, residual=w.residual, threads=threads)
+        if w.op == "bias_add":
+            threads = 1  # the oracle's BiasAdd is a single loop
+            O.bias_add(inputs["input"], inputs["bias"], inputs["skip"])
+        else:
+            O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"],
+                              w.eps, broadcast=w.broadcast, residual=w.residual, threads=threads,
+                              simplified=w.op == "simplified")
         reps += 1
         rows += w.rows
         el = time.perf_counter() - t0
@@ -270,14 +280,14 @@ def main(argv=None) -> int:
         print(json.dumps({"copy": time_copy(args.copy_bytes, args.steps, args.warmup)}), flush=True)
         return 0
 
-    w = W.WORKLOADS[args.workload]
+    w = W.get(args.workload)
     head = time_workload(w, args.steps, args.warmup, args.launch, args.variant)
     sweep = []
     if not args.no_sweep:
         for name in SWEEP:
             if name == w.name:
                 continue
-            big = W.WORKLOADS[name]
+            big = W.get(name)
             steps = max(5, min(args.steps, int(2.0 / max(big.algorithmic_bytes() / 5e12, 1e-9))))
             sweep.append(time_workload(big, steps, min(args.warmup, 10), args.launch, args.variant))
     base = None
@@ -317,7 +327,7 @@ def main(argv=None) -> int:
         "roofline": head["roofline"],
         "cpu_baseline": base,
         "sweep": [
-            {k: r[k] for k in ("workload", "rows", "hidden", "dtype", "kernel", "rows_per_s", "launch_us",
+            {k: r[k] for k in ("workload", "op", "rows", "hidden", "dtype", "kernel", "rows_per_s", "launch_us",
                                "roofline", "buffer_sets")}
             for r in sweep
         ],

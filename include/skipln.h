@@ -75,8 +75,17 @@ enum {
     SKIPLN_ERR_UNSUPPORTED = 7, /* a forced variant cannot run this shape */
     SKIPLN_ERR_LAUNCH = 8,      /* the HIP runtime refused the launch */
     SKIPLN_ERR_DEVICE = 9,      /* querying the current device failed */
-    SKIPLN_ERR_VARIANT = 10     /* unknown variant id */
+    SKIPLN_ERR_VARIANT = 10,    /* unknown variant, geometry or tiling */
+    SKIPLN_ERR_OP = 11          /* unknown operation */
 };
+
+/* Operations sharing the row kernels (for the _variant / _config / validate /
+ * select calls).  SKIPLN_OP_SIMPLIFIED is the root-mean-square form selected
+ * by the `simplified` template input of every SkipLayerNormalization variant
+ * (the manifest sets it false and does not spell it out; reading used here:
+ * no mean subtraction, the mean square in place of the variance).
+ * SKIPLN_OP_BIAS_ADD is the BiasAdd operator (com.microsoft BiasAdd manifest). */
+enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 2 };
 
 /* Kernel families, for skipln_forward_variant / skipln_select. */
 enum {
@@ -117,10 +126,34 @@ int skipln_forward(const void* input, const void* skip, int skip_mode, int64_t s
                    void* out, void* residual_out, int64_t rows, int64_t hidden,
                    float eps, int dtype, skipln_stream_t stream);
 
-/* skipln_forward with the kernel family forced (SKIPLN_VARIANT_*); the result
- * is the same operator.  Returns SKIPLN_ERR_UNSUPPORTED when the family cannot
- * run the shape or alignment. */
-int skipln_forward_variant(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+/*
+ * Root-mean-square ("simplified") form of skipln_forward, same arguments:
+ * s as above, ms = sum_c s[r,c]^2 / hidden,
+ * out[r,c] = s[r,c] / sqrt(ms + eps) * gamma[c] + beta[c] (beta optional).
+ * Source: the `simplified` template input of the SkipLayerNormalization
+ * manifest's variants (always false there; semantics inferred).
+ */
+int skipln_forward_simplified(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                              const void* gamma, const void* beta, const void* bias,
+                              void* out, void* residual_out, int64_t rows, int64_t hidden,
+                              float eps, int dtype, skipln_stream_t stream);
+
+/*
+ * BiasAdd (com.microsoft BiasAdd manifest, `description`, `inputs`,
+ * `outputs[Y]`): Y = (X + bias) + skip elementwise, the channel bias added to
+ * X first and the skip second, each add in IEEE binary32, Y rounded once to T.
+ * x, skip, y: rows x channels (an (N, S, C) tensor with rows = N*S), bias:
+ * channels.  y may equal x or skip exactly; other overlaps are an error.
+ */
+int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, int64_t rows, int64_t channels,
+                    int dtype, skipln_stream_t stream);
+
+/* Operation `op` (SKIPLN_OP_*) with the kernel family forced
+ * (SKIPLN_VARIANT_*); the result is the same operator.  For
+ * SKIPLN_OP_BIAS_ADD, gamma, beta, residual_out and eps are ignored, bias is
+ * required and the skip must be exact.  Returns SKIPLN_ERR_UNSUPPORTED when
+ * the family cannot run the shape or alignment. */
+int skipln_forward_variant(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                            const void* gamma, const void* beta, const void* bias,
                            void* out, void* residual_out, int64_t rows, int64_t hidden,
                            float eps, int dtype, int variant, skipln_stream_t stream);
@@ -135,7 +168,7 @@ enum {
                                        otherwise as SKIPLN_TILE_STRIDED */
 };
 
-/* skipln_forward with an explicit launch configuration, for tuning; the
+/* Operation `op` with an explicit launch configuration, for tuning; the
  * result is the same operator.  geometry: row-tile geometry
  * (0 <= geometry < skipln_rowtile_geometries()), or -1 for the automatic
  * choice.  tiles_per_block (T) > 0: row tiles (batches, for
@@ -145,24 +178,24 @@ enum {
  * SKIPLN_ERR_UNSUPPORTED when the geometry cannot hold the row or the tensors
  * are not 16-byte aligned, SKIPLN_ERR_SHAPE for tiles_per_block < 0,
  * SKIPLN_ERR_VARIANT for an unknown geometry or tiling. */
-int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+int skipln_forward_config(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                           const void* gamma, const void* beta, const void* bias,
                           void* out, void* residual_out, int64_t rows, int64_t hidden,
                           float eps, int dtype, int geometry, int64_t tiles_per_block, int tiling,
                           skipln_stream_t stream);
 
-/* The argument checks of skipln_forward alone: host code only, no HIP call,
+/* The argument checks of operation `op` alone: host code only, no HIP call,
  * no pointer is dereferenced. */
-int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+int skipln_validate(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                     const void* gamma, const void* beta, const void* bias,
                     const void* out, const void* residual_out, int64_t rows, int64_t hidden,
                     float eps, int dtype);
 
-/* Kernel that skipln_forward_variant would launch for this hidden size and
- * skip form: returns a kernel id >= 0 (name via skipln_kernel_name) or a
- * negative status code.  `aligned16` says whether every tensor pointer is
- * 16-byte aligned. */
-int skipln_select(int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
+/* Kernel that skipln_forward_variant would launch for this operation, hidden
+ * size and skip form: returns a kernel id >= 0 (name via skipln_kernel_name)
+ * or a negative status code.  `aligned16` says whether every tensor pointer
+ * is 16-byte aligned. */
+int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
 
 /* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte
  * aligned, bytes % 16 == 0, no overlap), with the access pattern of the
@@ -176,8 +209,9 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 /* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
 int skipln_rowtile_geometries(void);
 
-/* Stable name of a kernel id ("generic_f32", "rowtile_f16_g256_c4", ...);
- * "unknown" for an invalid id. */
+/* Stable name of a kernel id ("generic_f32", "rowtile_f16_g256_c4",
+ * "rms_rowtile_f32_g192_c1_b192", "biasadd_generic_f16", ...); "unknown" for
+ * an invalid id. */
 const char* skipln_kernel_name(int kernel_id);
 
 /* Static description of a status code. */

@@ -18,6 +18,7 @@ from transformer_residual_add_amd import _lib as L
 from oracle import oracle as O
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 2e-3)}
+OPS = {"layer_norm": L.OP_LAYER_NORM, "simplified": L.OP_SIMPLIFIED, "bias_add": L.OP_BIAS_ADD}
 
 
 def torch_dtype(dt: str):
@@ -79,13 +80,13 @@ class DeviceCase:
         T.forward_raw(p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
                       w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
                       w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
-                      stream, variant)
+                      stream, variant, OPS[w.op])
 
     def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0):
         w = self.w
         p = lambda t: None if t is None else t.data_ptr()
         st = L.load().skipln_forward_config(
-            p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
+            OPS[w.op], p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
             w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(self.out), p(self.res),
             w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16, geometry,
             tiles_per_block, strided, stream or None)
@@ -99,8 +100,25 @@ class DeviceCase:
 
 
 def oracle_rows(w, inputs, row_offset: int = 0, threads: int = 8):
+    """The oracle's result for ``w.op``: {"y": binary64 output, "residual": T}
+    for the normalizations; {"y": Y in T (BiasAdd's output is exact)}."""
+    if w.op == "bias_add":
+        y, _ = O.bias_add(inputs["input"], inputs["bias"], inputs["skip"])
+        return {"y": y, "residual": None}
     return O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"],
-                             w.eps, broadcast=w.broadcast, row_offset=row_offset, residual=True, threads=threads)
+                             w.eps, broadcast=w.broadcast, row_offset=row_offset, residual=True, threads=threads,
+                             simplified=w.op == "simplified")
+
+
+def compare(w, got_out, got_res, ref):
+    """BiasAdd: output bit for bit.  Normalizations: output within tolerance
+    of the binary64 value, residual bit for bit when emitted."""
+    if w.op == "bias_add":
+        assert_bits_equal(got_out, ref["y"], "bias_add output")
+        return
+    assert_out_close(got_out, ref["y"], w.dtype)
+    if got_res is not None:
+        assert_bits_equal(got_res, ref["residual"])
 
 
 def assert_out_close(got: np.ndarray, want: np.ndarray, dt: str, what: str = "out"):
@@ -136,7 +154,5 @@ def check_case(w, variant: int = L.VARIANT_AUTO, offset_elems: int = 0, inputs=N
     dc = DeviceCase(w, inputs, residual=w.residual, offset_elems=offset_elems)
     dc.run(variant)
     ref = oracle_rows(w, inputs)
-    assert_out_close(dc.host(dc.out), ref["y"], w.dtype)
-    if w.residual:
-        assert_bits_equal(dc.host(dc.res), ref["residual"])
+    compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, ref)
     return dc, ref

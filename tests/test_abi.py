@@ -39,7 +39,9 @@ def test_header_enums_match_binding():
         "SKIPLN_ERR_DTYPE": L.ERR_DTYPE, "SKIPLN_ERR_MODE": L.ERR_MODE, "SKIPLN_ERR_EPS": L.ERR_EPS,
         "SKIPLN_ERR_ALIAS": L.ERR_ALIAS, "SKIPLN_ERR_UNSUPPORTED": L.ERR_UNSUPPORTED,
         "SKIPLN_ERR_LAUNCH": L.ERR_LAUNCH, "SKIPLN_ERR_DEVICE": L.ERR_DEVICE,
-        "SKIPLN_ERR_VARIANT": L.ERR_VARIANT,
+        "SKIPLN_ERR_VARIANT": L.ERR_VARIANT, "SKIPLN_ERR_OP": L.ERR_OP,
+        "SKIPLN_OP_LAYER_NORM": L.OP_LAYER_NORM, "SKIPLN_OP_SIMPLIFIED": L.OP_SIMPLIFIED,
+        "SKIPLN_OP_BIAS_ADD": L.OP_BIAS_ADD,
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
@@ -50,7 +52,7 @@ def test_header_enums_match_binding():
 
 
 def test_status_strings():
-    for st in range(0, 11):
+    for st in range(0, 12):
         assert L.status_string(st) not in ("", "unknown status")
     assert L.status_string(99) == "unknown status"
 
@@ -60,8 +62,8 @@ IN, SK, GA, BE, BI, OUT, RES = (0x100000 * k for k in range(1, 8))
 
 
 def V(input=IN, skip=SK, mode=0, skip_rows=0, gamma=GA, beta=BE, bias=BI, out=OUT, res=RES, rows=4, hidden=8,
-      eps=1e-5, dtype=0):
-    return L.load().skipln_validate(input, skip, mode, skip_rows, gamma, beta, bias, out, res, rows, hidden, eps,
+      eps=1e-5, dtype=0, op=L.OP_LAYER_NORM):
+    return L.load().skipln_validate(op, input, skip, mode, skip_rows, gamma, beta, bias, out, res, rows, hidden, eps,
                                     dtype)
 
 
@@ -104,6 +106,23 @@ def test_validate_rejects(kw, status):
     assert V(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=3), L.ERR_OP),
+    (dict(op=-1), L.ERR_OP),
+    (dict(op=L.OP_SIMPLIFIED, gamma=None), L.ERR_NULL),
+    (dict(op=L.OP_SIMPLIFIED), L.OK),
+    (dict(op=L.OP_BIAS_ADD), L.OK),
+    (dict(op=L.OP_BIAS_ADD, gamma=None, beta=None, res=None, eps=-1.0), L.OK),  # ignored by BiasAdd
+    (dict(op=L.OP_BIAS_ADD, bias=None), L.ERR_NULL),
+    (dict(op=L.OP_BIAS_ADD, mode=1, skip_rows=2), L.ERR_MODE),
+    (dict(op=L.OP_BIAS_ADD, out=BI), L.ERR_ALIAS),
+    (dict(op=L.OP_BIAS_ADD, out=IN), L.OK),
+    (dict(op=L.OP_BIAS_ADD, out=SK), L.OK),
+])
+def test_validate_operations(kw, status):
+    assert V(**kw) == status
+
+
 def test_validate_rows_zero_is_a_noop_even_with_null_pointers():
     assert V(rows=0, input=None, skip=None, gamma=None, out=None) == L.OK
 
@@ -117,7 +136,7 @@ def test_validate_allows_exact_aliasing():
 
 def test_select_kernels():
     lib = L.load()
-    sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT: lib.skipln_select(h, dt, mode, al, v)
+    sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT, op=L.OP_LAYER_NORM: lib.skipln_select(op, h, dt, mode, al, v)
     name = lambda kid: L.kernel_name(kid)
     assert name(sel(768, 0)) == "rowtile_f32_g192_c1_b192"
     assert name(sel(1024, 1)) == "rowtile_f16_g128_c1"
@@ -143,6 +162,10 @@ def test_select_kernels():
     assert sel(64, 5) == -L.ERR_DTYPE
     assert sel(0, 0) == -L.ERR_SHAPE
     assert sel(64, 0, mode=3) == -L.ERR_MODE
+    assert sel(64, 0, op=7) == -L.ERR_OP
+    assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
+    assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
+    assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_generic_f16"
     assert L.kernel_name(-1) == "unknown" and L.kernel_name(10 ** 6) == "unknown"
 
 
@@ -153,13 +176,13 @@ def test_auto_choice_holds_every_hidden_size():
     for dt, v in ((0, 4), (1, 8)):
         for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST):
             for hv in range(1, 4097):
-                kid = lib.skipln_select(hv * v, dt, mode, 1, 0)
+                kid = lib.skipln_select(L.OP_LAYER_NORM, hv * v, dt, mode, 1, 0)
                 assert kid >= 0 and L.kernel_name(kid).startswith("rowtile_"), (dt, mode, hv)
                 n = L.kernel_name(kid)
                 g = int(n.split("_g")[1].split("_")[0])
                 c = int(n.split("_c")[1].split("_")[0])
                 assert g * c >= hv
-            assert L.kernel_name(lib.skipln_select(4097 * v, dt, mode, 1, 0)).startswith("generic_")
+            assert L.kernel_name(lib.skipln_select(L.OP_LAYER_NORM, 4097 * v, dt, mode, 1, 0)).startswith("generic_")
 
 
 def test_no_cpu_fallback_in_product_path():

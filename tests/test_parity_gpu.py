@@ -131,9 +131,11 @@ def test_hidden_sizes(dt, hidden):
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("geom", list(range(32)))
 @pytest.mark.parametrize("ragged", [False, True])
-def test_every_geometry(dt, geom, ragged):
-    """Each row-tile geometry at its full capacity and one chunk short of it,
-    with a ragged last tile of rows."""
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add"])
+def test_every_geometry(dt, geom, ragged, op):
+    """Each row-tile geometry, for each operation, at its full capacity and
+    one chunk short of it, with a ragged last tile of rows."""
+    op_code = U.OPS[op]
     lib = L.load()
     if geom >= lib.skipln_rowtile_geometries():
         pytest.skip("geometry not present")
@@ -142,16 +144,17 @@ def test_every_geometry(dt, geom, ragged):
     # capacity in chunks: the largest hidden size the geometry accepts
     cap = 0
     for hv in range(1, 4097):
-        if lib.skipln_select(hv * v, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom) < 0:
+        if lib.skipln_select(L.OP_LAYER_NORM, hv * v, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom) < 0:
             break
         cap = hv
     hidden = (cap - 1 if ragged and cap > 1 else cap) * v
-    name = L.kernel_name(lib.skipln_select(hidden, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom))
+    name = L.kernel_name(lib.skipln_select(op_code, hidden, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom))
     g = int(name.split("_g")[1].split("_")[0])
     block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
     rpb = block // g
     rows = 3 * rpb + 1
-    w = W.small_case(rows, hidden, dt, beta=True, bias=ragged, residual=True, eps=1e-5, seed=geom * 7 + ragged)
+    w = W.small_case(rows, hidden, dt, beta=True, bias=ragged, residual=True, eps=1e-5, seed=geom * 7 + ragged,
+                     op=op)
     U.note(f"geometry {geom} ({name}) H={hidden} rows={rows}")
     U.check_case(w, variant=L.VARIANT_GEOMETRY + geom)
 
@@ -250,6 +253,89 @@ def test_streaming_copy(nbytes):
     assert torch.equal(src, dst)
     assert L.load().skipln_copy(dst.data_ptr() + 8, src.data_ptr(), 16, None) == L.ERR_SHAPE
     assert L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), 24, None) == L.ERR_SHAPE
+
+
+# ------------------------------------------------- simplified and BiasAdd --
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("hidden", [1, 7, 64, 768, 1000, 1024, 4096, 8192, 20000])
+@pytest.mark.parametrize("flags", [(True, True, True, False), (False, False, False, False),
+                                   (True, False, True, True), (False, True, False, True)],
+                         ids=lambda f: "b%d_bi%d_r%d_bc%d" % tuple(map(int, f)))
+def test_simplified(dt, hidden, flags):
+    beta, bias, residual, bcast = flags
+    w = W.small_case(24, hidden, dt, skip_rows=4 if bcast else None, beta=beta, bias=bias, residual=residual,
+                     eps=1e-6, seed=hidden + 5, op="simplified")
+    U.note(f"simplified {dt} H={hidden} flags={flags}")
+    U.check_case(w)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("hidden", [1, 3, 8, 64, 768, 1000, 1024, 4096, 8192, 20000])
+@pytest.mark.parametrize("rows", [1, 37, 1000])
+def test_bias_add(dt, hidden, rows):
+    w = W.small_case(rows, hidden, dt, seed=hidden + rows, op="bias_add")
+    U.note(f"bias_add {dt} H={hidden} rows={rows}")
+    U.check_case(w)
+
+
+@pytest.mark.parametrize("op", ["simplified", "bias_add"])
+@pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_ROWTILE])
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_new_ops_forced_variants(op, variant, dt):
+    w = W.small_case(40, 1024, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=8, op=op)
+    U.check_case(w, variant=variant)
+
+
+@pytest.mark.parametrize("op", ["simplified", "bias_add"])
+def test_new_ops_misaligned(op):
+    w = W.small_case(20, 1024, "f16", beta=True, bias=True, residual=True, eps=1e-5, seed=9, op=op)
+    U.check_case(w, offset_elems=1)
+
+
+@pytest.mark.parametrize("name", list(W.EXTRA))
+def test_extra_workloads(name):
+    w = W.EXTRA[name]
+    U.note(f"workload {name}")
+    if w.rows * w.hidden > 50_000_000:
+        w = w.with_(shape=(2048, w.hidden) if len(w.shape) == 2 else (4,) + w.shape[1:],
+                    skip_shape=(2048, w.hidden) if len(w.shape) == 2 else (4,) + w.shape[1:])
+    U.check_case(w)
+
+
+def test_bias_add_in_place_and_wrapper():
+    import torch
+
+    w = W.small_case(64, 768, "f32", seed=3, op="bias_add")
+    inputs = W.make_inputs(w)
+    ref = U.oracle_rows(w, inputs)
+    x = torch.from_numpy(inputs["input"]).cuda().view(4, 16, 768)
+    sk = torch.from_numpy(inputs["skip"]).cuda().view(4, 16, 768)
+    b = torch.from_numpy(inputs["bias"]).cuda()
+    y = T.bias_add(x, b, sk)
+    torch.cuda.synchronize()
+    U.assert_bits_equal(y.cpu().numpy().reshape(64, 768), ref["y"])
+    T.bias_add(x, b, sk, out=x)  # in place over X
+    torch.cuda.synchronize()
+    U.assert_bits_equal(x.cpu().numpy().reshape(64, 768), ref["y"])
+    with pytest.raises(ValueError):
+        T.bias_add(x, b, sk[:2])
+    with pytest.raises(ValueError):
+        T.bias_add(x, b[:5], sk)
+
+
+def test_simplified_wrapper():
+    import torch
+
+    w = W.small_case(32, 1024, "f16", beta=False, bias=True, residual=True, eps=1e-6, seed=4, op="simplified")
+    inputs = W.make_inputs(w)
+    ref = U.oracle_rows(w, inputs)
+    d = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inputs.items()}
+    out, res = T.skip_layer_norm(d["input"], d["skip"], d["gamma"], None, d["bias"], epsilon=w.eps,
+                                 return_residual=True, simplified=True)
+    torch.cuda.synchronize()
+    U.assert_out_close(out.cpu().numpy(), ref["y"], "f16")
+    U.assert_bits_equal(res.cpu().numpy(), ref["residual"])
 
 
 # ------------------------------------------------------------ edge cases --

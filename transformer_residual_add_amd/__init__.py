@@ -18,24 +18,24 @@ from ._lib import SkiplnError  # noqa: F401
 # (SkipLayerNormalization manifest, `attributes.epsilon`).
 DEFAULT_EPSILON = 9.999999960041972e-13
 
-__all__ = ["skip_layer_norm", "forward_raw", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
+__all__ = ["skip_layer_norm", "bias_add", "forward_raw", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
 
 
-def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: int,
+def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: Optional[int],
                 beta_ptr: Optional[int], bias_ptr: Optional[int], out_ptr: int, residual_ptr: Optional[int],
                 rows: int, hidden: int, eps: float, dtype: int, stream: int = 0,
-                variant: int = _lib.VARIANT_AUTO) -> None:
+                variant: int = _lib.VARIANT_AUTO, op: int = _lib.OP_LAYER_NORM) -> None:
     """``skipln_forward_variant`` on raw device pointers; raises SkiplnError."""
     st = _lib.load().skipln_forward_variant(
-        input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr, beta_ptr or None, bias_ptr or None, out_ptr,
-        residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
+        op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
+        out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
     _lib.check(st, "skipln_forward")
 
 
 def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO,
-                  skip_mode: int = _lib.SKIP_EXACT) -> str:
-    """Name of the kernel a call with this hidden size and skip form would launch."""
-    kid = _lib.load().skipln_select(hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
+                  skip_mode: int = _lib.SKIP_EXACT, op: int = _lib.OP_LAYER_NORM) -> str:
+    """Name of the kernel a call with this operation, hidden size and skip form would launch."""
+    kid = _lib.load().skipln_select(op, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
     if kid < 0:
         raise SkiplnError(-kid, "skipln_select")
     return _lib.kernel_name(kid)
@@ -51,21 +51,7 @@ def _dtype_code(t) -> int:
     raise TypeError(f"SkipLayerNormalization supports float32 and float16, got {t.dtype}")
 
 
-def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = DEFAULT_EPSILON, *,
-                    return_residual: bool = False, out=None, residual_out=None, stream=None,
-                    variant: int = _lib.VARIANT_AUTO):
-    """SkipLayerNormalization on CUDA (HIP) tensors.
-
-    input: (N, S, H) or (rows, H).  skip: the input's shape, or for rank-3
-    input (1, S, H) or (S, H), broadcast over the batch.  gamma (H), optional
-    beta (H) and bias (H).  All tensors contiguous, of one dtype (float32 or
-    float16), on one device.  Returns ``out``, or ``(out, residual)`` with
-    ``return_residual=True`` (the input_skip_bias_sum output).
-    """
-    import torch
-
-    tensors = [t for t in (input, skip, gamma, beta, bias, out, residual_out) if t is not None]
-    code = _dtype_code(input)
+def _check_tensors(input, tensors):
     for t in tensors:
         if t.dtype != input.dtype:
             raise TypeError("all tensors must share one dtype")
@@ -73,6 +59,34 @@ def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = D
             raise ValueError("all tensors must be on the same GPU")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _stream_handle(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = DEFAULT_EPSILON, *,
+                    return_residual: bool = False, out=None, residual_out=None, stream=None,
+                    variant: int = _lib.VARIANT_AUTO, simplified: bool = False):
+    """SkipLayerNormalization on CUDA (HIP) tensors.
+
+    input: (N, S, H) or (rows, H).  skip: the input's shape, or for rank-3
+    input (1, S, H) or (S, H), broadcast over the batch.  gamma (H), optional
+    beta (H) and bias (H).  All tensors contiguous, of one dtype (float32 or
+    float16), on one device.  Returns ``out``, or ``(out, residual)`` with
+    ``return_residual=True`` (the input_skip_bias_sum output).
+    ``simplified=True`` selects the root-mean-square form (no mean
+    subtraction, mean square in place of the variance).
+    """
+    import torch
+
+    tensors = [t for t in (input, skip, gamma, beta, bias, out, residual_out) if t is not None]
+    code = _dtype_code(input)
+    _check_tensors(input, tensors)
     if input.dim() not in (2, 3):
         raise ValueError("input must have rank 2 or 3")
     h = input.shape[-1]
@@ -94,15 +108,41 @@ def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = D
         residual_out = torch.empty_like(input)
     if residual_out is not None and residual_out.shape != input.shape:
         raise ValueError("residual_out must have the input's shape")
-    if stream is None:
-        stream = torch.cuda.current_stream(input.device)
-    s = stream if isinstance(stream, int) else stream.cuda_stream
+    s = _stream_handle(stream, input.device)
     with torch.cuda.device(input.device):
         forward_raw(input.data_ptr(), skip.data_ptr(), mode, skip_rows, gamma.data_ptr(),
                     beta.data_ptr() if beta is not None else None,
                     bias.data_ptr() if bias is not None else None, out.data_ptr(),
                     residual_out.data_ptr() if residual_out is not None else None,
-                    rows, h, float(epsilon), code, s, variant)
+                    rows, h, float(epsilon), code, s, variant,
+                    _lib.OP_SIMPLIFIED if simplified else _lib.OP_LAYER_NORM)
     if return_residual:
         return out, residual_out
+    return out
+
+
+def bias_add(X, bias, skip, *, out=None, stream=None, variant: int = _lib.VARIANT_AUTO):
+    """BiasAdd on CUDA (HIP) tensors: ``(X + bias) + skip``.
+
+    X and skip: (N, S, C) (or any shape whose last axis is C), bias: (C,).
+    All tensors contiguous, of one dtype (float32 or float16), on one device.
+    """
+    import torch
+
+    code = _dtype_code(X)
+    _check_tensors(X, [t for t in (X, bias, skip, out) if t is not None])
+    if X.dim() < 1 or tuple(skip.shape) != tuple(X.shape):
+        raise ValueError("skip must have X's shape")
+    c = X.shape[-1]
+    if tuple(bias.shape) != (c,):
+        raise ValueError(f"bias must have shape ({c},)")
+    if out is None:
+        out = torch.empty_like(X)
+    elif out.shape != X.shape:
+        raise ValueError("out must have X's shape")
+    rows = X.numel() // c if c else 0
+    s = _stream_handle(stream, X.device)
+    with torch.cuda.device(X.device):
+        forward_raw(X.data_ptr(), skip.data_ptr(), _lib.SKIP_EXACT, 0, None, None, bias.data_ptr(), out.data_ptr(),
+                    None, rows, c, 0.0, code, s, variant, _lib.OP_BIAS_ADD)
     return out

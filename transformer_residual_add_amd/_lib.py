@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, "libskipln.so")
 F32, F16 = 0, 1
 SKIP_EXACT, SKIP_BROADCAST = 0, 1
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS = 0, 1, 2, 3, 4, 5, 6
-ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT = 7, 8, 9, 10
+ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT, ERR_OP = 7, 8, 9, 10, 11
+OP_LAYER_NORM, OP_SIMPLIFIED, OP_BIAS_ADD = 0, 1, 2
 VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE = 0, 1, 2, 3
 VARIANT_GEOMETRY = 64
 TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
@@ -26,12 +27,15 @@ TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
 _vp, _i64, _i32, _f32 = C.c_void_p, C.c_int64, C.c_int, C.c_float
 SIGNATURES = {
     "skipln_forward": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32, _vp]),
-    "skipln_forward_variant": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
+    "skipln_forward_simplified": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
+                                         _vp]),
+    "skipln_bias_add": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp]),
+    "skipln_forward_variant": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
                                       _i32, _vp]),
-    "skipln_forward_config": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
+    "skipln_forward_config": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
                                      _i32, _i64, _i32, _vp]),
-    "skipln_validate": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32]),
-    "skipln_select": (_i32, [_i64, _i32, _i32, _i32, _i32]),
+    "skipln_validate": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32]),
+    "skipln_select": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "skipln_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "skipln_rowtile_geometries": (_i32, []),
     "skipln_kernel_name": (C.c_char_p, [_i32]),

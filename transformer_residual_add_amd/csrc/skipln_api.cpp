@@ -5,13 +5,13 @@
 // hidden size positive and gamma/beta/bias of length H (`rank2CoreContract`,
 // `betaContract`), all tensors of one element type (`f32MainDtypes`,
 // `f16MainDtypes`), a broadcast skip (S, H) read cyclically by the (N*S) rows
-// (`broadcastSkipShapeOk`, `Params.skipRows`).  Aliasing rules are this
-// library's own: an output may only coincide exactly with a tensor that is
-// read row by row by the lane group that later writes the same row.
+// (`broadcastSkipShapeOk`, `Params.skipRows`).  BiasAdd (com.microsoft BiasAdd
+// manifest, `inputs`) takes X, a length-C bias and a skip of X's shape.
+// Aliasing rules are this library's own: an output may only coincide exactly
+// with a tensor that is read row by row by the lane group that later writes
+// the same row.
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
-
-#include <cmath>
 
 #include "../../include/skipln.h"
 #include "skipln_internal.h"
@@ -19,6 +19,9 @@
 static_assert(SKIPLN_TILE_CONTIGUOUS == skipln::kTileContiguous && SKIPLN_TILE_STRIDED == skipln::kTileStrided &&
                   SKIPLN_TILE_SKIP_STATIONARY == skipln::kTileSkipStationary,
               "tiling modes of the ABI and the kernels agree");
+static_assert(SKIPLN_OP_LAYER_NORM == skipln::kOpLayerNorm && SKIPLN_OP_SIMPLIFIED == skipln::kOpSimplified &&
+                  SKIPLN_OP_BIAS_ADD == skipln::kOpBiasAdd,
+              "operations of the ABI and the kernels agree");
 
 namespace {
 
@@ -32,38 +35,69 @@ Range span(const void* p, int64_t bytes) {
     return Range{a, a + static_cast<uintptr_t>(bytes)};
 }
 
-bool overlap(const Range& a, const Range& b) {
-    return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
-}
+bool overlap(const Range& a, const Range& b) { return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi; }
 
 bool same(const Range& a, const Range& b) { return a.lo == b.lo && a.hi == b.hi; }
 
-int elem_size(int dtype) { return dtype == SKIPLN_F32 ? 4 : 2; }
+bool known_op(int op) { return op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED || op == SKIPLN_OP_BIAS_ADD; }
 
-int validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
-             const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
-             int64_t hidden, float eps, int dtype) {
-    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return SKIPLN_ERR_DTYPE;
-    if (skip_mode != SKIPLN_SKIP_EXACT && skip_mode != SKIPLN_SKIP_BROADCAST) return SKIPLN_ERR_MODE;
-    if (!(eps >= 0.0f)) return SKIPLN_ERR_EPS;  // also rejects NaN
-    if (rows < 0 || hidden <= 0 || hidden > INT32_MAX) return SKIPLN_ERR_SHAPE;
-    const int64_t sz = elem_size(dtype);
-    if (rows > INT64_MAX / hidden / sz) return SKIPLN_ERR_SHAPE;
-    if (skip_mode == SKIPLN_SKIP_BROADCAST) {
-        if (skip_rows <= 0 || rows % skip_rows != 0) return SKIPLN_ERR_SHAPE;
-    }
-    if (rows == 0) return SKIPLN_OK;
-    if (!input || !skip || !gamma || !out) return SKIPLN_ERR_NULL;
+// One call's arguments after the operation's own rules: BiasAdd has no
+// gamma, beta, residual output or epsilon.
+struct Call {
+    int op;
+    const void *input, *skip, *gamma, *beta, *bias;
+    void *out, *residual;
+    int skip_mode;
+    int64_t skip_rows, rows, hidden;
+    float eps;
+    int dtype;
+};
 
-    const bool bcast = skip_mode == SKIPLN_SKIP_BROADCAST;
-    const int64_t row_bytes = hidden * sz;
-    const Range r_in = span(input, rows * row_bytes);
-    const Range r_skip = span(skip, (bcast ? skip_rows : rows) * row_bytes);
-    const Range r_gamma = span(gamma, row_bytes);
-    const Range r_beta = span(beta, beta ? row_bytes : 0);
-    const Range r_bias = span(bias, bias ? row_bytes : 0);
-    const Range r_out = span(out, rows * row_bytes);
-    const Range r_res = span(residual_out, residual_out ? rows * row_bytes : 0);
+Call make_call(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
+               const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
+               int64_t hidden, float eps, int dtype) {
+    const bool bias_add = op == SKIPLN_OP_BIAS_ADD;
+    Call c;
+    c.op = op;
+    c.input = input;
+    c.skip = skip;
+    c.gamma = bias_add ? nullptr : gamma;
+    c.beta = bias_add ? nullptr : beta;
+    c.bias = bias;
+    c.out = const_cast<void*>(out);
+    c.residual = bias_add ? nullptr : const_cast<void*>(residual_out);
+    c.skip_mode = skip_mode;
+    c.skip_rows = skip_rows;
+    c.rows = rows;
+    c.hidden = hidden;
+    c.eps = bias_add ? 0.0f : eps;
+    c.dtype = dtype;
+    return c;
+}
+
+int validate(const Call& c) {
+    if (!known_op(c.op)) return SKIPLN_ERR_OP;
+    if (c.dtype != SKIPLN_F32 && c.dtype != SKIPLN_F16) return SKIPLN_ERR_DTYPE;
+    if (c.skip_mode != SKIPLN_SKIP_EXACT && c.skip_mode != SKIPLN_SKIP_BROADCAST) return SKIPLN_ERR_MODE;
+    if (c.op == SKIPLN_OP_BIAS_ADD && c.skip_mode != SKIPLN_SKIP_EXACT) return SKIPLN_ERR_MODE;
+    if (!(c.eps >= 0.0f)) return SKIPLN_ERR_EPS;  // also rejects NaN
+    if (c.rows < 0 || c.hidden <= 0 || c.hidden > INT32_MAX) return SKIPLN_ERR_SHAPE;
+    const int64_t sz = c.dtype == SKIPLN_F32 ? 4 : 2;
+    if (c.rows > INT64_MAX / c.hidden / sz) return SKIPLN_ERR_SHAPE;
+    const bool bcast = c.skip_mode == SKIPLN_SKIP_BROADCAST;
+    if (bcast && (c.skip_rows <= 0 || c.rows % c.skip_rows != 0)) return SKIPLN_ERR_SHAPE;
+    if (c.rows == 0) return SKIPLN_OK;
+    if (!c.input || !c.skip || !c.out) return SKIPLN_ERR_NULL;
+    if (c.op == SKIPLN_OP_BIAS_ADD ? !c.bias : !c.gamma) return SKIPLN_ERR_NULL;
+
+    const int64_t row_bytes = c.hidden * sz;
+    const Range r_in = span(c.input, c.rows * row_bytes);
+    const Range r_skip = span(c.skip, (bcast ? c.skip_rows : c.rows) * row_bytes);
+    const Range r_gamma = span(c.gamma, c.gamma ? row_bytes : 0);
+    const Range r_beta = span(c.beta, c.beta ? row_bytes : 0);
+    const Range r_bias = span(c.bias, c.bias ? row_bytes : 0);
+    const Range r_out = span(c.out, c.rows * row_bytes);
+    const Range r_res = span(c.residual, c.residual ? c.rows * row_bytes : 0);
 
     for (const Range& o : {r_out, r_res}) {
         if (o.empty()) continue;
@@ -77,9 +111,14 @@ int validate(const void* input, const void* skip, int skip_mode, int64_t skip_ro
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool all_aligned16(const Call& c) {
+    return aligned16(c.input) && aligned16(c.skip) && aligned16(c.gamma) && aligned16(c.beta) && aligned16(c.bias) &&
+           aligned16(c.out) && aligned16(c.residual);
+}
+
 // Kernel id (>= 0) for this variant, or -status.
-int select(int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant) {
-    const int base = dtype * skipln::kIdsPerType;
+int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant) {
+    const int base = (op * 2 + dtype) * skipln::kIdsPerType;
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
     if (variant == SKIPLN_VARIANT_GENERIC) return base + skipln::kGenericIndex;
@@ -100,12 +139,6 @@ int select(int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant) 
     return -SKIPLN_ERR_VARIANT;
 }
 
-bool all_aligned16(const void* input, const void* skip, const void* gamma, const void* beta, const void* bias,
-                   const void* out, const void* residual_out) {
-    return aligned16(input) && aligned16(skip) && aligned16(gamma) && aligned16(beta) && aligned16(bias) &&
-           aligned16(out) && aligned16(residual_out);
-}
-
 // Tiling of the automatic launch.  Streaming rows (exact skip): one tile per
 // block, so blocks are dispatched in address order and the set of rows in
 // flight stays compact; this reached the 2-read/2-write streaming rate on
@@ -118,21 +151,19 @@ skipln::Tiling auto_tiling(bool broadcast) {
     return t;
 }
 
-skipln::Args make_args(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
-                       const void* beta, const void* bias, void* out, void* residual_out, int64_t rows,
-                       int64_t hidden, float eps) {
+skipln::Args make_args(const Call& c) {
     skipln::Args a;
-    a.input = input;
-    a.skip = skip;
-    a.gamma = gamma;
-    a.beta = beta;
-    a.bias = bias;
-    a.out = out;
-    a.residual = residual_out;
-    a.rows = rows;
-    a.skip_rows = skip_mode == SKIPLN_SKIP_BROADCAST ? skip_rows : 0;
-    a.hidden = static_cast<int32_t>(hidden);
-    a.eps = eps;
+    a.input = c.input;
+    a.skip = c.skip;
+    a.gamma = c.gamma;
+    a.beta = c.beta;
+    a.bias = c.bias;
+    a.out = c.out;
+    a.residual = c.residual;
+    a.rows = c.rows;
+    a.skip_rows = c.skip_mode == SKIPLN_SKIP_BROADCAST ? c.skip_rows : 0;
+    a.hidden = static_cast<int32_t>(c.hidden);
+    a.eps = c.eps;
     a.tiles_per_block = 1;
     a.tiling = skipln::kTileStrided;
     return a;
@@ -144,75 +175,83 @@ int status_of(hipError_t e) {
     return SKIPLN_ERR_LAUNCH;
 }
 
+// Validate, choose and launch; `tiling` == nullptr: automatic tiling.
+int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_t stream) {
+    const int st = validate(c);
+    if (st != SKIPLN_OK) return st;
+    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode == SKIPLN_SKIP_BROADCAST, all_aligned16(c), variant);
+    if (id < 0) return -id;
+    if (c.rows == 0) return SKIPLN_OK;
+    const skipln::Args a = make_args(c);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int index = id % skipln::kIdsPerType;
+    if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, c.op, c.dtype, s));
+    const skipln::Tiling t = tiling ? *tiling : auto_tiling(c.skip_mode == SKIPLN_SKIP_BROADCAST);
+    return status_of(skipln::launch_rowtile(a, c.op, c.dtype, index - skipln::kRowtileFirst, t, s));
+}
+
 }  // namespace
 
 extern "C" {
 
-int skipln_validate(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
+int skipln_validate(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
                     const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
                     int64_t hidden, float eps, int dtype) {
-    return validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
-                    dtype);
+    return validate(
+        make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps, dtype));
 }
 
-int skipln_select(int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
+int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
+    if (!known_op(op)) return -SKIPLN_ERR_OP;
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (skip_mode != SKIPLN_SKIP_EXACT && skip_mode != SKIPLN_SKIP_BROADCAST) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(hidden, dtype, skip_mode == SKIPLN_SKIP_BROADCAST, aligned != 0, variant);
+    return select(op, hidden, dtype, skip_mode == SKIPLN_SKIP_BROADCAST, aligned != 0, variant);
 }
 
-int skipln_forward_variant(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+int skipln_forward_variant(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                            const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
-                           int64_t rows, int64_t hidden, float eps, int dtype, int variant,
-                           skipln_stream_t stream) {
-    int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
-                      dtype);
-    if (st != SKIPLN_OK) return st;
-    const bool vec_ok = all_aligned16(input, skip, gamma, beta, bias, out, residual_out);
-    const int id = skipln_select(hidden, dtype, skip_mode, vec_ok ? 1 : 0, variant);
-    if (id < 0) return -id;
-    if (rows == 0) return SKIPLN_OK;
-
-    const skipln::Args a = make_args(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows,
-                                     hidden, eps);
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int index = id % skipln::kIdsPerType;
-    if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, dtype, s));
-    return status_of(skipln::launch_rowtile(a, dtype, index - skipln::kRowtileFirst,
-                                            auto_tiling(skip_mode == SKIPLN_SKIP_BROADCAST), s));
+                           int64_t rows, int64_t hidden, float eps, int dtype, int variant, skipln_stream_t stream) {
+    return run(make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                         dtype),
+               variant, nullptr, stream);
 }
 
-int skipln_forward_config(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+int skipln_forward_config(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                           const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
                           int64_t rows, int64_t hidden, float eps, int dtype, int geometry, int64_t tiles_per_block,
                           int tiling, skipln_stream_t stream) {
-    int st = validate(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
-                      dtype);
-    if (st != SKIPLN_OK) return st;
     if (tiles_per_block < 0) return SKIPLN_ERR_SHAPE;
     if (tiling != SKIPLN_TILE_CONTIGUOUS && tiling != SKIPLN_TILE_STRIDED && tiling != SKIPLN_TILE_SKIP_STATIONARY)
         return SKIPLN_ERR_VARIANT;
-    const bool vec_ok = all_aligned16(input, skip, gamma, beta, bias, out, residual_out);
     if (geometry < -1 || geometry >= skipln::rowtile_count()) return SKIPLN_ERR_VARIANT;
-    const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
-    const int id = skipln_select(hidden, dtype, skip_mode, vec_ok ? 1 : 0, variant);
-    if (id < 0) return -id;
-    if (rows == 0) return SKIPLN_OK;
-    const skipln::Args a = make_args(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows,
-                                     hidden, eps);
     skipln::Tiling t;
     t.tiles_per_block = tiles_per_block;
     t.mode = tiling;
-    return status_of(skipln::launch_rowtile(a, dtype, id % skipln::kIdsPerType - skipln::kRowtileFirst, t,
-                                            reinterpret_cast<hipStream_t>(stream)));
+    const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
+    return run(make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                         dtype),
+               variant, &t, stream);
 }
 
 int skipln_forward(const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
                    const void* beta, const void* bias, void* out, void* residual_out, int64_t rows, int64_t hidden,
                    float eps, int dtype, skipln_stream_t stream) {
-    return skipln_forward_variant(input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows,
-                                  hidden, eps, dtype, SKIPLN_VARIANT_AUTO, stream);
+    return skipln_forward_variant(SKIPLN_OP_LAYER_NORM, input, skip, skip_mode, skip_rows, gamma, beta, bias, out,
+                                  residual_out, rows, hidden, eps, dtype, SKIPLN_VARIANT_AUTO, stream);
+}
+
+int skipln_forward_simplified(const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                              const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
+                              int64_t rows, int64_t hidden, float eps, int dtype, skipln_stream_t stream) {
+    return skipln_forward_variant(SKIPLN_OP_SIMPLIFIED, input, skip, skip_mode, skip_rows, gamma, beta, bias, out,
+                                  residual_out, rows, hidden, eps, dtype, SKIPLN_VARIANT_AUTO, stream);
+}
+
+int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, int64_t rows, int64_t channels,
+                    int dtype, skipln_stream_t stream) {
+    return skipln_forward_variant(SKIPLN_OP_BIAS_ADD, x, skip, SKIPLN_SKIP_EXACT, 0, nullptr, nullptr, bias, y,
+                                  nullptr, rows, channels, 0.0f, dtype, SKIPLN_VARIANT_AUTO, stream);
 }
 
 int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t stream) {
@@ -234,13 +273,14 @@ const char* skipln_status_string(int status) {
         case SKIPLN_ERR_NULL: return "a required pointer is NULL";
         case SKIPLN_ERR_SHAPE: return "invalid shape (rows, hidden or skip_rows)";
         case SKIPLN_ERR_DTYPE: return "unsupported element type";
-        case SKIPLN_ERR_MODE: return "unknown skip mode";
+        case SKIPLN_ERR_MODE: return "unknown or unsupported skip mode";
         case SKIPLN_ERR_EPS: return "epsilon must be a non-negative number";
         case SKIPLN_ERR_ALIAS: return "an output overlaps an input or the other output";
         case SKIPLN_ERR_UNSUPPORTED: return "the forced kernel family cannot run this shape or alignment";
         case SKIPLN_ERR_LAUNCH: return "kernel launch failed";
         case SKIPLN_ERR_DEVICE: return "no usable HIP device";
-        case SKIPLN_ERR_VARIANT: return "unknown variant";
+        case SKIPLN_ERR_VARIANT: return "unknown variant, geometry or tiling";
+        case SKIPLN_ERR_OP: return "unknown operation";
         default: return "unknown status";
     }
 }

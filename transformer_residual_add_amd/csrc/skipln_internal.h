@@ -38,7 +38,14 @@ struct Tiling {
     int mode;                 // kTile*
 };
 
-// Kernel ids: dtype * kIdsPerType + index, index 0 = generic, 1.. = row tiles.
+// Operations sharing the row kernels.
+constexpr int kOpLayerNorm = 0;   // SkipLayerNormalization
+constexpr int kOpSimplified = 1;  // its root-mean-square ("simplified") form
+constexpr int kOpBiasAdd = 2;     // BiasAdd: (x + bias) + skip, no normalization
+constexpr int kNumOps = 3;
+
+// Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
+// 1.. = row tiles.
 constexpr int kIdsPerType = 32;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
@@ -53,8 +60,8 @@ bool rowtile_holds(int geometry, int64_t hidden, int dtype);
 const char* kernel_name(int kernel_id);
 
 // Enqueue one kernel; return 0 or a hipError_t value.
-hipError_t launch_generic(const Args& a, int dtype, hipStream_t stream);
-hipError_t launch_rowtile(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t stream);
+hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln

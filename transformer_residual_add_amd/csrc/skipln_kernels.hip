@@ -177,8 +177,9 @@ __device__ __forceinline__ float wave_elems(int hv, int w) {
     return static_cast<float>(n * V);
 }
 
-template <typename T, int G, int CH, int BLOCK>
+template <typename T, int OP, int G, int CH, int BLOCK>
 __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
+    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd, "operation");
     using E = Elem<T>;
     constexpr int V = E::kPerChunk;
     constexpr int RPB = BLOCK / G;                  // rows per block per tile
@@ -220,8 +221,10 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         for (int k = 0; k < CH; ++k) {
             const int c = k * G + lt;
             if (ok[k]) {
-                gam[k] = static_cast<const u32x4*>(a.gamma)[c];
-                if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
+                if constexpr (OP != kOpBiasAdd) {
+                    gam[k] = static_cast<const u32x4*>(a.gamma)[c];
+                    if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
+                }
                 if (has_bias) bia[k] = static_cast<const u32x4*>(a.bias)[c];
             }
         }
@@ -314,7 +317,8 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             }
         }
 
-        // s = (x + skip) + bias in binary32, and this lane's partial sum.
+        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip), and
+        // this lane's partial sum (sum of squares for the simplified form).
         float s[CH][V];
         float part = 0.0f;
 #pragma unroll
@@ -325,18 +329,40 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             E::widen(bia[k], bf);
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                float v = xf[e] + sf[e];
-                if (has_bias) v = v + bf[e];
+                float v;
+                if constexpr (OP == kOpBiasAdd) {
+                    v = xf[e] + bf[e];
+                    v = v + sf[e];
+                } else {
+                    v = xf[e] + sf[e];
+                    if (has_bias) v = v + bf[e];
+                }
                 s[k][e] = v;
             }
             if (ok[k]) {
 #pragma unroll
-                for (int e = 0; e < V; ++e) part += s[k][e];
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (OP == kOpSimplified)
+                        part += s[k][e] * s[k][e];
+                    else
+                        part += s[k][e];
+                }
             }
         }
 
         // Registers of x/skip are free again: start the next tile's loads.
         if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
+
+        if constexpr (OP == kOpBiasAdd) {
+            // BiasAdd ends here: the sum is the output.
+            if (live) {
+                u32x4* op = O + row * hv + lt;
+#pragma unroll
+                for (int k = 0; k < CH; ++k)
+                    if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), op + k * G);
+            }
+            continue;
+        }
 
         if (R != nullptr && live) {
             u32x4* rp = R + row * hv + lt;
@@ -346,7 +372,22 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
 
         float mean, var;
-        if constexpr (WPR == 1) {
+        if constexpr (OP == kOpSimplified) {
+            // Root mean square: no mean; the mean square takes the variance's place.
+            mean = 0.0f;
+            if constexpr (WPR == 1) {
+                var = group_sum<G>(part) / h;
+            } else {
+                const float wsq = wave_sum(part);
+                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float2(wsq, 0.0f);
+                __syncthreads();
+                float tot = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
+                var = tot / h;
+                parity ^= 1;
+            }
+        } else if constexpr (WPR == 1) {
             mean = group_sum<G>(part) / h;
             float q = 0.0f;
 #pragma unroll
@@ -420,7 +461,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
 // ------------------------------------------------------------------------
 constexpr int kGenericBlock = 256;
 
-template <typename T>
+template <typename T, int OP>
 __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
     using E = Elem<T>;
     constexpr int W = kGenericBlock / 64;
@@ -429,16 +470,54 @@ __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
     const int wave = tid >> 6;
     const int64_t H = a.hidden;
     const float h = static_cast<float>(a.hidden);
+    int rms_slot = 0;
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t srow = a.skip_rows > 0 ? row % a.skip_rows : row;
         const int64_t xo = row * H, so = srow * H;
         // The same binary32 operations in every pass, hence the same bits.
         auto sum_at = [&](int64_t c) {
-            float v = E::load1(a.input, xo + c) + E::load1(a.skip, so + c);
-            if (a.bias != nullptr) v = v + E::load1(a.bias, c);
+            float v;
+            if constexpr (OP == kOpBiasAdd) {
+                v = E::load1(a.input, xo + c) + E::load1(a.bias, c);
+                v = v + E::load1(a.skip, so + c);
+            } else {
+                v = E::load1(a.input, xo + c) + E::load1(a.skip, so + c);
+                if (a.bias != nullptr) v = v + E::load1(a.bias, c);
+            }
             return v;
         };
+
+        if constexpr (OP == kOpBiasAdd) {
+            for (int64_t c = tid; c < H; c += kGenericBlock) E::store1(a.out, xo + c, sum_at(c));
+            continue;
+        }
+        if constexpr (OP == kOpSimplified) {
+            float sq = 0.0f;
+            for (int64_t c = tid; c < H; c += kGenericBlock) {
+                const float v = sum_at(c);
+                sq += v * v;
+            }
+            // One barrier per row: consecutive rows use alternate LDS slots,
+            // and a slot is rewritten two rows later, after a barrier that
+            // every lane reaches only once it has read the slot.
+            const float wsq = wave_sum(sq);
+            if ((tid & 63) == 0) red[rms_slot][wave] = wsq;
+            __syncthreads();
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) tot += red[rms_slot][w];
+            rms_slot ^= 1;
+            const float rstd = rsqrtf(tot / h + a.eps);
+            for (int64_t c = tid; c < H; c += kGenericBlock) {
+                const float v = sum_at(c);
+                if (a.residual != nullptr) E::store1(a.residual, xo + c, v);
+                const float g = E::load1(a.gamma, c);
+                const float b = a.beta != nullptr ? E::load1(a.beta, c) : 0.0f;
+                E::store1(a.out, xo + c, v * rstd * g + b);
+            }
+            continue;
+        }
 
         float part = 0.0f;
         for (int64_t c = tid; c < H; c += kGenericBlock) part += sum_at(c);
@@ -580,11 +659,11 @@ hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipSt
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
 
-template <typename T, int I>
+template <typename T, int OP, int I>
 hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     constexpr Geom g = kGeoms[I];
     static int occ = 0;
-    auto kernel = rowtile_kernel<T, g.g, g.ch, g.block>;
+    auto kernel = rowtile_kernel<T, OP, g.g, g.ch, g.block>;
     const int64_t rpb = g.block / g.g;
     const int64_t tiles = (a0.rows + rpb - 1) / rpb;
     Args a = a0;
@@ -623,48 +702,53 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);
 }
 
-template <typename T, int... I>
+template <typename T, int OP, int... I>
 hipError_t launch_geom_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
     hipError_t r = hipErrorInvalidValue;
-    ((idx == I ? (r = launch_geom<T, I>(a, t, st), 0) : 0), ...);
+    ((idx == I ? (r = launch_geom<T, OP, I>(a, t, st), 0) : 0), ...);
     return r;
 }
 
-template <typename T>
+template <typename T, int OP>
 hipError_t launch_generic_t(const Args& a, hipStream_t st) {
     static int occ = 0;
     int64_t resident = 0;
-    const hipError_t e = resident_blocks(generic_kernel<T>, kGenericBlock, &occ, &resident);
+    const hipError_t e = resident_blocks(generic_kernel<T, OP>, kGenericBlock, &occ, &resident);
     if (e != hipSuccess) return e;
     const int64_t blocks = a.rows < resident ? a.rows : resident;
-    return launch_grid(generic_kernel<T>, kGenericBlock, blocks < 1 ? 1 : blocks, a, st);
+    return launch_grid(generic_kernel<T, OP>, kGenericBlock, blocks < 1 ? 1 : blocks, a, st);
 }
 
-// Names: "generic_<t>" and "rowtile_<t>_g<G>_c<CH>", with "_b<block>" when the
-// block is not the default max(256, G).
-char g_names[2][kIdsPerType][32];
-std::atomic<int> g_names_ready{0};
-
-void build_names() {
-    const char* tn[2] = {"f32", "f16"};
-    for (int t = 0; t < 2; ++t) {
-        for (int i = 0; i < kIdsPerType; ++i) {
-            char* dst = g_names[t][i];
-            if (i == kGenericIndex)
-                snprintf(dst, 32, "generic_%s", tn[t]);
-            else if (i - kRowtileFirst < kNumGeoms) {
-                const Geom& g = kGeoms[i - kRowtileFirst];
-                const int default_block = g.g > 256 ? g.g : 256;
-                if (g.block == default_block)
-                    snprintf(dst, 32, "rowtile_%s_g%d_c%d", tn[t], g.g, g.ch);
-                else
-                    snprintf(dst, 32, "rowtile_%s_g%d_c%d_b%d", tn[t], g.g, g.ch, g.block);
+// Kernel names: "<op>generic_<t>" and "<op>rowtile_<t>_g<G>_c<CH>", with
+// "_b<block>" when the block is not the default max(256, G); <op> is empty
+// for layer normalization, "rms_" for the simplified form, "biasadd_".
+struct NameTable {
+    char name[kNumOps][2][kIdsPerType][48];
+    NameTable() {
+        const char* op_prefix[kNumOps] = {"", "rms_", "biasadd_"};
+        const char* tn[2] = {"f32", "f16"};
+        for (int op = 0; op < kNumOps; ++op) {
+            for (int t = 0; t < 2; ++t) {
+                for (int i = 0; i < kIdsPerType; ++i) {
+                    char* dst = name[op][t][i];
+                    const int gi = i - kRowtileFirst;
+                    if (i == kGenericIndex) {
+                        snprintf(dst, 48, "%sgeneric_%s", op_prefix[op], tn[t]);
+                    } else if (gi >= 0 && gi < kNumGeoms) {
+                        const Geom& g = kGeoms[gi];
+                        const int default_block = g.g > 256 ? g.g : 256;
+                        if (g.block == default_block)
+                            snprintf(dst, 48, "%srowtile_%s_g%d_c%d", op_prefix[op], tn[t], g.g, g.ch);
+                        else
+                            snprintf(dst, 48, "%srowtile_%s_g%d_c%d_b%d", op_prefix[op], tn[t], g.g, g.ch, g.block);
+                    } else {
+                        snprintf(dst, 48, "unknown");
+                    }
+                }
             }
-            else
-                snprintf(dst, 32, "unknown");
         }
     }
-}
+};
 
 }  // namespace
 
@@ -696,18 +780,10 @@ bool rowtile_holds(int geometry, int64_t hidden, int dtype) {
 }
 
 const char* kernel_name(int kernel_id) {
-    static std::atomic<int> once{0};
-    if (g_names_ready.load(std::memory_order_acquire) == 0) {
-        int expected = 0;
-        if (once.compare_exchange_strong(expected, 1)) {
-            build_names();
-            g_names_ready.store(1, std::memory_order_release);
-        }
-        while (g_names_ready.load(std::memory_order_acquire) == 0) {
-        }
-    }
-    if (kernel_id < 0 || kernel_id >= 2 * kIdsPerType) return "unknown";
-    return g_names[kernel_id / kIdsPerType][kernel_id % kIdsPerType];
+    static const NameTable table;  // built once, thread-safe initialization
+    if (kernel_id < 0 || kernel_id >= kNumOps * 2 * kIdsPerType) return "unknown";
+    const int op = kernel_id / (2 * kIdsPerType), t = kernel_id / kIdsPerType % 2;
+    return table.name[op][t][kernel_id % kIdsPerType];
 }
 
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t st) {
@@ -725,15 +801,35 @@ hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t s
                            dim3(kCopyBlock), params, 0, st);
 }
 
-hipError_t launch_generic(const Args& a, int dtype, hipStream_t st) {
-    return dtype == 0 ? launch_generic_t<float>(a, st) : launch_generic_t<_Float16>(a, st);
+template <typename T>
+hipError_t launch_generic_op(const Args& a, int op, hipStream_t st) {
+    switch (op) {
+        case kOpLayerNorm: return launch_generic_t<T, kOpLayerNorm>(a, st);
+        case kOpSimplified: return launch_generic_t<T, kOpSimplified>(a, st);
+        case kOpBiasAdd: return launch_generic_t<T, kOpBiasAdd>(a, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
-hipError_t launch_rowtile(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t st) {
-    if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
+hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t st) {
+    return dtype == 0 ? launch_generic_op<float>(a, op, st) : launch_generic_op<_Float16>(a, op, st);
+}
+
+template <typename T>
+hipError_t launch_rowtile_op(const Args& a, int op, int geometry, Tiling tiling, hipStream_t st) {
     auto seq = std::make_integer_sequence<int, kNumGeoms>{};
-    return dtype == 0 ? launch_geom_dispatch<float>(geometry, a, tiling, st, seq)
-                      : launch_geom_dispatch<_Float16>(geometry, a, tiling, st, seq);
+    switch (op) {
+        case kOpLayerNorm: return launch_geom_dispatch<T, kOpLayerNorm>(geometry, a, tiling, st, seq);
+        case kOpSimplified: return launch_geom_dispatch<T, kOpSimplified>(geometry, a, tiling, st, seq);
+        case kOpBiasAdd: return launch_geom_dispatch<T, kOpBiasAdd>(geometry, a, tiling, st, seq);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t st) {
+    if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
+    return dtype == 0 ? launch_rowtile_op<float>(a, op, geometry, tiling, st)
+                      : launch_rowtile_op<_Float16>(a, op, geometry, tiling, st);
 }
 
 }  // namespace skipln

@@ -80,12 +80,14 @@ class Workload:
     skip_shape: Tuple[int, ...]
     input_dist: Dist
     skip_dist: Dist
-    gamma_dist: Dist = field(default_factory=lambda: uniform(0.5, 1.5))
+    gamma_dist: Optional[Dist] = field(default_factory=lambda: uniform(0.5, 1.5))
     beta_dist: Optional[Dist] = field(default_factory=lambda: normal(0.0, 0.1))
     bias_dist: Optional[Dist] = None
     residual: bool = False
     eps: float = 1e-12
     seed: int = 0
+    # "layer_norm", "simplified" (root-mean-square form) or "bias_add"
+    op: str = "layer_norm"
 
     @property
     def hidden(self) -> int:
@@ -117,7 +119,7 @@ class Workload:
         h, r, b = self.hidden, self.rows, self.itemsize
         n = r * h * b  # input
         n += self.skip_rows * h * b  # skip
-        n += h * b  # gamma
+        n += h * b if self.gamma_dist is not None else 0
         n += h * b if self.beta_dist is not None else 0
         n += h * b if self.bias_dist is not None else 0
         n += r * h * b  # output
@@ -198,6 +200,72 @@ WORKLOADS: Dict[str, Workload] = {
 
 # Workloads in the order they are listed above.
 ORDER = list(WORKLOADS)
+
+# The same data flows through the two other operations of the row kernels:
+# BiasAdd (com.microsoft BiasAdd manifest; (N, S, C) input, skip of the same
+# shape, length-C bias) and the root-mean-square ("simplified") form.
+EXTRA: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload(
+            name="biasadd_8x128x768_f32",
+            shape=(8, 128, 768),
+            dtype="f32",
+            skip_shape=(8, 128, 768),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 0.5),
+            gamma_dist=None,
+            beta_dist=None,
+            bias_dist=normal(0, 0.1),
+            seed=1011,
+            op="bias_add",
+        ),
+        Workload(
+            name="biasadd_64x512x4096_f16",
+            shape=(64, 512, 4096),
+            dtype="f16",
+            skip_shape=(64, 512, 4096),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 1),
+            gamma_dist=None,
+            beta_dist=None,
+            bias_dist=normal(0, 0.1),
+            seed=1012,
+            op="bias_add",
+        ),
+        Workload(
+            name="rms_rows65536_h8192_f16",
+            shape=(65536, 8192),
+            dtype="f16",
+            skip_shape=(65536, 8192),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 1),
+            bias_dist=normal(0, 0.1),
+            residual=True,
+            eps=1e-5,
+            seed=1013,
+            op="simplified",
+        ),
+        Workload(
+            name="rms_bert_base_8x128x768_f32",
+            shape=(8, 128, 768),
+            dtype="f32",
+            skip_shape=(8, 128, 768),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 0.5),
+            bias_dist=normal(0, 0.1),
+            residual=True,
+            eps=1e-6,
+            seed=1014,
+            op="simplified",
+        ),
+    ]
+}
+
+
+def get(name: str) -> Workload:
+    """A workload of WORKLOADS or EXTRA by name."""
+    return WORKLOADS[name] if name in WORKLOADS else EXTRA[name]
 
 
 def _round(a: np.ndarray, dtype) -> np.ndarray:
@@ -305,6 +373,7 @@ def small_case(
     seed: int = 7,
     input_dist: Dist = normal(0, 1),
     skip_dist: Dist = normal(0, 1),
+    op: str = "layer_norm",
 ) -> Workload:
     """A workload for the flag/shape matrix of the parity tests.
 
@@ -317,16 +386,19 @@ def small_case(
     else:
         assert skip_rows > 0 and rows % skip_rows == 0
         shape, skip_shape = (rows // skip_rows, skip_rows, hidden), (skip_rows, hidden)
+    bias_add = op == "bias_add"
     return Workload(
-        name=f"case_{rows}x{hidden}_{dtype}",
+        name=f"case_{op}_{rows}x{hidden}_{dtype}",
         shape=shape,
         dtype=dtype,
         skip_shape=skip_shape,
         input_dist=input_dist,
         skip_dist=skip_dist,
-        beta_dist=normal(0, 0.1) if beta else None,
-        bias_dist=normal(0, 0.1) if bias else None,
-        residual=residual,
+        gamma_dist=None if bias_add else uniform(0.5, 1.5),
+        beta_dist=normal(0, 0.1) if beta and not bias_add else None,
+        bias_dist=normal(0, 0.1) if bias or bias_add else None,
+        residual=residual and not bias_add,
         eps=eps,
         seed=seed,
+        op=op,
     )
