@@ -107,7 +107,7 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.
-    n_sets = max(1, min(64, -(-3 * CACHE_BYTES // alg)))
+    n_sets = max(1, min(96, -(-4 * CACHE_BYTES // alg)))
     log(f"{w.name}: generating inputs (rows={w.rows} H={w.hidden} {w.dtype}), {n_sets} buffer set(s)")
     t0 = time.perf_counter()
     inputs = W.make_inputs(w)

@@ -87,7 +87,10 @@ enum {
  * SKIPLN_OP_BIAS_ADD is the BiasAdd operator (com.microsoft BiasAdd manifest). */
 enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 2 };
 
-/* Kernel families, for skipln_forward_variant / skipln_select. */
+/* Kernel families, for skipln_forward_variant / skipln_select.  The automatic
+ * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
+ * kernel for longer rows of the normalizing operations, the generic kernel
+ * for anything unaligned, not a whole number of chunks, or longer still. */
 enum {
     SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
     SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
@@ -97,6 +100,10 @@ enum {
                                      aligned pointers, hidden <= 4096*16/sizeof(T) */
     SKIPLN_VARIANT_MULTIWAVE = 3, /* ROWTILE with at least two wavefronts per
                                      row (exercises the cross-wave combine) */
+    SKIPLN_VARIANT_LDSROW = 4,    /* long rows: one 1024-lane block per row, the
+                                     row's sums staged in LDS; layer norm and
+                                     simplified only, 16-byte chunks, aligned
+                                     pointers, hidden * 4 <= 163584 bytes */
     SKIPLN_VARIANT_GEOMETRY = 64  /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_rowtile_geometries(), for
                                      tests and tuning */

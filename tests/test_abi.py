@@ -44,6 +44,7 @@ def test_header_enums_match_binding():
         "SKIPLN_OP_BIAS_ADD": L.OP_BIAS_ADD,
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
+        "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
@@ -147,7 +148,8 @@ def test_select_kernels():
     # not a multiple of a 16-byte chunk, or misaligned, or too long: generic
     assert name(sel(1001, 0)) == "generic_f32"
     assert name(sel(1024, 0, al=0)) == "generic_f32"
-    assert name(sel(20000, 0)) == "generic_f32"
+    assert name(sel(20000, 0)) == "ldsrow_f32"
+    assert name(sel(50000, 0)) == "generic_f32"
     assert name(sel(8, 1, v=1)) == "generic_f16"
     assert sel(1001, 0, v=L.VARIANT_ROWTILE) == -L.ERR_UNSUPPORTED
     assert name(sel(64, 0, v=L.VARIANT_MULTIWAVE)).startswith("rowtile_f32_g128")
@@ -166,6 +168,16 @@ def test_select_kernels():
     assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
     assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_generic_f16"
+    # long rows: LDS-staged up to 163584 bytes of binary32 sums, then generic
+    assert name(sel(8192, 0)) == "rowtile_f32_g512_c4"
+    assert name(sel(8196, 0)) == "ldsrow_f32"
+    assert name(sel(40896, 0)) == "ldsrow_f32"
+    assert name(sel(40900, 0)) == "generic_f32"
+    assert name(sel(16392, 1, op=L.OP_SIMPLIFIED)) == "rms_ldsrow_f16"
+    assert name(sel(16392, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g1024_c3"
+    assert name(sel(64, 0, v=L.VARIANT_LDSROW)) == "ldsrow_f32"
+    assert sel(64, 0, v=L.VARIANT_LDSROW, op=L.OP_BIAS_ADD) == -L.ERR_UNSUPPORTED
+    assert sel(66, 0, v=L.VARIANT_LDSROW) == -L.ERR_UNSUPPORTED
     assert L.kernel_name(-1) == "unknown" and L.kernel_name(10 ** 6) == "unknown"
 
 
@@ -175,14 +187,18 @@ def test_auto_choice_holds_every_hidden_size():
     lib = L.load()
     for dt, v in ((0, 4), (1, 8)):
         for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST):
-            for hv in range(1, 4097):
+            for hv in range(1, 2049):
                 kid = lib.skipln_select(L.OP_LAYER_NORM, hv * v, dt, mode, 1, 0)
                 assert kid >= 0 and L.kernel_name(kid).startswith("rowtile_"), (dt, mode, hv)
                 n = L.kernel_name(kid)
                 g = int(n.split("_g")[1].split("_")[0])
                 c = int(n.split("_c")[1].split("_")[0])
                 assert g * c >= hv
-            assert L.kernel_name(lib.skipln_select(L.OP_LAYER_NORM, 4097 * v, dt, mode, 1, 0)).startswith("generic_")
+            for hv in range(2049, 4097):
+                kid = lib.skipln_select(L.OP_BIAS_ADD, hv * v, dt, mode and 0, 1, 0)
+                n = L.kernel_name(kid)
+                assert n.startswith("biasadd_rowtile_"), (dt, hv, n)
+            assert L.kernel_name(lib.skipln_select(L.OP_BIAS_ADD, 4097 * v, dt, 0, 1, 0)).startswith("biasadd_generic_")
 
 
 def test_no_cpu_fallback_in_product_path():

@@ -338,6 +338,65 @@ def test_simplified_wrapper():
     U.assert_bits_equal(res.cpu().numpy(), ref["residual"])
 
 
+# ------------------------------------------------------------- long rows --
+
+LDS_F32 = [4, 64, 1000, 4096, 8196, 12288, 16384, 20000, 32768, 40896]
+LDS_F16 = [8, 64, 1000, 8192, 16392, 24576, 32768, 40896]
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified"])
+@pytest.mark.parametrize("dt_hidden", [("f32", h) for h in LDS_F32] + [("f16", h) for h in LDS_F16],
+                         ids=lambda t: f"{t[0]}_h{t[1]}")
+@pytest.mark.parametrize("flags", [(True, True, True, False), (False, False, False, True)],
+                         ids=lambda f: "b%d_bi%d_r%d_bc%d" % tuple(map(int, f)))
+def test_long_rows_lds_staged(op, dt_hidden, flags):
+    """The LDS-staged kernel, forced, from a few chunks (ragged lanes) up to
+    the 160 KiB row limit."""
+    dt, hidden = dt_hidden
+    beta, bias, residual, bcast = flags
+    rows = 6 if hidden > 16384 else 21
+    w = W.small_case(rows, hidden, dt, skip_rows=3 if bcast else None, beta=beta, bias=bias, residual=residual,
+                     eps=1e-5, seed=hidden + 1, op=op)
+    U.note(f"ldsrow {op} {dt} H={hidden} flags={flags}")
+    U.check_case(w, variant=L.VARIANT_LDSROW)
+
+
+@pytest.mark.parametrize("dt,hidden", [("f32", 12288), ("f32", 40896), ("f16", 32768)])
+def test_long_rows_auto(dt, hidden):
+    w = W.small_case(300 if hidden < 20000 else 64, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5,
+                     seed=hidden, input_dist=W.normal(100, 1))
+    code = L.F32 if dt == "f32" else L.F16
+    assert T.select_kernel(hidden, code).startswith("ldsrow_")
+    U.note(f"ldsrow auto {dt} H={hidden}")
+    U.check_case(w)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("mu", [100.0, 1000.0])
+@pytest.mark.parametrize("hidden", [64, 768, 4096, 12288])
+@pytest.mark.parametrize("variant", [L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW])
+def test_large_offset_rows(dt, mu, hidden, variant):
+    """Rows whose mean is far from zero (variance cancellation) in every
+    kernel family, within the binary32 tolerance."""
+    lib = L.load()
+    code = L.F32 if dt == "f32" else L.F16
+    if lib.skipln_select(L.OP_LAYER_NORM, hidden, code, L.SKIP_EXACT, 1, variant) < 0:
+        pytest.skip("family does not take this shape")
+    w = W.small_case(40, hidden, dt, skip_rows=8, beta=True, bias=True, residual=True, eps=1e-5, seed=int(mu) + hidden,
+                     input_dist=W.normal(mu, 1))
+    U.note(f"offset {mu} {dt} H={hidden} variant={variant}")
+    U.check_case(w, variant=variant)
+
+
+def test_long_rows_reject_tiling():
+    w = W.small_case(4, 20000, "f32", residual=True)
+    dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
+    assert L.load().skipln_select(L.OP_LAYER_NORM, 20000, L.F32, L.SKIP_EXACT, 1, L.VARIANT_LDSROW) >= 0
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run_config(-1, 1, 1)  # no row-tile geometry holds 5000 chunks
+    assert e.value.status == L.ERR_UNSUPPORTED
+
+
 # ------------------------------------------------------------ edge cases --
 
 def test_rows_zero_is_noop():

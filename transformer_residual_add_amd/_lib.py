@@ -19,7 +19,7 @@ SKIP_EXACT, SKIP_BROADCAST = 0, 1
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS = 0, 1, 2, 3, 4, 5, 6
 ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT, ERR_OP = 7, 8, 9, 10, 11
 OP_LAYER_NORM, OP_SIMPLIFIED, OP_BIAS_ADD = 0, 1, 2
-VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE, VARIANT_LDSROW = 0, 1, 2, 3, 4
 VARIANT_GEOMETRY = 64
 TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
 

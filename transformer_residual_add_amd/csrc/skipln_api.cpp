@@ -122,6 +122,11 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int v
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
     if (variant == SKIPLN_VARIANT_GENERIC) return base + skipln::kGenericIndex;
+    const bool lds_ok = vec_ok && skipln::ldsrow_holds(op, hidden, dtype);
+    if (variant == SKIPLN_VARIANT_LDSROW) return lds_ok ? base + skipln::kLdsRowIndex : -SKIPLN_ERR_UNSUPPORTED;
+    // Long rows of the normalizing operations: staged in LDS.
+    if (variant == SKIPLN_VARIANT_AUTO && lds_ok && hidden / v > skipln::kRowtileMaxAutoChunks)
+        return base + skipln::kLdsRowIndex;
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
         variant == SKIPLN_VARIANT_MULTIWAVE) {
         const int g =
@@ -186,6 +191,10 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int index = id % skipln::kIdsPerType;
     if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, c.op, c.dtype, s));
+    if (index == skipln::kLdsRowIndex) {
+        if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
+        return status_of(skipln::launch_ldsrow(a, c.op, c.dtype, s));
+    }
     const skipln::Tiling t = tiling ? *tiling : auto_tiling(c.skip_mode == SKIPLN_SKIP_BROADCAST);
     return status_of(skipln::launch_rowtile(a, c.op, c.dtype, index - skipln::kRowtileFirst, t, s));
 }

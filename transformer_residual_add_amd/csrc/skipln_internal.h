@@ -45,10 +45,18 @@ constexpr int kOpBiasAdd = 2;     // BiasAdd: (x + bias) + skip, no normalizatio
 constexpr int kNumOps = 3;
 
 // Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
-// 1.. = row tiles.
+// 1.. = row tiles, kLdsRowIndex = the LDS-staged long-row kernel.
 constexpr int kIdsPerType = 32;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
+constexpr int kLdsRowIndex = 31;
+
+// LDS a block may use on gfx950 (160 KiB), less room for the reduction
+// scratch: the long-row kernel holds hidden * 4 bytes.
+constexpr int64_t kLdsRowBytes = 163840 - 256;
+// Row-tile geometries hold at most this many 16-byte chunks efficiently;
+// longer rows go to the long-row kernel (1024-lane row tiles spill).
+constexpr int64_t kRowtileMaxAutoChunks = 2048;
 
 // Number of row-tile geometries and the one chosen for `hidden` (elements)
 // and the skip form, or -1 when none holds the row.  multiwave_only: the
@@ -61,6 +69,10 @@ const char* kernel_name(int kernel_id);
 
 // Enqueue one kernel; return 0 or a hipError_t value.
 hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t stream);
+hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t stream);
+// Whether the long-row kernel runs this operation and row (16-byte chunks,
+// row of binary32 sums within kLdsRowBytes).
+bool ldsrow_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 

@@ -160,6 +160,19 @@ __device__ __forceinline__ float group_sum(float v) {
     }
 }
 
+// Value of the first lane of each aligned group of G lanes (G = 16, 32: the
+// group's lane 0; G >= 64: the wavefront's lane 0, wave-uniform).
+template <int G>
+__device__ __forceinline__ float group_first(float v) {
+    if constexpr (G >= 64) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    } else {
+        // swizzle bit mode within 32 lanes: lane & and_mask (0x10 for 16, 0 for 32)
+        constexpr int kPattern = G == 16 ? 0x0010 : 0x0000;
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kPattern));
+    }
+}
+
 // ------------------------------------------------------------------------
 // Row-tile kernel.
 // ------------------------------------------------------------------------
@@ -185,7 +198,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     constexpr int RPB = BLOCK / G;                  // rows per block per tile
     constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
     static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
-    __shared__ float2 partial[2][RPB][WPR];
+    __shared__ float4 partial[2][RPB][WPR];
 
     const int tid = threadIdx.x;
     // Row of the tile handled by this group; wave-uniform when G >= 64, and
@@ -234,6 +247,10 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
 #pragma unroll
     for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
     const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
+    // Reciprocals once per block: the per-row statistics multiply (<= 1.5 ulp)
+    // instead of dividing, which shortens the latency of short launches.
+    const float inv_h = 1.0f / h;
+    const float inv_own_n = own_n > 0.0f ? 1.0f / own_n : 0.0f;
 
     // Tiles (RPB consecutive rows each) of this block, T = tiles_per_block:
     //   contiguous:      b*T, b*T + 1, ..., b*T + T - 1
@@ -317,10 +334,8 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             }
         }
 
-        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip), and
-        // this lane's partial sum (sum of squares for the simplified form).
+        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip).
         float s[CH][V];
-        float part = 0.0f;
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             float xf[V], sf[V], bf[V];
@@ -338,15 +353,6 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                     if (has_bias) v = v + bf[e];
                 }
                 s[k][e] = v;
-            }
-            if (ok[k]) {
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    if constexpr (OP == kOpSimplified)
-                        part += s[k][e] * s[k][e];
-                    else
-                        part += s[k][e];
-                }
             }
         }
 
@@ -371,70 +377,107 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                 if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), rp + k * G);
         }
 
-        float mean, var;
+        // Statistics are taken relative to a value of the row itself (lane
+        // 0's first element), subtracted from s in place once the residual is
+        // out: the mean is kept as shift + dmean and the row normalized as
+        // (s - shift) - dmean, so rounding scales with the row's spread, not
+        // with its offset from zero (s - shift is exact when both are near the
+        // row mean; a binary32 mean near 1000 could not be held to better than
+        // 3e-5).  Lane 0 of a group always holds chunk 0; with several
+        // wavefronts per row each uses its own lane 0.  This lane's partial
+        // sum (of squares, for the simplified form) follows.
+        const float shift = OP == kOpLayerNorm ? group_first<G>(s[0][0]) : 0.0f;
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            if (ok[k]) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (OP == kOpSimplified) {
+                        part += s[k][e] * s[k][e];
+                    } else {
+                        s[k][e] = s[k][e] - shift;
+                        part += s[k][e];
+                    }
+                }
+            }
+        }
+
+        // off: what to subtract from the shifted s to center it on the row mean.
+        float off = 0.0f, var;
         if constexpr (OP == kOpSimplified) {
             // Root mean square: no mean; the mean square takes the variance's place.
-            mean = 0.0f;
             if constexpr (WPR == 1) {
-                var = group_sum<G>(part) / h;
+                var = group_sum<G>(part) * inv_h;
             } else {
                 const float wsq = wave_sum(part);
-                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float2(wsq, 0.0f);
+                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(wsq, 0.0f, 0.0f, 0.0f);
                 __syncthreads();
                 float tot = 0.0f;
 #pragma unroll
                 for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
-                var = tot / h;
+                var = tot * inv_h;
                 parity ^= 1;
             }
         } else if constexpr (WPR == 1) {
-            mean = group_sum<G>(part) / h;
+            const float dmean = group_sum<G>(part) * inv_h;
+            off = dmean;
             float q = 0.0f;
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 if (ok[k]) {
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
-                        const float d = s[k][e] - mean;
+                        const float d = s[k][e] - dmean;
                         q += d * d;
                     }
                 }
             }
-            var = group_sum<G>(q) / h;
+            var = group_sum<G>(q) * inv_h;
         } else {
-            // Per-wavefront count, sum and squared deviations from the
-            // wavefront mean, merged across wavefronts (Chan et al.'s
-            // pairwise update: M2 = sum_w M2_w + n_w (mean_w - mean)^2).
-            const float wsum = wave_sum(part);
-            const float wmean = own_n > 0.0f ? wsum / own_n : 0.0f;
+            // Per wavefront: shift_w, the mean relative to it, and the squared
+            // deviations from the wavefront mean; merged across wavefronts by
+            // Chan et al.'s pairwise update (M2 = sum_w M2_w + n_w d_w^2)
+            // relative to wavefront 0's shift (wavefront 0 always has
+            // elements), so the merge only adds small numbers.
+            const float wd = wave_sum(part) * inv_own_n;
             float q = 0.0f;
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 if (ok[k]) {
 #pragma unroll
                     for (int e = 0; e < V; ++e) {
-                        const float d = s[k][e] - wmean;
+                        const float d = s[k][e] - wd;
                         q += d * d;
                     }
                 }
             }
             const float wm2 = wave_sum(q);
-            if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float2(wsum, wm2);
+            if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(shift, wd, wm2, 0.0f);
             __syncthreads();
-            float tot = 0.0f;
+            const float row_shift = partial[parity][slot][0].x;
+            float dsum = 0.0f;
 #pragma unroll
-            for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
-            mean = tot / h;
+            for (int w = 0; w < WPR; ++w) {
+                if (nw[w] > 0.0f) {
+                    const float4 p = partial[parity][slot][w];
+                    dsum += nw[w] * ((p.x - row_shift) + p.y);
+                }
+            }
+            const float dmean = dsum * inv_h;
             float m2 = 0.0f;
 #pragma unroll
             for (int w = 0; w < WPR; ++w) {
                 if (nw[w] > 0.0f) {
-                    const float2 p = partial[parity][slot][w];
-                    const float dm = p.x / nw[w] - mean;
-                    m2 += p.y + nw[w] * dm * dm;
+                    const float4 p = partial[parity][slot][w];
+                    const float dm = ((p.x - row_shift) + p.y) - dmean;
+                    m2 += p.z + nw[w] * dm * dm;
                 }
             }
-            var = m2 / h;
+            var = m2 * inv_h;
+            // s holds s - shift_w; the row is centered by subtracting
+            // dmean - (shift_w - row_shift) (both small).
+            off = dmean - (shift - row_shift);
             parity ^= 1;
         }
         const float rstd = rsqrtf(var + a.eps);
@@ -448,10 +491,154 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                     E::widen(gam[k], gf);
                     E::widen(bet[k], bf);
 #pragma unroll
-                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - mean) * rstd * gf[e] + bf[e];
+                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - off) * rstd * gf[e] + bf[e];
                     __builtin_nontemporal_store(E::narrow(y), op + k * G);
                 }
             }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Long-row kernel: the row is staged in LDS.
+// ------------------------------------------------------------------------
+// One 1024-lane block per row at a time (persistent over rows).  Lane t owns
+// chunks t, t + 1024, ...; it loads them (kLdsBatch chunks in flight per
+// lane), forms the binary32 sums, stores the residual, and parks its sums in
+// LDS -- up to 160 KiB, i.e. rows of up to ~40K values whatever T is -- so x
+// and skip cross HBM once.  Each lane re-reads only the LDS words it wrote,
+// so the row data needs no barrier; only the block reductions do.
+constexpr int kLdsBlock = 1024;
+constexpr int kLdsBatch = 4;
+
+template <typename T, int OP>
+__global__ void __launch_bounds__(kLdsBlock) ldsrow_kernel(const Args a) {
+    static_assert(OP == kOpLayerNorm || OP == kOpSimplified, "normalizing operations only");
+    using E = Elem<T>;
+    constexpr int V = E::kPerChunk;
+    constexpr int Q = V / 4;  // float4 words of binary32 sums per chunk
+    constexpr int W = kLdsBlock / 64;
+    extern __shared__ float4 srow[];
+    __shared__ float red[2][W];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int hv = a.hidden / V;
+    const float h = static_cast<float>(a.hidden);
+    const bool has_bias = a.bias != nullptr;
+    const bool has_beta = a.beta != nullptr;
+    const bool bcast = a.skip_rows > 0;
+    const u32x4* __restrict__ X = static_cast<const u32x4*>(a.input);
+    const u32x4* __restrict__ S = static_cast<const u32x4*>(a.skip);
+    const u32x4* __restrict__ Bz = static_cast<const u32x4*>(a.bias);
+    const u32x4* __restrict__ Gm = static_cast<const u32x4*>(a.gamma);
+    const u32x4* __restrict__ Bt = static_cast<const u32x4*>(a.beta);
+    u32x4* __restrict__ R = static_cast<u32x4*>(a.residual);
+    u32x4* __restrict__ O = static_cast<u32x4*>(a.out);
+
+    // Block sum; `buf` alternates so that a slot is rewritten only after a
+    // barrier every lane passes after reading it.
+    auto block_sum = [&](float v, int buf) {
+        const float ws = wave_sum(v);
+        if ((tid & 63) == 0) red[buf][wave] = ws;
+        __syncthreads();
+        float t = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) t += red[buf][w];
+        return t;
+    };
+
+    int rms_buf = 0;
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t srow_i = bcast ? row % a.skip_rows : row;
+        const u32x4* xp = X + row * hv;
+        const u32x4* sp = S + srow_i * hv;
+        // Shift of the sums (see the row-tile kernel): the row's first sum,
+        // formed by every lane with the same operations, hence the same bits.
+        float shift = 0.0f;
+        if constexpr (OP == kOpLayerNorm) {
+            shift = E::load1(a.input, row * a.hidden) + E::load1(a.skip, srow_i * a.hidden);
+            if (has_bias) shift = shift + E::load1(a.bias, 0);
+        }
+
+        float part = 0.0f;
+        for (int c0 = tid; c0 < hv; c0 += kLdsBlock * kLdsBatch) {
+            u32x4 xr[kLdsBatch], sr[kLdsBatch], br[kLdsBatch];
+#pragma unroll
+            for (int b = 0; b < kLdsBatch; ++b) {
+                const int c = c0 + b * kLdsBlock;
+                xr[b] = sr[b] = br[b] = u32x4{0, 0, 0, 0};
+                if (c < hv) {
+                    xr[b] = __builtin_nontemporal_load(xp + c);
+                    sr[b] = bcast ? sp[c] : __builtin_nontemporal_load(sp + c);
+                    if (has_bias) br[b] = Bz[c];
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kLdsBatch; ++b) {
+                const int c = c0 + b * kLdsBlock;
+                if (c < hv) {
+                    float xf[V], sf[V], bf[V], sv[V];
+                    E::widen(xr[b], xf);
+                    E::widen(sr[b], sf);
+                    E::widen(br[b], bf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        float v = xf[e] + sf[e];
+                        if (has_bias) v = v + bf[e];
+                        sv[e] = v;
+                        if constexpr (OP == kOpSimplified)
+                            part += v * v;
+                        else
+                            part += v - shift;
+                    }
+                    if (R != nullptr) __builtin_nontemporal_store(E::narrow(sv), R + row * hv + c);
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        srow[c * Q + q] = make_float4(sv[4 * q], sv[4 * q + 1], sv[4 * q + 2], sv[4 * q + 3]);
+                }
+            }
+        }
+
+        // The mean is kept as shift + dmean (see the row-tile kernel).
+        float dmean = 0.0f, var;
+        if constexpr (OP == kOpSimplified) {
+            var = block_sum(part, rms_buf) / h;
+            rms_buf ^= 1;
+        } else {
+            dmean = block_sum(part, 0) / h;
+            float q2 = 0.0f;
+            for (int c = tid; c < hv; c += kLdsBlock) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 v = srow[c * Q + q];
+                    const float d0 = (v.x - shift) - dmean, d1 = (v.y - shift) - dmean;
+                    const float d2 = (v.z - shift) - dmean, d3 = (v.w - shift) - dmean;
+                    q2 += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+                }
+            }
+            var = block_sum(q2, 1) / h;
+        }
+        const float rstd = rsqrtf(var + a.eps);
+
+        for (int c = tid; c < hv; c += kLdsBlock) {
+            float gf[V], bf[V], y[V];
+            E::widen(Gm[c], gf);
+            if (has_beta) {
+                E::widen(Bt[c], bf);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) bf[e] = 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const float4 v = srow[c * Q + q];
+                y[4 * q] = ((v.x - shift) - dmean) * rstd * gf[4 * q] + bf[4 * q];
+                y[4 * q + 1] = ((v.y - shift) - dmean) * rstd * gf[4 * q + 1] + bf[4 * q + 1];
+                y[4 * q + 2] = ((v.z - shift) - dmean) * rstd * gf[4 * q + 2] + bf[4 * q + 2];
+                y[4 * q + 3] = ((v.w - shift) - dmean) * rstd * gf[4 * q + 3] + bf[4 * q + 3];
+            }
+            __builtin_nontemporal_store(E::narrow(y), O + row * hv + c);
         }
     }
 }
@@ -519,19 +706,21 @@ __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
             continue;
         }
 
+        // Sums relative to the row's first sum (see the row-tile kernel).
+        const float shift = sum_at(0);
         float part = 0.0f;
-        for (int64_t c = tid; c < H; c += kGenericBlock) part += sum_at(c);
+        for (int64_t c = tid; c < H; c += kGenericBlock) part += sum_at(c) - shift;
         float ws = wave_sum(part);
         if ((tid & 63) == 0) red[0][wave] = ws;
         __syncthreads();
         float tot = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) tot += red[0][w];
-        const float mean = tot / h;
+        const float dmean = tot / h;  // the mean is shift + dmean (see the row-tile kernel)
 
         float q = 0.0f;
         for (int64_t c = tid; c < H; c += kGenericBlock) {
-            const float d = sum_at(c) - mean;
+            const float d = (sum_at(c) - shift) - dmean;
             q += d * d;
         }
         ws = wave_sum(q);
@@ -549,7 +738,7 @@ __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
             if (a.residual != nullptr) E::store1(a.residual, xo + c, v);
             const float g = E::load1(a.gamma, c);
             const float b = a.beta != nullptr ? E::load1(a.beta, c) : 0.0f;
-            E::store1(a.out, xo + c, (v - mean) * rstd * g + b);
+            E::store1(a.out, xo + c, ((v - shift) - dmean) * rstd * g + b);
         }
     }
 }
@@ -592,6 +781,7 @@ constexpr Geom kGeoms[] = {
     {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256},
 };
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
+static_assert(kRowtileFirst + kNumGeoms <= kLdsRowIndex, "kernel index ranges are disjoint");
 
 // Automatic choice: the first entry whose capacity holds the row's chunks.
 // Short rows are latency bound: one chunk per lane spreads a row over more
@@ -734,6 +924,8 @@ struct NameTable {
                     const int gi = i - kRowtileFirst;
                     if (i == kGenericIndex) {
                         snprintf(dst, 48, "%sgeneric_%s", op_prefix[op], tn[t]);
+                    } else if (i == kLdsRowIndex) {
+                        snprintf(dst, 48, "%sldsrow_%s", op_prefix[op], tn[t]);
                     } else if (gi >= 0 && gi < kNumGeoms) {
                         const Geom& g = kGeoms[gi];
                         const int default_block = g.g > 256 ? g.g : 256;
@@ -801,6 +993,25 @@ hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t s
                            dim3(kCopyBlock), params, 0, st);
 }
 
+template <typename T, int OP>
+hipError_t launch_ldsrow_t(const Args& a, hipStream_t st) {
+    auto kernel = ldsrow_kernel<T, OP>;
+    const size_t lds = static_cast<size_t>(a.hidden) * sizeof(float);
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    int occ = 0;  // depends on the row's LDS footprint, so it is not cached
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kLdsBlock, lds);
+    if (e != hipSuccess) return e;
+    if (occ < 1) return hipErrorInvalidConfiguration;
+    int64_t blocks = static_cast<int64_t>(cus) * occ;
+    if (a.rows < blocks) blocks = a.rows;
+    Args arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks)),
+                           dim3(kLdsBlock), params, lds, st);
+}
+
 template <typename T>
 hipError_t launch_generic_op(const Args& a, int op, hipStream_t st) {
     switch (op) {
@@ -809,6 +1020,21 @@ hipError_t launch_generic_op(const Args& a, int op, hipStream_t st) {
         case kOpBiasAdd: return launch_generic_t<T, kOpBiasAdd>(a, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t st) {
+    if (op == kOpLayerNorm)
+        return dtype == 0 ? launch_ldsrow_t<float, kOpLayerNorm>(a, st) : launch_ldsrow_t<_Float16, kOpLayerNorm>(a, st);
+    if (op == kOpSimplified)
+        return dtype == 0 ? launch_ldsrow_t<float, kOpSimplified>(a, st)
+                          : launch_ldsrow_t<_Float16, kOpSimplified>(a, st);
+    return hipErrorInvalidValue;
+}
+
+bool ldsrow_holds(int op, int64_t hidden, int dtype) {
+    const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
+    return (op == kOpLayerNorm || op == kOpSimplified) && hidden > 0 && hidden % v == 0 &&
+           hidden * static_cast<int64_t>(sizeof(float)) <= kLdsRowBytes;
 }
 
 hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t st) {
