@@ -52,6 +52,8 @@ def _load(path: str) -> C.CDLL:
         L.oracle_f16_to_f32_array.restype = None
         L.oracle_f32_to_f16_array.argtypes = [vp, vp, i64]
         L.oracle_f32_to_f16_array.restype = None
+        L.oracle_bias_softmax.argtypes = [vp, vp, i32, i64, i64, i64, i32, vp]
+        L.oracle_bias_softmax.restype = i32
         L.oracle_version.restype = i32
         _LIBS[path] = L
     return _LIBS[path]
@@ -157,3 +159,21 @@ def bias_add(x: np.ndarray, bias: np.ndarray, skip: np.ndarray):
     if st != 0:
         raise RuntimeError(f"oracle_bias_add failed with status {st}")
     return y, ye
+
+
+def bias_softmax(data: np.ndarray, bias: np.ndarray, inner: bool) -> np.ndarray:
+    """Reference BiasSoftmax over rows: ``data`` is (batch_count, block_size),
+    ``bias`` (bias_rows, block_size) with bias_rows dividing batch_count; row r
+    adds bias row r // (batch_count // bias_rows) (inner) or r % bias_rows
+    (outer).  Returns the binary64 softmax of the binary32 sum."""
+    data = np.ascontiguousarray(data)
+    bias = np.ascontiguousarray(bias)
+    code = _code(data, bias)
+    if data.ndim != 2 or bias.ndim != 2 or bias.shape[1] != data.shape[1]:
+        raise ValueError("data (rows, block) and bias (bias_rows, block) expected")
+    y = np.empty(data.shape, dtype=np.float64)
+    st = lib().oracle_bias_softmax(_ptr(data), _ptr(bias), code, data.shape[0], data.shape[1], bias.shape[0],
+                                   int(bool(inner)), _ptr(y))
+    if st != 0:
+        raise RuntimeError(f"oracle_bias_softmax failed with status {st}")
+    return y

@@ -360,4 +360,53 @@ int oracle_bias_add(const void* x, const void* bias, const void* skip, int dtype
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* BiasSoftmax                                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Reference BiasSoftmax (com.microsoft BiasSoftmax WebGPU manifest,
+ * `description`, `attributeDescriptions`, `derive`): the data is
+ * batch_count rows of block_size values (the dimensions from `axis` on,
+ * flattened); bias holds bias_rows rows of block_size values, bias_rows
+ * dividing batch_count.  Data row r adds bias row r / (batch_count /
+ * bias_rows) when inner != 0 (consecutive groups of rows share a bias row)
+ * and bias row r mod bias_rows otherwise (cyclic reuse).  z = data + bias is
+ * one IEEE binary32 add; y = exp(z - max z) / sum exp(z - max z) over the row
+ * in binary64, returned unrounded.
+ */
+int oracle_bias_softmax(const void* data, const void* bias, int dtype, int64_t batch_count, int64_t block_size,
+                        int64_t bias_rows, int inner, double* y_out) {
+    if (batch_count < 0 || block_size <= 0 || bias_rows <= 0 || bias_rows > batch_count ||
+        batch_count % bias_rows != 0)
+        return batch_count == 0 ? 0 : -1;
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16)
+        return -1;
+    if (!data || !bias || !y_out)
+        return -1;
+    const int64_t repeat = batch_count / bias_rows;
+    double* z = (double*)malloc((size_t)block_size * sizeof(double));
+    if (!z)
+        return -2;
+    for (int64_t r = 0; r < batch_count; ++r) {
+        const int64_t j = inner ? r / repeat : r % bias_rows;
+        /* The row maximum; a NaN never compares greater, and then makes every
+         * exp() below, and so the whole row, NaN. */
+        double m = -INFINITY;
+        for (int64_t c = 0; c < block_size; ++c) {
+            float zf = load_t(data, r * block_size + c, dtype) + load_t(bias, j * block_size + c, dtype);
+            z[c] = (double)zf;
+            if (z[c] > m)
+                m = z[c];
+        }
+        double sum = 0.0;
+        for (int64_t c = 0; c < block_size; ++c)
+            sum += exp(z[c] - m);
+        for (int64_t c = 0; c < block_size; ++c)
+            y_out[r * block_size + c] = exp(z[c] - m) / sum;
+    }
+    free(z);
+    return 0;
+}
+
 int oracle_version(void) { return 1; }

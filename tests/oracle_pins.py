@@ -374,6 +374,84 @@ def check_bias_add():
     assert y.tolist() == [[111.0, 222.0]], "bias_add hand row"
 
 
+# ------------------------------------------------------------ BiasSoftmax --
+
+def check_bias_softmax_closed_forms():
+    """BiasSoftmax (com.microsoft BiasSoftmax manifest, `description`,
+    `attributeDescriptions.is_inner_broadcast`, `derive.biasContract`):
+    softmax([0, a]) is the logistic pair (1/(1+e^a), e^a/(1+e^a)); a constant
+    row is uniform; a row offset by 1000 is unchanged (the maximum is taken
+    out before exponentiating); bias rows are reused in consecutive groups
+    (inner) or cyclically (outer)."""
+    f32 = np.float32
+    a = f32(0.75)
+    y = O.bias_softmax(np.array([[0.0, a]], f32), np.zeros((1, 2), f32), True)
+    e = math.exp(float(a))
+    _close(y, [[1 / (1 + e), e / (1 + e)]], 1e-16, 1e-15, "logistic pair")
+    y = O.bias_softmax(np.full((3, 5), 2.5, f32), np.zeros((1, 5), f32), False)
+    _close(y, np.full((3, 5), 0.2), 1e-16, 1e-15, "constant rows")
+    ln3 = f32(math.log(3.0))
+    e3 = math.exp(float(ln3))
+    y = O.bias_softmax(np.array([[1000.0, 1000.0 + float(ln3)]], f32), np.zeros((1, 2), f32), True)
+    z1 = float(f32(1000.0 + float(ln3))) - 1000.0  # the binary32 input is what the row holds
+    _close(y, [[1 / (1 + math.exp(z1)), math.exp(z1) / (1 + math.exp(z1))]], 1e-15, 1e-14, "offset row")
+    # The maximum is not the first value and e^800 overflows binary64: only
+    # subtracting the true maximum gives the closed form [~0, 1].
+    y = O.bias_softmax(np.array([[0.0, 800.0]], f32), np.zeros((1, 2), f32), True)
+    _close(y, [[0.0, 1.0]], 1e-300, 1e-15, "maximum last, large spread")
+    # Two bias rows [0, ln3] and [ln3, 0] over four zero data rows.
+    bias = np.array([[0.0, ln3], [ln3, 0.0]], f32)
+    lo, hi = 1 / (1 + e3), e3 / (1 + e3)
+    y_in = O.bias_softmax(np.zeros((4, 2), f32), bias, True)
+    _close(y_in, [[lo, hi], [lo, hi], [hi, lo], [hi, lo]], 1e-16, 1e-15, "inner broadcast groups")
+    y_out = O.bias_softmax(np.zeros((4, 2), f32), bias, False)
+    _close(y_out, [[lo, hi], [hi, lo], [lo, hi], [hi, lo]], 1e-16, 1e-15, "outer broadcast cycles")
+    # a NaN or a fully masked (-inf) row gives NaN, in that row only
+    d = np.zeros((3, 4), f32)
+    d[1, 2] = np.nan
+    d[2, :] = -np.inf
+    y = O.bias_softmax(d, np.zeros((1, 4), f32), True)
+    assert np.isnan(y[1]).all() and np.isnan(y[2]).all() and not np.isnan(y[0]).any(), "NaN rows"
+
+
+def check_bias_softmax_libraries():
+    """torch's and scipy's float64 softmax of the binary32 sum formed by numpy."""
+    import scipy.special
+    import torch
+
+    rng = np.random.default_rng(17)
+    for dt, rows, cols, brows, inner in [(np.float32, 24, 512, 4, True), (np.float32, 18, 77, 6, False),
+                                         (np.float16, 32, 256, 8, True), (np.float16, 12, 1000, 3, False)]:
+        data = (3 * rng.standard_normal((rows, cols))).astype(dt)
+        bias = (rng.standard_normal((brows, cols)) - 2 * (rng.random((brows, cols)) < 0.3)).astype(dt)
+        rep = rows // brows
+        idx = np.arange(rows) // rep if inner else np.arange(rows) % brows
+        z = (data.astype(np.float32) + bias[idx].astype(np.float32)).astype(np.float64)
+        y = O.bias_softmax(data, bias, inner)
+        _close(y, torch.softmax(torch.from_numpy(z), dim=1).numpy(), 1e-15, 1e-12, "torch softmax")
+        _close(y, scipy.special.softmax(z, axis=1), 1e-15, 1e-12, "scipy softmax")
+
+
+def check_bias_softmax_invariants():
+    rng = np.random.default_rng(23)
+    data = (rng.integers(-40, 41, (12, 33)) / 8).astype(np.float32)
+    bias = (rng.integers(-40, 41, (4, 33)) / 8).astype(np.float32)
+    for inner in (True, False):
+        y = O.bias_softmax(data, bias, inner)
+        _close(y.sum(axis=1), np.ones(12), 1e-14, 0, "rows sum to 1")
+        # ratios follow exp of differences (dyadic data: the sums are exact)
+        rep = 12 // 4
+        idx = np.arange(12) // rep if inner else np.arange(12) % 4
+        z = data.astype(np.float64) + bias[idx].astype(np.float64)
+        _close(y[:, 1:] / y[:, :1], np.exp(z[:, 1:] - z[:, :1]), 0, 1e-13, "ratios")
+        # adding a constant to a data row changes nothing
+        y2 = O.bias_softmax((data.astype(np.float64) + 4.0).astype(np.float32), bias, inner)
+        _close(y2, y, 1e-15, 1e-13, "shift invariance")
+    # one bias row for all: inner and outer agree
+    b1 = bias[:1]
+    assert np.array_equal(O.bias_softmax(data, b1, True), O.bias_softmax(data, b1, False)), "single bias row"
+
+
 ALL_CHECKS = [
     check_f16_decode_exhaustive,
     check_f16_encode,
@@ -385,4 +463,7 @@ ALL_CHECKS = [
     check_cancellation_rows,
     check_simplified,
     check_bias_add,
+    check_bias_softmax_closed_forms,
+    check_bias_softmax_libraries,
+    check_bias_softmax_invariants,
 ]

@@ -40,6 +40,11 @@ MUTANTS = [
     ("f16_decode_subnormal_scale", "ldexpf((float)m, -24)", "ldexpf((float)m, -23)"),
     ("bias_add_skip_first", "float a = xv + bv;\n            a = a + sv;", "float a = xv + sv;\n            a = a + bv;"),
     ("rms_keeps_mean", "if (!J->simplified) {", "if (1) {"),
+    ("softmax_inner_outer_swapped", "const int64_t j = inner ? r / repeat : r % bias_rows;",
+     "const int64_t j = inner ? r % bias_rows : r / repeat;"),
+    ("softmax_max_not_subtracted", "sum += exp(z[c] - m);", "sum += exp(z[c]);"),
+    ("softmax_bias_ignored", "+ load_t(bias, j * block_size + c, dtype);", ";"),
+    ("softmax_max_from_first_column", "if (z[c] > m)", "if (c == 0)"),
 ]
 
 
