@@ -30,8 +30,9 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 HEADLINE = "bert_base_8x128x768_f32"
 SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_mean100",
-         "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16"]
-OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2}  # SKIPLN_OP_*
+         "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "softmax_attn_16x16x512x512_f16_padmask",
+         "softmax_relpos_64x12x128x128_f32"]
+OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*
 KERNEL_SRC = os.path.join(ROOT, "transformer_residual_add_amd", "csrc", "skipln_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
@@ -94,6 +95,13 @@ class DeviceSets:
             self.sets.append(d)
 
 
+def skip_mode(w, L) -> int:
+    """SKIPLN_SKIP_* of a workload: exact, cyclic broadcast, or grouped (inner)."""
+    if not w.broadcast:
+        return L.SKIP_EXACT
+    return L.SKIP_BROADCAST_INNER if w.inner else L.SKIP_BROADCAST
+
+
 def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     import torch
 
@@ -103,7 +111,8 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
 
     code = L.F32 if w.dtype == "f32" else L.F16
     op = OPS[w.op]
-    kernel = T.select_kernel(w.hidden, code, True, variant, L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT, op)
+    mode = skip_mode(w, L)
+    kernel = T.select_kernel(w.hidden, code, True, variant, mode, op)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.
@@ -116,7 +125,6 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     torch.cuda.synchronize()
     log(f"{w.name}: inputs ready in {time.perf_counter() - t0:.1f}s; kernel {kernel}")
 
-    mode = L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT
     srows = w.skip_rows if w.broadcast else 0
     eps = float(w.eps)
     ptr = lambda t: None if t is None else t.data_ptr()
@@ -227,6 +235,9 @@ def cpu_baseline(w, seconds: float):
         if w.op == "bias_add":
             threads = 1  # the oracle's BiasAdd is a single loop
             O.bias_add(inputs["input"], inputs["bias"], inputs["skip"])
+        elif w.op == "bias_softmax":
+            threads = 1  # the oracle's BiasSoftmax is a single loop
+            O.bias_softmax(inputs["input"], inputs["skip"], w.inner)
         else:
             O.skip_layer_norm(inputs["input"], inputs["skip"], inputs["gamma"], inputs["beta"], inputs["bias"],
                               w.eps, broadcast=w.broadcast, residual=w.residual, threads=threads,

@@ -59,8 +59,10 @@ typedef struct ihipStream_t* skipln_stream_t;
 enum { SKIPLN_F32 = 0, SKIPLN_F16 = 1 };
 
 /* Skip forms (`inputs[skip]`): exact shape, or S rows broadcast over the
- * batch, where row r of the input reads skip row r mod S. */
-enum { SKIPLN_SKIP_EXACT = 0, SKIPLN_SKIP_BROADCAST = 1 };
+ * batch, where row r of the input reads skip row r mod S.  The grouped form
+ * (BiasSoftmax's inner broadcast only) has row r read skip row
+ * r / (rows / S): consecutive groups of rows / S rows share one skip row. */
+enum { SKIPLN_SKIP_EXACT = 0, SKIPLN_SKIP_BROADCAST = 1, SKIPLN_SKIP_BROADCAST_INNER = 2 };
 
 /* Status codes. */
 enum {
@@ -69,7 +71,8 @@ enum {
     SKIPLN_ERR_SHAPE = 2,       /* rows < 0, hidden <= 0 or > 2^31-1, size
                                    overflow, bad skip_rows for a broadcast */
     SKIPLN_ERR_DTYPE = 3,       /* dtype is neither SKIPLN_F32 nor SKIPLN_F16 */
-    SKIPLN_ERR_MODE = 4,        /* unknown skip_mode */
+    SKIPLN_ERR_MODE = 4,        /* unknown skip_mode, or one the operation
+                                   does not take */
     SKIPLN_ERR_EPS = 5,         /* eps < 0 or NaN */
     SKIPLN_ERR_ALIAS = 6,       /* outputs overlap inputs or each other */
     SKIPLN_ERR_UNSUPPORTED = 7, /* a forced variant cannot run this shape */
@@ -84,8 +87,10 @@ enum {
  * by the `simplified` template input of every SkipLayerNormalization variant
  * (the manifest sets it false and does not spell it out; reading used here:
  * no mean subtraction, the mean square in place of the variance).
- * SKIPLN_OP_BIAS_ADD is the BiasAdd operator (com.microsoft BiasAdd manifest). */
-enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 2 };
+ * SKIPLN_OP_BIAS_ADD is the BiasAdd operator (com.microsoft BiasAdd manifest).
+ * SKIPLN_OP_BIAS_SOFTMAX is the BiasSoftmax operator (com.microsoft
+ * BiasSoftmax manifest), with the data as `input` and the bias as `skip`. */
+enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 2, SKIPLN_OP_BIAS_SOFTMAX = 3 };
 
 /* Kernel families, for skipln_forward_variant / skipln_select.  The automatic
  * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
@@ -101,9 +106,10 @@ enum {
     SKIPLN_VARIANT_MULTIWAVE = 3, /* ROWTILE with at least two wavefronts per
                                      row (exercises the cross-wave combine) */
     SKIPLN_VARIANT_LDSROW = 4,    /* long rows: one 1024-lane block per row, the
-                                     row's sums staged in LDS; layer norm and
-                                     simplified only, 16-byte chunks, aligned
-                                     pointers, hidden * 4 <= 163584 bytes */
+                                     row's binary32 values staged in LDS; layer
+                                     norm, simplified and BiasSoftmax, 16-byte
+                                     chunks, aligned pointers,
+                                     hidden * 4 <= 163584 bytes */
     SKIPLN_VARIANT_GEOMETRY = 64  /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_rowtile_geometries(), for
                                      tests and tuning */
@@ -155,11 +161,44 @@ int skipln_forward_simplified(const void* input, const void* skip, int skip_mode
 int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, int64_t rows, int64_t channels,
                     int dtype, skipln_stream_t stream);
 
+/*
+ * BiasSoftmax (com.microsoft BiasSoftmax manifest, `description`,
+ * `attributes.is_inner_broadcast`, `derive.batchCount`, `derive.blockSize`,
+ * `derive.biasBlockCount`, `derive.biasContract`, `innerRepeat`): a softmax
+ * over each of batch_count rows of block_size values of data + bias.
+ *
+ * data, out     batch_count x block_size, T (the flattened data tensor: rows
+ *               are the dimensions before `axis`, a row the suffix from it)
+ * bias          bias_batch_count x block_size, T
+ * For row r, bias row j = r / (batch_count / bias_batch_count) when
+ * is_inner_broadcast != 0 (consecutive groups share a bias row), else
+ * j = r mod bias_batch_count (cyclic reuse), and
+ *   z[r,c] = fl32(data[r,c] + bias[j,c]),  M = max_c z[r,c],
+ *   out[r,c] = exp(z[r,c] - M) / sum_c' exp(z[r,c'] - M), rounded to T.
+ * The exponentials are evaluated in binary32 (2^x on the exponent scaled by
+ * log2 e) and summed in binary32; the result follows the definition within
+ * a few binary32 rounding steps per term.  A row containing NaN or +inf, or
+ * made of -inf only, comes out NaN; -inf terms of other rows give 0.
+ *
+ * Shapes (`biasContract`): all counts >= 0; empty data with an empty bias
+ * (batch_count or block_size 0, and bias_batch_count or block_size 0) is a
+ * valid no-op; otherwise block_size >= 1 and 1 <= bias_batch_count <=
+ * batch_count with batch_count a multiple of bias_batch_count, else
+ * SKIPLN_ERR_SHAPE.  out may equal data exactly, or bias when
+ * bias_batch_count == batch_count; other overlaps are SKIPLN_ERR_ALIAS.
+ * Ownership, streams and errors as for skipln_forward.
+ */
+int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t batch_count, int64_t block_size,
+                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, skipln_stream_t stream);
+
 /* Operation `op` (SKIPLN_OP_*) with the kernel family forced
  * (SKIPLN_VARIANT_*); the result is the same operator.  For
  * SKIPLN_OP_BIAS_ADD, gamma, beta, residual_out and eps are ignored, bias is
- * required and the skip must be exact.  Returns SKIPLN_ERR_UNSUPPORTED when
- * the family cannot run the shape or alignment. */
+ * required and the skip must be exact.  For SKIPLN_OP_BIAS_SOFTMAX, input is
+ * the data, skip the bias (skip_rows bias rows; SKIPLN_SKIP_BROADCAST is the
+ * cyclic and SKIPLN_SKIP_BROADCAST_INNER the grouped reuse), and gamma, beta,
+ * bias, residual_out and eps are ignored.  Returns SKIPLN_ERR_UNSUPPORTED
+ * when the family cannot run the shape or alignment. */
 int skipln_forward_variant(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                            const void* gamma, const void* beta, const void* bias,
                            void* out, void* residual_out, int64_t rows, int64_t hidden,
@@ -217,8 +256,8 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 int skipln_rowtile_geometries(void);
 
 /* Stable name of a kernel id ("generic_f32", "rowtile_f16_g256_c4",
- * "rms_rowtile_f32_g192_c1_b192", "biasadd_generic_f16", ...); "unknown" for
- * an invalid id. */
+ * "rms_rowtile_f32_g192_c1_b192", "biasadd_generic_f16",
+ * "softmax_rowtile_f16_g8_c1", ...); "unknown" for an invalid id. */
 const char* skipln_kernel_name(int kernel_id);
 
 /* Static description of a status code. */

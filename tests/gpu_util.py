@@ -4,7 +4,17 @@ through the C ABI, compare with the oracle.
 Tolerances: the normalized output is compared with the oracle's unrounded
 binary64 value, |out - y| <= atol + rtol * |y| with (1e-5, 1e-5) for float32
 and (2e-3, 2e-3) for float16; the residual (input_skip_bias_sum) must match
-bit for bit.
+bit for bit; BiasAdd's output bit for bit.
+
+BiasSoftmax (SOFTMAX_TOL): the kernels form the same binary32 z = data + bias
+and maximum M as the oracle; each exponential 2^t, t = (z - M) log2 e, has a
+relative error of about |t| 9.2e-8 (three binary32 roundings in t) plus
+1.2e-7 (the exp2 instruction), the binary32 sum at most depth x 6e-8 (about
+4e-6 for the longest per-lane chains here), the scaling 1.2e-7.  For every
+y >= 1e-20 (|t| <= 67) that stays below 1.1e-5: float32 uses rtol 2e-5 and
+atol 1e-20 (smaller values, and results flushed below the binary32 normal
+range).  float16 adds one rounding to nearest (2^-11 relative, at most 2^-25
+absolute among subnormals): rtol 1e-3, atol 2^-24.
 """
 from __future__ import annotations
 
@@ -18,7 +28,16 @@ from transformer_residual_add_amd import _lib as L
 from oracle import oracle as O
 
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-3, 2e-3)}
-OPS = {"layer_norm": L.OP_LAYER_NORM, "simplified": L.OP_SIMPLIFIED, "bias_add": L.OP_BIAS_ADD}
+SOFTMAX_TOL = {"f32": (1e-20, 2e-5), "f16": (2.0 ** -24, 1e-3)}
+OPS = {"layer_norm": L.OP_LAYER_NORM, "simplified": L.OP_SIMPLIFIED, "bias_add": L.OP_BIAS_ADD,
+       "bias_softmax": L.OP_BIAS_SOFTMAX}
+
+
+def skip_mode(w) -> int:
+    """The ABI's skip form for a workload."""
+    if not w.broadcast:
+        return L.SKIP_EXACT
+    return L.SKIP_BROADCAST_INNER if w.inner else L.SKIP_BROADCAST
 
 
 def torch_dtype(dt: str):
@@ -77,8 +96,7 @@ class DeviceCase:
         p = lambda t: None if t is None else t.data_ptr()
         o = self.out if out is None else out
         r = self.res if res == "default" else res
-        T.forward_raw(p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
-                      w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
+        T.forward_raw(p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
                       w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
                       stream, variant, OPS[w.op])
 
@@ -86,8 +104,7 @@ class DeviceCase:
         w = self.w
         p = lambda t: None if t is None else t.data_ptr()
         st = L.load().skipln_forward_config(
-            OPS[w.op], p(self.x), p(self.skip), L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT,
-            w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(self.out), p(self.res),
+            OPS[w.op], p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(self.out), p(self.res),
             w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16, geometry,
             tiles_per_block, strided, stream or None)
         L.check(st, "skipln_forward_config")
@@ -101,7 +118,17 @@ class DeviceCase:
 
 def oracle_rows(w, inputs, row_offset: int = 0, threads: int = 8):
     """The oracle's result for ``w.op``: {"y": binary64 output, "residual": T}
-    for the normalizations; {"y": Y in T (BiasAdd's output is exact)}."""
+    for the normalizations and BiasSoftmax; {"y": Y in T (BiasAdd's output is
+    exact)}.  ``inputs["input"]`` may hold rows ``row_offset ..`` only."""
+    if w.op == "bias_softmax":
+        n = inputs["input"].shape[0]
+        if row_offset == 0 and n == w.rows:
+            y = O.bias_softmax(inputs["input"], inputs["skip"], w.inner)
+        else:
+            # A slice of rows: hand the oracle the bias row each one reads.
+            bias = inputs["skip"][w.skip_row_of(np.arange(row_offset, row_offset + n))]
+            y = O.bias_softmax(inputs["input"], bias, False)
+        return {"y": y, "residual": None}
     if w.op == "bias_add":
         y, _ = O.bias_add(inputs["input"], inputs["bias"], inputs["skip"])
         return {"y": y, "residual": None}
@@ -116,13 +143,16 @@ def compare(w, got_out, got_res, ref):
     if w.op == "bias_add":
         assert_bits_equal(got_out, ref["y"], "bias_add output")
         return
+    if w.op == "bias_softmax":
+        assert_out_close(got_out, ref["y"], w.dtype, "softmax out", tol=SOFTMAX_TOL)
+        return
     assert_out_close(got_out, ref["y"], w.dtype)
     if got_res is not None:
         assert_bits_equal(got_res, ref["residual"])
 
 
-def assert_out_close(got: np.ndarray, want: np.ndarray, dt: str, what: str = "out"):
-    atol, rtol = TOL[dt]
+def assert_out_close(got: np.ndarray, want: np.ndarray, dt: str, what: str = "out", tol=None):
+    atol, rtol = (TOL if tol is None else tol)[dt]
     g = got.astype(np.float64)
     nan_w = np.isnan(want)
     assert np.array_equal(np.isnan(g), nan_w), f"{what}: NaN pattern differs ({int(np.isnan(g).sum())} vs " \

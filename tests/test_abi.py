@@ -35,13 +35,14 @@ def test_header_enums_match_binding():
     expect = {
         "SKIPLN_F32": L.F32, "SKIPLN_F16": L.F16,
         "SKIPLN_SKIP_EXACT": L.SKIP_EXACT, "SKIPLN_SKIP_BROADCAST": L.SKIP_BROADCAST,
+        "SKIPLN_SKIP_BROADCAST_INNER": L.SKIP_BROADCAST_INNER,
         "SKIPLN_OK": L.OK, "SKIPLN_ERR_NULL": L.ERR_NULL, "SKIPLN_ERR_SHAPE": L.ERR_SHAPE,
         "SKIPLN_ERR_DTYPE": L.ERR_DTYPE, "SKIPLN_ERR_MODE": L.ERR_MODE, "SKIPLN_ERR_EPS": L.ERR_EPS,
         "SKIPLN_ERR_ALIAS": L.ERR_ALIAS, "SKIPLN_ERR_UNSUPPORTED": L.ERR_UNSUPPORTED,
         "SKIPLN_ERR_LAUNCH": L.ERR_LAUNCH, "SKIPLN_ERR_DEVICE": L.ERR_DEVICE,
         "SKIPLN_ERR_VARIANT": L.ERR_VARIANT, "SKIPLN_ERR_OP": L.ERR_OP,
         "SKIPLN_OP_LAYER_NORM": L.OP_LAYER_NORM, "SKIPLN_OP_SIMPLIFIED": L.OP_SIMPLIFIED,
-        "SKIPLN_OP_BIAS_ADD": L.OP_BIAS_ADD,
+        "SKIPLN_OP_BIAS_ADD": L.OP_BIAS_ADD, "SKIPLN_OP_BIAS_SOFTMAX": L.OP_BIAS_SOFTMAX,
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
         "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW,
@@ -108,7 +109,7 @@ def test_validate_rejects(kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(op=3), L.ERR_OP),
+    (dict(op=4), L.ERR_OP),
     (dict(op=-1), L.ERR_OP),
     (dict(op=L.OP_SIMPLIFIED, gamma=None), L.ERR_NULL),
     (dict(op=L.OP_SIMPLIFIED), L.OK),
@@ -119,9 +120,57 @@ def test_validate_rejects(kw, status):
     (dict(op=L.OP_BIAS_ADD, out=BI), L.ERR_ALIAS),
     (dict(op=L.OP_BIAS_ADD, out=IN), L.OK),
     (dict(op=L.OP_BIAS_ADD, out=SK), L.OK),
+    (dict(op=L.OP_BIAS_ADD, mode=2, skip_rows=2), L.ERR_MODE),
+    (dict(op=L.OP_SIMPLIFIED, mode=2, skip_rows=2), L.ERR_MODE),   # grouped reuse is BiasSoftmax's
+    # BiasSoftmax: input = data, skip = bias rows; gamma/beta/bias/residual/eps ignored
+    (dict(op=L.OP_BIAS_SOFTMAX), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, gamma=None, beta=None, bias=None, res=None, eps=-1.0), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, res=IN + 4, bias=OUT), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=1, skip_rows=2), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=2, skip_rows=2), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=2, skip_rows=4), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=2, skip_rows=3), L.ERR_SHAPE),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=2, skip_rows=0), L.ERR_SHAPE),
+    (dict(op=L.OP_BIAS_SOFTMAX, mode=3, skip_rows=2), L.ERR_MODE),
+    (dict(op=L.OP_BIAS_SOFTMAX, skip=None), L.ERR_NULL),
+    (dict(op=L.OP_BIAS_SOFTMAX, out=IN), L.OK),
+    (dict(op=L.OP_BIAS_SOFTMAX, out=SK), L.OK),                  # exact bias: read row by row
+    (dict(op=L.OP_BIAS_SOFTMAX, out=SK, mode=2, skip_rows=2), L.ERR_ALIAS),
+    (dict(op=L.OP_BIAS_SOFTMAX, out=IN + 16), L.ERR_ALIAS),
 ])
 def test_validate_operations(kw, status):
     assert V(**kw) == status
+
+
+def S(data=IN, bias=SK, out=OUT, batch=4, block=8, bias_rows=2, inner=0, dtype=0):
+    return L.load().skipln_bias_softmax(data, bias, out, batch, block, bias_rows, inner, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # `biasContract`: empty data with an empty bias is a no-op (no HIP call)
+    (dict(batch=0, bias_rows=0), L.OK),
+    (dict(block=0, bias_rows=3), L.OK),
+    (dict(batch=0, block=0, bias_rows=0, data=None, bias=None, out=None), L.OK),
+    (dict(batch=0, bias_rows=0, dtype=7), L.ERR_DTYPE),
+    (dict(batch=0, bias_rows=1), L.ERR_SHAPE),    # bias rows but no data rows
+    (dict(bias_rows=0), L.ERR_SHAPE),
+    (dict(bias_rows=3), L.ERR_SHAPE),             # 4 rows not a multiple of 3
+    (dict(bias_rows=8), L.ERR_SHAPE),             # more bias rows than data rows
+    (dict(batch=-4), L.ERR_SHAPE),
+    (dict(block=-8), L.ERR_SHAPE),
+    (dict(bias_rows=-2), L.ERR_SHAPE),
+    (dict(block=2 ** 31), L.ERR_SHAPE),
+    (dict(dtype=2), L.ERR_DTYPE),
+    (dict(data=None), L.ERR_NULL),
+    (dict(bias=None, inner=1), L.ERR_NULL),
+    (dict(out=None), L.ERR_NULL),
+    (dict(out=SK), L.ERR_ALIAS),                  # broadcast bias is read by several rows
+    (dict(out=SK, inner=1), L.ERR_ALIAS),
+    (dict(out=IN + 4), L.ERR_ALIAS),
+])
+def test_bias_softmax_argument_checks(kw, status):
+    """Every status reached here returns before any HIP call."""
+    assert S(**kw) == status
 
 
 def test_validate_rows_zero_is_a_noop_even_with_null_pointers():
@@ -156,7 +205,7 @@ def test_select_kernels():
     ng = lib.skipln_rowtile_geometries()
     assert ng >= 13
     for g in range(ng):
-        kid = sel(64, 0, v=L.VARIANT_GEOMETRY + g)
+        kid = sel(16, 0, v=L.VARIANT_GEOMETRY + g)   # 4 chunks: every geometry holds them
         assert kid >= 0 and name(kid).startswith("rowtile_f32_g")
     assert sel(16384, 0, v=L.VARIANT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED
     assert sel(64, 0, v=L.VARIANT_GEOMETRY + ng) == -L.ERR_VARIANT
@@ -177,6 +226,19 @@ def test_select_kernels():
     assert name(sel(16392, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g1024_c3"
     assert name(sel(64, 0, v=L.VARIANT_LDSROW)) == "ldsrow_f32"
     assert sel(64, 0, v=L.VARIANT_LDSROW, op=L.OP_BIAS_ADD) == -L.ERR_UNSUPPORTED
+    # tiny rows pack 64 or 32 rows into a 256-lane block
+    assert name(sel(16, 0)) == "rowtile_f32_g4_c1"
+    assert name(sel(32, 1)) == "rowtile_f16_g4_c1"
+    assert name(sel(32, 0)) == "rowtile_f32_g8_c1"
+    # BiasSoftmax: every skip form, the same families
+    assert name(sel(512, 1, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST_INNER)) == "softmax_rowtile_f16_g32_c2"
+    assert name(sel(8, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowtile_f16_g4_c1"
+    assert name(sel(8, 0, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowtile_f32_g4_c1"
+    assert name(sel(4096, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowtile_f16_g128_c4"
+    assert name(sel(20000, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_ldsrow_f32"
+    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_generic_f32"
+    assert name(sel(64, 1, op=L.OP_BIAS_SOFTMAX, v=L.VARIANT_LDSROW)) == "softmax_ldsrow_f16"
+    assert sel(64, 0, mode=L.SKIP_BROADCAST_INNER) == -L.ERR_MODE
     assert sel(66, 0, v=L.VARIANT_LDSROW) == -L.ERR_UNSUPPORTED
     assert L.kernel_name(-1) == "unknown" and L.kernel_name(10 ** 6) == "unknown"
 
@@ -199,6 +261,13 @@ def test_auto_choice_holds_every_hidden_size():
                 n = L.kernel_name(kid)
                 assert n.startswith("biasadd_rowtile_"), (dt, hv, n)
             assert L.kernel_name(lib.skipln_select(L.OP_BIAS_ADD, 4097 * v, dt, 0, 1, 0)).startswith("biasadd_generic_")
+        for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST, L.SKIP_BROADCAST_INNER):
+            for hv in range(1, 2049):
+                n = L.kernel_name(lib.skipln_select(L.OP_BIAS_SOFTMAX, hv * v, dt, mode, 1, 0))
+                assert n.startswith("softmax_rowtile_"), (dt, mode, hv, n)
+                g = int(n.split("_g")[1].split("_")[0])
+                c = int(n.split("_c")[1].split("_")[0])
+                assert g * c >= hv and (g * c < 2 * hv or g * c == 4), (hv, n)
 
 
 def test_no_cpu_fallback_in_product_path():

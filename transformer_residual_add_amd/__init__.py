@@ -4,8 +4,10 @@
 ``s = input + skip (+ bias)`` and ``(s - mean) / sqrt(var + epsilon) * gamma
 (+ beta)``, optionally returning ``s`` as ``input_skip_bias_sum``
 (com.microsoft SkipLayerNormalization WebGPU manifest: `description`,
-`inputs`, `outputs`, `attributes.epsilon`).  The computation runs in the HIP
-kernels of ``libskipln.so``; PyTorch only provides device memory and streams.
+`inputs`, `outputs`, `attributes.epsilon`).  ``bias_add`` and
+``bias_softmax`` are the com.microsoft BiasAdd and BiasSoftmax operators on the
+same row kernels.  The computation runs in the HIP kernels of
+``libskipln.so``; PyTorch only provides device memory and streams.
 """
 from __future__ import annotations
 
@@ -18,7 +20,8 @@ from ._lib import SkiplnError  # noqa: F401
 # (SkipLayerNormalization manifest, `attributes.epsilon`).
 DEFAULT_EPSILON = 9.999999960041972e-13
 
-__all__ = ["skip_layer_norm", "bias_add", "forward_raw", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
+__all__ = ["skip_layer_norm", "bias_add", "bias_softmax", "bias_softmax_raw", "softmax_shape", "forward_raw",
+           "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
 
 
 def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: Optional[int],
@@ -30,6 +33,15 @@ def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, g
         op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
         out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
     _lib.check(st, "skipln_forward")
+
+
+def bias_softmax_raw(data_ptr: int, bias_ptr: int, out_ptr: int, batch_count: int, block_size: int,
+                     bias_batch_count: int, is_inner_broadcast: bool, dtype: int, stream: int = 0) -> None:
+    """``skipln_bias_softmax`` on raw device pointers; raises SkiplnError."""
+    st = _lib.load().skipln_bias_softmax(data_ptr or None, bias_ptr or None, out_ptr or None, batch_count,
+                                         block_size, bias_batch_count, 1 if is_inner_broadcast else 0, dtype,
+                                         stream or None)
+    _lib.check(st, "skipln_bias_softmax")
 
 
 def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO,
@@ -145,4 +157,55 @@ def bias_add(X, bias, skip, *, out=None, stream=None, variant: int = _lib.VARIAN
     with torch.cuda.device(X.device):
         forward_raw(X.data_ptr(), skip.data_ptr(), _lib.SKIP_EXACT, 0, None, None, bias.data_ptr(), out.data_ptr(),
                     None, rows, c, 0.0, code, s, variant, _lib.OP_BIAS_ADD)
+    return out
+
+
+def softmax_shape(data_shape, bias_numel: int, axis: int = 1):
+    """(batch_count, block_size, bias_batch_count) of BiasSoftmax for a data
+    shape, a bias element count and ``axis`` (BiasSoftmax manifest,
+    `derive.axisNorm`, `batchCount`, `blockSize`, `biasBlockCount`)."""
+    rank = len(data_shape)
+    if rank < 1 or not -rank <= axis < rank:
+        raise ValueError(f"axis {axis} out of range for rank {rank}")
+    a = axis if axis >= 0 else axis + rank
+    batch = 1
+    for d in data_shape[:a]:
+        batch *= int(d)
+    block = 1
+    for d in data_shape[a:]:
+        block *= int(d)
+    if block > 0 and bias_numel % block != 0:
+        raise ValueError(f"bias has {bias_numel} elements, not a whole number of rows of {block}")
+    return batch, block, (bias_numel // block if block > 0 else 0)
+
+
+def bias_softmax(data, bias, is_inner_broadcast: bool, axis: int = 1, *, out=None, stream=None,
+                 variant: int = _lib.VARIANT_AUTO):
+    """BiasSoftmax on CUDA (HIP) tensors: ``softmax(data + bias)`` over the
+    flattened dimensions from ``axis`` on.
+
+    The bias holds a whole number of softmax rows, a divisor of the data's row
+    count; they are reused by consecutive groups of rows
+    (``is_inner_broadcast=True``) or cyclically (False).  Tensors contiguous,
+    of one dtype (float32 or float16), on one device.
+    """
+    import torch
+
+    code = _dtype_code(data)
+    _check_tensors(data, [t for t in (data, bias, out) if t is not None])
+    batch, block, bias_rows = softmax_shape(tuple(data.shape), bias.numel(), axis)
+    if out is None:
+        out = torch.empty_like(data)
+    elif out.shape != data.shape:
+        raise ValueError("out must have data's shape")
+    s = _stream_handle(stream, data.device)
+    with torch.cuda.device(data.device):
+        if variant == _lib.VARIANT_AUTO:
+            bias_softmax_raw(data.data_ptr(), bias.data_ptr(), out.data_ptr(), batch, block, bias_rows,
+                             is_inner_broadcast, code, s)
+        elif batch * block > 0:
+            mode = (_lib.SKIP_EXACT if bias_rows == batch
+                    else _lib.SKIP_BROADCAST_INNER if is_inner_broadcast else _lib.SKIP_BROADCAST)
+            forward_raw(data.data_ptr(), bias.data_ptr(), mode, bias_rows, None, None, None, out.data_ptr(), None,
+                        batch, block, 0.0, code, s, variant, _lib.OP_BIAS_SOFTMAX)
     return out

@@ -7,6 +7,11 @@
 // `f16MainDtypes`), a broadcast skip (S, H) read cyclically by the (N*S) rows
 // (`broadcastSkipShapeOk`, `Params.skipRows`).  BiasAdd (com.microsoft BiasAdd
 // manifest, `inputs`) takes X, a length-C bias and a skip of X's shape.
+// BiasSoftmax (com.microsoft BiasSoftmax manifest, `derive.biasContract`)
+// takes batchCount rows of blockSize values and biasBlockCount bias rows that
+// divide the row count, reused cyclically (outer broadcast) or by consecutive
+// groups of batchCount / biasBlockCount rows (inner broadcast); its bias
+// travels in the skip slot of the shared kernels.
 // Aliasing rules are this library's own: an output may only coincide exactly
 // with a tensor that is read row by row by the lane group that later writes
 // the same row.
@@ -20,7 +25,7 @@ static_assert(SKIPLN_TILE_CONTIGUOUS == skipln::kTileContiguous && SKIPLN_TILE_S
                   SKIPLN_TILE_SKIP_STATIONARY == skipln::kTileSkipStationary,
               "tiling modes of the ABI and the kernels agree");
 static_assert(SKIPLN_OP_LAYER_NORM == skipln::kOpLayerNorm && SKIPLN_OP_SIMPLIFIED == skipln::kOpSimplified &&
-                  SKIPLN_OP_BIAS_ADD == skipln::kOpBiasAdd,
+                  SKIPLN_OP_BIAS_ADD == skipln::kOpBiasAdd && SKIPLN_OP_BIAS_SOFTMAX == skipln::kOpBiasSoftmax,
               "operations of the ABI and the kernels agree");
 
 namespace {
@@ -39,10 +44,24 @@ bool overlap(const Range& a, const Range& b) { return !a.empty() && !b.empty() &
 
 bool same(const Range& a, const Range& b) { return a.lo == b.lo && a.hi == b.hi; }
 
-bool known_op(int op) { return op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED || op == SKIPLN_OP_BIAS_ADD; }
+bool known_op(int op) {
+    return op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED || op == SKIPLN_OP_BIAS_ADD ||
+           op == SKIPLN_OP_BIAS_SOFTMAX;
+}
+
+bool normalizing(int op) { return op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED; }
+
+// Skip forms an operation accepts: grouped (inner) reuse is BiasSoftmax's.
+bool mode_ok(int op, int skip_mode) {
+    if (skip_mode == SKIPLN_SKIP_EXACT) return true;
+    if (skip_mode == SKIPLN_SKIP_BROADCAST) return op != SKIPLN_OP_BIAS_ADD;
+    if (skip_mode == SKIPLN_SKIP_BROADCAST_INNER) return op == SKIPLN_OP_BIAS_SOFTMAX;
+    return false;
+}
 
 // One call's arguments after the operation's own rules: BiasAdd has no
-// gamma, beta, residual output or epsilon.
+// gamma, beta, residual output or epsilon; BiasSoftmax has none of these and
+// no separate bias either (its bias is the skip).
 struct Call {
     int op;
     const void *input, *skip, *gamma, *beta, *bias;
@@ -56,21 +75,21 @@ struct Call {
 Call make_call(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows, const void* gamma,
                const void* beta, const void* bias, const void* out, const void* residual_out, int64_t rows,
                int64_t hidden, float eps, int dtype) {
-    const bool bias_add = op == SKIPLN_OP_BIAS_ADD;
+    const bool norm = normalizing(op);
     Call c;
     c.op = op;
     c.input = input;
     c.skip = skip;
-    c.gamma = bias_add ? nullptr : gamma;
-    c.beta = bias_add ? nullptr : beta;
-    c.bias = bias;
+    c.gamma = norm ? gamma : nullptr;
+    c.beta = norm ? beta : nullptr;
+    c.bias = op == SKIPLN_OP_BIAS_SOFTMAX ? nullptr : bias;
     c.out = const_cast<void*>(out);
-    c.residual = bias_add ? nullptr : const_cast<void*>(residual_out);
+    c.residual = norm ? const_cast<void*>(residual_out) : nullptr;
     c.skip_mode = skip_mode;
     c.skip_rows = skip_rows;
     c.rows = rows;
     c.hidden = hidden;
-    c.eps = bias_add ? 0.0f : eps;
+    c.eps = norm ? eps : 0.0f;
     c.dtype = dtype;
     return c;
 }
@@ -78,17 +97,17 @@ Call make_call(int op, const void* input, const void* skip, int skip_mode, int64
 int validate(const Call& c) {
     if (!known_op(c.op)) return SKIPLN_ERR_OP;
     if (c.dtype != SKIPLN_F32 && c.dtype != SKIPLN_F16) return SKIPLN_ERR_DTYPE;
-    if (c.skip_mode != SKIPLN_SKIP_EXACT && c.skip_mode != SKIPLN_SKIP_BROADCAST) return SKIPLN_ERR_MODE;
-    if (c.op == SKIPLN_OP_BIAS_ADD && c.skip_mode != SKIPLN_SKIP_EXACT) return SKIPLN_ERR_MODE;
+    if (!mode_ok(c.op, c.skip_mode)) return SKIPLN_ERR_MODE;
     if (!(c.eps >= 0.0f)) return SKIPLN_ERR_EPS;  // also rejects NaN
     if (c.rows < 0 || c.hidden <= 0 || c.hidden > INT32_MAX) return SKIPLN_ERR_SHAPE;
     const int64_t sz = c.dtype == SKIPLN_F32 ? 4 : 2;
     if (c.rows > INT64_MAX / c.hidden / sz) return SKIPLN_ERR_SHAPE;
-    const bool bcast = c.skip_mode == SKIPLN_SKIP_BROADCAST;
+    const bool bcast = c.skip_mode != SKIPLN_SKIP_EXACT;
     if (bcast && (c.skip_rows <= 0 || c.rows % c.skip_rows != 0)) return SKIPLN_ERR_SHAPE;
     if (c.rows == 0) return SKIPLN_OK;
     if (!c.input || !c.skip || !c.out) return SKIPLN_ERR_NULL;
-    if (c.op == SKIPLN_OP_BIAS_ADD ? !c.bias : !c.gamma) return SKIPLN_ERR_NULL;
+    if (normalizing(c.op) && !c.gamma) return SKIPLN_ERR_NULL;
+    if (c.op == SKIPLN_OP_BIAS_ADD && !c.bias) return SKIPLN_ERR_NULL;
 
     const int64_t row_bytes = c.hidden * sz;
     const Range r_in = span(c.input, c.rows * row_bytes);
@@ -130,7 +149,7 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int v
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
         variant == SKIPLN_VARIANT_MULTIWAVE) {
         const int g =
-            chunked ? skipln::rowtile_pick(hidden, dtype, broadcast, variant == SKIPLN_VARIANT_MULTIWAVE) : -1;
+            chunked ? skipln::rowtile_pick(op, hidden, dtype, broadcast, variant == SKIPLN_VARIANT_MULTIWAVE) : -1;
         if (g >= 0) return base + skipln::kRowtileFirst + g;
         if (variant == SKIPLN_VARIANT_AUTO) return base + skipln::kGenericIndex;
         return -SKIPLN_ERR_UNSUPPORTED;
@@ -147,12 +166,16 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int v
 // Tiling of the automatic launch.  Streaming rows (exact skip): one tile per
 // block, so blocks are dispatched in address order and the set of rows in
 // flight stays compact; this reached the 2-read/2-write streaming rate on
-// MI355X.  A broadcast skip is shared by every batch: each block keeps its
-// skip rows (and gamma/beta) in registers and walks the batches.
-skipln::Tiling auto_tiling(bool broadcast) {
+// MI355X.  A cyclic broadcast skip is shared by every batch: each block of a
+// normalization keeps its skip rows (and gamma/beta) in registers and walks
+// the batches.  BiasSoftmax has no parameters to keep and measured faster
+// streaming its rows in address order, its bias rows served by the caches,
+// as is grouped (inner) reuse, whose consecutive rows share a bias row.
+skipln::Tiling auto_tiling(int op, int skip_mode) {
+    const bool cyclic = skip_mode == SKIPLN_SKIP_BROADCAST && op != SKIPLN_OP_BIAS_SOFTMAX;
     skipln::Tiling t;
-    t.tiles_per_block = broadcast ? 0 : 1;
-    t.mode = broadcast ? skipln::kTileSkipStationary : skipln::kTileStrided;
+    t.tiles_per_block = cyclic ? 0 : 1;
+    t.mode = cyclic ? skipln::kTileSkipStationary : skipln::kTileStrided;
     return t;
 }
 
@@ -167,6 +190,7 @@ skipln::Args make_args(const Call& c) {
     a.residual = c.residual;
     a.rows = c.rows;
     a.skip_rows = c.skip_mode == SKIPLN_SKIP_BROADCAST ? c.skip_rows : 0;
+    a.skip_group = c.skip_mode == SKIPLN_SKIP_BROADCAST_INNER ? c.rows / c.skip_rows : 0;
     a.hidden = static_cast<int32_t>(c.hidden);
     a.eps = c.eps;
     a.tiles_per_block = 1;
@@ -184,7 +208,7 @@ int status_of(hipError_t e) {
 int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_t stream) {
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
-    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode == SKIPLN_SKIP_BROADCAST, all_aligned16(c), variant);
+    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c), variant);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
     const skipln::Args a = make_args(c);
@@ -195,7 +219,7 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
         return status_of(skipln::launch_ldsrow(a, c.op, c.dtype, s));
     }
-    const skipln::Tiling t = tiling ? *tiling : auto_tiling(c.skip_mode == SKIPLN_SKIP_BROADCAST);
+    const skipln::Tiling t = tiling ? *tiling : auto_tiling(c.op, c.skip_mode);
     return status_of(skipln::launch_rowtile(a, c.op, c.dtype, index - skipln::kRowtileFirst, t, s));
 }
 
@@ -213,9 +237,9 @@ int skipln_validate(int op, const void* input, const void* skip, int skip_mode, 
 int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
     if (!known_op(op)) return -SKIPLN_ERR_OP;
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
-    if (skip_mode != SKIPLN_SKIP_EXACT && skip_mode != SKIPLN_SKIP_BROADCAST) return -SKIPLN_ERR_MODE;
+    if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode == SKIPLN_SKIP_BROADCAST, aligned != 0, variant);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant);
 }
 
 int skipln_forward_variant(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
@@ -263,6 +287,26 @@ int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, 
                                   nullptr, rows, channels, 0.0f, dtype, SKIPLN_VARIANT_AUTO, stream);
 }
 
+int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t batch_count, int64_t block_size,
+                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, skipln_stream_t stream) {
+    if (batch_count < 0 || block_size < 0 || bias_batch_count < 0) return SKIPLN_ERR_SHAPE;
+    // `biasContract`: empty data with an empty bias is valid and does nothing.
+    if ((batch_count == 0 || block_size == 0) && (bias_batch_count == 0 || block_size == 0)) {
+        if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return SKIPLN_ERR_DTYPE;
+        return SKIPLN_OK;
+    }
+    if (block_size == 0 || bias_batch_count == 0 || bias_batch_count > batch_count ||
+        batch_count % bias_batch_count != 0)
+        return SKIPLN_ERR_SHAPE;
+    // One bias row per data row: both reuse forms read bias row r.
+    const int mode = bias_batch_count == batch_count
+                         ? SKIPLN_SKIP_EXACT
+                         : (is_inner_broadcast ? SKIPLN_SKIP_BROADCAST_INNER : SKIPLN_SKIP_BROADCAST);
+    return skipln_forward_variant(SKIPLN_OP_BIAS_SOFTMAX, data, bias, mode, bias_batch_count, nullptr, nullptr,
+                                  nullptr, out, nullptr, batch_count, block_size, 0.0f, dtype, SKIPLN_VARIANT_AUTO,
+                                  stream);
+}
+
 int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t stream) {
     if (bytes < 0 || bytes % 16 != 0) return SKIPLN_ERR_SHAPE;
     if (bytes == 0) return SKIPLN_OK;
@@ -280,7 +324,7 @@ const char* skipln_status_string(int status) {
     switch (status) {
         case SKIPLN_OK: return "ok";
         case SKIPLN_ERR_NULL: return "a required pointer is NULL";
-        case SKIPLN_ERR_SHAPE: return "invalid shape (rows, hidden or skip_rows)";
+        case SKIPLN_ERR_SHAPE: return "invalid shape (rows, hidden, skip_rows or bias rows)";
         case SKIPLN_ERR_DTYPE: return "unsupported element type";
         case SKIPLN_ERR_MODE: return "unknown or unsupported skip mode";
         case SKIPLN_ERR_EPS: return "epsilon must be a non-negative number";

@@ -17,7 +17,9 @@ struct Args {
     void* out;
     void* residual;    // nullptr: residual not written
     int64_t rows;
-    int64_t skip_rows; // 0: exact skip; > 0: row r reads skip row r % skip_rows
+    int64_t skip_rows; // > 0: row r reads skip row r % skip_rows (cyclic)
+    int64_t skip_group;// > 0: row r reads skip row r / skip_group (grouped);
+                       // both 0: exact skip (row r reads skip row r)
     int32_t hidden;
     float eps;
     // Row-tile kernels: tiles (RPB rows each) per block and how a block
@@ -42,14 +44,15 @@ struct Tiling {
 constexpr int kOpLayerNorm = 0;   // SkipLayerNormalization
 constexpr int kOpSimplified = 1;  // its root-mean-square ("simplified") form
 constexpr int kOpBiasAdd = 2;     // BiasAdd: (x + bias) + skip, no normalization
-constexpr int kNumOps = 3;
+constexpr int kOpBiasSoftmax = 3; // BiasSoftmax: softmax over the row of x + skip
+constexpr int kNumOps = 4;
 
 // Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
 // 1.. = row tiles, kLdsRowIndex = the LDS-staged long-row kernel.
-constexpr int kIdsPerType = 32;
+constexpr int kIdsPerType = 64;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
-constexpr int kLdsRowIndex = 31;
+constexpr int kLdsRowIndex = 63;
 
 // LDS a block may use on gfx950 (160 KiB), less room for the reduction
 // scratch: the long-row kernel holds hidden * 4 bytes.
@@ -58,11 +61,12 @@ constexpr int64_t kLdsRowBytes = 163840 - 256;
 // longer rows go to the long-row kernel (1024-lane row tiles spill).
 constexpr int64_t kRowtileMaxAutoChunks = 2048;
 
-// Number of row-tile geometries and the one chosen for `hidden` (elements)
-// and the skip form, or -1 when none holds the row.  multiwave_only: the
-// smallest geometry whose row group spans two or more wavefronts.
+// Number of row-tile geometries and the one chosen for operation `op`,
+// `hidden` (elements) and the skip form, or -1 when none holds the row.
+// multiwave_only: the smallest geometry whose row group spans two or more
+// wavefronts.
 int rowtile_count();
-int rowtile_pick(int64_t hidden, int dtype, bool broadcast, bool multiwave_only);
+int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only);
 // Whether geometry g holds a row of `hidden` elements (16-byte chunks).
 bool rowtile_holds(int geometry, int64_t hidden, int dtype);
 const char* kernel_name(int kernel_id);
@@ -71,7 +75,7 @@ const char* kernel_name(int kernel_id);
 hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t stream);
 hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t stream);
 // Whether the long-row kernel runs this operation and row (16-byte chunks,
-// row of binary32 sums within kLdsRowBytes).
+// row of binary32 values within kLdsRowBytes).
 bool ldsrow_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);

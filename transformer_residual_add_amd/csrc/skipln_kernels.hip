@@ -110,13 +110,16 @@ struct Elem<_Float16> {
 };
 
 // ------------------------------------------------------------------------
-// Cross-lane sums with DPP (data-parallel primitives: a VALU operand read
-// from another lane of the same row of 16 lanes, no LDS traffic).
+// Cross-lane reductions with DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row of 16 lanes, no LDS traffic).
 // ------------------------------------------------------------------------
+// Lanes that a DPP move does not write (rows outside row_mask) return `Id`,
+// the identity of the reduction: 0 for sums, -inf for maxima.
 template <int Ctrl, int RowMask = 0xF>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, RowMask, 0xF, false));
+__device__ __forceinline__ float dpp(float v, float id) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id),
+                                                                 __builtin_bit_cast(int, v), Ctrl, RowMask, 0xF,
+                                                                 false));
 }
 
 constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
@@ -126,51 +129,82 @@ constexpr int kRowMirror = 0x140;
 constexpr int kRowBcast15 = 0x142;  // lane 15 of each row into the next row
 constexpr int kRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
 
-// Sum over aligned groups of 16 lanes; every lane of a group gets the same
-// bits (each step adds a commutative pair).
-__device__ __forceinline__ float sum16(float v) {
-    v += dpp<kQuadSwap1>(v);
-    v += dpp<kQuadSwap2>(v);
-    v += dpp<kRowHalfMirror>(v);  // lane i <-> 7-i within 8: other quad
-    v += dpp<kRowMirror>(v);      // lane i <-> 15-i within 16: other half
+struct SumOp {
+    __device__ static float id() { return 0.0f; }
+    __device__ static float apply(float a, float b) { return a + b; }
+};
+// IEEE maxNum (v_max_f32): a NaN operand yields the other one.
+struct MaxOp {
+    __device__ static float id() { return -__builtin_inff(); }
+    __device__ static float apply(float a, float b) { return __builtin_fmaxf(a, b); }
+};
+
+// Reduction over aligned groups of G = 4, 8 or 16 lanes; every lane of a
+// group gets the same bits (each step combines a commutative pair).
+template <typename Op, int G>
+__device__ __forceinline__ float reduce_upto16(float v) {
+    static_assert(G == 4 || G == 8 || G == 16, "4, 8 or 16 lanes");
+    v = Op::apply(v, dpp<kQuadSwap1>(v, Op::id()));
+    v = Op::apply(v, dpp<kQuadSwap2>(v, Op::id()));
+    if constexpr (G >= 8) v = Op::apply(v, dpp<kRowHalfMirror>(v, Op::id()));  // lane i <-> 7-i: other quad
+    if constexpr (G >= 16) v = Op::apply(v, dpp<kRowMirror>(v, Op::id()));     // lane i <-> 15-i: other half
     return v;
 }
 
-// Sum over the whole wavefront, returned as a wave-uniform value.
-__device__ __forceinline__ float wave_sum(float v) {
-    v = sum16(v);
-    v += dpp<kRowBcast15, 0xA>(v);  // rows 1, 3 += rows 0, 2
-    v += dpp<kRowBcast31, 0xC>(v);  // rows 2, 3 += rows 0+1
+// Reduction over the whole wavefront, returned as a wave-uniform value.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v) {
+    v = reduce_upto16<Op, 16>(v);
+    v = Op::apply(v, dpp<kRowBcast15, 0xA>(v, Op::id()));  // rows 1, 3 combine rows 0, 2
+    v = Op::apply(v, dpp<kRowBcast31, 0xC>(v, Op::id()));  // rows 2, 3 combine rows 0+1
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Sum over an aligned group of G lanes (G = 16, 32 or 64).
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    static_assert(G == 16 || G == 32 || G == 64, "group of 16, 32 or 64 lanes");
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<SumOp>(v); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<MaxOp>(v); }
+
+// Reduction over an aligned group of G lanes (G = 4, 8, 16, 32 or 64).
+template <typename Op, int G>
+__device__ __forceinline__ float group_reduce(float v) {
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group of 4..64 lanes");
     if constexpr (G == 64) {
-        return wave_sum(v);
+        return wave_reduce<Op>(v);
+    } else if constexpr (G <= 16) {
+        return reduce_upto16<Op, G>(v);
     } else {
-        v = sum16(v);
-        if constexpr (G == 32) {
-            // lane ^ 16 within each half-wave (swizzle bit mode: and 0x1F, xor 0x10)
-            v += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-        }
-        return v;
+        v = reduce_upto16<Op, 16>(v);
+        // lane ^ 16 within each half-wave (swizzle bit mode: and 0x1F, xor 0x10)
+        return Op::apply(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
     }
 }
 
-// Value of the first lane of each aligned group of G lanes (G = 16, 32: the
+template <int G>
+__device__ __forceinline__ float group_sum(float v) { return group_reduce<SumOp, G>(v); }
+
+// Value of the first lane of each aligned group of G lanes (G <= 32: the
 // group's lane 0; G >= 64: the wavefront's lane 0, wave-uniform).
 template <int G>
 __device__ __forceinline__ float group_first(float v) {
     if constexpr (G >= 64) {
         return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
     } else {
-        // swizzle bit mode within 32 lanes: lane & and_mask (0x10 for 16, 0 for 32)
-        constexpr int kPattern = G == 16 ? 0x0010 : 0x0000;
+        // swizzle bit mode within 32 lanes: new lane = lane & and_mask
+        constexpr int kPattern = G == 4 ? 0x001C : G == 8 ? 0x0018 : G == 16 ? 0x0010 : 0x0000;
         return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kPattern));
     }
+}
+
+// Skip (bias) row read by data row `row`: the same row (exact), row mod
+// skip_rows (cyclic reuse), or row / skip_group (consecutive groups of rows
+// share one).  32-bit division whenever the row count fits.
+__device__ __forceinline__ int64_t skip_row_of(int64_t row, const Args& a, bool small_rows) {
+    if (a.skip_group > 0)
+        return small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) / static_cast<uint32_t>(a.skip_group))
+                          : row / a.skip_group;
+    if (a.skip_rows > 0)
+        return small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) % static_cast<uint32_t>(a.skip_rows))
+                          : row % a.skip_rows;
+    return row;
 }
 
 // ------------------------------------------------------------------------
@@ -192,9 +226,12 @@ __device__ __forceinline__ float wave_elems(int hv, int w) {
 
 template <typename T, int OP, int G, int CH, int BLOCK>
 __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
-    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd, "operation");
+    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd || OP == kOpBiasSoftmax,
+                  "operation");
     using E = Elem<T>;
     constexpr int V = E::kPerChunk;
+    constexpr bool kNorm = OP == kOpLayerNorm || OP == kOpSimplified;  // gamma/beta
+    constexpr bool kParams = OP != kOpBiasSoftmax;                       // any per-column parameter
     constexpr int RPB = BLOCK / G;                  // rows per block per tile
     constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
     static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
@@ -212,9 +249,9 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     const u32x4* __restrict__ S = static_cast<const u32x4*>(a.skip);
     u32x4* __restrict__ R = static_cast<u32x4*>(a.residual);
     u32x4* __restrict__ O = static_cast<u32x4*>(a.out);
-    const bool has_bias = a.bias != nullptr;
+    const bool has_bias = kParams && a.bias != nullptr;
     const bool has_beta = a.beta != nullptr;
-    const bool bcast = a.skip_rows > 0;
+    const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
     const bool small_rows = a.rows <= 0xFFFFFFFFll;
 
     bool ok[CH];
@@ -234,7 +271,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         for (int k = 0; k < CH; ++k) {
             const int c = k * G + lt;
             if (ok[k]) {
-                if constexpr (OP != kOpBiasAdd) {
+                if constexpr (kNorm) {
                     gam[k] = static_cast<const u32x4*>(a.gamma)[c];
                     if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
                 }
@@ -289,11 +326,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     auto issue_loads = [&](int64_t tile, bool with_skip) {
         const int64_t row = tile * RPB + slot;
         if (row < a.rows) {
-            // 32-bit remainder whenever the row count fits (always, in practice).
-            const int64_t srow = !bcast ? row
-                                 : (small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) %
-                                                                      static_cast<uint32_t>(a.skip_rows))
-                                               : row % a.skip_rows);
+            const int64_t srow = skip_row_of(row, a, small_rows);
             const u32x4* xp = X + row * hv + lt;
             const u32x4* sp = S + srow * hv + lt;
 #pragma unroll
@@ -324,7 +357,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     for (; tile < t_end; tile += stride) {
         const int64_t row = tile * RPB + slot;
         const bool live = row < a.rows;
-        if constexpr (V == 8) {
+        if constexpr (V == 8 && kParams) {
             // Keep gamma/beta/bias packed (2 fp16 per VGPR): without this the
             // compiler hoists their widening out of the loop and triples
             // their register footprint, which costs occupancy.
@@ -334,7 +367,8 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             }
         }
 
-        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip).
+        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip;
+        // BiasSoftmax: data + bias, the bias arriving through the skip slot).
         float s[CH][V];
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
@@ -358,6 +392,84 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
 
         // Registers of x/skip are free again: start the next tile's loads.
         if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
+
+        if constexpr (OP == kOpBiasSoftmax) {
+            // Softmax over the row: exponentials relative to a reference
+            // value r taken from the row, computed as 2^((z - r) log2 e), so
+            // that the rounding of the exponent scales with z - r (small for
+            // the terms that matter) rather than with z.
+            //   one wavefront or less per row: r = the row maximum M and
+            //     y = e / sum(e);
+            //   several wavefronts: each wavefront w uses its own maximum m_w
+            //     and its own sum s_w, exchanged through LDS (one barrier);
+            //     then M = max m_w, S = sum_w s_w 2^((m_w - M) log2 e) and
+            //     y = e 2^((m_w - M) log2 e) / S.
+            // Chunks past the row end take part as -inf / 0.  Special values
+            // follow the definition: any NaN in the row, a +inf, or a row
+            // that is -inf throughout makes the whole row NaN; a wavefront
+            // whose elements are all -inf contributes zeros.
+            constexpr float kLog2e = 1.4426950408889634f;
+            constexpr float kNegInf = -__builtin_inff();
+            float mx = kNegInf;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (ok[k])
+#pragma unroll
+                    for (int e = 0; e < V; ++e) mx = __builtin_fmaxf(mx, s[k][e]);
+            float m, r;
+            if constexpr (WPR == 1) {
+                m = group_reduce<MaxOp, G>(mx);
+                r = m;
+            } else {
+                m = wave_max(mx);
+                r = m != kNegInf ? m : 0.0f;
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        s[k][e] = __builtin_amdgcn_exp2f((s[k][e] - r) * kLog2e);
+                        part += s[k][e];
+                    }
+                }
+            }
+            float scale;
+            if constexpr (WPR == 1) {
+                scale = 1.0f / group_sum<G>(part);
+            } else {
+                const float ws = wave_sum(part);
+                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(m, ws, 0.0f, 0.0f);
+                __syncthreads();
+                float row_max = kNegInf;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) row_max = __builtin_fmaxf(row_max, partial[parity][slot][w].x);
+                float total = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    const float4 p = partial[parity][slot][w];
+                    const float f = p.x == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((p.x - row_max) * kLog2e);
+                    total += p.y * f;
+                }
+                const float own = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m - row_max) * kLog2e);
+                scale = own / total;
+                parity ^= 1;
+            }
+            if (live) {
+                u32x4* op = O + row * hv + lt;
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    if (ok[k]) {
+                        float y[V];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) y[e] = s[k][e] * scale;
+                        __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                    }
+                }
+            }
+            continue;
+        }
 
         if constexpr (OP == kOpBiasAdd) {
             // BiasAdd ends here: the sum is the output.
@@ -513,7 +625,7 @@ constexpr int kLdsBatch = 4;
 
 template <typename T, int OP>
 __global__ void __launch_bounds__(kLdsBlock) ldsrow_kernel(const Args a) {
-    static_assert(OP == kOpLayerNorm || OP == kOpSimplified, "normalizing operations only");
+    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasSoftmax, "row-reducing operations");
     using E = Elem<T>;
     constexpr int V = E::kPerChunk;
     constexpr int Q = V / 4;  // float4 words of binary32 sums per chunk
@@ -525,9 +637,10 @@ __global__ void __launch_bounds__(kLdsBlock) ldsrow_kernel(const Args a) {
     const int wave = tid >> 6;
     const int hv = a.hidden / V;
     const float h = static_cast<float>(a.hidden);
-    const bool has_bias = a.bias != nullptr;
+    const bool has_bias = OP != kOpBiasSoftmax && a.bias != nullptr;
     const bool has_beta = a.beta != nullptr;
-    const bool bcast = a.skip_rows > 0;
+    const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
+    const bool small_rows = a.rows <= 0xFFFFFFFFll;
     const u32x4* __restrict__ X = static_cast<const u32x4*>(a.input);
     const u32x4* __restrict__ S = static_cast<const u32x4*>(a.skip);
     const u32x4* __restrict__ Bz = static_cast<const u32x4*>(a.bias);
@@ -536,23 +649,92 @@ __global__ void __launch_bounds__(kLdsBlock) ldsrow_kernel(const Args a) {
     u32x4* __restrict__ R = static_cast<u32x4*>(a.residual);
     u32x4* __restrict__ O = static_cast<u32x4*>(a.out);
 
-    // Block sum; `buf` alternates so that a slot is rewritten only after a
-    // barrier every lane passes after reading it.
-    auto block_sum = [&](float v, int buf) {
-        const float ws = wave_sum(v);
+    // Block reduction (SumOp or MaxOp); `buf` alternates so that a slot is
+    // rewritten only after a barrier every lane passes after reading it.
+    auto block_reduce = [&](float v, int buf, auto op) {
+        using Op = decltype(op);
+        const float ws = wave_reduce<Op>(v);
         if ((tid & 63) == 0) red[buf][wave] = ws;
         __syncthreads();
-        float t = 0.0f;
+        float t = Op::id();
 #pragma unroll
-        for (int w = 0; w < W; ++w) t += red[buf][w];
+        for (int w = 0; w < W; ++w) t = Op::apply(t, red[buf][w]);
         return t;
     };
+    auto block_sum = [&](float v, int buf) { return block_reduce(v, buf, SumOp{}); };
 
     int rms_buf = 0;
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const int64_t srow_i = bcast ? row % a.skip_rows : row;
+        const int64_t srow_i = skip_row_of(row, a, small_rows);
         const u32x4* xp = X + row * hv;
         const u32x4* sp = S + srow_i * hv;
+
+        if constexpr (OP == kOpBiasSoftmax) {
+            // Softmax over the row of z = data + bias (bias through the skip
+            // slot): z parked in LDS while the block finds the maximum M, then
+            // replaced by 2^((z - M) log2 e) while the block sums them, then
+            // scaled by 1 / sum.  Special values as in the row-tile kernel
+            // (one reference, the row maximum).
+            constexpr float kLog2e = 1.4426950408889634f;
+            float mx = -__builtin_inff();
+            for (int c0 = tid; c0 < hv; c0 += kLdsBlock * kLdsBatch) {
+                u32x4 xr[kLdsBatch], sr[kLdsBatch];
+#pragma unroll
+                for (int b = 0; b < kLdsBatch; ++b) {
+                    const int c = c0 + b * kLdsBlock;
+                    xr[b] = sr[b] = u32x4{0, 0, 0, 0};
+                    if (c < hv) {
+                        xr[b] = __builtin_nontemporal_load(xp + c);
+                        sr[b] = bcast ? sp[c] : __builtin_nontemporal_load(sp + c);
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < kLdsBatch; ++b) {
+                    const int c = c0 + b * kLdsBlock;
+                    if (c < hv) {
+                        float xf[V], sf[V], zv[V];
+                        E::widen(xr[b], xf);
+                        E::widen(sr[b], sf);
+#pragma unroll
+                        for (int e = 0; e < V; ++e) {
+                            zv[e] = xf[e] + sf[e];
+                            mx = __builtin_fmaxf(mx, zv[e]);
+                        }
+#pragma unroll
+                        for (int q = 0; q < Q; ++q)
+                            srow[c * Q + q] = make_float4(zv[4 * q], zv[4 * q + 1], zv[4 * q + 2], zv[4 * q + 3]);
+                    }
+                }
+            }
+            const float m = block_reduce(mx, 0, MaxOp{});
+            float part = 0.0f;
+            for (int c = tid; c < hv; c += kLdsBlock) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    float4 v = srow[c * Q + q];
+                    v.x = __builtin_amdgcn_exp2f((v.x - m) * kLog2e);
+                    v.y = __builtin_amdgcn_exp2f((v.y - m) * kLog2e);
+                    v.z = __builtin_amdgcn_exp2f((v.z - m) * kLog2e);
+                    v.w = __builtin_amdgcn_exp2f((v.w - m) * kLog2e);
+                    part += v.x + v.y + v.z + v.w;
+                    srow[c * Q + q] = v;
+                }
+            }
+            const float scale = 1.0f / block_sum(part, 1);
+            for (int c = tid; c < hv; c += kLdsBlock) {
+                float y[V];
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 v = srow[c * Q + q];
+                    y[4 * q] = v.x * scale;
+                    y[4 * q + 1] = v.y * scale;
+                    y[4 * q + 2] = v.z * scale;
+                    y[4 * q + 3] = v.w * scale;
+                }
+                __builtin_nontemporal_store(E::narrow(y), O + row * hv + c);
+            }
+            continue;
+        }
         // Shift of the sums (see the row-tile kernel): the row's first sum,
         // formed by every lane with the same operations, hence the same bits.
         float shift = 0.0f;
@@ -659,8 +841,21 @@ __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
     const float h = static_cast<float>(a.hidden);
     int rms_slot = 0;
 
+    const bool small_rows = a.rows <= 0xFFFFFFFFll;
+    // Block reduction (SumOp or MaxOp) through LDS slot `buf`.
+    auto block_reduce = [&](float v, int buf, auto op) {
+        using Op = decltype(op);
+        const float ws = wave_reduce<Op>(v);
+        if ((tid & 63) == 0) red[buf][wave] = ws;
+        __syncthreads();
+        float t = Op::id();
+#pragma unroll
+        for (int w = 0; w < W; ++w) t = Op::apply(t, red[buf][w]);
+        return t;
+    };
+
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
-        const int64_t srow = a.skip_rows > 0 ? row % a.skip_rows : row;
+        const int64_t srow = skip_row_of(row, a, small_rows);
         const int64_t xo = row * H, so = srow * H;
         // The same binary32 operations in every pass, hence the same bits.
         auto sum_at = [&](int64_t c) {
@@ -670,13 +865,31 @@ __global__ void __launch_bounds__(kGenericBlock) generic_kernel(const Args a) {
                 v = v + E::load1(a.skip, so + c);
             } else {
                 v = E::load1(a.input, xo + c) + E::load1(a.skip, so + c);
-                if (a.bias != nullptr) v = v + E::load1(a.bias, c);
+                if (OP != kOpBiasSoftmax && a.bias != nullptr) v = v + E::load1(a.bias, c);
             }
             return v;
         };
 
         if constexpr (OP == kOpBiasAdd) {
             for (int64_t c = tid; c < H; c += kGenericBlock) E::store1(a.out, xo + c, sum_at(c));
+            continue;
+        }
+        if constexpr (OP == kOpBiasSoftmax) {
+            // Softmax over the row of z = data + bias (bias through the skip
+            // slot): the maximum M, then the sum of 2^((z - M) log2 e), then
+            // the scaled exponentials, recomputed from the same bits in each
+            // pass.  Slot 0 holds the maximum, slot 1 the sum: a slot is
+            // rewritten only after the other slot's barrier, which every lane
+            // passes after reading it.
+            constexpr float kLog2e = 1.4426950408889634f;
+            float mx = -__builtin_inff();
+            for (int64_t c = tid; c < H; c += kGenericBlock) mx = __builtin_fmaxf(mx, sum_at(c));
+            const float m = block_reduce(mx, 0, MaxOp{});
+            float part = 0.0f;
+            for (int64_t c = tid; c < H; c += kGenericBlock) part += __builtin_amdgcn_exp2f((sum_at(c) - m) * kLog2e);
+            const float scale = 1.0f / block_reduce(part, 1, SumOp{});
+            for (int64_t c = tid; c < H; c += kGenericBlock)
+                E::store1(a.out, xo + c, __builtin_amdgcn_exp2f((sum_at(c) - m) * kLog2e) * scale);
             continue;
         }
         if constexpr (OP == kOpSimplified) {
@@ -778,26 +991,38 @@ constexpr Geom kGeoms[] = {
     {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
     {512, 2, 512}, {128, 8, 256},  {256, 2, 512},  {256, 4, 512},  {64, 2, 64},
     {64, 3, 64},   {32, 6, 256},  {192, 1, 192},  {192, 2, 192},  {512, 1, 512},
-    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256},
+    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256}, {4, 1, 256},   {8, 1, 256},
+    {4, 2, 256},   {8, 2, 256},   {8, 4, 256},    {16, 2, 256},   {16, 4, 256},
+    {32, 2, 256},  {128, 2, 256}, {32, 4, 256},   {16, 8, 256},
 };
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 static_assert(kRowtileFirst + kNumGeoms <= kLdsRowIndex, "kernel index ranges are disjoint");
 
 // Automatic choice: the first entry whose capacity holds the row's chunks.
 // Short rows are latency bound: one chunk per lane spreads a row over more
-// lanes and shortens the per-lane load/reduce chain.  Long rows use 256-lane
+// lanes and shortens the per-lane load/reduce chain; rows of 8 chunks or
+// fewer (e.g. attention rows of a few keys) pack 32 or 64 rows into a
+// 256-lane block instead of leaving most of a 16-lane group idle.  Long rows use 256-lane
 // groups (4 wavefronts; 1024-lane groups pay for 16-wavefront barriers).
 // A broadcast skip uses the same geometries with skip-stationary tiling.
 struct AutoEntry {
     int max_chunks, geom;
 };
 constexpr AutoEntry kAutoExact[] = {
-    {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
+    {4, 28}, {8, 29}, {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
     {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
 };
 constexpr AutoEntry kAutoBroadcast[] = {
-    {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
+    {4, 28}, {8, 29}, {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
     {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+};
+// BiasSoftmax streams one tensor in and one out and has no per-column
+// parameters; on MI355X it runs fastest with two to four chunks per lane
+// (more independent loads in flight per lane, fewer lanes per reduction)
+// until a row needs several wavefronts (measured over 2..2048 chunks).
+constexpr AutoEntry kAutoSoftmax[] = {
+    {4, 28},   {8, 29},   {16, 31},  {32, 33},   {64, 35},   {128, 37},  {256, 5},
+    {512, 6},  {1024, 15}, {2048, 10}, {3072, 11}, {4096, 12},
 };
 
 hipError_t cu_count(int* out) {
@@ -911,11 +1136,12 @@ hipError_t launch_generic_t(const Args& a, hipStream_t st) {
 
 // Kernel names: "<op>generic_<t>" and "<op>rowtile_<t>_g<G>_c<CH>", with
 // "_b<block>" when the block is not the default max(256, G); <op> is empty
-// for layer normalization, "rms_" for the simplified form, "biasadd_".
+// for layer normalization, "rms_" for the simplified form, "biasadd_",
+// "softmax_".
 struct NameTable {
     char name[kNumOps][2][kIdsPerType][48];
     NameTable() {
-        const char* op_prefix[kNumOps] = {"", "rms_", "biasadd_"};
+        const char* op_prefix[kNumOps] = {"", "rms_", "biasadd_", "softmax_"};
         const char* tn[2] = {"f32", "f16"};
         for (int op = 0; op < kNumOps; ++op) {
             for (int t = 0; t < 2; ++t) {
@@ -946,11 +1172,16 @@ struct NameTable {
 
 int rowtile_count() { return kNumGeoms; }
 
-int rowtile_pick(int64_t hidden, int dtype, bool broadcast, bool multiwave_only) {
+int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only) {
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     if (hidden <= 0 || hidden % v != 0) return -1;
     const int64_t hv = hidden / v;
     if (!multiwave_only) {
+        if (op == kOpBiasSoftmax) {
+            for (const AutoEntry& e : kAutoSoftmax)
+                if (hv <= e.max_chunks) return e.geom;
+            return -1;
+        }
         for (const AutoEntry& e : (broadcast ? kAutoBroadcast : kAutoExact))
             if (hv <= e.max_chunks) return e.geom;
         return -1;
@@ -1018,6 +1249,7 @@ hipError_t launch_generic_op(const Args& a, int op, hipStream_t st) {
         case kOpLayerNorm: return launch_generic_t<T, kOpLayerNorm>(a, st);
         case kOpSimplified: return launch_generic_t<T, kOpSimplified>(a, st);
         case kOpBiasAdd: return launch_generic_t<T, kOpBiasAdd>(a, st);
+        case kOpBiasSoftmax: return launch_generic_t<T, kOpBiasSoftmax>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1028,12 +1260,15 @@ hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t st) {
     if (op == kOpSimplified)
         return dtype == 0 ? launch_ldsrow_t<float, kOpSimplified>(a, st)
                           : launch_ldsrow_t<_Float16, kOpSimplified>(a, st);
+    if (op == kOpBiasSoftmax)
+        return dtype == 0 ? launch_ldsrow_t<float, kOpBiasSoftmax>(a, st)
+                          : launch_ldsrow_t<_Float16, kOpBiasSoftmax>(a, st);
     return hipErrorInvalidValue;
 }
 
 bool ldsrow_holds(int op, int64_t hidden, int dtype) {
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
-    return (op == kOpLayerNorm || op == kOpSimplified) && hidden > 0 && hidden % v == 0 &&
+    return (op == kOpLayerNorm || op == kOpSimplified || op == kOpBiasSoftmax) && hidden > 0 && hidden % v == 0 &&
            hidden * static_cast<int64_t>(sizeof(float)) <= kLdsRowBytes;
 }
 
@@ -1048,6 +1283,7 @@ hipError_t launch_rowtile_op(const Args& a, int op, int geometry, Tiling tiling,
         case kOpLayerNorm: return launch_geom_dispatch<T, kOpLayerNorm>(geometry, a, tiling, st, seq);
         case kOpSimplified: return launch_geom_dispatch<T, kOpSimplified>(geometry, a, tiling, st, seq);
         case kOpBiasAdd: return launch_geom_dispatch<T, kOpBiasAdd>(geometry, a, tiling, st, seq);
+        case kOpBiasSoftmax: return launch_geom_dispatch<T, kOpBiasSoftmax>(geometry, a, tiling, st, seq);
         default: return hipErrorInvalidValue;
     }
 }

@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the SkipLayerNormalization row kernel.
+"""Seeded synthetic inputs for the row kernels (SkipLayerNormalization,
+its root-mean-square form, BiasAdd and BiasSoftmax).
 
 This module only draws random numbers and rounds them to the I/O element
 type; it holds none of the operator's arithmetic.  Both the HIP path (via the
@@ -9,7 +10,11 @@ Tensor roles follow the com.microsoft SkipLayerNormalization WebGPU manifest
 (`inputs`: input, skip, gamma, beta, bias; `outputs`: output and the optional
 input_skip_bias_sum).  Rank-3 input ``(N, S, H)`` is addressed as
 ``rows = N * S`` rows of ``H`` contiguous elements; a broadcast skip has
-``S`` rows (the manifest's `Params.skipRows` = numel(skip) / H).
+``S`` rows (the manifest's `Params.skipRows` = numel(skip) / H).  For
+BiasSoftmax (com.microsoft BiasSoftmax manifest) ``input`` is the data,
+``rows`` its batchCount, ``H`` its blockSize, and ``skip`` the bias rows
+(biasBlockCount of them), reused cyclically or, with ``inner``, by
+consecutive groups of rows.
 
 Recipe (one per tensor, fixed draw order input, skip, bias, gamma, beta):
 
@@ -22,6 +27,10 @@ Recipe (one per tensor, fixed draw order input, skip, bias, gamma, beta):
   ``uniform(lo, hi)``) and rounded once, round-to-nearest-even, to the I/O
   type (numpy converts float64 to float16 directly, without passing through
   float32).
+* An additive key-padding mask (``padmask(min_keep, fill)``): each row keeps
+  its first ``ceil(H * u)`` columns at 0, ``u ~ uniform(min_keep, 1)`` drawn
+  per row, and sets the rest to ``fill`` (e.g. -10000 or -inf) -- the
+  length mix of padded attention batches.
 """
 from __future__ import annotations
 
@@ -53,6 +62,12 @@ class Dist:
             return self.a + self.b * rng.standard_normal(shape)
         if self.kind == "uniform":
             return rng.uniform(self.a, self.b, shape)
+        if self.kind == "padmask":
+            n_rows, h = shape
+            keep = np.maximum(1, np.ceil(h * rng.uniform(self.a, 1.0, n_rows))).astype(np.int64)
+            out = np.zeros(shape)
+            out[np.arange(h)[None, :] >= keep[:, None]] = self.b
+            return out
         raise ValueError(f"unknown distribution {self.kind!r}")
 
 
@@ -62,6 +77,10 @@ def normal(mu: float, sigma: float) -> Dist:
 
 def uniform(lo: float, hi: float) -> Dist:
     return Dist("uniform", float(lo), float(hi))
+
+
+def padmask(min_keep: float, fill: float) -> Dist:
+    return Dist("padmask", float(min_keep), float(fill))
 
 
 @dataclass(frozen=True)
@@ -86,8 +105,12 @@ class Workload:
     residual: bool = False
     eps: float = 1e-12
     seed: int = 0
-    # "layer_norm", "simplified" (root-mean-square form) or "bias_add"
+    # "layer_norm", "simplified" (root-mean-square form), "bias_add" or
+    # "bias_softmax"
     op: str = "layer_norm"
+    # BiasSoftmax: bias rows reused by consecutive groups of rows (inner
+    # broadcast) instead of cyclically
+    inner: bool = False
 
     @property
     def hidden(self) -> int:
@@ -125,6 +148,18 @@ class Workload:
         n += r * h * b  # output
         n += r * h * b if self.residual else 0
         return int(n)
+
+    @property
+    def skip_group(self) -> int:
+        """Rows sharing one skip row under inner (grouped) reuse, else 0."""
+        return self.rows // self.skip_rows if self.inner and self.broadcast and self.skip_rows else 0
+
+    def skip_row_of(self, rows: np.ndarray) -> np.ndarray:
+        """Index of the skip row that each of ``rows`` reads."""
+        rows = np.asarray(rows, dtype=np.int64)
+        if not self.broadcast:
+            return rows
+        return rows // self.skip_group if self.inner else rows % self.skip_rows
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -245,6 +280,36 @@ EXTRA: Dict[str, Workload] = {
             eps=1e-5,
             seed=1013,
             op="simplified",
+        ),
+        # BiasSoftmax on attention scores: (batch, heads, queries, keys) data,
+        # softmax over the keys.  A per-sequence key-padding mask (B, 1, 1, K)
+        # is shared by the heads x queries rows of each sequence (inner
+        # broadcast); a per-head position bias (1, heads, Q, K) is shared by
+        # every sequence of the batch (outer broadcast).
+        Workload(
+            name="softmax_attn_16x16x512x512_f16_padmask",
+            shape=(16 * 16 * 512, 512),
+            dtype="f16",
+            skip_shape=(16, 512),
+            input_dist=normal(0, 2),
+            skip_dist=padmask(0.25, -float("inf")),
+            gamma_dist=None,
+            beta_dist=None,
+            seed=1021,
+            op="bias_softmax",
+            inner=True,
+        ),
+        Workload(
+            name="softmax_relpos_64x12x128x128_f32",
+            shape=(64 * 12 * 128, 128),
+            dtype="f32",
+            skip_shape=(12 * 128, 128),
+            input_dist=normal(0, 2),
+            skip_dist=normal(0, 1),
+            gamma_dist=None,
+            beta_dist=None,
+            seed=1022,
+            op="bias_softmax",
         ),
         Workload(
             name="rms_bert_base_8x128x768_f32",
@@ -374,18 +439,42 @@ def small_case(
     input_dist: Dist = normal(0, 1),
     skip_dist: Dist = normal(0, 1),
     op: str = "layer_norm",
+    inner: bool = False,
 ) -> Workload:
     """A workload for the flag/shape matrix of the parity tests.
 
     Rank 2 ``(rows, H)`` with an exact skip, or, when ``skip_rows`` is given
     and differs from ``rows``, rank 3 ``(rows // skip_rows, skip_rows, H)``
-    with an ``(S, H)`` skip broadcast across the batch.
+    with an ``(S, H)`` skip broadcast across the batch.  BiasSoftmax keeps
+    rank 2: ``(rows, H)`` data and ``(skip_rows, H)`` bias rows, reused by
+    groups (``inner``) or cyclically.
     """
+    softmax = op == "bias_softmax"
     if skip_rows is None or skip_rows == rows:
         shape, skip_shape = (rows, hidden), (rows, hidden)
+    elif softmax:
+        assert skip_rows > 0 and rows % skip_rows == 0
+        shape, skip_shape = (rows, hidden), (skip_rows, hidden)
     else:
         assert skip_rows > 0 and rows % skip_rows == 0
         shape, skip_shape = (rows // skip_rows, skip_rows, hidden), (skip_rows, hidden)
+    if softmax:
+        return Workload(
+            name=f"case_{op}_{rows}x{hidden}_{dtype}",
+            shape=shape,
+            dtype=dtype,
+            skip_shape=skip_shape,
+            input_dist=input_dist,
+            skip_dist=skip_dist,
+            gamma_dist=None,
+            beta_dist=None,
+            bias_dist=None,
+            residual=False,
+            eps=0.0,
+            seed=seed,
+            op=op,
+            inner=inner,
+        )
     bias_add = op == "bias_add"
     return Workload(
         name=f"case_{op}_{rows}x{hidden}_{dtype}",
