@@ -33,7 +33,9 @@ SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_me
          "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "softmax_attn_16x16x512x512_f16_padmask",
          "softmax_relpos_64x12x128x128_f32"]
 OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*
-KERNEL_SRC = os.path.join(ROOT, "transformer_residual_add_amd", "csrc", "skipln_kernels.hip")
+# Sources of the row kernels: counters taken on other sources are stale.
+KERNEL_SRC = [os.path.join(ROOT, "transformer_residual_add_amd", "csrc", f)
+              for f in ("skipln_device.h", "skipln_kernels.hip")]
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -58,8 +60,11 @@ def parse_args(argv=None):
 
 
 def source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def counter_traffic(kernel: str, workload: str):

@@ -1,0 +1,185 @@
+// Device-side building blocks shared by the row kernels (gfx950, wave64):
+// 16-byte chunk element types, DPP/swizzle cross-lane reductions, and the
+// skip-row mapping.  Included by the kernel sources only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "skipln_internal.h"
+
+namespace skipln {
+namespace device {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------------
+// Element types: a 16-byte chunk holds kPerChunk elements.
+// ------------------------------------------------------------------------
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static constexpr int kPerChunk = 4;
+    // Components are passed by value: __builtin_bit_cast applied directly to
+    // a vector component (r.y) reads component 0 with this compiler.
+    __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+    __device__ __forceinline__ static u32x4 narrow(const float* f) {
+        u32x4 r;
+        r.x = __float_as_uint(f[0]);
+        r.y = __float_as_uint(f[1]);
+        r.z = __float_as_uint(f[2]);
+        r.w = __float_as_uint(f[3]);
+        return r;
+    }
+    __device__ __forceinline__ static float load1(const void* p, int64_t i) {
+        return static_cast<const float*>(p)[i];
+    }
+    __device__ __forceinline__ static void store1(void* p, int64_t i, float v) {
+        static_cast<float*>(p)[i] = v;
+    }
+};
+
+template <>
+struct Elem<_Float16> {
+    static constexpr int kPerChunk = 8;
+    __device__ __forceinline__ static float lo(unsigned w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xFFFFu)));
+    }
+    __device__ __forceinline__ static float hi(unsigned w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
+    }
+    // Round to nearest even (the default rounding mode of the conversion).
+    __device__ __forceinline__ static unsigned pack(float a, float b) {
+        unsigned short ha = __builtin_bit_cast(unsigned short, static_cast<_Float16>(a));
+        unsigned short hb = __builtin_bit_cast(unsigned short, static_cast<_Float16>(b));
+        return static_cast<unsigned>(ha) | (static_cast<unsigned>(hb) << 16);
+    }
+    __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
+        f[0] = lo(r.x); f[1] = hi(r.x);
+        f[2] = lo(r.y); f[3] = hi(r.y);
+        f[4] = lo(r.z); f[5] = hi(r.z);
+        f[6] = lo(r.w); f[7] = hi(r.w);
+    }
+    __device__ __forceinline__ static u32x4 narrow(const float* f) {
+        u32x4 r;
+        r.x = pack(f[0], f[1]);
+        r.y = pack(f[2], f[3]);
+        r.z = pack(f[4], f[5]);
+        r.w = pack(f[6], f[7]);
+        return r;
+    }
+    __device__ __forceinline__ static float load1(const void* p, int64_t i) {
+        return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+    }
+    __device__ __forceinline__ static void store1(void* p, int64_t i, float v) {
+        static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+    }
+};
+
+// ------------------------------------------------------------------------
+// Cross-lane reductions with DPP (data-parallel primitives: a VALU operand
+// read from another lane of the same row of 16 lanes, no LDS traffic).
+// ------------------------------------------------------------------------
+// Lanes that a DPP move does not write (rows outside row_mask) return `Id`,
+// the identity of the reduction: 0 for sums, -inf for maxima.
+template <int Ctrl, int RowMask = 0xF>
+__device__ __forceinline__ float dpp(float v, float id) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, id),
+                                                                 __builtin_bit_cast(int, v), Ctrl, RowMask, 0xF,
+                                                                 false));
+}
+
+constexpr int kQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;  // lane 15 of each row into the next row
+constexpr int kRowBcast31 = 0x143;  // lane 31 into rows 2 and 3
+
+struct SumOp {
+    __device__ static float id() { return 0.0f; }
+    __device__ static float apply(float a, float b) { return a + b; }
+};
+// IEEE maxNum (v_max_f32): a NaN operand yields the other one.
+struct MaxOp {
+    __device__ static float id() { return -__builtin_inff(); }
+    __device__ static float apply(float a, float b) { return __builtin_fmaxf(a, b); }
+};
+
+// Reduction over aligned groups of G = 4, 8 or 16 lanes; every lane of a
+// group gets the same bits (each step combines a commutative pair).
+template <typename Op, int G>
+__device__ __forceinline__ float reduce_upto16(float v) {
+    static_assert(G == 4 || G == 8 || G == 16, "4, 8 or 16 lanes");
+    v = Op::apply(v, dpp<kQuadSwap1>(v, Op::id()));
+    v = Op::apply(v, dpp<kQuadSwap2>(v, Op::id()));
+    if constexpr (G >= 8) v = Op::apply(v, dpp<kRowHalfMirror>(v, Op::id()));  // lane i <-> 7-i: other quad
+    if constexpr (G >= 16) v = Op::apply(v, dpp<kRowMirror>(v, Op::id()));     // lane i <-> 15-i: other half
+    return v;
+}
+
+// Reduction over the whole wavefront, returned as a wave-uniform value.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v) {
+    v = reduce_upto16<Op, 16>(v);
+    v = Op::apply(v, dpp<kRowBcast15, 0xA>(v, Op::id()));  // rows 1, 3 combine rows 0, 2
+    v = Op::apply(v, dpp<kRowBcast31, 0xC>(v, Op::id()));  // rows 2, 3 combine rows 0+1
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce<SumOp>(v); }
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce<MaxOp>(v); }
+
+// Reduction over an aligned group of G lanes (G = 4, 8, 16, 32 or 64).
+template <typename Op, int G>
+__device__ __forceinline__ float group_reduce(float v) {
+    static_assert(G == 4 || G == 8 || G == 16 || G == 32 || G == 64, "group of 4..64 lanes");
+    if constexpr (G == 64) {
+        return wave_reduce<Op>(v);
+    } else if constexpr (G <= 16) {
+        return reduce_upto16<Op, G>(v);
+    } else {
+        v = reduce_upto16<Op, 16>(v);
+        // lane ^ 16 within each half-wave (swizzle bit mode: and 0x1F, xor 0x10)
+        return Op::apply(v, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F)));
+    }
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) { return group_reduce<SumOp, G>(v); }
+
+// Value of the first lane of each aligned group of G lanes (G <= 32: the
+// group's lane 0; G >= 64: the wavefront's lane 0, wave-uniform).
+template <int G>
+__device__ __forceinline__ float group_first(float v) {
+    if constexpr (G >= 64) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    } else {
+        // swizzle bit mode within 32 lanes: new lane = lane & and_mask
+        constexpr int kPattern = G == 4 ? 0x001C : G == 8 ? 0x0018 : G == 16 ? 0x0010 : 0x0000;
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), kPattern));
+    }
+}
+
+// Skip (bias) row read by data row `row`: the same row (exact), row mod
+// skip_rows (cyclic reuse), or row / skip_group (consecutive groups of rows
+// share one).  32-bit division whenever the row count fits.
+__device__ __forceinline__ int64_t skip_row_of(int64_t row, const Args& a, bool small_rows) {
+    if (a.skip_group > 0)
+        return small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) / static_cast<uint32_t>(a.skip_group))
+                          : row / a.skip_group;
+    if (a.skip_rows > 0)
+        return small_rows ? static_cast<int64_t>(static_cast<uint32_t>(row) % static_cast<uint32_t>(a.skip_rows))
+                          : row % a.skip_rows;
+    return row;
+}
+
+}  // namespace device
+}  // namespace skipln
