@@ -56,6 +56,12 @@ def parse_args(argv=None):
     p.add_argument("--variant", type=int, default=0, help="kernel family (SKIPLN_VARIANT_*), 0 = auto")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the operator, time the streaming copy of this many bytes")
+    p.add_argument("--summarize-counters", metavar="DIR", default=None,
+                   help="no GPU work: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR "
+                        "(<workload>_<COUNTER>/run_counter_collection.csv, copy1g_<COUNTER>/...) into "
+                        "a counters JSON (--counters-out)")
+    p.add_argument("--counters-out", default=None, help="where --summarize-counters writes (default: "
+                   "profiles/counters.json); run it on the tree the counters were taken on")
     return p.parse_args(argv)
 
 
@@ -275,8 +281,83 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _counter_rows(path: str, counter: str):
+    """(kernel name, value) of every dispatch in one rocprofv3 --pmc CSV."""
+    import csv
+
+    with open(path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") == counter:
+                yield row["Kernel_Name"], float(row["Counter_Value"])
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def summarize_counters(root: str, out_path: str) -> int:
+    """Per-dispatch medians of the library's kernel in each counter run,
+    scaled by the 1 GiB copy's reading of the same counter; writes
+    profiles/counters.json and prints a markdown table."""
+    import transformer_residual_add_amd as T
+    from transformer_residual_add_amd import _lib as L
+    from transformer_residual_add_amd import workloads as W
+
+    def lib_median(name, counter):
+        path = os.path.join(root, f"{name}_{counter}", "run_counter_collection.csv")
+        by = {}
+        for k, v in _counter_rows(path, counter):
+            if "skipln" in k:  # demangled or mangled (_ZN6skipln...) names
+                by.setdefault(k, []).append(v)
+        if not by:
+            raise SystemExit(f"no library dispatch in {path}")
+        k = max(by, key=lambda n: len(by[n]))
+        return _median(by[k]), len(by[k])
+
+    copy_bytes = 1 << 30
+    fetch_raw, _ = lib_median("copy1g", "FETCH_SIZE")
+    write_raw, _ = lib_median("copy1g", "WRITE_SIZE")
+    fetch_scale = copy_bytes / 1024 / fetch_raw
+    write_scale = copy_bytes / 1024 / write_raw
+    entries = []
+    print("| workload | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes | traffic / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    for name in [HEADLINE] + SWEEP:
+        if not os.path.isdir(os.path.join(root, f"{name}_FETCH_SIZE")):
+            continue
+        w = W.get(name)
+        kernel = T.select_kernel(w.hidden, L.F32 if w.dtype == "f32" else L.F16, True, 0, skip_mode(w, L), OPS[w.op])
+        f, n = lib_median(name, "FETCH_SIZE")
+        wr, _ = lib_median(name, "WRITE_SIZE")
+        fb, wb = int(round(f * 1024 * fetch_scale)), int(round(wr * 1024 * write_scale))
+        alg = w.algorithmic_bytes()
+        entries.append({"kernel": kernel, "workload": name, "dispatches": n, "fetch_kib_raw": round(f, 1),
+                        "write_kib_raw": round(wr, 1), "fetch_bytes": fb, "write_bytes": wb,
+                        "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 4),
+                        "source_sha256": source_sha()})
+        print(f"| {name} | {kernel} | {f:,.1f} | {wr:,.1f} | {fb:,} | {wb:,} | {(fb + wb) / alg:.3f} |")
+    data = {
+        "about": "HBM bytes per dispatch from rocprofv3 FETCH_SIZE and WRITE_SIZE (separate --pmc runs), each "
+                 "scaled by what the same counter reads for the streaming copy of 1 GiB (skipln_copy: 1 GiB "
+                 "read, 1 GiB written). source_sha256 is the kernel source the counters were taken on.",
+        "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                             "fetch_kib_raw": round(fetch_raw, 1), "write_kib_raw": round(write_raw, 1),
+                             "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5)},
+        "entries": entries,
+    }
+    with open(out_path, "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    print(f"calibration: FETCH_SIZE x{fetch_scale:.5f}, WRITE_SIZE x{write_scale:.5f}; wrote {out_path}")
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.counters_out or COUNTERS)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the operator has no multi-GPU path to time "
               f"(rows shard across GPUs with no communication); got --gpus {args.gpus}", file=sys.stderr)
