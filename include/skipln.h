@@ -79,7 +79,10 @@ enum {
     SKIPLN_ERR_LAUNCH = 8,      /* the HIP runtime refused the launch */
     SKIPLN_ERR_DEVICE = 9,      /* querying the current device failed */
     SKIPLN_ERR_VARIANT = 10,    /* unknown variant, geometry or tiling */
-    SKIPLN_ERR_OP = 11          /* unknown operation */
+    SKIPLN_ERR_OP = 11,         /* unknown operation */
+    SKIPLN_ERR_WORKSPACE = 12   /* the chosen kernels need a workspace: missing,
+                                   not 16-byte aligned, or smaller than
+                                   skipln_workspace_bytes() */
 };
 
 /* Operations sharing the row kernels (for the _variant / _config / validate /
@@ -94,8 +97,10 @@ enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 
 
 /* Kernel families, for skipln_forward_variant / skipln_select.  The automatic
  * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
- * kernel for longer rows of the normalizing operations, the generic kernel
- * for anything unaligned, not a whole number of chunks, or longer still. */
+ * kernel for longer rows of the reducing operations, then -- for calls that
+ * bring a workspace (skipln_forward_ws) -- the split-row kernels, and the
+ * generic kernel for anything unaligned, not a whole number of chunks, or
+ * longer still. */
 enum {
     SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
     SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
@@ -110,6 +115,14 @@ enum {
                                      norm, simplified and BiasSoftmax, 16-byte
                                      chunks, aligned pointers,
                                      hidden * 4 <= 163584 bytes */
+    SKIPLN_VARIANT_SPLITROW = 5,  /* rows cut into slices of 16 KiB per tensor,
+                                     one workgroup per slice, two kernels
+                                     (partial results, then merge and
+                                     normalize) through a workspace: layer norm,
+                                     simplified and BiasSoftmax, 16-byte chunks,
+                                     aligned pointers, at most 64 slices
+                                     (262144 float32 / 524288 float16 values);
+                                     skipln_forward_ws only */
     SKIPLN_VARIANT_GEOMETRY = 64  /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_rowtile_geometries(), for
                                      tests and tuning */
@@ -186,10 +199,39 @@ int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, 
  * batch_count with batch_count a multiple of bias_batch_count, else
  * SKIPLN_ERR_SHAPE.  out may equal data exactly, or bias when
  * bias_batch_count == batch_count; other overlaps are SKIPLN_ERR_ALIAS.
- * Ownership, streams and errors as for skipln_forward.
+ * workspace / workspace_bytes: NULL / 0, or a workspace as for
+ * skipln_forward_ws (size from skipln_workspace_bytes with
+ * SKIPLN_OP_BIAS_SOFTMAX, rows = batch_count, hidden = block_size and the
+ * skip form above), which lets rows longer than 40896 values split across
+ * workgroups (the manifest's long-row variants); without one they take the
+ * generic kernel.  Ownership, streams and errors as for skipln_forward.
  */
 int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t batch_count, int64_t block_size,
-                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, skipln_stream_t stream);
+                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, void* workspace,
+                        int64_t workspace_bytes, skipln_stream_t stream);
+
+/*
+ * Operation `op` with a caller-provided workspace, which lets the kernel
+ * choice (`variant`, SKIPLN_VARIANT_AUTO included) take the split-row kernels
+ * for rows too long for one workgroup.  workspace: device memory, 16-byte
+ * aligned, overlapping no tensor, of at least skipln_workspace_bytes() bytes
+ * for the same arguments; its contents on entry do not matter and are
+ * undefined afterwards; it must stay untouched until the enqueued work ends,
+ * and two calls in flight at once need two workspaces.  When the chosen
+ * kernel needs no workspace, workspace may be NULL.  Otherwise as
+ * skipln_forward_variant; SKIPLN_ERR_WORKSPACE when the workspace does not
+ * serve.
+ */
+int skipln_forward_ws(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                      const void* gamma, const void* beta, const void* bias,
+                      void* out, void* residual_out, int64_t rows, int64_t hidden,
+                      float eps, int dtype, int variant, void* workspace, int64_t workspace_bytes,
+                      skipln_stream_t stream);
+
+/* Workspace bytes skipln_forward_ws needs for these arguments (0: none), or a
+ * negative status code.  Host code only. */
+int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode, int64_t skip_rows,
+                               int variant);
 
 /* Operation `op` (SKIPLN_OP_*) with the kernel family forced
  * (SKIPLN_VARIANT_*); the result is the same operator.  For
@@ -242,6 +284,9 @@ int skipln_validate(int op, const void* input, const void* skip, int skip_mode, 
  * or a negative status code.  `aligned16` says whether every tensor pointer
  * is 16-byte aligned. */
 int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
+
+/* The same for skipln_forward_ws given a sufficient workspace. */
+int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
 
 /* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte
  * aligned, bytes % 16 == 0, no overlap), with the access pattern of the

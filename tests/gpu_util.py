@@ -91,14 +91,29 @@ class DeviceCase:
         self.out = empty(n)
         self.res = empty(n) if residual else None
 
-    def run(self, variant: int = L.VARIANT_AUTO, stream: int = 0, out=None, res="default"):
+    def workspace(self, variant: int = L.VARIANT_AUTO):
+        """(pointer, bytes) of a fresh device workspace for ``skipln_forward_ws``."""
+        import torch
+
+        w = self.w
+        n = T.workspace_bytes(OPS[w.op], w.rows, w.hidden, L.F32 if w.dtype == "f32" else L.F16, skip_mode(w),
+                              w.skip_rows if w.broadcast else 0, variant)
+        buf = torch.empty(max(n, 16), dtype=torch.uint8, device="cuda")
+        self._keep.append(buf)
+        return buf.data_ptr(), n
+
+    def run(self, variant: int = L.VARIANT_AUTO, stream: int = 0, out=None, res="default", workspace=None):
+        """``workspace``: None (skipln_forward_variant), True (a fresh one of the
+        size the call needs, through skipln_forward_ws) or (pointer, bytes)."""
         w = self.w
         p = lambda t: None if t is None else t.data_ptr()
         o = self.out if out is None else out
         r = self.res if res == "default" else res
+        if workspace is True:
+            workspace = self.workspace(variant)
         T.forward_raw(p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
                       w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
-                      stream, variant, OPS[w.op])
+                      stream, variant, OPS[w.op], workspace=workspace)
 
     def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0):
         w = self.w
@@ -176,13 +191,13 @@ def assert_bits_equal(got: np.ndarray, want: np.ndarray, what: str = "residual")
                              f"{got[tuple(idx)]!r} vs {want[tuple(idx)]!r}")
 
 
-def check_case(w, variant: int = L.VARIANT_AUTO, offset_elems: int = 0, inputs=None):
+def check_case(w, variant: int = L.VARIANT_AUTO, offset_elems: int = 0, inputs=None, workspace=None):
     """Run one workload through the C ABI and compare all rows with the oracle."""
     from transformer_residual_add_amd import workloads as W
 
     inputs = W.make_inputs(w) if inputs is None else inputs
     dc = DeviceCase(w, inputs, residual=w.residual, offset_elems=offset_elems)
-    dc.run(variant)
+    dc.run(variant, workspace=workspace)
     ref = oracle_rows(w, inputs)
     compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, ref)
     return dc, ref

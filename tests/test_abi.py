@@ -21,7 +21,7 @@ def _header():
 
 def test_header_functions_are_exported_and_bound():
     text = _header()
-    declared = set(re.findall(r"^(?:int|const char\*)\s+(skipln_\w+)\s*\(", text, re.M))
+    declared = set(re.findall(r"^(?:int|int64_t|const char\*)\s+(skipln_\w+)\s*\(", text, re.M))
     assert declared, "no declarations found"
     assert declared == set(L.SIGNATURES), f"binding and header differ: {declared ^ set(L.SIGNATURES)}"
     lib = L.load()
@@ -40,12 +40,12 @@ def test_header_enums_match_binding():
         "SKIPLN_ERR_DTYPE": L.ERR_DTYPE, "SKIPLN_ERR_MODE": L.ERR_MODE, "SKIPLN_ERR_EPS": L.ERR_EPS,
         "SKIPLN_ERR_ALIAS": L.ERR_ALIAS, "SKIPLN_ERR_UNSUPPORTED": L.ERR_UNSUPPORTED,
         "SKIPLN_ERR_LAUNCH": L.ERR_LAUNCH, "SKIPLN_ERR_DEVICE": L.ERR_DEVICE,
-        "SKIPLN_ERR_VARIANT": L.ERR_VARIANT, "SKIPLN_ERR_OP": L.ERR_OP,
+        "SKIPLN_ERR_VARIANT": L.ERR_VARIANT, "SKIPLN_ERR_OP": L.ERR_OP, "SKIPLN_ERR_WORKSPACE": L.ERR_WORKSPACE,
         "SKIPLN_OP_LAYER_NORM": L.OP_LAYER_NORM, "SKIPLN_OP_SIMPLIFIED": L.OP_SIMPLIFIED,
         "SKIPLN_OP_BIAS_ADD": L.OP_BIAS_ADD, "SKIPLN_OP_BIAS_SOFTMAX": L.OP_BIAS_SOFTMAX,
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
-        "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW,
+        "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW, "SKIPLN_VARIANT_SPLITROW": L.VARIANT_SPLITROW,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
@@ -54,7 +54,7 @@ def test_header_enums_match_binding():
 
 
 def test_status_strings():
-    for st in range(0, 12):
+    for st in range(0, 13):
         assert L.status_string(st) not in ("", "unknown status")
     assert L.status_string(99) == "unknown status"
 
@@ -143,7 +143,7 @@ def test_validate_operations(kw, status):
 
 
 def S(data=IN, bias=SK, out=OUT, batch=4, block=8, bias_rows=2, inner=0, dtype=0):
-    return L.load().skipln_bias_softmax(data, bias, out, batch, block, bias_rows, inner, dtype, None)
+    return L.load().skipln_bias_softmax(data, bias, out, batch, block, bias_rows, inner, dtype, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -279,3 +279,62 @@ def test_no_cpu_fallback_in_product_path():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from\s+oracle|import\s+oracle)|liboracle|skipln_oracle", text, re.M), \
                     f"{f} reaches into the oracle"
+
+
+# ------------------------------------------------------------- workspace --
+
+def test_workspace_sizes_and_split_selection():
+    lib = L.load()
+    wb = lambda op, rows, h, dt, mode=L.SKIP_EXACT, srows=0, v=L.VARIANT_AUTO: \
+        lib.skipln_workspace_bytes(op, rows, h, dt, mode, srows, v)
+    name_ws = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: \
+        L.kernel_name(lib.skipln_select_ws(op, h, dt, mode, 1, v))
+    name = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select(op, h, dt, mode, 1, v))
+    # 65536 float32 = 16 slices of 4096; 64 MiB of inputs per batch = 128 rows of x and skip
+    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == 64 * 16 * 16
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == 128 * 16 * 16
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 256 * 16 * 16  # skip not streamed
+    assert wb(L.OP_LAYER_NORM, 0, 65536, L.F32) == 0
+    assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32) == 0                       # row tiles need none
+    assert wb(L.OP_LAYER_NORM, 64, 20000, L.F32) == 0                      # LDS-staged
+    assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_SPLITROW) == 64 * 1 * 16
+    assert wb(L.OP_BIAS_ADD, 64, 65536, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert wb(L.OP_LAYER_NORM, 64, 65536, 9) == -L.ERR_DTYPE
+    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32, L.SKIP_BROADCAST, 3) == -L.ERR_SHAPE
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 64 * 16 * 16
+    # the automatic choice: split rows only where a workspace is at hand
+    assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
+    assert name_ws(L.OP_LAYER_NORM, 65536, L.F32) == "splitrow_f32"
+    assert name_ws(L.OP_SIMPLIFIED, 65536, L.F16) == "rms_splitrow_f16"
+    assert name_ws(L.OP_BIAS_SOFTMAX, 128256, L.F16) == "softmax_splitrow_f16"
+    assert name_ws(L.OP_LAYER_NORM, 20000, L.F32) == "ldsrow_f32"
+    assert name_ws(L.OP_LAYER_NORM, 4096, L.F32) == "rowtile_f32_g256_c4"
+    assert name_ws(L.OP_LAYER_NORM, 64 * 4096, L.F32) == "splitrow_f32"        # 64 slices
+    assert name_ws(L.OP_LAYER_NORM, 64 * 4096 + 4, L.F32) == "generic_f32"     # 65 slices
+    assert name_ws(L.OP_BIAS_ADD, 65536, L.F32) == "biasadd_generic_f32"
+    assert name(L.OP_LAYER_NORM, 64, L.F32, v=L.VARIANT_SPLITROW) == "splitrow_f32"
+    assert lib.skipln_select(L.OP_BIAS_ADD, 64, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert lib.skipln_select(L.OP_LAYER_NORM, 66, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+
+
+def FW(ws, nbytes, hidden=65536, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM):
+    return L.load().skipln_forward_ws(op, IN, SK, 0, 0, GA, BE, BI, OUT, RES, 4, hidden, 1e-5, L.F32, variant, ws,
+                                      nbytes, None)
+
+
+WS = 0x10000000  # beyond every fake tensor (4 rows of 65536 float32 = 1 MiB each)
+
+
+def test_forward_ws_workspace_checks():
+    """Each status here returns before any HIP call."""
+    need = L.load().skipln_workspace_bytes(L.OP_LAYER_NORM, 4, 65536, L.F32, 0, 0, 0)
+    assert need == 4 * 16 * 16
+    assert FW(None, 0) == L.ERR_WORKSPACE
+    assert FW(WS, need - 1) == L.ERR_WORKSPACE
+    assert FW(WS + 8, need) == L.ERR_WORKSPACE          # not 16-byte aligned
+    assert FW(WS, -1) == L.ERR_WORKSPACE
+    assert FW(IN, need) == L.ERR_ALIAS                  # overlaps the input
+    assert FW(OUT + 64, need) == L.ERR_ALIAS
+    assert FW(WS, need, variant=L.VARIANT_LDSROW) == L.ERR_UNSUPPORTED
+    assert FW(None, 0, hidden=64, variant=L.VARIANT_SPLITROW) == L.ERR_WORKSPACE
+    assert FW(WS, need, op=L.OP_BIAS_ADD, variant=L.VARIANT_SPLITROW) == L.ERR_UNSUPPORTED

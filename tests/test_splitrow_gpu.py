@@ -1,0 +1,199 @@
+"""GPU parity of the split-row kernels: rows cut into 16 KiB slices, one
+workgroup per slice, partial results merged through a workspace -- layer
+normalization, its root-mean-square form and BiasSoftmax, against the
+oracle with the same tolerances as the single-workgroup kernels."""
+import numpy as np
+import pytest
+
+import transformer_residual_add_amd as T
+from transformer_residual_add_amd import _lib as L
+from transformer_residual_add_amd import workloads as W
+
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+SPLIT = L.VARIANT_SPLITROW
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    L.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def norm_case(rows, hidden, dt, op, bcast=False, flags=(True, True, True), seed=1, mu=0.0):
+    beta, bias, residual = flags
+    return W.small_case(rows, hidden, dt, skip_rows=4 if bcast else None, beta=beta, bias=bias, residual=residual,
+                        eps=1e-5, seed=seed, input_dist=W.normal(mu, 1), op=op)
+
+
+def softmax_case(rows, hidden, dt, mode="exact", seed=1, bias_rows=4):
+    return W.small_case(rows, hidden, dt, skip_rows=None if mode == "exact" else bias_rows, seed=seed,
+                        input_dist=W.normal(0, 2), skip_dist=W.normal(0, 1), op="bias_softmax",
+                        inner=mode == "inner")
+
+
+# one slice (ragged and full), several slices with a ragged last one, many slices
+SIZES_F32 = [4, 64, 4096, 4100, 12288, 40960, 65536, 100000]
+SIZES_F16 = [8, 64, 8192, 8200, 40960, 131072, 128256]
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified"])
+@pytest.mark.parametrize("dt_hidden", [("f32", h) for h in SIZES_F32] + [("f16", h) for h in SIZES_F16],
+                         ids=lambda t: f"{t[0]}_h{t[1]}")
+@pytest.mark.parametrize("form", [(False, (True, True, True)), (True, (False, False, False)),
+                                  (False, (True, False, True))], ids=["exact_all", "bcast_none", "exact_beta_res"])
+def test_split_normalizations(op, dt_hidden, form):
+    dt, hidden = dt_hidden
+    bcast, flags = form
+    rows = 12 if hidden > 50000 else 24
+    w = norm_case(rows, hidden, dt, op, bcast, flags, seed=hidden % 977)
+    U.note(f"split {op} {dt} H={hidden} bcast={bcast} flags={flags}")
+    U.check_case(w, variant=SPLIT, workspace=True)
+
+
+@pytest.mark.parametrize("dt_hidden", [("f32", h) for h in SIZES_F32] + [("f16", h) for h in SIZES_F16],
+                         ids=lambda t: f"{t[0]}_h{t[1]}")
+@pytest.mark.parametrize("mode", ["exact", "outer", "inner"])
+def test_split_softmax(dt_hidden, mode):
+    dt, hidden = dt_hidden
+    rows = 12 if hidden > 50000 else 24
+    w = softmax_case(rows, hidden, dt, mode, seed=hidden % 991)
+    U.note(f"split softmax {dt} H={hidden} {mode}")
+    U.check_case(w, variant=SPLIT, workspace=True)
+
+
+@pytest.mark.parametrize("dt,hidden,op", [("f32", 65536, "layer_norm"), ("f16", 131072, "simplified"),
+                                          ("f16", 128256, "bias_softmax"), ("f32", 262144, "layer_norm")])
+def test_split_auto_with_workspace(dt, hidden, op):
+    """Rows beyond the LDS capacity: the automatic choice with a workspace."""
+    code = L.F32 if dt == "f32" else L.F16
+    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True).endswith(f"splitrow_{dt}")
+    w = (softmax_case(8, hidden, dt, "inner", bias_rows=2) if op == "bias_softmax"
+         else norm_case(8, hidden, dt, op, seed=3))
+    U.note(f"split auto {op} {dt} H={hidden}")
+    U.check_case(w, workspace=True)
+
+
+@pytest.mark.parametrize("dt,hidden", [("f32", 65536), ("f16", 131072)])
+def test_split_several_batches(dt, hidden):
+    """More rows than one batch holds (64 MiB of streamed inputs): the
+    workspace is reused batch after batch on the same stream."""
+    row_bytes = hidden * (4 if dt == "f32" else 2)
+    per_batch = (64 << 20) // (2 * row_bytes)
+    rows = 2 * per_batch + 7
+    w = norm_case(rows, hidden, dt, "layer_norm", seed=11)
+    U.note(f"split batches {dt} H={hidden} rows={rows} ({per_batch} per batch)")
+    U.check_case(w, workspace=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("mu", [100.0, 1000.0])
+def test_split_large_offset_rows(dt, mu):
+    w = norm_case(8, 65536, dt, "layer_norm", seed=int(mu), mu=mu if dt == "f32" else mu / 10)
+    U.note(f"split offset {mu} {dt}")
+    U.check_case(w, variant=SPLIT, workspace=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_split_softmax_special_rows(dt):
+    """Masked slices (-inf over whole workgroups), a row of -inf (NaN), a NaN,
+    +inf, huge spread, a large offset."""
+    hidden = 40960 if dt == "f32" else 81920  # 10 slices
+    rng = np.random.default_rng(4)
+    rows = 8
+    x = rng.standard_normal((rows, hidden)) * 2
+    b = np.zeros((rows, hidden))
+    b[0, 5000:] = -np.inf           # slices 2.. fully masked
+    b[1, :] = -np.inf               # NaN row
+    x[2, 12345] = np.nan
+    x[3, hidden - 1] = np.inf
+    x[4] *= 30
+    x[5] += 1000.0 if dt == "f32" else 50000.0
+    b[6, : hidden - 3] = -np.inf    # only the last slice's tail kept
+    w = softmax_case(rows, hidden, dt, "exact", seed=0)
+    inputs = {"input": x.astype(w.np_dtype), "skip": b.astype(w.np_dtype), "gamma": None, "beta": None,
+              "bias": None}
+    U.note(f"split softmax special {dt}")
+    dc, _ = U.check_case(w, variant=SPLIT, inputs=inputs, workspace=True)
+    y = dc.host(dc.out)
+    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2])) and np.all(np.isnan(y[3]))
+    assert np.all(y[0, 5000:] == 0) and not np.isnan(y[6]).any()
+
+
+def test_split_workspace_errors_enqueue_nothing():
+    import torch
+
+    w = norm_case(4, 65536, "f32", "layer_norm", seed=2)
+    dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
+    ptr, need = dc.workspace()
+    before = dc.out.clone()
+    for ws in ((None, 0), (ptr, need - 16), (ptr + 8, need)):
+        with pytest.raises(T.SkiplnError) as e:
+            dc.run(workspace=ws)
+        assert e.value.status == L.ERR_WORKSPACE
+    with pytest.raises(T.SkiplnError) as e:
+        dc.run(workspace=(dc.x.data_ptr(), need))
+    assert e.value.status == L.ERR_ALIAS
+    torch.cuda.synchronize()
+    assert torch.equal(dc.out.view(torch.int32), before.view(torch.int32))
+
+
+def test_split_wrappers_allocate_their_workspace():
+    import torch
+
+    from oracle import oracle as O
+
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((2, 3, 65536)).astype(np.float32)
+    sk = rng.standard_normal((2, 3, 65536)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, 65536).astype(np.float32)
+    out, res = T.skip_layer_norm(torch.from_numpy(x).cuda(), torch.from_numpy(sk).cuda(), torch.from_numpy(g).cuda(),
+                                 epsilon=1e-5, return_residual=True)
+    torch.cuda.synchronize()
+    ref = O.skip_layer_norm(x.reshape(6, -1), sk.reshape(6, -1), g, None, None, 1e-5, residual=True)
+    U.assert_out_close(out.cpu().numpy().reshape(6, -1), ref["y"], "f32")
+    U.assert_bits_equal(res.cpu().numpy().reshape(6, -1), ref["residual"])
+    logits = (rng.standard_normal((4, 1, 128256)) * 3).astype(np.float16)
+    bias = (rng.standard_normal(128256)).astype(np.float16)
+    y = T.bias_softmax(torch.from_numpy(logits).cuda(), torch.from_numpy(bias).cuda(), True, axis=-1)
+    torch.cuda.synchronize()
+    ref = O.bias_softmax(logits.reshape(4, -1), bias.reshape(1, -1), True)
+    U.assert_out_close(y.cpu().numpy().reshape(4, -1), ref, "f16", "vocab softmax", tol=U.SOFTMAX_TOL)
+    # on a side stream: the workspace outlives the call until the stream's work ends
+    s = torch.cuda.Stream()
+    ld, bd = torch.from_numpy(logits).cuda(), torch.from_numpy(bias).cuda()
+    s.wait_stream(torch.cuda.current_stream())
+    y2 = T.bias_softmax(ld, bd, True, axis=-1, stream=s)
+    s.synchronize()
+    assert torch.equal(y2, y)
+
+
+def test_split_graph_replay():
+    import torch
+
+    w = softmax_case(16, 65536, "f32", "outer", bias_rows=4, seed=5)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=False)
+    ws = dc.workspace()
+    dc.run(workspace=ws)
+    first = dc.out.clone()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dc.run(stream=s.cuda_stream, workspace=ws)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        dc.run(stream=s.cuda_stream, workspace=ws)
+    for _ in range(3):
+        dc.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out.view(torch.int32), first.view(torch.int32))
+    U.compare(w, dc.host(dc.out), None, U.oracle_rows(w, inputs))

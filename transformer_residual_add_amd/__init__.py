@@ -21,33 +21,78 @@ from ._lib import SkiplnError  # noqa: F401
 DEFAULT_EPSILON = 9.999999960041972e-13
 
 __all__ = ["skip_layer_norm", "bias_add", "bias_softmax", "bias_softmax_raw", "softmax_shape", "forward_raw",
-           "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
+           "workspace_bytes", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
 
 
 def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: Optional[int],
                 beta_ptr: Optional[int], bias_ptr: Optional[int], out_ptr: int, residual_ptr: Optional[int],
                 rows: int, hidden: int, eps: float, dtype: int, stream: int = 0,
-                variant: int = _lib.VARIANT_AUTO, op: int = _lib.OP_LAYER_NORM) -> None:
-    """``skipln_forward_variant`` on raw device pointers; raises SkiplnError."""
-    st = _lib.load().skipln_forward_variant(
-        op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
-        out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
+                variant: int = _lib.VARIANT_AUTO, op: int = _lib.OP_LAYER_NORM,
+                workspace: Optional[tuple] = None) -> None:
+    """``skipln_forward_variant`` on raw device pointers, or
+    ``skipln_forward_ws`` when ``workspace`` = (pointer, bytes) is given;
+    raises SkiplnError."""
+    lib = _lib.load()
+    if workspace is None:
+        st = lib.skipln_forward_variant(
+            op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
+            out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
+    else:
+        st = lib.skipln_forward_ws(
+            op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
+            out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, workspace[0] or None, workspace[1],
+            stream or None)
     _lib.check(st, "skipln_forward")
 
 
+def workspace_bytes(op: int, rows: int, hidden: int, dtype: int, skip_mode: int = _lib.SKIP_EXACT,
+                    skip_rows: int = 0, variant: int = _lib.VARIANT_AUTO) -> int:
+    """Device workspace ``skipln_forward_ws`` needs for these arguments (0: none)."""
+    n = _lib.load().skipln_workspace_bytes(op, rows, hidden, dtype, skip_mode, skip_rows, variant)
+    if n < 0:
+        raise SkiplnError(-n, "skipln_workspace_bytes")
+    return int(n)
+
+
+def _hold(t, stream) -> None:
+    """Keep workspace ``t`` (allocated on the current stream) from being reused
+    before work enqueued on ``stream`` ends."""
+    import torch
+
+    if t is None or stream is None:
+        return
+    t.record_stream(torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream)
+
+
+def _workspace(nbytes: int, device):
+    """(tensor, (pointer, bytes)) of a device workspace, or (None, None)."""
+    import torch
+
+    if nbytes <= 0:
+        return None, None
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t, (t.data_ptr(), nbytes)
+
+
 def bias_softmax_raw(data_ptr: int, bias_ptr: int, out_ptr: int, batch_count: int, block_size: int,
-                     bias_batch_count: int, is_inner_broadcast: bool, dtype: int, stream: int = 0) -> None:
-    """``skipln_bias_softmax`` on raw device pointers; raises SkiplnError."""
+                     bias_batch_count: int, is_inner_broadcast: bool, dtype: int, stream: int = 0,
+                     workspace: Optional[tuple] = None) -> None:
+    """``skipln_bias_softmax`` on raw device pointers (``workspace`` = (pointer,
+    bytes) or None); raises SkiplnError."""
+    ws_ptr, ws_bytes = workspace if workspace is not None else (None, 0)
     st = _lib.load().skipln_bias_softmax(data_ptr or None, bias_ptr or None, out_ptr or None, batch_count,
                                          block_size, bias_batch_count, 1 if is_inner_broadcast else 0, dtype,
-                                         stream or None)
+                                         ws_ptr or None, ws_bytes, stream or None)
     _lib.check(st, "skipln_bias_softmax")
 
 
 def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO,
-                  skip_mode: int = _lib.SKIP_EXACT, op: int = _lib.OP_LAYER_NORM) -> str:
-    """Name of the kernel a call with this operation, hidden size and skip form would launch."""
-    kid = _lib.load().skipln_select(op, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
+                  skip_mode: int = _lib.SKIP_EXACT, op: int = _lib.OP_LAYER_NORM, workspace: bool = False) -> str:
+    """Name of the kernel a call with this operation, hidden size and skip form
+    would launch (``workspace``: a call that brings a workspace)."""
+    lib = _lib.load()
+    fn = lib.skipln_select_ws if workspace else lib.skipln_select
+    kid = fn(op, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
     if kid < 0:
         raise SkiplnError(-kid, "skipln_select")
     return _lib.kernel_name(kid)
@@ -121,13 +166,18 @@ def skip_layer_norm(input, skip, gamma, beta=None, bias=None, epsilon: float = D
     if residual_out is not None and residual_out.shape != input.shape:
         raise ValueError("residual_out must have the input's shape")
     s = _stream_handle(stream, input.device)
+    op = _lib.OP_SIMPLIFIED if simplified else _lib.OP_LAYER_NORM
     with torch.cuda.device(input.device):
+        # Rows too long for one workgroup split across workgroups through a
+        # small workspace (torch's caching allocator provides it).
+        ws_t, ws = _workspace(workspace_bytes(op, rows, h, code, mode, skip_rows, variant) if rows else 0,
+                              input.device)
         forward_raw(input.data_ptr(), skip.data_ptr(), mode, skip_rows, gamma.data_ptr(),
                     beta.data_ptr() if beta is not None else None,
                     bias.data_ptr() if bias is not None else None, out.data_ptr(),
                     residual_out.data_ptr() if residual_out is not None else None,
-                    rows, h, float(epsilon), code, s, variant,
-                    _lib.OP_SIMPLIFIED if simplified else _lib.OP_LAYER_NORM)
+                    rows, h, float(epsilon), code, s, variant, op, workspace=ws)
+        _hold(ws_t, stream)
     if return_residual:
         return out, residual_out
     return out
@@ -199,13 +249,18 @@ def bias_softmax(data, bias, is_inner_broadcast: bool, axis: int = 1, *, out=Non
     elif out.shape != data.shape:
         raise ValueError("out must have data's shape")
     s = _stream_handle(stream, data.device)
+    mode = (_lib.SKIP_EXACT if bias_rows == batch
+            else _lib.SKIP_BROADCAST_INNER if is_inner_broadcast else _lib.SKIP_BROADCAST)
     with torch.cuda.device(data.device):
+        ws_t, ws = None, None
+        if batch * block > 0 and 0 < bias_rows <= batch and batch % bias_rows == 0:
+            ws_t, ws = _workspace(workspace_bytes(_lib.OP_BIAS_SOFTMAX, batch, block, code, mode, bias_rows, variant),
+                                  data.device)
         if variant == _lib.VARIANT_AUTO:
             bias_softmax_raw(data.data_ptr(), bias.data_ptr(), out.data_ptr(), batch, block, bias_rows,
-                             is_inner_broadcast, code, s)
+                             is_inner_broadcast, code, s, workspace=ws)
         elif batch * block > 0:
-            mode = (_lib.SKIP_EXACT if bias_rows == batch
-                    else _lib.SKIP_BROADCAST_INNER if is_inner_broadcast else _lib.SKIP_BROADCAST)
             forward_raw(data.data_ptr(), bias.data_ptr(), mode, bias_rows, None, None, None, out.data_ptr(), None,
-                        batch, block, 0.0, code, s, variant, _lib.OP_BIAS_SOFTMAX)
+                        batch, block, 0.0, code, s, variant, _lib.OP_BIAS_SOFTMAX, workspace=ws)
+        _hold(ws_t, stream)
     return out

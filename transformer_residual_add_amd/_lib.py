@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(PKG, "libskipln.so")
 F32, F16 = 0, 1
 SKIP_EXACT, SKIP_BROADCAST, SKIP_BROADCAST_INNER = 0, 1, 2
 OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS = 0, 1, 2, 3, 4, 5, 6
-ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT, ERR_OP = 7, 8, 9, 10, 11
+ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT, ERR_OP, ERR_WORKSPACE = 7, 8, 9, 10, 11, 12
 OP_LAYER_NORM, OP_SIMPLIFIED, OP_BIAS_ADD, OP_BIAS_SOFTMAX = 0, 1, 2, 3
-VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE, VARIANT_LDSROW = 0, 1, 2, 3, 4
+VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE, VARIANT_LDSROW, VARIANT_SPLITROW = 0, 1, 2, 3, 4, 5
 VARIANT_GEOMETRY = 64
 TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
 
@@ -30,7 +30,11 @@ SIGNATURES = {
     "skipln_forward_simplified": (_i32, [_vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
                                          _vp]),
     "skipln_bias_add": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp]),
-    "skipln_bias_softmax": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp]),
+    "skipln_bias_softmax": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _vp]),
+    "skipln_forward_ws": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32, _i32,
+                                 _vp, _i64, _vp]),
+    "skipln_workspace_bytes": (_i64, [_i32, _i64, _i64, _i32, _i32, _i64, _i32]),
+    "skipln_select_ws": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "skipln_forward_variant": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,
                                       _i32, _vp]),
     "skipln_forward_config": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32,

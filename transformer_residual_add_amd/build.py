@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskipln.so")
-SOURCES = [os.path.join(CSRC, "skipln_kernels.hip"), os.path.join(CSRC, "skipln_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_api.cpp")]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -135,17 +135,23 @@ bool all_aligned16(const Call& c) {
            aligned16(c.out) && aligned16(c.residual);
 }
 
-// Kernel id (>= 0) for this variant, or -status.
-int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant) {
+// Kernel id (>= 0) for this variant, or -status.  with_workspace: the call
+// brings a workspace, so the automatic choice may take the split-row kernels.
+int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant, bool with_workspace) {
     const int base = (op * 2 + dtype) * skipln::kIdsPerType;
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
     if (variant == SKIPLN_VARIANT_GENERIC) return base + skipln::kGenericIndex;
     const bool lds_ok = vec_ok && skipln::ldsrow_holds(op, hidden, dtype);
+    const bool split_ok = vec_ok && skipln::split_holds(op, hidden, dtype);
     if (variant == SKIPLN_VARIANT_LDSROW) return lds_ok ? base + skipln::kLdsRowIndex : -SKIPLN_ERR_UNSUPPORTED;
-    // Long rows of the normalizing operations: staged in LDS.
-    if (variant == SKIPLN_VARIANT_AUTO && lds_ok && hidden / v > skipln::kRowtileMaxAutoChunks)
-        return base + skipln::kLdsRowIndex;
+    if (variant == SKIPLN_VARIANT_SPLITROW) return split_ok ? base + skipln::kSplitRowIndex : -SKIPLN_ERR_UNSUPPORTED;
+    // Long rows of the reducing operations: staged in LDS; beyond its
+    // capacity split across workgroups when a workspace is at hand.
+    if (variant == SKIPLN_VARIANT_AUTO && hidden / v > skipln::kRowtileMaxAutoChunks) {
+        if (lds_ok) return base + skipln::kLdsRowIndex;
+        if (split_ok && with_workspace) return base + skipln::kSplitRowIndex;
+    }
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
         variant == SKIPLN_VARIANT_MULTIWAVE) {
         const int g =
@@ -204,16 +210,43 @@ int status_of(hipError_t e) {
     return SKIPLN_ERR_LAUNCH;
 }
 
-// Validate, choose and launch; `tiling` == nullptr: automatic tiling.
-int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_t stream) {
+// A caller's workspace: device memory for partial results.
+struct Workspace {
+    void* ptr;
+    int64_t bytes;
+};
+
+// The workspace a split-row launch of this call needs.
+int64_t workspace_needed(const Call& c) { return skipln::split_workspace_bytes(make_args(c), c.dtype); }
+
+// Validate, choose and launch; `tiling` == nullptr: automatic tiling;
+// `ws` == nullptr: the call brings no workspace.
+int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_t stream,
+        const Workspace* ws = nullptr) {
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
-    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c), variant);
+    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c), variant,
+                          ws != nullptr);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
     const skipln::Args a = make_args(c);
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int index = id % skipln::kIdsPerType;
+    if (index == skipln::kSplitRowIndex) {
+        if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the split-row kernels have no tiling
+        if (!ws || !ws->ptr || !aligned16(ws->ptr) || ws->bytes < workspace_needed(c)) return SKIPLN_ERR_WORKSPACE;
+        const int64_t row_bytes = c.hidden * (c.dtype == SKIPLN_F32 ? 4 : 2);
+        const Range w = span(ws->ptr, ws->bytes);
+        const Range tensors[] = {
+            span(c.input, c.rows * row_bytes),
+            span(c.skip, (c.skip_mode != SKIPLN_SKIP_EXACT ? c.skip_rows : c.rows) * row_bytes),
+            span(c.gamma, c.gamma ? row_bytes : 0), span(c.beta, c.beta ? row_bytes : 0),
+            span(c.bias, c.bias ? row_bytes : 0), span(c.out, c.rows * row_bytes),
+            span(c.residual, c.residual ? c.rows * row_bytes : 0)};
+        for (const Range& t : tensors)
+            if (overlap(w, t)) return SKIPLN_ERR_ALIAS;
+        return status_of(skipln::launch_split(a, c.op, c.dtype, ws->ptr, s));
+    }
     if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, c.op, c.dtype, s));
     if (index == skipln::kLdsRowIndex) {
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
@@ -239,7 +272,41 @@ int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned,
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant, false);
+}
+
+int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
+    if (!known_op(op)) return -SKIPLN_ERR_OP;
+    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
+    if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
+    if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant, true);
+}
+
+int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode, int64_t skip_rows,
+                               int variant) {
+    if (!known_op(op)) return -SKIPLN_ERR_OP;
+    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
+    if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
+    if (rows < 0 || hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
+    if (skip_mode != SKIPLN_SKIP_EXACT && (skip_rows <= 0 || rows % skip_rows != 0)) return -SKIPLN_ERR_SHAPE;
+    const int id = select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, true, variant, true);
+    if (id < 0) return id;
+    if (id % skipln::kIdsPerType != skipln::kSplitRowIndex || rows == 0) return 0;
+    Call c = make_call(op, nullptr, nullptr, skip_mode, skip_rows, nullptr, nullptr, nullptr, nullptr, nullptr, rows,
+                       hidden, 0.0f, dtype);
+    return workspace_needed(c);
+}
+
+int skipln_forward_ws(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                      const void* gamma, const void* beta, const void* bias, void* out, void* residual_out,
+                      int64_t rows, int64_t hidden, float eps, int dtype, int variant, void* workspace,
+                      int64_t workspace_bytes, skipln_stream_t stream) {
+    if (workspace_bytes < 0) return SKIPLN_ERR_WORKSPACE;
+    const Workspace ws{workspace, workspace_bytes};
+    return run(make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                         dtype),
+               variant, nullptr, stream, &ws);
 }
 
 int skipln_forward_variant(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
@@ -288,7 +355,8 @@ int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, 
 }
 
 int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t batch_count, int64_t block_size,
-                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, skipln_stream_t stream) {
+                        int64_t bias_batch_count, int is_inner_broadcast, int dtype, void* workspace,
+                        int64_t workspace_bytes, skipln_stream_t stream) {
     if (batch_count < 0 || block_size < 0 || bias_batch_count < 0) return SKIPLN_ERR_SHAPE;
     // `biasContract`: empty data with an empty bias is valid and does nothing.
     if ((batch_count == 0 || block_size == 0) && (bias_batch_count == 0 || block_size == 0)) {
@@ -302,9 +370,13 @@ int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t b
     const int mode = bias_batch_count == batch_count
                          ? SKIPLN_SKIP_EXACT
                          : (is_inner_broadcast ? SKIPLN_SKIP_BROADCAST_INNER : SKIPLN_SKIP_BROADCAST);
-    return skipln_forward_variant(SKIPLN_OP_BIAS_SOFTMAX, data, bias, mode, bias_batch_count, nullptr, nullptr,
-                                  nullptr, out, nullptr, batch_count, block_size, 0.0f, dtype, SKIPLN_VARIANT_AUTO,
-                                  stream);
+    if (workspace == nullptr)
+        return skipln_forward_variant(SKIPLN_OP_BIAS_SOFTMAX, data, bias, mode, bias_batch_count, nullptr, nullptr,
+                                      nullptr, out, nullptr, batch_count, block_size, 0.0f, dtype, SKIPLN_VARIANT_AUTO,
+                                      stream);
+    return skipln_forward_ws(SKIPLN_OP_BIAS_SOFTMAX, data, bias, mode, bias_batch_count, nullptr, nullptr, nullptr,
+                             out, nullptr, batch_count, block_size, 0.0f, dtype, SKIPLN_VARIANT_AUTO, workspace,
+                             workspace_bytes, stream);
 }
 
 int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t stream) {
@@ -334,6 +406,7 @@ const char* skipln_status_string(int status) {
         case SKIPLN_ERR_DEVICE: return "no usable HIP device";
         case SKIPLN_ERR_VARIANT: return "unknown variant, geometry or tiling";
         case SKIPLN_ERR_OP: return "unknown operation";
+        case SKIPLN_ERR_WORKSPACE: return "the workspace is missing, misaligned or too small";
         default: return "unknown status";
     }
 }

@@ -48,10 +48,12 @@ constexpr int kOpBiasSoftmax = 3; // BiasSoftmax: softmax over the row of x + sk
 constexpr int kNumOps = 4;
 
 // Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
-// 1.. = row tiles, kLdsRowIndex = the LDS-staged long-row kernel.
+// 1.. = row tiles, kSplitRowIndex = the split-row kernel pair, kLdsRowIndex =
+// the LDS-staged long-row kernel.
 constexpr int kIdsPerType = 64;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
+constexpr int kSplitRowIndex = 62;
 constexpr int kLdsRowIndex = 63;
 
 // LDS a block may use on gfx950 (160 KiB), less room for the reduction
@@ -78,6 +80,13 @@ hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t stream);
 // row of binary32 values within kLdsRowBytes).
 bool ldsrow_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+// Split-row kernels (rows cut into slices of 1024 chunks, one workgroup per
+// slice, partials through a caller-provided workspace): whether they run
+// this operation and row (16-byte chunks, at most 64 slices), the workspace
+// bytes a launch needs, and the launch (workspace 16-byte aligned).
+bool split_holds(int op, int64_t hidden, int dtype);
+int64_t split_workspace_bytes(const Args& a, int dtype);
+hipError_t launch_split(const Args& a, int op, int dtype, void* workspace, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln

@@ -835,7 +835,7 @@ constexpr Geom kGeoms[] = {
     {32, 2, 256},  {128, 2, 256}, {32, 4, 256},   {16, 8, 256},
 };
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
-static_assert(kRowtileFirst + kNumGeoms <= kLdsRowIndex, "kernel index ranges are disjoint");
+static_assert(kRowtileFirst + kNumGeoms <= kSplitRowIndex, "kernel index ranges are disjoint");
 
 // Automatic choice: the first entry whose capacity holds the row's chunks.
 // Short rows are latency bound: one chunk per lane spreads a row over more
@@ -991,6 +991,8 @@ struct NameTable {
                         snprintf(dst, 48, "%sgeneric_%s", op_prefix[op], tn[t]);
                     } else if (i == kLdsRowIndex) {
                         snprintf(dst, 48, "%sldsrow_%s", op_prefix[op], tn[t]);
+                    } else if (i == kSplitRowIndex) {
+                        snprintf(dst, 48, "%ssplitrow_%s", op_prefix[op], tn[t]);
                     } else if (gi >= 0 && gi < kNumGeoms) {
                         const Geom& g = kGeoms[gi];
                         const int default_block = g.g > 256 ? g.g : 256;
