@@ -31,11 +31,11 @@ CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 HEADLINE = "bert_base_8x128x768_f32"
 SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_mean100",
          "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "softmax_attn_16x16x512x512_f16_padmask",
-         "softmax_relpos_64x12x128x128_f32"]
+         "softmax_relpos_64x12x128x128_f32", "softmax_vocab_4096x128256_f16"]
 OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*
 # Sources of the row kernels: counters taken on other sources are stale.
 KERNEL_SRC = [os.path.join(ROOT, "transformer_residual_add_amd", "csrc", f)
-              for f in ("skipln_device.h", "skipln_kernels.hip")]
+              for f in ("skipln_device.h", "skipln_kernels.hip", "skipln_split.hip")]
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -62,6 +62,8 @@ def parse_args(argv=None):
                         "a counters JSON (--counters-out)")
     p.add_argument("--counters-out", default=None, help="where --summarize-counters writes (default: "
                    "profiles/counters.json); run it on the tree the counters were taken on")
+    p.add_argument("--counter-steps", type=int, default=12,
+                   help="steps (warm-up included) each counter run made, for --summarize-counters")
     return p.parse_args(argv)
 
 
@@ -123,7 +125,10 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     code = L.F32 if w.dtype == "f32" else L.F16
     op = OPS[w.op]
     mode = skip_mode(w, L)
-    kernel = T.select_kernel(w.hidden, code, True, variant, mode, op)
+    # Rows too long for one workgroup split across workgroups through a
+    # workspace (one suffices: the steps run in order on one stream).
+    ws_bytes = T.workspace_bytes(op, w.rows, w.hidden, code, mode, w.skip_rows if w.broadcast else 0, variant)
+    kernel = T.select_kernel(w.hidden, code, True, variant, mode, op, workspace=ws_bytes > 0)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.
@@ -139,12 +144,14 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     srows = w.skip_rows if w.broadcast else 0
     eps = float(w.eps)
     ptr = lambda t: None if t is None else t.data_ptr()
+    ws_t = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes > 0 else None
+    ws = (ws_t.data_ptr(), ws_bytes) if ws_t is not None else None
 
     def step(i: int, stream: int):
         d = dev.sets[i % n_sets]
         T.forward_raw(ptr(d["input"]), ptr(d["skip"]), mode, srows, ptr(d["gamma"]), ptr(d["beta"]),
                       ptr(d["bias"]), ptr(d["out"]), ptr(d["res"]), w.rows, w.hidden, eps, code, stream, variant,
-                      op)
+                      op, workspace=ws)
 
     main = torch.cuda.current_stream()
     for i in range(warmup):
@@ -201,7 +208,7 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
         },
         "buffer_sets": n_sets,
     }
-    del dev
+    del dev, ws_t
     torch.cuda.empty_cache()
     log(f"{w.name}: {res['launch_us']:.2f} us/launch, {achieved:.0f} GB/s algorithmic "
         f"({achieved / HBM_PEAK_GBS:.1%} of peak), {res['rows_per_s']:.3e} rows/s")
@@ -297,7 +304,7 @@ def _median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
-def summarize_counters(root: str, out_path: str) -> int:
+def summarize_counters(root: str, out_path: str, steps: int) -> int:
     """Per-dispatch medians of the library's kernel in each counter run,
     scaled by the 1 GiB copy's reading of the same counter; writes
     profiles/counters.json and prints a markdown table."""
@@ -306,6 +313,10 @@ def summarize_counters(root: str, out_path: str) -> int:
     from transformer_residual_add_amd import workloads as W
 
     def lib_median(name, counter):
+        """Counter per step and library dispatches seen.  One kernel per
+        step: the median over its dispatches.  Several (the split-row pair,
+        per batch of rows): the sum over all of them divided by the steps run
+        (``steps``)."""
         path = os.path.join(root, f"{name}_{counter}", "run_counter_collection.csv")
         by = {}
         for k, v in _counter_rows(path, counter):
@@ -313,8 +324,10 @@ def summarize_counters(root: str, out_path: str) -> int:
                 by.setdefault(k, []).append(v)
         if not by:
             raise SystemExit(f"no library dispatch in {path}")
-        k = max(by, key=lambda n: len(by[n]))
-        return _median(by[k]), len(by[k])
+        n = sum(len(v) for v in by.values())
+        if len(by) == 1 and n == steps:
+            return _median(next(iter(by.values()))), n
+        return sum(sum(v) for v in by.values()) / steps, n
 
     copy_bytes = 1 << 30
     fetch_raw, _ = lib_median("copy1g", "FETCH_SIZE")
@@ -357,7 +370,7 @@ def summarize_counters(root: str, out_path: str) -> int:
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.summarize_counters:
-        return summarize_counters(args.summarize_counters, args.counters_out or COUNTERS)
+        return summarize_counters(args.summarize_counters, args.counters_out or COUNTERS, args.counter_steps)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the operator has no multi-GPU path to time "
               f"(rows shard across GPUs with no communication); got --gpus {args.gpus}", file=sys.stderr)

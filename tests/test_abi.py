@@ -290,10 +290,10 @@ def test_workspace_sizes_and_split_selection():
     name_ws = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: \
         L.kernel_name(lib.skipln_select_ws(op, h, dt, mode, 1, v))
     name = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select(op, h, dt, mode, 1, v))
-    # 65536 float32 = 16 slices of 4096; 64 MiB of inputs per batch = 128 rows of x and skip
+    # 65536 float32 = 16 slices of 4096; 128 MiB of inputs per batch = 256 rows of x and skip
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == 64 * 16 * 16
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == 128 * 16 * 16
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 256 * 16 * 16  # skip not streamed
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == 256 * 16 * 16
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 512 * 16 * 16  # skip not streamed
     assert wb(L.OP_LAYER_NORM, 0, 65536, L.F32) == 0
     assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32) == 0                       # row tiles need none
     assert wb(L.OP_LAYER_NORM, 64, 20000, L.F32) == 0                      # LDS-staged

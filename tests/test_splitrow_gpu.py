@@ -82,10 +82,10 @@ def test_split_auto_with_workspace(dt, hidden, op):
 
 @pytest.mark.parametrize("dt,hidden", [("f32", 65536), ("f16", 131072)])
 def test_split_several_batches(dt, hidden):
-    """More rows than one batch holds (64 MiB of streamed inputs): the
+    """More rows than one batch holds (128 MiB of streamed inputs): the
     workspace is reused batch after batch on the same stream."""
     row_bytes = hidden * (4 if dt == "f32" else 2)
-    per_batch = (64 << 20) // (2 * row_bytes)
+    per_batch = (128 << 20) // (2 * row_bytes)
     rows = 2 * per_batch + 7
     w = norm_case(rows, hidden, dt, "layer_norm", seed=11)
     U.note(f"split batches {dt} H={hidden} rows={rows} ({per_batch} per batch)")

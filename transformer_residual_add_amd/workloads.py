@@ -311,6 +311,21 @@ EXTRA: Dict[str, Workload] = {
             seed=1022,
             op="bias_softmax",
         ),
+        # Softmax over a vocabulary (sampling from language-model logits): rows
+        # of 128256 values, beyond one workgroup's LDS, so they split across
+        # workgroups; one bias row (a logit bias) shared by every row.
+        Workload(
+            name="softmax_vocab_4096x128256_f16",
+            shape=(4096, 128256),
+            dtype="f16",
+            skip_shape=(1, 128256),
+            input_dist=normal(0, 3),
+            skip_dist=normal(0, 0.5),
+            gamma_dist=None,
+            beta_dist=None,
+            seed=1023,
+            op="bias_softmax",
+        ),
         Workload(
             name="rms_bert_base_8x128x768_f32",
             shape=(8, 128, 768),
