@@ -35,7 +35,8 @@ SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_me
 OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*
 # Sources of the row kernels: counters taken on other sources are stale.
 KERNEL_SRC = [os.path.join(ROOT, "transformer_residual_add_amd", "csrc", f)
-              for f in ("skipln_device.h", "skipln_kernels.hip", "skipln_split.hip")]
+              for f in ("skipln_device.h", "skipln_rowtile.h", "skipln_rowtile_op.hip", "skipln_kernels.hip",
+                        "skipln_split.hip")]
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 

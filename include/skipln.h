@@ -98,9 +98,9 @@ enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 
 /* Kernel families, for skipln_forward_variant / skipln_select.  The automatic
  * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
  * kernel for longer rows of the reducing operations, then -- for calls that
- * bring a workspace (skipln_forward_ws) -- the split-row kernels, and the
- * generic kernel for anything unaligned, not a whole number of chunks, or
- * longer still. */
+ * bring a workspace (skipln_forward_ws) -- the split-row kernels; rows that
+ * are not whole chunks, or tensors not 16-byte aligned, take element-wise
+ * row tiles up to 16384 values, and the generic kernel anything else. */
 enum {
     SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
     SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
@@ -123,9 +123,16 @@ enum {
                                      aligned pointers, at most 64 slices
                                      (262144 float32 / 524288 float16 values);
                                      skipln_forward_ws only */
-    SKIPLN_VARIANT_GEOMETRY = 64  /* + g: ROWTILE with row-tile geometry g,
+    SKIPLN_VARIANT_ELEMENT = 6,   /* row held in registers, one element per
+                                     access: any hidden size up to 16384,
+                                     tensors aligned to their element size
+                                     (what the automatic choice takes for rows
+                                     that are not whole 16-byte chunks) */
+    SKIPLN_VARIANT_GEOMETRY = 64, /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_rowtile_geometries(), for
                                      tests and tuning */
+    SKIPLN_VARIANT_ELEMENT_GEOMETRY = 128 /* + g: ELEMENT with geometry g,
+                                     0 <= g < skipln_element_geometries() */
 };
 
 /*
@@ -258,8 +265,8 @@ enum {
 
 /* Operation `op` with an explicit launch configuration, for tuning; the
  * result is the same operator.  geometry: row-tile geometry
- * (0 <= geometry < skipln_rowtile_geometries()), or -1 for the automatic
- * choice.  tiles_per_block (T) > 0: row tiles (batches, for
+ * (0 <= geometry < skipln_rowtile_geometries()), -1 for the automatic
+ * choice, or SKIPLN_VARIANT_ELEMENT_GEOMETRY + g for element-wise geometry g.  tiles_per_block (T) > 0: row tiles (batches, for
  * SKIPLN_TILE_SKIP_STATIONARY) per block; 0: sized so the grid matches the
  * blocks the device holds at once (SKIPLN_TILE_CONTIGUOUS then behaves as
  * SKIPLN_TILE_STRIDED).  tiling: SKIPLN_TILE_*.  Returns
@@ -299,6 +306,9 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 
 /* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
 int skipln_rowtile_geometries(void);
+
+/* Number of element-wise row-tile geometries (SKIPLN_VARIANT_ELEMENT_GEOMETRY + g). */
+int skipln_element_geometries(void);
 
 /* Stable name of a kernel id ("generic_f32", "rowtile_f16_g256_c4",
  * "rms_rowtile_f32_g192_c1_b192", "biasadd_generic_f16",

@@ -46,6 +46,7 @@ def test_header_enums_match_binding():
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
         "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW, "SKIPLN_VARIANT_SPLITROW": L.VARIANT_SPLITROW,
+        "SKIPLN_VARIANT_ELEMENT": L.VARIANT_ELEMENT, "SKIPLN_VARIANT_ELEMENT_GEOMETRY": L.VARIANT_ELEMENT_GEOMETRY,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
@@ -194,9 +195,23 @@ def test_select_kernels():
     assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4"
     assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
     assert name(sel(64, 0)) == "rowtile_f32_g16_c1"
-    # not a multiple of a 16-byte chunk, or misaligned, or too long: generic
-    assert name(sel(1001, 0)) == "generic_f32"
-    assert name(sel(1024, 0, al=0)) == "generic_f32"
+    # not a multiple of a 16-byte chunk, or misaligned: element-wise row tiles;
+    # too long for every family: generic
+    assert name(sel(1001, 0)) == "rowelem_f32_g128_c8"
+    assert name(sel(1024, 0, al=0)) == "rowelem_f32_g128_c8"
+    assert name(sel(77, 1)) == "rowelem_f16_g32_c4"
+    assert name(sel(3, 1)) == "rowelem_f16_g4_c1"
+    assert name(sel(16384, 1, al=0)) == "rowelem_f16_g1024_c16"
+    assert name(sel(16385, 1, al=0)) == "generic_f16"
+    assert sel(16385, 1, v=L.VARIANT_ELEMENT) == -L.ERR_UNSUPPORTED
+    assert name(sel(1000, 0, v=L.VARIANT_ELEMENT)) == "rowelem_f32_g128_c8"
+    assert sel(1000, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED   # 4 elements
+    assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0)) == "rowelem_f32_g4_c1"
+    ne = lib.skipln_element_geometries()
+    assert ne >= 13
+    assert sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + ne) == -L.ERR_VARIANT
+    for g in range(ne):
+        assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + g)).startswith("rowelem_f32_g")
     assert name(sel(20000, 0)) == "ldsrow_f32"
     assert name(sel(50000, 0)) == "generic_f32"
     assert name(sel(8, 1, v=1)) == "generic_f16"
@@ -216,7 +231,7 @@ def test_select_kernels():
     assert sel(64, 0, op=7) == -L.ERR_OP
     assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
-    assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_generic_f16"
+    assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
     # long rows: LDS-staged up to 163584 bytes of binary32 sums, then generic
     assert name(sel(8192, 0)) == "rowtile_f32_g512_c4"
     assert name(sel(8196, 0)) == "ldsrow_f32"
@@ -236,7 +251,7 @@ def test_select_kernels():
     assert name(sel(8, 0, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowtile_f32_g4_c1"
     assert name(sel(4096, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowtile_f16_g128_c4"
     assert name(sel(20000, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_ldsrow_f32"
-    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_generic_f32"
+    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f32_g4_c2"
     assert name(sel(64, 1, op=L.OP_BIAS_SOFTMAX, v=L.VARIANT_LDSROW)) == "softmax_ldsrow_f16"
     assert sel(64, 0, mode=L.SKIP_BROADCAST_INNER) == -L.ERR_MODE
     assert sel(66, 0, v=L.VARIANT_LDSROW) == -L.ERR_UNSUPPORTED

@@ -160,7 +160,52 @@ def test_every_geometry(dt, geom, ragged, op):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_ROWTILE])
+@pytest.mark.parametrize("geom", list(range(24)))
+@pytest.mark.parametrize("shape", ["full", "odd", "short"])
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])
+def test_every_element_geometry(dt, geom, shape, op):
+    """Each element-wise row-tile geometry, for each operation: at its full
+    capacity, at an odd length just below, and at a quarter (idle lanes),
+    with a ragged last tile of rows and a broadcast skip."""
+    lib = L.load()
+    if geom >= lib.skipln_element_geometries():
+        pytest.skip("geometry not present")
+    code = L.F32 if dt == "f32" else L.F16
+    cap = 0
+    for h in (16384, 8192, 4096, 2048, 1024, 512, 256, 128, 64, 32, 16, 8, 4, 2, 1):
+        if lib.skipln_select(L.OP_LAYER_NORM, h, code, L.SKIP_EXACT, 1, L.VARIANT_ELEMENT_GEOMETRY + geom) >= 0:
+            cap = h
+            break
+    hidden = {"full": cap, "odd": max(1, cap - 1), "short": max(1, cap // 4 + 1)}[shape]
+    variant = L.VARIANT_ELEMENT_GEOMETRY + geom
+    name = L.kernel_name(lib.skipln_select(U.OPS[op], hidden, code, L.SKIP_EXACT, 1, variant))
+    g = int(name.split("_g")[1].split("_")[0])
+    block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
+    rows = 3 * (block // g) + 1 if hidden <= 4096 else 9
+    bcast = op != "bias_add" and rows % 3 == 0
+    w = W.small_case(rows, hidden, dt, skip_rows=3 if bcast else None, beta=True, bias=shape != "full",
+                     residual=True, eps=1e-5, seed=geom * 5 + len(shape), op=op)
+    U.note(f"element geometry {geom} ({name}) {op} H={hidden} rows={rows}")
+    U.check_case(w, variant=variant)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (3, 1), (0, 2), (2, 2)], ids=lambda t: f"tpb{t[0]}_m{t[1]}")
+@pytest.mark.parametrize("geom_hidden", [(0, 3), (5, 77), (8, 1000), (13, 63)], ids=lambda g: f"e{g[0]}_h{g[1]}")
+def test_element_launch_configs(dt, tiling, geom_hidden):
+    geom, hidden = geom_hidden
+    w = W.small_case(203, hidden, dt, skip_rows=7, beta=True, bias=True, residual=True, eps=1e-5, seed=31)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=True)
+    U.note(f"element config {dt} geometry={geom} H={hidden} tiling={tiling}")
+    dc.run_config(L.VARIANT_ELEMENT_GEOMETRY + geom, *tiling)
+    ref = U.oracle_rows(w, inputs)
+    U.assert_out_close(dc.host(dc.out), ref["y"], dt)
+    U.assert_bits_equal(dc.host(dc.res), ref["residual"])
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_ROWTILE, L.VARIANT_ELEMENT])
 @pytest.mark.parametrize("hidden", [64, 1024, 4096])
 def test_forced_variants(dt, variant, hidden):
     w = W.small_case(40, hidden, dt, skip_rows=8, beta=True, bias=True, residual=True, eps=1e-5, seed=3)
@@ -374,7 +419,8 @@ def test_long_rows_auto(dt, hidden):
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("mu", [100.0, 1000.0])
 @pytest.mark.parametrize("hidden", [64, 768, 4096, 12288])
-@pytest.mark.parametrize("variant", [L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW])
+@pytest.mark.parametrize("variant", [L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW,
+                                     L.VARIANT_ELEMENT])
 def test_large_offset_rows(dt, mu, hidden, variant):
     """Rows whose mean is far from zero (variance cancellation) in every
     kernel family, within the binary32 tolerance."""

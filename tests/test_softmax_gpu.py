@@ -77,7 +77,8 @@ def test_hidden_sizes(dt, hidden, mode):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_ROWTILE, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW])
+@pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_ROWTILE, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW,
+                                     L.VARIANT_ELEMENT])
 @pytest.mark.parametrize("hidden", [8, 64, 1024, 4096])
 @pytest.mark.parametrize("mode", MODES)
 def test_forced_variants(dt, variant, hidden, mode):
@@ -134,7 +135,7 @@ def test_misaligned_pointers(dt):
 
 # ------------------------------------------------------ special values --
 
-SPECIAL_VARIANTS = [L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW]
+SPECIAL_VARIANTS = [L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW, L.VARIANT_ELEMENT]
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])

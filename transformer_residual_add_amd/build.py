@@ -14,7 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskipln.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_api.cpp")]
+# (source, extra flags): the row tiles compile once per operation (kOp* = 0..3).
+SOURCES = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_api.cpp")] + [
+    (os.path.join(CSRC, "skipln_rowtile_op.hip"), [f"-DSKIPLN_ROWTILE_OP={op}"]) for op in range(4)]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -22,7 +24,6 @@ FLAGS = [
     "-std=c++17",
     f"--offload-arch={ARCH}",
     "-fPIC",
-    "-shared",
     "-Wall",
     # No packed fp32 instructions anywhere in device code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,17 +39,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc()] + FLAGS + SOURCES + ["-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode}) building {LIB}")
-    if verbose:
-        noise = "packed-fp32-ops"  # the host pass does not know this feature
-        for line in (res.stdout + res.stderr).splitlines():
-            if noise not in line:
-                print(line)
+    """Compile every source to an object (in parallel), link libskipln.so."""
+    import tempfile
+
+    cc = hipcc()
+    noise = "packed-fp32-ops"  # the host pass does not know this feature
+    with tempfile.TemporaryDirectory(prefix="skipln_build_") as tmpdir:
+        jobs = []
+        for i, (src, extra) in enumerate(SOURCES):
+            obj = os.path.join(tmpdir, f"{i}_{os.path.basename(src)}.o")
+            cmd = [cc] + FLAGS + extra + ["-c", src, "-o", obj]
+            jobs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                    text=True)))
+        failed = []
+        for src, obj, proc in jobs:
+            out, _ = proc.communicate()
+            if proc.returncode != 0:
+                failed.append(src)
+                sys.stderr.write(out)
+            elif verbose:
+                for line in out.splitlines():
+                    if noise not in line:
+                        print(line)
+        if failed:
+            raise RuntimeError(f"hipcc failed building {', '.join(failed)}")
+        tmp = LIB + f".tmp{os.getpid()}"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + [obj for _, obj, _ in jobs] + ["-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed ({res.returncode}) linking {LIB}")
     os.replace(tmp, LIB)
     return LIB
 

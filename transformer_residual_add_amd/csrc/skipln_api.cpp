@@ -135,13 +135,33 @@ bool all_aligned16(const Call& c) {
            aligned16(c.out) && aligned16(c.residual);
 }
 
-// Kernel id (>= 0) for this variant, or -status.  with_workspace: the call
+// Every tensor aligned to its element size (what element-wise accesses need).
+bool all_element_aligned(const Call& c) {
+    const uintptr_t m = c.dtype == SKIPLN_F32 ? 3u : 1u;
+    for (const void* p : {c.input, c.skip, c.gamma, c.beta, c.bias, static_cast<const void*>(c.out),
+                          static_cast<const void*>(c.residual)})
+        if (reinterpret_cast<uintptr_t>(p) & m) return false;
+    return true;
+}
+
+// Kernel id (>= 0) for this variant, or -status.  vec_ok: tensors 16-byte
+// aligned; elem_ok: aligned to their element size.  with_workspace: the call
 // brings a workspace, so the automatic choice may take the split-row kernels.
-int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int variant, bool with_workspace) {
+int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool elem_ok, int variant,
+           bool with_workspace) {
     const int base = (op * 2 + dtype) * skipln::kIdsPerType;
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
     if (variant == SKIPLN_VARIANT_GENERIC) return base + skipln::kGenericIndex;
+    if (variant == SKIPLN_VARIANT_ELEMENT) {
+        const int g = elem_ok ? skipln::elem_pick(op, hidden) : -1;
+        return g >= 0 ? base + skipln::kElemFirst + g : -SKIPLN_ERR_UNSUPPORTED;
+    }
+    if (variant >= SKIPLN_VARIANT_ELEMENT_GEOMETRY && variant < SKIPLN_VARIANT_ELEMENT_GEOMETRY + skipln::elem_count()) {
+        const int g = variant - SKIPLN_VARIANT_ELEMENT_GEOMETRY;
+        if (!elem_ok || !skipln::elem_holds(g, hidden)) return -SKIPLN_ERR_UNSUPPORTED;
+        return base + skipln::kElemFirst + g;
+    }
     const bool lds_ok = vec_ok && skipln::ldsrow_holds(op, hidden, dtype);
     const bool split_ok = vec_ok && skipln::split_holds(op, hidden, dtype);
     if (variant == SKIPLN_VARIANT_LDSROW) return lds_ok ? base + skipln::kLdsRowIndex : -SKIPLN_ERR_UNSUPPORTED;
@@ -157,8 +177,12 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, int v
         const int g =
             chunked ? skipln::rowtile_pick(op, hidden, dtype, broadcast, variant == SKIPLN_VARIANT_MULTIWAVE) : -1;
         if (g >= 0) return base + skipln::kRowtileFirst + g;
-        if (variant == SKIPLN_VARIANT_AUTO) return base + skipln::kGenericIndex;
-        return -SKIPLN_ERR_UNSUPPORTED;
+        if (variant != SKIPLN_VARIANT_AUTO) return -SKIPLN_ERR_UNSUPPORTED;
+        // Rows that are not whole chunks (or tensors not 16-byte aligned):
+        // element-wise row tiles, then the generic kernel.
+        const int e = elem_ok && !chunked ? skipln::elem_pick(op, hidden) : -1;
+        if (e >= 0) return base + skipln::kElemFirst + e;
+        return base + skipln::kGenericIndex;
     }
     if (variant >= SKIPLN_VARIANT_GEOMETRY && variant < SKIPLN_VARIANT_GEOMETRY + skipln::rowtile_count()) {
         const int g = variant - SKIPLN_VARIANT_GEOMETRY;
@@ -225,8 +249,8 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
         const Workspace* ws = nullptr) {
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
-    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c), variant,
-                          ws != nullptr);
+    const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c),
+                          all_element_aligned(c), variant, ws != nullptr);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
     const skipln::Args a = make_args(c);
@@ -252,6 +276,10 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
         return status_of(skipln::launch_ldsrow(a, c.op, c.dtype, s));
     }
+    if (index >= skipln::kElemFirst) {
+        const int g = index - skipln::kElemFirst;
+        return status_of(skipln::launch_elem(a, c.op, c.dtype, g, tiling ? *tiling : skipln::elem_tiling(g), s));
+    }
     const skipln::Tiling t = tiling ? *tiling : auto_tiling(c.op, c.skip_mode);
     return status_of(skipln::launch_rowtile(a, c.op, c.dtype, index - skipln::kRowtileFirst, t, s));
 }
@@ -272,7 +300,7 @@ int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned,
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant, false);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, false);
 }
 
 int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
@@ -280,7 +308,7 @@ int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int align
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, variant, true);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, true);
 }
 
 int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode, int64_t skip_rows,
@@ -290,7 +318,7 @@ int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, 
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (rows < 0 || hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
     if (skip_mode != SKIPLN_SKIP_EXACT && (skip_rows <= 0 || rows % skip_rows != 0)) return -SKIPLN_ERR_SHAPE;
-    const int id = select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, true, variant, true);
+    const int id = select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, true, true, variant, true);
     if (id < 0) return id;
     if (id % skipln::kIdsPerType != skipln::kSplitRowIndex || rows == 0) return 0;
     Call c = make_call(op, nullptr, nullptr, skip_mode, skip_rows, nullptr, nullptr, nullptr, nullptr, nullptr, rows,
@@ -324,11 +352,14 @@ int skipln_forward_config(int op, const void* input, const void* skip, int skip_
     if (tiles_per_block < 0) return SKIPLN_ERR_SHAPE;
     if (tiling != SKIPLN_TILE_CONTIGUOUS && tiling != SKIPLN_TILE_STRIDED && tiling != SKIPLN_TILE_SKIP_STATIONARY)
         return SKIPLN_ERR_VARIANT;
-    if (geometry < -1 || geometry >= skipln::rowtile_count()) return SKIPLN_ERR_VARIANT;
+    const bool elem = geometry >= SKIPLN_VARIANT_ELEMENT_GEOMETRY;
+    if (elem ? geometry >= SKIPLN_VARIANT_ELEMENT_GEOMETRY + skipln::elem_count()
+             : (geometry < -1 || geometry >= skipln::rowtile_count()))
+        return SKIPLN_ERR_VARIANT;
     skipln::Tiling t;
     t.tiles_per_block = tiles_per_block;
     t.mode = tiling;
-    const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
+    const int variant = elem ? geometry : geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
     return run(make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
                          dtype),
                variant, &t, stream);
@@ -389,6 +420,8 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 }
 
 int skipln_rowtile_geometries(void) { return skipln::rowtile_count(); }
+
+int skipln_element_geometries(void) { return skipln::elem_count(); }
 
 const char* skipln_kernel_name(int kernel_id) { return skipln::kernel_name(kernel_id); }
 

@@ -21,7 +21,9 @@ struct Elem;
 
 template <>
 struct Elem<float> {
+    typedef u32x4 Raw;
     static constexpr int kPerChunk = 4;
+    __device__ __forceinline__ static Raw zero() { return u32x4{0, 0, 0, 0}; }
     // Components are passed by value: __builtin_bit_cast applied directly to
     // a vector component (r.y) reads component 0 with this compiler.
     __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
@@ -48,7 +50,9 @@ struct Elem<float> {
 
 template <>
 struct Elem<_Float16> {
+    typedef u32x4 Raw;
     static constexpr int kPerChunk = 8;
+    __device__ __forceinline__ static Raw zero() { return u32x4{0, 0, 0, 0}; }
     __device__ __forceinline__ static float lo(unsigned w) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w & 0xFFFFu)));
     }
@@ -80,6 +84,35 @@ struct Elem<_Float16> {
     }
     __device__ __forceinline__ static void store1(void* p, int64_t i, float v) {
         static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+    }
+};
+
+// Element-wise access (rows that are not whole 16-byte chunks, or tensors
+// not 16-byte aligned): a "chunk" of one element, loaded and stored on its
+// own.  Same interface as Elem.
+template <typename T>
+struct Single;
+
+template <>
+struct Single<float> {
+    typedef unsigned int Raw;
+    static constexpr int kPerChunk = 1;
+    __device__ __forceinline__ static Raw zero() { return 0u; }
+    __device__ __forceinline__ static void widen(const Raw& r, float* f) { f[0] = __uint_as_float(r); }
+    __device__ __forceinline__ static Raw narrow(const float* f) { return __float_as_uint(f[0]); }
+};
+
+template <>
+struct Single<_Float16> {
+    typedef unsigned short Raw;
+    static constexpr int kPerChunk = 1;
+    __device__ __forceinline__ static Raw zero() { return 0; }
+    __device__ __forceinline__ static void widen(const Raw& r, float* f) {
+        f[0] = static_cast<float>(__builtin_bit_cast(_Float16, r));
+    }
+    // Round to nearest even.
+    __device__ __forceinline__ static Raw narrow(const float* f) {
+        return __builtin_bit_cast(unsigned short, static_cast<_Float16>(f[0]));
     }
 };
 

@@ -48,13 +48,15 @@ constexpr int kOpBiasSoftmax = 3; // BiasSoftmax: softmax over the row of x + sk
 constexpr int kNumOps = 4;
 
 // Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
-// 1.. = row tiles, kSplitRowIndex = the split-row kernel pair, kLdsRowIndex =
+// kRowtileFirst.. = row tiles of 16-byte chunks, kElemFirst.. = row tiles of
+// single elements, kSplitRowIndex = the split-row kernel pair, kLdsRowIndex =
 // the LDS-staged long-row kernel.
-constexpr int kIdsPerType = 64;
+constexpr int kIdsPerType = 128;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
-constexpr int kSplitRowIndex = 62;
-constexpr int kLdsRowIndex = 63;
+constexpr int kElemFirst = 64;
+constexpr int kSplitRowIndex = 126;
+constexpr int kLdsRowIndex = 127;
 
 // LDS a block may use on gfx950 (160 KiB), less room for the reduction
 // scratch: the long-row kernel holds hidden * 4 bytes.
@@ -71,6 +73,14 @@ int rowtile_count();
 int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only);
 // Whether geometry g holds a row of `hidden` elements (16-byte chunks).
 bool rowtile_holds(int geometry, int64_t hidden, int dtype);
+// The same for the element-wise row tiles (rows of any length, tensors
+// aligned to their element size only): number of geometries, the automatic
+// choice (or -1: none holds the row), and whether geometry g holds it.
+int elem_count();
+int elem_pick(int op, int64_t hidden);
+bool elem_holds(int geometry, int64_t hidden);
+// Tiling of an automatic element-wise launch with geometry g.
+Tiling elem_tiling(int geometry);
 const char* kernel_name(int kernel_id);
 
 // Enqueue one kernel; return 0 or a hipError_t value.
@@ -80,6 +90,13 @@ hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t stream);
 // row of binary32 values within kLdsRowBytes).
 bool ldsrow_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+hipError_t launch_elem(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+// One operation's row tiles (chunks / elements), instantiated per operation
+// in its own translation unit.
+template <int OP>
+hipError_t launch_rowtile_for(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+template <int OP>
+hipError_t launch_elem_for(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 // Split-row kernels (rows cut into slices of 1024 chunks, one workgroup per
 // slice, partials through a caller-provided workspace): whether they run
 // this operation and row (16-byte chunks, at most 64 slices), the workspace

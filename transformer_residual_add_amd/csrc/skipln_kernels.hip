@@ -41,414 +41,19 @@
 
 #include "skipln_device.h"
 #include "skipln_internal.h"
+#include "skipln_rowtile.h"
 
 namespace skipln {
 namespace {
 using namespace device;
-
-// ------------------------------------------------------------------------
-// Row-tile kernel.
-// ------------------------------------------------------------------------
-// Thread t of a row group owns chunks k*G + t (k < CH) of the row; a chunk
-// past the row end (ragged hidden size) is skipped.  Number of elements of
-// wavefront w of the group, for the cross-wave combine.
-template <int G, int CH, int V>
-__device__ __forceinline__ float wave_elems(int hv, int w) {
-    int n = 0;
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-        int left = hv - (k * G + 64 * w);
-        n += left <= 0 ? 0 : (left >= 64 ? 64 : left);
-    }
-    return static_cast<float>(n * V);
-}
-
-template <typename T, int OP, int G, int CH, int BLOCK>
-__global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
-    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd || OP == kOpBiasSoftmax,
-                  "operation");
-    using E = Elem<T>;
-    constexpr int V = E::kPerChunk;
-    constexpr bool kNorm = OP == kOpLayerNorm || OP == kOpSimplified;  // gamma/beta
-    constexpr bool kParams = OP != kOpBiasSoftmax;                       // any per-column parameter
-    constexpr int RPB = BLOCK / G;                  // rows per block per tile
-    constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
-    static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
-    __shared__ float4 partial[2][RPB][WPR];
-
-    const int tid = threadIdx.x;
-    // Row of the tile handled by this group; wave-uniform when G >= 64, and
-    // said so, so that row addresses live in scalar registers.
-    const int slot = G >= 64 ? __builtin_amdgcn_readfirstlane(tid / G) : tid / G;
-    const int lt = tid - slot * G; // lane within the group
-    const int hv = a.hidden / V;   // chunks per row
-    const float h = static_cast<float>(a.hidden);
-
-    const u32x4* __restrict__ X = static_cast<const u32x4*>(a.input);
-    const u32x4* __restrict__ S = static_cast<const u32x4*>(a.skip);
-    u32x4* __restrict__ R = static_cast<u32x4*>(a.residual);
-    u32x4* __restrict__ O = static_cast<u32x4*>(a.out);
-    const bool has_bias = kParams && a.bias != nullptr;
-    const bool has_beta = a.beta != nullptr;
-    const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
-    const bool small_rows = a.rows <= 0xFFFFFFFFll;
-
-    bool ok[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) ok[k] = k * G + lt < hv;
-
-    // Parameters: loaded once per block, kept in registers (raw T bits).
-    u32x4 gam[CH], bet[CH], bia[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-        gam[k] = u32x4{0, 0, 0, 0};
-        bet[k] = u32x4{0, 0, 0, 0};
-        bia[k] = u32x4{0, 0, 0, 0};
-    }
-    auto load_params = [&]() {
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-            const int c = k * G + lt;
-            if (ok[k]) {
-                if constexpr (kNorm) {
-                    gam[k] = static_cast<const u32x4*>(a.gamma)[c];
-                    if (has_beta) bet[k] = static_cast<const u32x4*>(a.beta)[c];
-                }
-                if (has_bias) bia[k] = static_cast<const u32x4*>(a.bias)[c];
-            }
-        }
-    };
-
-    float nw[WPR];
-#pragma unroll
-    for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
-    const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
-    // Reciprocals once per block: the per-row statistics multiply (<= 1.5 ulp)
-    // instead of dividing, which shortens the latency of short launches.
-    const float inv_h = 1.0f / h;
-    const float inv_own_n = own_n > 0.0f ? 1.0f / own_n : 0.0f;
-
-    // Tiles (RPB consecutive rows each) of this block, T = tiles_per_block:
-    //   contiguous:      b*T, b*T + 1, ..., b*T + T - 1
-    //   strided:         b, b + grid, b + 2*grid, ...
-    //   skip-stationary: with P = skip_rows / RPB tiles per batch, block b
-    //                    owns tile column p = b mod P (the same skip rows in
-    //                    every batch) and batches [c*T, c*T + T), c = b div P:
-    //                    tiles p + n*P.  Its skip rows are loaded once.
-    const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
-    int64_t t_first, stride, t_end;
-    const bool stationary = a.tiling == kTileSkipStationary;
-    if (a.tiling == kTileContiguous) {
-        t_first = blockIdx.x * a.tiles_per_block;
-        stride = 1;
-        t_end = t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles;
-    } else if (a.tiling == kTileStrided) {
-        t_first = blockIdx.x;
-        stride = gridDim.x;
-        t_end = n_tiles;
-    } else {
-        const int64_t P = a.skip_rows / RPB;
-        const int64_t batches = a.rows / a.skip_rows;
-        const int64_t n0 = (blockIdx.x / P) * a.tiles_per_block;
-        const int64_t n1 = n0 + a.tiles_per_block < batches ? n0 + a.tiles_per_block : batches;
-        t_first = n0 * P + blockIdx.x % P;
-        stride = P;
-        t_end = n1 * P;
-    }
-
-    u32x4 xr[CH], sr[CH];
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-        xr[k] = u32x4{0, 0, 0, 0};
-        sr[k] = u32x4{0, 0, 0, 0};
-    }
-    auto issue_loads = [&](int64_t tile, bool with_skip) {
-        const int64_t row = tile * RPB + slot;
-        if (row < a.rows) {
-            const int64_t srow = skip_row_of(row, a, small_rows);
-            const u32x4* xp = X + row * hv + lt;
-            const u32x4* sp = S + srow * hv + lt;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                if (ok[k]) {
-                    xr[k] = __builtin_nontemporal_load(xp + k * G);
-                    // The broadcast skip is re-read by every batch: keep it cached.
-                    if (with_skip) sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
-                }
-            }
-        }
-    };
-
-    // Order of the first loads (measured): a block that handles one tile
-    // needs bias as soon as x and skip arrive, so parameters go first; a
-    // long-lived skip-stationary block gets its first tile moving first.
-    int64_t tile = t_first;
-    if (stationary) {
-        if (tile < t_end) issue_loads(tile, true);
-        load_params();
-    } else {
-        load_params();
-        if (tile < t_end) issue_loads(tile, true);
-    }
-
-    int parity = 0;
-
-    for (; tile < t_end; tile += stride) {
-        const int64_t row = tile * RPB + slot;
-        const bool live = row < a.rows;
-        if constexpr (V == 8 && kParams) {
-            // Keep gamma/beta/bias packed (2 fp16 per VGPR): without this the
-            // compiler hoists their widening out of the loop and triples
-            // their register footprint, which costs occupancy.
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                asm volatile("" : "+v"(gam[k]), "+v"(bet[k]), "+v"(bia[k]));
-            }
-        }
-
-        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip;
-        // BiasSoftmax: data + bias, the bias arriving through the skip slot).
-        float s[CH][V];
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-            float xf[V], sf[V], bf[V];
-            E::widen(xr[k], xf);
-            E::widen(sr[k], sf);
-            E::widen(bia[k], bf);
-#pragma unroll
-            for (int e = 0; e < V; ++e) {
-                float v;
-                if constexpr (OP == kOpBiasAdd) {
-                    v = xf[e] + bf[e];
-                    v = v + sf[e];
-                } else {
-                    v = xf[e] + sf[e];
-                    if (has_bias) v = v + bf[e];
-                }
-                s[k][e] = v;
-            }
-        }
-
-        // Registers of x/skip are free again: start the next tile's loads.
-        if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
-
-        if constexpr (OP == kOpBiasSoftmax) {
-            // Softmax over the row: exponentials relative to a reference
-            // value r taken from the row, computed as 2^((z - r) log2 e), so
-            // that the rounding of the exponent scales with z - r (small for
-            // the terms that matter) rather than with z.
-            //   one wavefront or less per row: r = the row maximum M and
-            //     y = e / sum(e);
-            //   several wavefronts: each wavefront w uses its own maximum m_w
-            //     and its own sum s_w, exchanged through LDS (one barrier);
-            //     then M = max m_w, S = sum_w s_w 2^((m_w - M) log2 e) and
-            //     y = e 2^((m_w - M) log2 e) / S.
-            // Chunks past the row end take part as -inf / 0.  Special values
-            // follow the definition: any NaN in the row, a +inf, or a row
-            // that is -inf throughout makes the whole row NaN; a wavefront
-            // whose elements are all -inf contributes zeros.
-            constexpr float kLog2e = 1.4426950408889634f;
-            constexpr float kNegInf = -__builtin_inff();
-            float mx = kNegInf;
-#pragma unroll
-            for (int k = 0; k < CH; ++k)
-                if (ok[k])
-#pragma unroll
-                    for (int e = 0; e < V; ++e) mx = __builtin_fmaxf(mx, s[k][e]);
-            float m, r;
-            if constexpr (WPR == 1) {
-                m = group_reduce<MaxOp, G>(mx);
-                r = m;
-            } else {
-                m = wave_max(mx);
-                r = m != kNegInf ? m : 0.0f;
-            }
-            float part = 0.0f;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                if (ok[k]) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        s[k][e] = __builtin_amdgcn_exp2f((s[k][e] - r) * kLog2e);
-                        part += s[k][e];
-                    }
-                }
-            }
-            float scale;
-            if constexpr (WPR == 1) {
-                scale = 1.0f / group_sum<G>(part);
-            } else {
-                const float ws = wave_sum(part);
-                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(m, ws, 0.0f, 0.0f);
-                __syncthreads();
-                float row_max = kNegInf;
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) row_max = __builtin_fmaxf(row_max, partial[parity][slot][w].x);
-                float total = 0.0f;
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) {
-                    const float4 p = partial[parity][slot][w];
-                    const float f = p.x == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((p.x - row_max) * kLog2e);
-                    total += p.y * f;
-                }
-                const float own = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m - row_max) * kLog2e);
-                scale = own / total;
-                parity ^= 1;
-            }
-            if (live) {
-                u32x4* op = O + row * hv + lt;
-#pragma unroll
-                for (int k = 0; k < CH; ++k) {
-                    if (ok[k]) {
-                        float y[V];
-#pragma unroll
-                        for (int e = 0; e < V; ++e) y[e] = s[k][e] * scale;
-                        __builtin_nontemporal_store(E::narrow(y), op + k * G);
-                    }
-                }
-            }
-            continue;
-        }
-
-        if constexpr (OP == kOpBiasAdd) {
-            // BiasAdd ends here: the sum is the output.
-            if (live) {
-                u32x4* op = O + row * hv + lt;
-#pragma unroll
-                for (int k = 0; k < CH; ++k)
-                    if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), op + k * G);
-            }
-            continue;
-        }
-
-        if (R != nullptr && live) {
-            u32x4* rp = R + row * hv + lt;
-#pragma unroll
-            for (int k = 0; k < CH; ++k)
-                if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), rp + k * G);
-        }
-
-        // Statistics are taken relative to a value of the row itself (lane
-        // 0's first element), subtracted from s in place once the residual is
-        // out: the mean is kept as shift + dmean and the row normalized as
-        // (s - shift) - dmean, so rounding scales with the row's spread, not
-        // with its offset from zero (s - shift is exact when both are near the
-        // row mean; a binary32 mean near 1000 could not be held to better than
-        // 3e-5).  Lane 0 of a group always holds chunk 0; with several
-        // wavefronts per row each uses its own lane 0.  This lane's partial
-        // sum (of squares, for the simplified form) follows.
-        const float shift = OP == kOpLayerNorm ? group_first<G>(s[0][0]) : 0.0f;
-        float part = 0.0f;
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-            if (ok[k]) {
-#pragma unroll
-                for (int e = 0; e < V; ++e) {
-                    if constexpr (OP == kOpSimplified) {
-                        part += s[k][e] * s[k][e];
-                    } else {
-                        s[k][e] = s[k][e] - shift;
-                        part += s[k][e];
-                    }
-                }
-            }
-        }
-
-        // off: what to subtract from the shifted s to center it on the row mean.
-        float off = 0.0f, var;
-        if constexpr (OP == kOpSimplified) {
-            // Root mean square: no mean; the mean square takes the variance's place.
-            if constexpr (WPR == 1) {
-                var = group_sum<G>(part) * inv_h;
-            } else {
-                const float wsq = wave_sum(part);
-                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(wsq, 0.0f, 0.0f, 0.0f);
-                __syncthreads();
-                float tot = 0.0f;
-#pragma unroll
-                for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
-                var = tot * inv_h;
-                parity ^= 1;
-            }
-        } else if constexpr (WPR == 1) {
-            const float dmean = group_sum<G>(part) * inv_h;
-            off = dmean;
-            float q = 0.0f;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                if (ok[k]) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        const float d = s[k][e] - dmean;
-                        q += d * d;
-                    }
-                }
-            }
-            var = group_sum<G>(q) * inv_h;
-        } else {
-            // Per wavefront: shift_w, the mean relative to it, and the squared
-            // deviations from the wavefront mean; merged across wavefronts by
-            // Chan et al.'s pairwise update (M2 = sum_w M2_w + n_w d_w^2)
-            // relative to wavefront 0's shift (wavefront 0 always has
-            // elements), so the merge only adds small numbers.
-            const float wd = wave_sum(part) * inv_own_n;
-            float q = 0.0f;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                if (ok[k]) {
-#pragma unroll
-                    for (int e = 0; e < V; ++e) {
-                        const float d = s[k][e] - wd;
-                        q += d * d;
-                    }
-                }
-            }
-            const float wm2 = wave_sum(q);
-            if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(shift, wd, wm2, 0.0f);
-            __syncthreads();
-            const float row_shift = partial[parity][slot][0].x;
-            float dsum = 0.0f;
-#pragma unroll
-            for (int w = 0; w < WPR; ++w) {
-                if (nw[w] > 0.0f) {
-                    const float4 p = partial[parity][slot][w];
-                    dsum += nw[w] * ((p.x - row_shift) + p.y);
-                }
-            }
-            const float dmean = dsum * inv_h;
-            float m2 = 0.0f;
-#pragma unroll
-            for (int w = 0; w < WPR; ++w) {
-                if (nw[w] > 0.0f) {
-                    const float4 p = partial[parity][slot][w];
-                    const float dm = ((p.x - row_shift) + p.y) - dmean;
-                    m2 += p.z + nw[w] * dm * dm;
-                }
-            }
-            var = m2 * inv_h;
-            // s holds s - shift_w; the row is centered by subtracting
-            // dmean - (shift_w - row_shift) (both small).
-            off = dmean - (shift - row_shift);
-            parity ^= 1;
-        }
-        const float rstd = rsqrtf(var + a.eps);
-
-        if (live) {
-            u32x4* op = O + row * hv + lt;
-#pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                if (ok[k]) {
-                    float gf[V], bf[V], y[V];
-                    E::widen(gam[k], gf);
-                    E::widen(bet[k], bf);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - off) * rstd * gf[e] + bf[e];
-                    __builtin_nontemporal_store(E::narrow(y), op + k * G);
-                }
-            }
-        }
-    }
-}
+using rowtile::cu_count;
+using rowtile::Geom;
+using rowtile::kElemGeoms;
+using rowtile::kGeoms;
+using rowtile::kNumElemGeoms;
+using rowtile::kNumGeoms;
+using rowtile::launch_grid;
+using rowtile::resident_blocks;
 
 // ------------------------------------------------------------------------
 // Long-row kernel: the row is staged in LDS.
@@ -815,27 +420,7 @@ __global__ void __launch_bounds__(kCopyBlock) copy_kernel(u32x4* __restrict__ ds
     for (; i < chunks; i += step) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
-// ------------------------------------------------------------------------
-// Host side: geometry table, occupancy-sized persistent grids.
-// ------------------------------------------------------------------------
-struct Geom {
-    int g, ch, block;
-};
 
-// Auto order (increasing capacity G*CH chunks) first, then geometries only
-// reachable through the multi-wavefront variant.
-constexpr Geom kGeoms[] = {
-    {16, 1, 256},  {32, 1, 256},  {64, 1, 256},   {64, 2, 256},   {64, 3, 256},
-    {64, 4, 256},  {128, 4, 256}, {256, 3, 256},  {256, 4, 256},  {512, 3, 512},
-    {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
-    {512, 2, 512}, {128, 8, 256},  {256, 2, 512},  {256, 4, 512},  {64, 2, 64},
-    {64, 3, 64},   {32, 6, 256},  {192, 1, 192},  {192, 2, 192},  {512, 1, 512},
-    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256}, {4, 1, 256},   {8, 1, 256},
-    {4, 2, 256},   {8, 2, 256},   {8, 4, 256},    {16, 2, 256},   {16, 4, 256},
-    {32, 2, 256},  {128, 2, 256}, {32, 4, 256},   {16, 8, 256},
-};
-constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
-static_assert(kRowtileFirst + kNumGeoms <= kSplitRowIndex, "kernel index ranges are disjoint");
 
 // Automatic choice: the first entry whose capacity holds the row's chunks.
 // Short rows are latency bound: one chunk per lane spreads a row over more
@@ -864,104 +449,12 @@ constexpr AutoEntry kAutoSoftmax[] = {
     {512, 6},  {1024, 15}, {2048, 10}, {3072, 11}, {4096, 12},
 };
 
-hipError_t cu_count(int* out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    static std::atomic<int> cache[64];
-    if (dev >= 0 && dev < 64) {
-        const int c = cache[dev].load(std::memory_order_relaxed);
-        if (c > 0) {
-            *out = c;
-            return hipSuccess;
-        }
-    }
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (n < 1) n = 1;
-    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-    *out = n;
-    return hipSuccess;
-}
-
-// Blocks of `kernel` the device holds at once (occupancy limit x CUs); the
-// per-kernel occupancy is cached after the first query.
-template <typename K>
-hipError_t resident_blocks(K kernel, int block, int* occupancy_cache, int64_t* out) {
-    int cus = 0;
-    hipError_t e = cu_count(&cus);
-    if (e != hipSuccess) return e;
-    int occ = __atomic_load_n(occupancy_cache, __ATOMIC_RELAXED);
-    if (occ <= 0) {
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
-        if (e != hipSuccess) return e;
-        if (occ < 1) occ = 1;
-        __atomic_store_n(occupancy_cache, occ, __ATOMIC_RELAXED);
-    }
-    *out = static_cast<int64_t>(cus) * occ;
-    return hipSuccess;
-}
-
-template <typename K>
-hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipStream_t st) {
-    Args arg = a;
-    void* params[] = {&arg};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
-                           dim3(block), params, 0, st);
-}
-
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;
-
-template <typename T, int OP, int I>
-hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
-    constexpr Geom g = kGeoms[I];
-    static int occ = 0;
-    auto kernel = rowtile_kernel<T, OP, g.g, g.ch, g.block>;
-    const int64_t rpb = g.block / g.g;
-    const int64_t tiles = (a0.rows + rpb - 1) / rpb;
-    Args a = a0;
-    int mode = tiling.mode;
-    int64_t per = tiling.tiles_per_block;
-    // Skip-stationary needs a broadcast skip whose rows split into whole tiles.
-    if (mode == kTileSkipStationary && (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > kMaxGrid))
-        mode = kTileStrided;
-    int64_t resident = 0;
-    if (per <= 0) {
-        const hipError_t e = resident_blocks(kernel, g.block, &occ, &resident);
-        if (e != hipSuccess) return e;
-    }
-    int64_t blocks = 1;
-    if (mode == kTileSkipStationary) {
-        const int64_t P = a.skip_rows / rpb;
-        const int64_t batches = a.rows / a.skip_rows;
-        if (per <= 0) {
-            // Enough batch chunks per tile column to fill the resident grid.
-            const int64_t chunks = resident > P ? resident / P : 1;
-            per = (batches + chunks - 1) / chunks;
-        }
-        if (P * ((batches + per - 1) / per) > kMaxGrid) per = (batches * P + kMaxGrid - 1) / kMaxGrid;
-        blocks = P * ((batches + per - 1) / per);
-    } else {
-        if (per <= 0) {
-            // Persistent: one wave of resident blocks walks all tiles, strided.
-            per = (tiles + resident - 1) / resident;
-            mode = kTileStrided;
-        }
-        if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
-        blocks = (tiles + per - 1) / per;
-    }
-    a.tiles_per_block = per;
-    a.tiling = mode;
-    return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);
-}
-
-template <typename T, int OP, int... I>
-hipError_t launch_geom_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
-    hipError_t r = hipErrorInvalidValue;
-    ((idx == I ? (r = launch_geom<T, OP, I>(a, t, st), 0) : 0), ...);
-    return r;
-}
+// Automatic choice by elements per row (measured on MI355X: four elements
+// per lane up to 512 per row, eight beyond).
+constexpr AutoEntry kAutoElem[] = {
+    {4, 0},    {8, 1},     {16, 2},    {32, 3},    {64, 4},    {128, 5},   {256, 6},
+    {512, 7},  {1024, 12}, {2048, 19}, {4096, 20}, {8192, 16}, {16384, 21},
+};
 
 template <typename T, int OP>
 hipError_t launch_generic_t(const Args& a, hipStream_t st) {
@@ -973,12 +466,21 @@ hipError_t launch_generic_t(const Args& a, hipStream_t st) {
     return launch_grid(generic_kernel<T, OP>, kGenericBlock, blocks < 1 ? 1 : blocks, a, st);
 }
 
-// Kernel names: "<op>generic_<t>" and "<op>rowtile_<t>_g<G>_c<CH>", with
-// "_b<block>" when the block is not the default max(256, G); <op> is empty
+// Kernel names: "<op>generic_<t>", "<op>ldsrow_<t>", "<op>splitrow_<t>",
+// "<op>rowtile_<t>_g<G>_c<CH>" and "<op>rowelem_<t>_g<G>_c<CH>" (element-wise
+// row tiles), with "_b<block>" when the block is not the default max(256,
+// G); <op> is empty
 // for layer normalization, "rms_" for the simplified form, "biasadd_",
 // "softmax_".
 struct NameTable {
     char name[kNumOps][2][kIdsPerType][48];
+    static void geom_name(char* dst, const char* op, const char* family, const char* type, const Geom& g) {
+        const int default_block = g.g > 256 ? g.g : 256;
+        if (g.block == default_block)
+            snprintf(dst, 48, "%s%s_%s_g%d_c%d", op, family, type, g.g, g.ch);
+        else
+            snprintf(dst, 48, "%s%s_%s_g%d_c%d_b%d", op, family, type, g.g, g.ch, g.block);
+    }
     NameTable() {
         const char* op_prefix[kNumOps] = {"", "rms_", "biasadd_", "softmax_"};
         const char* tn[2] = {"f32", "f16"};
@@ -994,12 +496,9 @@ struct NameTable {
                     } else if (i == kSplitRowIndex) {
                         snprintf(dst, 48, "%ssplitrow_%s", op_prefix[op], tn[t]);
                     } else if (gi >= 0 && gi < kNumGeoms) {
-                        const Geom& g = kGeoms[gi];
-                        const int default_block = g.g > 256 ? g.g : 256;
-                        if (g.block == default_block)
-                            snprintf(dst, 48, "%srowtile_%s_g%d_c%d", op_prefix[op], tn[t], g.g, g.ch);
-                        else
-                            snprintf(dst, 48, "%srowtile_%s_g%d_c%d_b%d", op_prefix[op], tn[t], g.g, g.ch, g.block);
+                        geom_name(dst, op_prefix[op], "rowtile", tn[t], kGeoms[gi]);
+                    } else if (i >= kElemFirst && i < kElemFirst + kNumElemGeoms) {
+                        geom_name(dst, op_prefix[op], "rowelem", tn[t], kElemGeoms[i - kElemFirst]);
                     } else {
                         snprintf(dst, 48, "unknown");
                     }
@@ -1035,6 +534,31 @@ int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwa
         if (best < 0 || cap < static_cast<int64_t>(kGeoms[best].g) * kGeoms[best].ch) best = i;
     }
     return best;
+}
+
+int elem_count() { return kNumElemGeoms; }
+
+int elem_pick(int op, int64_t hidden) {
+    (void)op;
+    if (hidden <= 0) return -1;
+    for (const AutoEntry& e : kAutoElem)
+        if (hidden <= e.max_chunks) return e.geom;
+    return -1;
+}
+
+Tiling elem_tiling(int geometry) {
+    // Measured: two tiles per block walked in address order, except for
+    // 1024-lane rows, which run best on a persistent grid.
+    Tiling t;
+    const bool wide = geometry >= 0 && geometry < kNumElemGeoms && kElemGeoms[geometry].g >= 1024;
+    t.tiles_per_block = wide ? 0 : 2;
+    t.mode = wide ? kTileStrided : kTileContiguous;
+    return t;
+}
+
+bool elem_holds(int geometry, int64_t hidden) {
+    if (geometry < 0 || geometry >= kNumElemGeoms || hidden <= 0) return false;
+    return hidden <= static_cast<int64_t>(kElemGeoms[geometry].g) * kElemGeoms[geometry].ch;
 }
 
 bool rowtile_holds(int geometry, int64_t hidden, int dtype) {
@@ -1117,22 +641,26 @@ hipError_t launch_generic(const Args& a, int op, int dtype, hipStream_t st) {
     return dtype == 0 ? launch_generic_op<float>(a, op, st) : launch_generic_op<_Float16>(a, op, st);
 }
 
-template <typename T>
-hipError_t launch_rowtile_op(const Args& a, int op, int geometry, Tiling tiling, hipStream_t st) {
-    auto seq = std::make_integer_sequence<int, kNumGeoms>{};
+// The row tiles of each operation are compiled in their own translation unit
+// (skipln_rowtile_op.hip, once per operation).
+hipError_t launch_elem(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t st) {
     switch (op) {
-        case kOpLayerNorm: return launch_geom_dispatch<T, kOpLayerNorm>(geometry, a, tiling, st, seq);
-        case kOpSimplified: return launch_geom_dispatch<T, kOpSimplified>(geometry, a, tiling, st, seq);
-        case kOpBiasAdd: return launch_geom_dispatch<T, kOpBiasAdd>(geometry, a, tiling, st, seq);
-        case kOpBiasSoftmax: return launch_geom_dispatch<T, kOpBiasSoftmax>(geometry, a, tiling, st, seq);
+        case kOpLayerNorm: return launch_elem_for<kOpLayerNorm>(a, dtype, geometry, tiling, st);
+        case kOpSimplified: return launch_elem_for<kOpSimplified>(a, dtype, geometry, tiling, st);
+        case kOpBiasAdd: return launch_elem_for<kOpBiasAdd>(a, dtype, geometry, tiling, st);
+        case kOpBiasSoftmax: return launch_elem_for<kOpBiasSoftmax>(a, dtype, geometry, tiling, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t st) {
-    if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
-    return dtype == 0 ? launch_rowtile_op<float>(a, op, geometry, tiling, st)
-                      : launch_rowtile_op<_Float16>(a, op, geometry, tiling, st);
+    switch (op) {
+        case kOpLayerNorm: return launch_rowtile_for<kOpLayerNorm>(a, dtype, geometry, tiling, st);
+        case kOpSimplified: return launch_rowtile_for<kOpSimplified>(a, dtype, geometry, tiling, st);
+        case kOpBiasAdd: return launch_rowtile_for<kOpBiasAdd>(a, dtype, geometry, tiling, st);
+        case kOpBiasSoftmax: return launch_rowtile_for<kOpBiasSoftmax>(a, dtype, geometry, tiling, st);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace skipln

@@ -1,0 +1,567 @@
+// Row-tile kernels of 16-byte chunks or single elements, their geometry
+// tables and their launch templates; shared by the sources that instantiate
+// them (one translation unit per operation, compiled in parallel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <utility>
+
+#include "skipln_device.h"
+#include "skipln_internal.h"
+
+namespace skipln {
+namespace rowtile {
+using namespace device;
+
+// ------------------------------------------------------------------------
+// Row-tile kernel.
+// ------------------------------------------------------------------------
+// Thread t of a row group owns chunks k*G + t (k < CH) of the row; a chunk
+// past the row end (ragged hidden size) is skipped.  Number of elements of
+// wavefront w of the group, for the cross-wave combine.
+template <int G, int CH, int V>
+__device__ __forceinline__ float wave_elems(int hv, int w) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        int left = hv - (k * G + 64 * w);
+        n += left <= 0 ? 0 : (left >= 64 ? 64 : left);
+    }
+    return static_cast<float>(n * V);
+}
+
+template <typename E, int OP, int G, int CH, int BLOCK>
+__global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
+    static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd || OP == kOpBiasSoftmax,
+                  "operation");
+    using Raw = typename E::Raw;
+    constexpr int V = E::kPerChunk;
+    constexpr bool kNorm = OP == kOpLayerNorm || OP == kOpSimplified;  // gamma/beta
+    constexpr bool kParams = OP != kOpBiasSoftmax;                       // any per-column parameter
+    constexpr int RPB = BLOCK / G;                  // rows per block per tile
+    constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
+    static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
+    __shared__ float4 partial[2][RPB][WPR];
+
+    const int tid = threadIdx.x;
+    // Row of the tile handled by this group; wave-uniform when G >= 64, and
+    // said so, so that row addresses live in scalar registers.
+    const int slot = G >= 64 ? __builtin_amdgcn_readfirstlane(tid / G) : tid / G;
+    const int lt = tid - slot * G; // lane within the group
+    const int hv = a.hidden / V;   // chunks per row
+    const float h = static_cast<float>(a.hidden);
+
+    const Raw* __restrict__ X = static_cast<const Raw*>(a.input);
+    const Raw* __restrict__ S = static_cast<const Raw*>(a.skip);
+    Raw* __restrict__ R = static_cast<Raw*>(a.residual);
+    Raw* __restrict__ O = static_cast<Raw*>(a.out);
+    const bool has_bias = kParams && a.bias != nullptr;
+    const bool has_beta = a.beta != nullptr;
+    const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
+    const bool small_rows = a.rows <= 0xFFFFFFFFll;
+
+    bool ok[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) ok[k] = k * G + lt < hv;
+
+    // Parameters: loaded once per block, kept in registers (raw T bits).
+    Raw gam[CH], bet[CH], bia[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        gam[k] = E::zero();
+        bet[k] = E::zero();
+        bia[k] = E::zero();
+    }
+    auto load_params = [&]() {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int c = k * G + lt;
+            if (ok[k]) {
+                if constexpr (kNorm) {
+                    gam[k] = static_cast<const Raw*>(a.gamma)[c];
+                    if (has_beta) bet[k] = static_cast<const Raw*>(a.beta)[c];
+                }
+                if (has_bias) bia[k] = static_cast<const Raw*>(a.bias)[c];
+            }
+        }
+    };
+
+    float nw[WPR];
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) nw[w] = wave_elems<G, CH, V>(hv, w);
+    const float own_n = wave_elems<G, CH, V>(hv, lt / 64);
+    // Reciprocals once per block: the per-row statistics multiply (<= 1.5 ulp)
+    // instead of dividing, which shortens the latency of short launches.
+    const float inv_h = 1.0f / h;
+    const float inv_own_n = own_n > 0.0f ? 1.0f / own_n : 0.0f;
+
+    // Tiles (RPB consecutive rows each) of this block, T = tiles_per_block:
+    //   contiguous:      b*T, b*T + 1, ..., b*T + T - 1
+    //   strided:         b, b + grid, b + 2*grid, ...
+    //   skip-stationary: with P = skip_rows / RPB tiles per batch, block b
+    //                    owns tile column p = b mod P (the same skip rows in
+    //                    every batch) and batches [c*T, c*T + T), c = b div P:
+    //                    tiles p + n*P.  Its skip rows are loaded once.
+    const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
+    int64_t t_first, stride, t_end;
+    const bool stationary = a.tiling == kTileSkipStationary;
+    if (a.tiling == kTileContiguous) {
+        t_first = blockIdx.x * a.tiles_per_block;
+        stride = 1;
+        t_end = t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles;
+    } else if (a.tiling == kTileStrided) {
+        t_first = blockIdx.x;
+        stride = gridDim.x;
+        t_end = n_tiles;
+    } else {
+        const int64_t P = a.skip_rows / RPB;
+        const int64_t batches = a.rows / a.skip_rows;
+        const int64_t n0 = (blockIdx.x / P) * a.tiles_per_block;
+        const int64_t n1 = n0 + a.tiles_per_block < batches ? n0 + a.tiles_per_block : batches;
+        t_first = n0 * P + blockIdx.x % P;
+        stride = P;
+        t_end = n1 * P;
+    }
+
+    Raw xr[CH], sr[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        xr[k] = E::zero();
+        sr[k] = E::zero();
+    }
+    auto issue_loads = [&](int64_t tile, bool with_skip) {
+        const int64_t row = tile * RPB + slot;
+        if (row < a.rows) {
+            const int64_t srow = skip_row_of(row, a, small_rows);
+            const Raw* xp = X + row * hv + lt;
+            const Raw* sp = S + srow * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+                    xr[k] = __builtin_nontemporal_load(xp + k * G);
+                    // The broadcast skip is re-read by every batch: keep it cached.
+                    if (with_skip) sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
+                }
+            }
+        }
+    };
+
+    // Order of the first loads (measured): a block that handles one tile
+    // needs bias as soon as x and skip arrive, so parameters go first; a
+    // long-lived skip-stationary block gets its first tile moving first.
+    int64_t tile = t_first;
+    if (stationary) {
+        if (tile < t_end) issue_loads(tile, true);
+        load_params();
+    } else {
+        load_params();
+        if (tile < t_end) issue_loads(tile, true);
+    }
+
+    int parity = 0;
+
+    for (; tile < t_end; tile += stride) {
+        const int64_t row = tile * RPB + slot;
+        const bool live = row < a.rows;
+        if constexpr (V == 8 && kParams) {
+            // Keep gamma/beta/bias packed (2 fp16 per VGPR): without this the
+            // compiler hoists their widening out of the loop and triples
+            // their register footprint, which costs occupancy.
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                asm volatile("" : "+v"(gam[k]), "+v"(bet[k]), "+v"(bia[k]));
+            }
+        }
+
+        // s = (x + skip) + bias in binary32 (BiasAdd: (x + bias) + skip;
+        // BiasSoftmax: data + bias, the bias arriving through the skip slot).
+        float s[CH][V];
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            float xf[V], sf[V], bf[V];
+            E::widen(xr[k], xf);
+            E::widen(sr[k], sf);
+            E::widen(bia[k], bf);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float v;
+                if constexpr (OP == kOpBiasAdd) {
+                    v = xf[e] + bf[e];
+                    v = v + sf[e];
+                } else {
+                    v = xf[e] + sf[e];
+                    if (has_bias) v = v + bf[e];
+                }
+                s[k][e] = v;
+            }
+        }
+
+        // Registers of x/skip are free again: start the next tile's loads.
+        if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
+
+        if constexpr (OP == kOpBiasSoftmax) {
+            // Softmax over the row: exponentials relative to a reference
+            // value r taken from the row, computed as 2^((z - r) log2 e), so
+            // that the rounding of the exponent scales with z - r (small for
+            // the terms that matter) rather than with z.
+            //   one wavefront or less per row: r = the row maximum M and
+            //     y = e / sum(e);
+            //   several wavefronts: each wavefront w uses its own maximum m_w
+            //     and its own sum s_w, exchanged through LDS (one barrier);
+            //     then M = max m_w, S = sum_w s_w 2^((m_w - M) log2 e) and
+            //     y = e 2^((m_w - M) log2 e) / S.
+            // Chunks past the row end take part as -inf / 0.  Special values
+            // follow the definition: any NaN in the row, a +inf, or a row
+            // that is -inf throughout makes the whole row NaN; a wavefront
+            // whose elements are all -inf contributes zeros.
+            constexpr float kLog2e = 1.4426950408889634f;
+            constexpr float kNegInf = -__builtin_inff();
+            float mx = kNegInf;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (ok[k])
+#pragma unroll
+                    for (int e = 0; e < V; ++e) mx = __builtin_fmaxf(mx, s[k][e]);
+            float m, r;
+            if constexpr (WPR == 1) {
+                m = group_reduce<MaxOp, G>(mx);
+                r = m;
+            } else {
+                m = wave_max(mx);
+                r = m != kNegInf ? m : 0.0f;
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        s[k][e] = __builtin_amdgcn_exp2f((s[k][e] - r) * kLog2e);
+                        part += s[k][e];
+                    }
+                }
+            }
+            float scale;
+            if constexpr (WPR == 1) {
+                scale = 1.0f / group_sum<G>(part);
+            } else {
+                const float ws = wave_sum(part);
+                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(m, ws, 0.0f, 0.0f);
+                __syncthreads();
+                float row_max = kNegInf;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) row_max = __builtin_fmaxf(row_max, partial[parity][slot][w].x);
+                float total = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) {
+                    const float4 p = partial[parity][slot][w];
+                    const float f = p.x == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((p.x - row_max) * kLog2e);
+                    total += p.y * f;
+                }
+                const float own = m == kNegInf ? 0.0f : __builtin_amdgcn_exp2f((m - row_max) * kLog2e);
+                scale = own / total;
+                parity ^= 1;
+            }
+            if (live) {
+                Raw* op = O + row * hv + lt;
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    if (ok[k]) {
+                        float y[V];
+#pragma unroll
+                        for (int e = 0; e < V; ++e) y[e] = s[k][e] * scale;
+                        __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                    }
+                }
+            }
+            continue;
+        }
+
+        if constexpr (OP == kOpBiasAdd) {
+            // BiasAdd ends here: the sum is the output.
+            if (live) {
+                Raw* op = O + row * hv + lt;
+#pragma unroll
+                for (int k = 0; k < CH; ++k)
+                    if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), op + k * G);
+            }
+            continue;
+        }
+
+        if (R != nullptr && live) {
+            Raw* rp = R + row * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+                if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), rp + k * G);
+        }
+
+        // Statistics are taken relative to a value of the row itself (lane
+        // 0's first element), subtracted from s in place once the residual is
+        // out: the mean is kept as shift + dmean and the row normalized as
+        // (s - shift) - dmean, so rounding scales with the row's spread, not
+        // with its offset from zero (s - shift is exact when both are near the
+        // row mean; a binary32 mean near 1000 could not be held to better than
+        // 3e-5).  Lane 0 of a group always holds chunk 0; with several
+        // wavefronts per row each uses its own lane 0.  This lane's partial
+        // sum (of squares, for the simplified form) follows.
+        const float shift = OP == kOpLayerNorm ? group_first<G>(s[0][0]) : 0.0f;
+        float part = 0.0f;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            if (ok[k]) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    if constexpr (OP == kOpSimplified) {
+                        part += s[k][e] * s[k][e];
+                    } else {
+                        s[k][e] = s[k][e] - shift;
+                        part += s[k][e];
+                    }
+                }
+            }
+        }
+
+        // off: what to subtract from the shifted s to center it on the row mean.
+        float off = 0.0f, var;
+        if constexpr (OP == kOpSimplified) {
+            // Root mean square: no mean; the mean square takes the variance's place.
+            if constexpr (WPR == 1) {
+                var = group_sum<G>(part) * inv_h;
+            } else {
+                const float wsq = wave_sum(part);
+                if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(wsq, 0.0f, 0.0f, 0.0f);
+                __syncthreads();
+                float tot = 0.0f;
+#pragma unroll
+                for (int w = 0; w < WPR; ++w) tot += partial[parity][slot][w].x;
+                var = tot * inv_h;
+                parity ^= 1;
+            }
+        } else if constexpr (WPR == 1) {
+            const float dmean = group_sum<G>(part) * inv_h;
+            off = dmean;
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = s[k][e] - dmean;
+                        q += d * d;
+                    }
+                }
+            }
+            var = group_sum<G>(q) * inv_h;
+        } else {
+            // Per wavefront: shift_w, the mean relative to it, and the squared
+            // deviations from the wavefront mean; merged across wavefronts by
+            // Chan et al.'s pairwise update (M2 = sum_w M2_w + n_w d_w^2)
+            // relative to wavefront 0's shift (wavefront 0 always has
+            // elements), so the merge only adds small numbers.
+            const float wd = wave_sum(part) * inv_own_n;
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float d = s[k][e] - wd;
+                        q += d * d;
+                    }
+                }
+            }
+            const float wm2 = wave_sum(q);
+            if ((lt & 63) == 0) partial[parity][slot][lt >> 6] = make_float4(shift, wd, wm2, 0.0f);
+            __syncthreads();
+            const float row_shift = partial[parity][slot][0].x;
+            float dsum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                if (nw[w] > 0.0f) {
+                    const float4 p = partial[parity][slot][w];
+                    dsum += nw[w] * ((p.x - row_shift) + p.y);
+                }
+            }
+            const float dmean = dsum * inv_h;
+            float m2 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < WPR; ++w) {
+                if (nw[w] > 0.0f) {
+                    const float4 p = partial[parity][slot][w];
+                    const float dm = ((p.x - row_shift) + p.y) - dmean;
+                    m2 += p.z + nw[w] * dm * dm;
+                }
+            }
+            var = m2 * inv_h;
+            // s holds s - shift_w; the row is centered by subtracting
+            // dmean - (shift_w - row_shift) (both small).
+            off = dmean - (shift - row_shift);
+            parity ^= 1;
+        }
+        const float rstd = rsqrtf(var + a.eps);
+
+        if (live) {
+            Raw* op = O + row * hv + lt;
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                if (ok[k]) {
+                    float gf[V], bf[V], y[V];
+                    E::widen(gam[k], gf);
+                    E::widen(bet[k], bf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - off) * rstd * gf[e] + bf[e];
+                    __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Host side: geometry table, occupancy-sized persistent grids.
+// ------------------------------------------------------------------------
+struct Geom {
+    int g, ch, block;
+};
+
+// Auto order (increasing capacity G*CH chunks) first, then geometries only
+// reachable through the multi-wavefront variant.
+constexpr Geom kGeoms[] = {
+    {16, 1, 256},  {32, 1, 256},  {64, 1, 256},   {64, 2, 256},   {64, 3, 256},
+    {64, 4, 256},  {128, 4, 256}, {256, 3, 256},  {256, 4, 256},  {512, 3, 512},
+    {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
+    {512, 2, 512}, {128, 8, 256},  {256, 2, 512},  {256, 4, 512},  {64, 2, 64},
+    {64, 3, 64},   {32, 6, 256},  {192, 1, 192},  {192, 2, 192},  {512, 1, 512},
+    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256}, {4, 1, 256},   {8, 1, 256},
+    {4, 2, 256},   {8, 2, 256},   {8, 4, 256},    {16, 2, 256},   {16, 4, 256},
+    {32, 2, 256},  {128, 2, 256}, {32, 4, 256},   {16, 8, 256},
+};
+constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
+static_assert(kRowtileFirst + kNumGeoms <= kElemFirst, "kernel index ranges are disjoint");
+
+// Element-wise row tiles (one element per access): rows that are not whole
+// 16-byte chunks, or tensors aligned to their element size only.  Two to
+// sixteen elements per lane keep several loads in flight per lane.
+constexpr Geom kElemGeoms[] = {
+    {4, 1, 256},   {4, 2, 256},   {8, 2, 256},    {8, 4, 256},    {16, 4, 256},   {32, 4, 256},
+    {64, 4, 256},  {128, 4, 256}, {256, 4, 256},  {512, 4, 512},  {1024, 4, 1024}, {16, 8, 256},
+    {128, 8, 256}, {32, 2, 256},  {64, 2, 256},   {256, 2, 256},  {1024, 8, 1024}, {16, 2, 256},
+    {64, 8, 256},  {256, 8, 256}, {512, 8, 512},  {1024, 16, 1024},
+};
+constexpr int kNumElemGeoms = sizeof(kElemGeoms) / sizeof(kElemGeoms[0]);
+static_assert(kElemFirst + kNumElemGeoms <= kSplitRowIndex, "kernel index ranges are disjoint");
+
+inline hipError_t cu_count(int* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::atomic<int> cache[64];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (n < 1) n = 1;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
+}
+
+// Blocks of `kernel` the device holds at once (occupancy limit x CUs); the
+// per-kernel occupancy is cached after the first query.
+template <typename K>
+hipError_t resident_blocks(K kernel, int block, int* occupancy_cache, int64_t* out) {
+    int cus = 0;
+    hipError_t e = cu_count(&cus);
+    if (e != hipSuccess) return e;
+    int occ = __atomic_load_n(occupancy_cache, __ATOMIC_RELAXED);
+    if (occ <= 0) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, block, 0);
+        if (e != hipSuccess) return e;
+        if (occ < 1) occ = 1;
+        __atomic_store_n(occupancy_cache, occ, __ATOMIC_RELAXED);
+    }
+    *out = static_cast<int64_t>(cus) * occ;
+    return hipSuccess;
+}
+
+template <typename K>
+hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipStream_t st) {
+    Args arg = a;
+    void* params[] = {&arg};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
+                           dim3(block), params, 0, st);
+}
+
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+template <typename E, int OP, int GG, int CH, int BLOCK>
+hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
+    constexpr Geom g = {GG, CH, BLOCK};
+    static int occ = 0;
+    auto kernel = rowtile_kernel<E, OP, g.g, g.ch, g.block>;
+    const int64_t rpb = g.block / g.g;
+    const int64_t tiles = (a0.rows + rpb - 1) / rpb;
+    Args a = a0;
+    int mode = tiling.mode;
+    int64_t per = tiling.tiles_per_block;
+    // Skip-stationary needs a broadcast skip whose rows split into whole tiles.
+    if (mode == kTileSkipStationary && (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > kMaxGrid))
+        mode = kTileStrided;
+    int64_t resident = 0;
+    if (per <= 0) {
+        const hipError_t e = resident_blocks(kernel, g.block, &occ, &resident);
+        if (e != hipSuccess) return e;
+    }
+    int64_t blocks = 1;
+    if (mode == kTileSkipStationary) {
+        const int64_t P = a.skip_rows / rpb;
+        const int64_t batches = a.rows / a.skip_rows;
+        if (per <= 0) {
+            // Enough batch chunks per tile column to fill the resident grid.
+            const int64_t chunks = resident > P ? resident / P : 1;
+            per = (batches + chunks - 1) / chunks;
+        }
+        if (P * ((batches + per - 1) / per) > kMaxGrid) per = (batches * P + kMaxGrid - 1) / kMaxGrid;
+        blocks = P * ((batches + per - 1) / per);
+    } else {
+        if (per <= 0) {
+            // Persistent: one wave of resident blocks walks all tiles, strided.
+            per = (tiles + resident - 1) / resident;
+            mode = kTileStrided;
+        }
+        if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
+        blocks = (tiles + per - 1) / per;
+    }
+    a.tiles_per_block = per;
+    a.tiling = mode;
+    return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);
+}
+
+template <typename T, int OP, int... I>
+hipError_t launch_geom_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((idx == I ? (r = launch_geom<Elem<T>, OP, kGeoms[I].g, kGeoms[I].ch, kGeoms[I].block>(a, t, st), 0) : 0), ...);
+    return r;
+}
+
+template <typename T, int OP, int... I>
+hipError_t launch_elem_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((idx == I ? (r = launch_geom<Single<T>, OP, kElemGeoms[I].g, kElemGeoms[I].ch, kElemGeoms[I].block>(a, t, st),
+                  0)
+               : 0),
+     ...);
+    return r;
+}
+
+}  // namespace rowtile
+}  // namespace skipln
