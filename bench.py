@@ -57,6 +57,9 @@ def parse_args(argv=None):
     p.add_argument("--variant", type=int, default=0, help="kernel family (SKIPLN_VARIANT_*), 0 = auto")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the operator, time the streaming copy of this many bytes")
+    p.add_argument("--stream-ceilings", type=int, default=0, metavar="BYTES",
+                   help="instead of the operator, time the streaming probe (skipln_stream) for every mix of "
+                        "0-2 read and 0-2 written streams of BYTES each")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="no GPU work: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR "
                         "(<workload>_<COUNTER>/run_counter_collection.csv, copy1g_<COUNTER>/...) into "
@@ -240,6 +243,55 @@ def time_copy(nbytes: int, steps: int, warmup: int):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "launch_us": dt * 1e6, "gb_per_s": 2 * nbytes / dt / 1e9}
 
 
+def time_streams(nbytes: int, steps: int, warmup: int):
+    """HBM rate of the streaming probe for each mix of read and written
+    streams (the attainable ceilings of the row kernels' access pattern)."""
+    import torch
+
+    from transformer_residual_add_amd import _lib as L
+
+    nbytes -= nbytes % 16
+    lib = L.load()
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
+    s = torch.cuda.current_stream().cuda_stream
+    out = []
+    for reads in (0, 1, 2):
+        for writes in (0, 1, 2):
+            if reads + writes == 0:
+                continue
+            src = [bufs[i].data_ptr() for i in range(reads)] + [None] * (2 - reads)
+            dst = [bufs[2 + i].data_ptr() for i in range(writes)] + [None] * (2 - writes)
+
+            moved = (reads + writes) * nbytes
+            shapes = []
+            for block in (64, 256, 1024):
+                for per_lane in (1, 4):
+                    def launch():
+                        L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, s),
+                                "skipln_stream")
+
+                    for _ in range(warmup):
+                        launch()
+                    torch.cuda.synchronize()
+                    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    ev0.record()
+                    for _ in range(steps):
+                        launch()
+                    ev1.record()
+                    torch.cuda.synchronize()
+                    dt = ev0.elapsed_time(ev1) * 1e-3 / steps
+                    shapes.append({"block": block, "chunks_per_lane": per_lane, "launch_us": round(dt * 1e6, 2),
+                                   "gb_per_s": round(moved / dt / 1e9, 1)})
+            best = max(shapes, key=lambda r: r["gb_per_s"])
+            out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "best_gb_per_s": best["gb_per_s"],
+                        "best_frac_of_peak": round(best["gb_per_s"] / HBM_PEAK_GBS, 4),
+                        "best_shape": [best["block"], best["chunks_per_lane"]], "shapes": shapes})
+            log(f"stream {reads}R{writes}W: best {best['gb_per_s']:.0f} GB/s (block {best['block']}, "
+                f"{best['chunks_per_lane']} chunk(s)/lane); " +
+                ", ".join(f"{r['block']}x{r['chunks_per_lane']}: {r['gb_per_s']:.0f}" for r in shapes))
+    return out
+
+
 def cpu_baseline(w, seconds: float):
     """The oracle (as it stands) on this host's cores, on repeated full
     batches of the workload until about ``seconds`` of wall time."""
@@ -342,7 +394,9 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
         if not os.path.isdir(os.path.join(root, f"{name}_FETCH_SIZE")):
             continue
         w = W.get(name)
-        kernel = T.select_kernel(w.hidden, L.F32 if w.dtype == "f32" else L.F16, True, 0, skip_mode(w, L), OPS[w.op])
+        code = L.F32 if w.dtype == "f32" else L.F16
+        ws = T.workspace_bytes(OPS[w.op], w.rows, w.hidden, code, skip_mode(w, L), w.skip_rows if w.broadcast else 0)
+        kernel = T.select_kernel(w.hidden, code, True, 0, skip_mode(w, L), OPS[w.op], workspace=ws > 0)
         f, n = lib_median(name, "FETCH_SIZE")
         wr, _ = lib_median(name, "WRITE_SIZE")
         fb, wb = int(round(f * 1024 * fetch_scale)), int(round(wr * 1024 * write_scale))
@@ -389,6 +443,9 @@ def main(argv=None) -> int:
 
     if args.copy_bytes:
         print(json.dumps({"copy": time_copy(args.copy_bytes, args.steps, args.warmup)}), flush=True)
+        return 0
+    if args.stream_ceilings:
+        print(json.dumps({"stream": time_streams(args.stream_ceilings, args.steps, args.warmup)}), flush=True)
         return 0
 
     w = W.get(args.workload)

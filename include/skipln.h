@@ -304,6 +304,21 @@ int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int align
  * multiple of 16, misaligned pointers), SKIPLN_ERR_ALIAS or SKIPLN_ERR_LAUNCH. */
 int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t stream);
 
+/* Streaming probe with the access pattern of the row kernels (16-byte
+ * non-temporal accesses, one tile of `block` lanes x `chunks_per_lane`
+ * chunks per stream and workgroup, in address order; block 64, 256 or 1024,
+ * chunks_per_lane 1 or 4): reads 0-2 input streams (src0, then src1; NULL =
+ * not read) and writes 0-2 output streams (dst0, then dst1) of `bytes` bytes
+ * each.  It measures the HBM rate a kernel of that pattern attains for each
+ * mix of reads and writes, the ceiling the row kernels are compared with.
+ * Outputs: dst0 = src0 XOR src1 (a chunk's index when nothing is read),
+ * dst1 = dst0 + 1 per 32-bit word.  Device memory, 16-byte aligned, bytes %
+ * 16 == 0, outputs overlapping nothing.  Returns SKIPLN_OK, SKIPLN_ERR_NULL
+ * (no stream, or src1/dst1 without src0/dst0), SKIPLN_ERR_SHAPE,
+ * SKIPLN_ERR_ALIAS, SKIPLN_ERR_VARIANT (tile shape) or SKIPLN_ERR_LAUNCH. */
+int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
+                  int chunks_per_lane, skipln_stream_t stream);
+
 /* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
 int skipln_rowtile_geometries(void);
 

@@ -353,3 +353,19 @@ def test_forward_ws_workspace_checks():
     assert FW(WS, need, variant=L.VARIANT_LDSROW) == L.ERR_UNSUPPORTED
     assert FW(None, 0, hidden=64, variant=L.VARIANT_SPLITROW) == L.ERR_WORKSPACE
     assert FW(WS, need, op=L.OP_BIAS_ADD, variant=L.VARIANT_SPLITROW) == L.ERR_UNSUPPORTED
+
+
+def test_stream_probe_argument_checks():
+    """skipln_stream returns these statuses before any HIP call."""
+    st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4: L.load().skipln_stream(s0, s1, d0, d1, n, b, u,
+                                                                                            None)
+    assert st(s0=None, d0=None) == L.ERR_NULL
+    assert st(s0=None, s1=SK) == L.ERR_NULL
+    assert st(d0=None, d1=RES) == L.ERR_NULL
+    assert st(n=-16) == L.ERR_SHAPE
+    assert st(n=24) == L.ERR_SHAPE
+    assert st(s0=IN + 8) == L.ERR_SHAPE
+    assert st(d0=IN + 16) == L.ERR_ALIAS
+    assert st(d0=OUT, d1=OUT + 2048) == L.ERR_ALIAS
+    assert st(n=0) == L.OK
+    assert st(b=128) == L.ERR_VARIANT and st(u=2) == L.ERR_VARIANT

@@ -300,6 +300,34 @@ def test_streaming_copy(nbytes):
     assert L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), 24, None) == L.ERR_SHAPE
 
 
+def test_stream_probe_outputs():
+    """The streaming probe's outputs: a copy, the XOR of two inputs, the copy
+    plus one, and the chunk index when nothing is read."""
+    import torch
+
+    lib = L.load()
+    n = (1 << 20) + 48
+    a = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    b = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
+    c, d = torch.zeros_like(a), torch.zeros_like(a)
+    for blk, u in ((64, 1), (256, 4), (1024, 1), (1024, 4)):
+        c.zero_(), d.zero_()
+        L.check(lib.skipln_stream(a.data_ptr(), None, c.data_ptr(), d.data_ptr(), n, blk, u, None), "skipln_stream")
+        torch.cuda.synchronize()
+        assert torch.equal(c, a) and torch.equal(d, a + 1)
+    L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, n, 256, 1, None), "skipln_stream")
+    torch.cuda.synchronize()
+    assert torch.equal(c, a ^ b)
+    L.check(lib.skipln_stream(None, None, c.data_ptr(), None, n, 64, 4, None), "skipln_stream")
+    torch.cuda.synchronize()
+    idx = torch.arange(n // 16, dtype=torch.int32, device="cuda")
+    assert torch.equal(c.view(-1, 4)[:, 0], idx) and not c.view(-1, 4)[:, 1:].any()
+    before = c.clone()
+    L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), None, None, n, 1024, 4, None), "skipln_stream")
+    torch.cuda.synchronize()
+    assert torch.equal(c, before)
+
+
 # ------------------------------------------------- simplified and BiasAdd --
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])

@@ -419,6 +419,27 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
     return status_of(skipln::launch_copy(dst, src, bytes / 16, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
+                  int chunks_per_lane, skipln_stream_t stream) {
+    if (!skipln::stream_shape_ok(block, chunks_per_lane)) return SKIPLN_ERR_VARIANT;
+    if (bytes < 0 || bytes % 16 != 0) return SKIPLN_ERR_SHAPE;
+    if (src1 && !src0) return SKIPLN_ERR_NULL;   // inputs fill src0 first
+    if (dst1 && !dst0) return SKIPLN_ERR_NULL;   // outputs fill dst0 first
+    const int reads = (src0 != nullptr) + (src1 != nullptr);
+    const int writes = (dst0 != nullptr) + (dst1 != nullptr);
+    if (reads + writes == 0) return SKIPLN_ERR_NULL;
+    if (bytes == 0) return SKIPLN_OK;
+    for (const void* p : {src0, src1, static_cast<const void*>(dst0), static_cast<const void*>(dst1)})
+        if (p && !aligned16(p)) return SKIPLN_ERR_SHAPE;
+    const Range r[4] = {span(src0, src0 ? bytes : 0), span(src1, src1 ? bytes : 0), span(dst0, dst0 ? bytes : 0),
+                        span(dst1, dst1 ? bytes : 0)};
+    for (int o = 2; o < 4; ++o)
+        for (int i = 0; i < 4; ++i)
+            if (i != o && overlap(r[o], r[i])) return SKIPLN_ERR_ALIAS;
+    return status_of(skipln::launch_stream(reads, writes, block, chunks_per_lane, src0, src1, dst0, dst1, bytes / 16,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
 int skipln_rowtile_geometries(void) { return skipln::rowtile_count(); }
 
 int skipln_element_geometries(void) { return skipln::elem_count(); }

@@ -105,5 +105,11 @@ bool split_holds(int op, int64_t hidden, int dtype);
 int64_t split_workspace_bytes(const Args& a, int dtype);
 hipError_t launch_split(const Args& a, int op, int dtype, void* workspace, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
+// Streaming probe: `reads` (0-2) input streams s0, s1 to `writes` (0-2)
+// output streams d0, d1 of `chunks` 16-byte chunks each, in tiles of `block`
+// lanes x `per_lane` chunks (shapes stream_shape_ok accepts).
+bool stream_shape_ok(int block, int per_lane);
+hipError_t launch_stream(int reads, int writes, int block, int per_lane, const void* s0, const void* s1, void* d0,
+                         void* d1, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln
