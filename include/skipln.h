@@ -122,7 +122,9 @@ enum {
                                      simplified and BiasSoftmax, 16-byte chunks,
                                      aligned pointers, at most 64 slices
                                      (262144 float32 / 524288 float16 values);
-                                     skipln_forward_ws only */
+                                     skipln_forward_ws only; the residual may
+                                     not alias input or skip (the automatic
+                                     choice then takes the generic kernel) */
     SKIPLN_VARIANT_ELEMENT = 6,   /* row held in registers, one element per
                                      access: any hidden size up to 16384,
                                      tensors aligned to their element size

@@ -305,18 +305,23 @@ def test_workspace_sizes_and_split_selection():
     name_ws = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: \
         L.kernel_name(lib.skipln_select_ws(op, h, dt, mode, 1, v))
     name = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select(op, h, dt, mode, 1, v))
-    # 65536 float32 = 16 slices of 4096; 128 MiB of inputs per batch = 256 rows of x and skip
-    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == 64 * 16 * 16
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == 256 * 16 * 16
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 512 * 16 * 16  # skip not streamed
+    # header (16 B) + one arrival counter per row (padded to 16 B) + one float4
+    # partial per slice; 65536 float32 = 16 slices of 4096
+    # one float4 partial per slice of a batch of rows; a batch streams at most
+    # 128 MiB of inputs (x, and skip when it is not broadcast)
+    ws = lambda rows, slices: rows * slices * 16
+    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == ws(64, 16)
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == ws(256, 16)
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == ws(512, 16)
+    assert wb(L.OP_LAYER_NORM, 201, 65540, L.F32) == ws(201, 17)
     assert wb(L.OP_LAYER_NORM, 0, 65536, L.F32) == 0
     assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32) == 0                       # row tiles need none
     assert wb(L.OP_LAYER_NORM, 64, 20000, L.F32) == 0                      # LDS-staged
-    assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_SPLITROW) == 64 * 1 * 16
+    assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_SPLITROW) == ws(64, 1)
     assert wb(L.OP_BIAS_ADD, 64, 65536, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
     assert wb(L.OP_LAYER_NORM, 64, 65536, 9) == -L.ERR_DTYPE
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32, L.SKIP_BROADCAST, 3) == -L.ERR_SHAPE
-    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 64 * 16 * 16
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == ws(64, 16)
     # the automatic choice: split rows only where a workspace is at hand
     assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
     assert name_ws(L.OP_LAYER_NORM, 65536, L.F32) == "splitrow_f32"
@@ -353,6 +358,9 @@ def test_forward_ws_workspace_checks():
     assert FW(WS, need, variant=L.VARIANT_LDSROW) == L.ERR_UNSUPPORTED
     assert FW(None, 0, hidden=64, variant=L.VARIANT_SPLITROW) == L.ERR_WORKSPACE
     assert FW(WS, need, op=L.OP_BIAS_ADD, variant=L.VARIANT_SPLITROW) == L.ERR_UNSUPPORTED
+    # a residual over the input cannot take the split-row kernels (they read x twice)
+    assert L.load().skipln_forward_ws(L.OP_LAYER_NORM, IN, SK, 0, 0, GA, BE, BI, OUT, IN, 4, 65536, 1e-5, L.F32,
+                                      L.VARIANT_SPLITROW, WS, need, None) == L.ERR_UNSUPPORTED
 
 
 def test_stream_probe_argument_checks():

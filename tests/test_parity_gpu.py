@@ -482,15 +482,22 @@ def test_rows_zero_is_noop():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("variant", [L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE])
+@pytest.mark.parametrize("variant_hidden", [(L.VARIANT_AUTO, 1024), (L.VARIANT_GENERIC, 1024),
+                                            (L.VARIANT_MULTIWAVE, 1024), (L.VARIANT_LDSROW, 12288),
+                                            (L.VARIANT_ELEMENT, 1000), (L.VARIANT_AUTO, 1000)],
+                         ids=lambda t: f"v{t[0]}_h{t[1]}")
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_in_place(variant, dt):
-    """out over input and residual over the (exact) skip."""
-    w = W.small_case(33, 1024, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=21)
+@pytest.mark.parametrize("op", ["layer_norm", "simplified"])
+def test_in_place(variant_hidden, dt, op):
+    """out over input and residual over the (exact) skip, in every family:
+    no lane may read a value another lane has already overwritten."""
+    variant, hidden = variant_hidden
+    w = W.small_case(33, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=21,
+                     input_dist=W.normal(50, 1), op=op)
     inputs = W.make_inputs(w)
     ref = U.oracle_rows(w, inputs)
     dc = U.DeviceCase(w, inputs, residual=True)
-    U.note(f"in place {dt} variant {variant}")
+    U.note(f"in place {op} {dt} variant {variant} H={hidden}")
     dc.run(variant, out=dc.x, res=dc.skip)
     U.assert_out_close(dc.host(dc.x), ref["y"], dt)
     U.assert_bits_equal(dc.host(dc.skip), ref["residual"])

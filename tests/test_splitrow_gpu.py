@@ -81,49 +81,13 @@ def test_split_auto_with_workspace(dt, hidden, op):
 
 
 @pytest.mark.parametrize("dt,hidden", [("f32", 65536), ("f16", 131072)])
-def test_split_several_batches(dt, hidden):
+def test_split_many_rows(dt, hidden):
     """More rows than one batch holds (128 MiB of streamed inputs): the
     workspace is reused batch after batch on the same stream."""
-    row_bytes = hidden * (4 if dt == "f32" else 2)
-    per_batch = (128 << 20) // (2 * row_bytes)
-    rows = 2 * per_batch + 7
+    rows = 519
     w = norm_case(rows, hidden, dt, "layer_norm", seed=11)
-    U.note(f"split batches {dt} H={hidden} rows={rows} ({per_batch} per batch)")
+    U.note(f"split many rows {dt} H={hidden} rows={rows}")
     U.check_case(w, workspace=True)
-
-
-@pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("mu", [100.0, 1000.0])
-def test_split_large_offset_rows(dt, mu):
-    w = norm_case(8, 65536, dt, "layer_norm", seed=int(mu), mu=mu if dt == "f32" else mu / 10)
-    U.note(f"split offset {mu} {dt}")
-    U.check_case(w, variant=SPLIT, workspace=True)
-
-
-@pytest.mark.parametrize("dt", ["f32", "f16"])
-def test_split_softmax_special_rows(dt):
-    """Masked slices (-inf over whole workgroups), a row of -inf (NaN), a NaN,
-    +inf, huge spread, a large offset."""
-    hidden = 40960 if dt == "f32" else 81920  # 10 slices
-    rng = np.random.default_rng(4)
-    rows = 8
-    x = rng.standard_normal((rows, hidden)) * 2
-    b = np.zeros((rows, hidden))
-    b[0, 5000:] = -np.inf           # slices 2.. fully masked
-    b[1, :] = -np.inf               # NaN row
-    x[2, 12345] = np.nan
-    x[3, hidden - 1] = np.inf
-    x[4] *= 30
-    x[5] += 1000.0 if dt == "f32" else 50000.0
-    b[6, : hidden - 3] = -np.inf    # only the last slice's tail kept
-    w = softmax_case(rows, hidden, dt, "exact", seed=0)
-    inputs = {"input": x.astype(w.np_dtype), "skip": b.astype(w.np_dtype), "gamma": None, "beta": None,
-              "bias": None}
-    U.note(f"split softmax special {dt}")
-    dc, _ = U.check_case(w, variant=SPLIT, inputs=inputs, workspace=True)
-    y = dc.host(dc.out)
-    assert np.all(np.isnan(y[1])) and np.all(np.isnan(y[2])) and np.all(np.isnan(y[3]))
-    assert np.all(y[0, 5000:] == 0) and not np.isnan(y[6]).any()
 
 
 def test_split_workspace_errors_enqueue_nothing():
@@ -197,3 +161,31 @@ def test_split_graph_replay():
         torch.cuda.synchronize()
         assert torch.equal(dc.out.view(torch.int32), first.view(torch.int32))
     U.compare(w, dc.host(dc.out), None, U.oracle_rows(w, inputs))
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_softmax"])
+@pytest.mark.parametrize("over", ["input", "skip"])
+def test_split_in_place(op, over):
+    """out over the input (or the exact skip): a workgroup reads its own
+    slice before writing it.  A residual over an input cannot take the
+    split-row kernels: forced, the call is refused; automatic, it runs the
+    generic kernel."""
+    dt, hidden = "f32", 65536
+    w = (softmax_case(16, hidden, dt, "exact", seed=7) if op == "bias_softmax"
+         else norm_case(16, hidden, dt, op, seed=7, mu=100.0))
+    inputs = W.make_inputs(w)
+    ref = U.oracle_rows(w, inputs)
+    norm = op != "bias_softmax"
+    dc = U.DeviceCase(w, inputs, residual=norm)
+    U.note(f"split in place {op} over {over}")
+    target = dc.x if over == "input" else dc.skip
+    dc.run(SPLIT, out=target, workspace=dc.workspace(SPLIT))
+    U.compare(w, dc.host(target), dc.host(dc.res) if norm else None, ref)
+    if norm:
+        dc2 = U.DeviceCase(w, inputs, residual=True)
+        other = dc2.skip if over == "input" else dc2.x
+        with pytest.raises(T.SkiplnError) as e:
+            dc2.run(SPLIT, out=dc2.out, res=other, workspace=dc2.workspace(SPLIT))
+        assert e.value.status == L.ERR_UNSUPPORTED
+        dc2.run(L.VARIANT_AUTO, out=dc2.out, res=other, workspace=dc2.workspace())
+        U.compare(w, dc2.host(dc2.out), dc2.host(other), ref)

@@ -256,6 +256,12 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
     const skipln::Args a = make_args(c);
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int index = id % skipln::kIdsPerType;
+    if (index == skipln::kSplitRowIndex && c.residual && (c.residual == c.input || c.residual == c.skip)) {
+        // The split-row kernels read x and skip twice, so a residual written
+        // over either cannot take them: the generic kernel can.
+        if (variant != SKIPLN_VARIANT_AUTO) return SKIPLN_ERR_UNSUPPORTED;
+        return status_of(skipln::launch_generic(make_args(c), c.op, c.dtype, reinterpret_cast<hipStream_t>(stream)));
+    }
     if (index == skipln::kSplitRowIndex) {
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the split-row kernels have no tiling
         if (!ws || !ws->ptr || !aligned16(ws->ptr) || ws->bytes < workspace_needed(c)) return SKIPLN_ERR_WORKSPACE;

@@ -185,6 +185,9 @@ __global__ void __launch_bounds__(kLdsBlock) ldsrow_kernel(const Args a) {
         if constexpr (OP == kOpLayerNorm) {
             shift = E::load1(a.input, row * a.hidden) + E::load1(a.skip, srow_i * a.hidden);
             if (has_bias) shift = shift + E::load1(a.bias, 0);
+            // Every lane has read the row's first sum before lane 0 may store
+            // its residual over an aliased skip (or input).
+            __syncthreads();
         }
 
         float part = 0.0f;

@@ -6,15 +6,18 @@
 // rows.  Two kernels per batch of rows:
 //   split_stats_kernel: loads its slice once (x, skip, bias), stores the
 //     residual, and writes the slice's partial result to the workspace:
-//       layer norm   (n_p, mean of (s - shift), M2 about that mean)
+//       layer norm   (n_p, mean of (s - shift_p), M2 about that mean, shift_p)
 //       simplified   (n_p, sum of s^2)
 //       BiasSoftmax  (n_p, slice maximum m_p, sum of exp(z - m_p))
-//     `shift` is the row's first sum (recomputed by every workgroup with the
-//     same operations, hence the same bits), as in the row-tile kernel, so the
-//     merge only adds small numbers.
+//     shift_p is the slice's first sum (as the row-tile kernel shifts by a
+//     value of the row), so the merge, relative to slice 0's shift, only adds
+//     small numbers.
 //   split_apply_kernel: every wavefront merges the row's P partials on its own
 //     (Chan's update for (mean, M2); max and rescaled sums for the softmax),
 //     reloads its slice, forms the same sums again and writes the output.
+//     A workgroup reads only its own slice before writing it, so the output
+//     may alias an input; the residual may not (the second pass re-reads x and
+//     skip), and the selection sends such calls elsewhere.
 // The second pass re-reads x and skip, so a launch moves one more read stream
 // than the single-workgroup kernels (the cost of needing no inter-workgroup
 // synchronization: no workgroup ever waits for another).  Rows are processed
@@ -44,13 +47,13 @@ struct Split {
     int64_t row0;    // first row of this batch
 };
 
-// The row's first sum: input + skip (+ bias), the value every slice of the
-// row shifts by.
+// The sum at column `col` of a row: input + skip (+ bias), formed with the
+// operations of the slice loops, hence the same bits.
 template <typename T>
-__device__ __forceinline__ float row_first_sum(const Args& a, int64_t row, int64_t srow) {
+__device__ __forceinline__ float sum_at(const Args& a, int64_t row, int64_t srow, int64_t col) {
     using E = Elem<T>;
-    float v = E::load1(a.input, row * a.hidden) + E::load1(a.skip, srow * a.hidden);
-    if (a.bias != nullptr) v = v + E::load1(a.bias, 0);
+    float v = E::load1(a.input, row * a.hidden + col) + E::load1(a.skip, srow * a.hidden + col);
+    if (a.bias != nullptr) v = v + E::load1(a.bias, col);
     return v;
 }
 
@@ -130,7 +133,7 @@ __global__ void __launch_bounds__(kSplitBlock) split_stats_kernel(const Args a, 
 
     float4 out;
     if constexpr (OP == kOpLayerNorm) {
-        const float shift = row_first_sum<T>(a, row, srow);
+        const float shift = sum_at<T>(a, row, srow, static_cast<int64_t>(c0) * V);
         float part = 0.0f;
 #pragma unroll
         for (int k = 0; k < kSplitCh; ++k)
@@ -147,7 +150,7 @@ __global__ void __launch_bounds__(kSplitBlock) split_stats_kernel(const Args a, 
                     const float d = (s[k][e] - shift) - dm;
                     q += d * d;
                 }
-        out = make_float4(n_p, dm, block_reduce(q, 1, SumOp{}), 0.0f);
+        out = make_float4(n_p, dm, block_reduce(q, 1, SumOp{}), shift);
     } else if constexpr (OP == kOpSimplified) {
         float sq = 0.0f;
 #pragma unroll
@@ -206,11 +209,18 @@ __global__ void __launch_bounds__(kSplitBlock) split_apply_kernel(const Args a, 
     const float4 q = mine ? sp.ws[lrow * sp.slices + lane] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float shift = 0.0f, off = 0.0f, scale, ref = 0.0f;
     if constexpr (OP == kOpLayerNorm) {
-        shift = row_first_sum<T>(a, row, srow);
-        const float dmean = wave_sum(q.x * q.y) / h;
-        const float dd = q.y - dmean;
+        // This slice's shift, read by every lane before any lane stores over
+        // an aliased input; slice means relative to slice 0's shift.
+        shift = sum_at<T>(a, row, srow, static_cast<int64_t>(c0) * V);
+        __syncthreads();
+        const float row_shift = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, q.w)));
+        const float d = mine ? (q.w - row_shift) + q.y : 0.0f;
+        const float dmean = wave_sum(q.x * d) / h;
+        const float dd = d - dmean;
         const float m2 = wave_sum(mine ? q.z + q.x * dd * dd : 0.0f);
-        off = dmean;
+        // s - shift is centered on the row mean by subtracting
+        // dmean - (shift - row_shift).
+        off = dmean - (shift - row_shift);
         scale = rsqrtf(m2 / h + a.eps);
     } else if constexpr (OP == kOpSimplified) {
         scale = rsqrtf(wave_sum(q.y) / h + a.eps);
