@@ -33,10 +33,19 @@ SWEEP = ["rows16384_h1024_f16", "bcast_64x512x4096_f32", "rows65536_h8192_f16_me
          "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "softmax_attn_16x16x512x512_f16_padmask",
          "softmax_relpos_64x12x128x128_f32", "softmax_vocab_4096x128256_f16"]
 OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*
-# Sources of the row kernels: counters taken on other sources are stale.
-KERNEL_SRC = [os.path.join(ROOT, "transformer_residual_add_amd", "csrc", f)
-              for f in ("skipln_device.h", "skipln_rowtile.h", "skipln_rowtile_op.hip", "skipln_kernels.hip",
-                        "skipln_split.hip")]
+CSRC = os.path.join(ROOT, "transformer_residual_add_amd", "csrc")
+
+
+def kernel_sources(kernel: str):
+    """The source files that define a kernel (by its library name): counters
+    taken on other versions of them are stale."""
+    if "rowtile_" in kernel or "rowelem_" in kernel:
+        files = ("skipln_device.h", "skipln_rowtile.h", "skipln_rowtile_op.hip")
+    elif "splitrow_" in kernel:
+        files = ("skipln_device.h", "skipln_split.hip")
+    else:
+        files = ("skipln_device.h", "skipln_kernels.hip")
+    return [os.path.join(CSRC, f) for f in files]
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -71,9 +80,9 @@ def parse_args(argv=None):
     return p.parse_args(argv)
 
 
-def source_sha() -> str:
+def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRC:
+    for path in kernel_sources(kernel):
         with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -90,7 +99,7 @@ def counter_traffic(kernel: str, workload: str):
         return None
     for e in data.get("entries", []):
         if e.get("kernel") == kernel and e.get("workload") == workload:
-            if e.get("source_sha256") != source_sha():
+            if e.get("source_sha256") != source_sha(kernel):
                 return None
             return int(e["fetch_bytes"] + e["write_bytes"])
     return None
@@ -404,12 +413,14 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
         entries.append({"kernel": kernel, "workload": name, "dispatches": n, "fetch_kib_raw": round(f, 1),
                         "write_kib_raw": round(wr, 1), "fetch_bytes": fb, "write_bytes": wb,
                         "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 4),
-                        "source_sha256": source_sha()})
+                        "sources": [os.path.basename(f) for f in kernel_sources(kernel)],
+                        "source_sha256": source_sha(kernel)})
         print(f"| {name} | {kernel} | {f:,.1f} | {wr:,.1f} | {fb:,} | {wb:,} | {(fb + wb) / alg:.3f} |")
     data = {
         "about": "HBM bytes per dispatch from rocprofv3 FETCH_SIZE and WRITE_SIZE (separate --pmc runs), each "
                  "scaled by what the same counter reads for the streaming copy of 1 GiB (skipln_copy: 1 GiB "
-                 "read, 1 GiB written). source_sha256 is the kernel source the counters were taken on.",
+                 "read, 1 GiB written). source_sha256 hashes the sources that define the kernel (`sources`) as they "
+                 "were when the counters were taken.",
         "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
                              "fetch_kib_raw": round(fetch_raw, 1), "write_kib_raw": round(write_raw, 1),
                              "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5)},
