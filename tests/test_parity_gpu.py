@@ -561,6 +561,51 @@ def test_non_default_stream():
     U.assert_bits_equal(dc.host(dc.res), ref["residual"])
 
 
+def test_concurrent_host_threads_and_streams():
+    """Eight host threads, each with its own stream and problem (every
+    operation and kernel family), launching at once: each result equals the
+    oracle (the library keeps no mutable state besides an attribute cache)."""
+    import threading
+
+    import torch
+
+    cases = [W.small_case(64, 1024, "f16", beta=True, bias=True, residual=True, eps=1e-5, seed=61),
+             W.small_case(40, 768, "f32", skip_rows=8, residual=True, eps=1e-5, seed=62),
+             W.small_case(33, 1000, "f32", bias=True, residual=True, eps=1e-5, seed=63, op="simplified"),
+             W.small_case(48, 12288, "f32", beta=True, residual=True, eps=1e-5, seed=64),
+             W.small_case(64, 4096, "f16", seed=65, op="bias_add"),
+             W.small_case(96, 77, "f16", skip_rows=3, seed=66, op="bias_softmax", inner=True),
+             W.small_case(256, 512, "f32", skip_rows=4, seed=67, op="bias_softmax"),
+             W.small_case(8, 65536, "f32", beta=True, residual=True, eps=1e-5, seed=68)]
+    devs = []
+    for w in cases:
+        inputs = W.make_inputs(w)
+        devs.append((w, inputs, U.DeviceCase(w, inputs, residual=w.residual)))
+    torch.cuda.synchronize()
+    errors = []
+    start = threading.Barrier(len(devs))
+
+    def work(dc):
+        try:
+            s = torch.cuda.Stream()
+            start.wait()
+            for _ in range(5):
+                dc.run(stream=s.cuda_stream, workspace=True)
+            s.synchronize()
+        except Exception as e:  # reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(dc,)) for _, _, dc in devs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for w, inputs, dc in devs:
+        U.note(f"concurrent {w.name}")
+        U.compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, U.oracle_rows(w, inputs))
+
+
 @pytest.mark.parametrize("name", ["bert_base_8x128x768_f32", "bcast_64x512x4096_f32"])
 def test_graph_replay_matches_eager(name):
     """Captured into a HIP graph, every replay (with eager work and
