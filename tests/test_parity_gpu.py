@@ -561,6 +561,37 @@ def test_non_default_stream():
     U.assert_bits_equal(dc.host(dc.res), ref["residual"])
 
 
+def test_more_than_2_to_the_32_rows():
+    """Row indices past 32 bits (2^32 + 8 rows of one value, float16): the
+    64-bit row and broadcast-skip paths.  With H = 1 the output is beta
+    exactly; the residual must equal x + skip[r mod 4] bit for bit."""
+    import torch
+
+    rows, S = (1 << 32) + 8, 4
+    g = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(rows, 1, device="cuda", dtype=torch.float16, generator=g)
+    skip = torch.randn(S, 1, device="cuda", dtype=torch.float16, generator=g)
+    gamma = torch.full((1,), 1.5, device="cuda", dtype=torch.float16)
+    beta = torch.full((1,), 0.25, device="cuda", dtype=torch.float16)
+    out = torch.empty_like(x)
+    res = torch.empty_like(x)
+    torch.cuda.synchronize()
+    U.note(f"rows={rows} H=1 f16 inputs ready; launching {T.select_kernel(1, L.F16, skip_mode=L.SKIP_BROADCAST)}")
+    T.forward_raw(x.data_ptr(), skip.data_ptr(), L.SKIP_BROADCAST, S, gamma.data_ptr(), beta.data_ptr(), None,
+                  out.data_ptr(), res.data_ptr(), rows, 1, 1e-5, L.F16)
+    torch.cuda.synchronize()
+    U.note("kernel done; checking")
+    assert bool((out == 0.25).all()), "H = 1 must give beta"
+    step = 1 << 28
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        want = (x[r0:r1].float() + skip.repeat((r1 - r0) // S, 1).float()).half()
+        assert torch.equal(res[r0:r1].view(torch.int16), want.view(torch.int16)), f"residual rows {r0}:{r1}"
+    # the last rows, past 2^32, by hand
+    for r in (rows - 1, rows - 5, (1 << 32) + 1):
+        assert res[r].item() == (x[r].float() + skip[r % S].float()).half().item()
+
+
 def test_concurrent_host_threads_and_streams():
     """Eight host threads, each with its own stream and problem (every
     operation and kernel family), launching at once: each result equals the

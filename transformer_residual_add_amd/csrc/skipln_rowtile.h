@@ -502,6 +502,8 @@ hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipSt
 }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+// A dispatch counts its work-items in 32 bits: blocks x block stays below 2^32.
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
 template <typename E, int OP, int GG, int CH, int BLOCK>
 hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
@@ -513,8 +515,10 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     Args a = a0;
     int mode = tiling.mode;
     int64_t per = tiling.tiles_per_block;
+    const int64_t max_blocks = kMaxWorkItems / g.block < kMaxGrid ? kMaxWorkItems / g.block : kMaxGrid;
     // Skip-stationary needs a broadcast skip whose rows split into whole tiles.
-    if (mode == kTileSkipStationary && (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > kMaxGrid))
+    if (mode == kTileSkipStationary &&
+        (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > max_blocks))
         mode = kTileStrided;
     int64_t resident = 0;
     if (per <= 0) {
@@ -530,7 +534,9 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
             const int64_t chunks = resident > P ? resident / P : 1;
             per = (batches + chunks - 1) / chunks;
         }
-        if (P * ((batches + per - 1) / per) > kMaxGrid) per = (batches * P + kMaxGrid - 1) / kMaxGrid;
+        // At most max_blocks / P batch chunks per tile column.
+        const int64_t chunks_max = max_blocks / P;
+        if ((batches + per - 1) / per > chunks_max) per = (batches + chunks_max - 1) / chunks_max;
         blocks = P * ((batches + per - 1) / per);
     } else {
         if (per <= 0) {
@@ -538,7 +544,7 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
             per = (tiles + resident - 1) / resident;
             mode = kTileStrided;
         }
-        if ((tiles + per - 1) / per > kMaxGrid) per = (tiles + kMaxGrid - 1) / kMaxGrid;
+        if ((tiles + per - 1) / per > max_blocks) per = (tiles + max_blocks - 1) / max_blocks;
         blocks = (tiles + per - 1) / per;
     }
     a.tiles_per_block = per;

@@ -301,6 +301,8 @@ hipError_t launch_split_t(const Args& a, float4* ws, hipStream_t st) {
         sp.slices = P;
         sp.row0 = row0;
         void* params[] = {&arg, &sp};
+        // n * P * kSplitBlock work-items: a batch streams at most
+        // kBatchInputBytes, i.e. at most 2^23 rows of 16 bytes, one slice each.
         const dim3 grid(static_cast<unsigned>(n * P));
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(split_stats_kernel<T, OP>), grid,
                                        dim3(kSplitBlock), params, 0, st);

@@ -59,7 +59,8 @@ hipError_t launch_stream_t(const void* s0, const void* s1, void* d0, void* d1, i
     u32x4* d = static_cast<u32x4*>(d1);
     void* params[] = {&a, &b, &c, &d, &chunks};
     const int64_t blocks = (chunks + BLOCK * U - 1) / (BLOCK * U);
-    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    // A dispatch counts its work-items in 32 bits.
+    if (blocks > 0x7FFFFFFF || blocks * BLOCK > 0xFFFFFFFFll) return hipErrorInvalidValue;
     return hipLaunchKernel(reinterpret_cast<const void*>(stream_kernel<NR, NW, BLOCK, U>),
                            dim3(static_cast<unsigned>(blocks)), dim3(BLOCK), params, 0, st);
 }
