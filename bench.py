@@ -43,6 +43,8 @@ def kernel_sources(kernel: str):
         files = ("skipln_device.h", "skipln_rowtile.h", "skipln_rowtile_op.hip")
     elif "splitrow_" in kernel:
         files = ("skipln_device.h", "skipln_split.hip")
+    elif "regrow_" in kernel:
+        files = ("skipln_device.h", "skipln_regrow.hip")
     else:
         files = ("skipln_device.h", "skipln_kernels.hip")
     return [os.path.join(CSRC, f) for f in files]
@@ -252,9 +254,20 @@ def time_copy(nbytes: int, steps: int, warmup: int):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "launch_us": dt * 1e6, "gb_per_s": 2 * nbytes / dt / 1e9}
 
 
+# Tile shapes of the streaming probe: (lanes, chunks per lane, XCD granule in
+# tiles).  Granule 1 is address order: consecutive tiles on different XCDs.
+# The 64 x 1 tile at granules 2, 3, 4 and 16 hands each XCD 2, 3, 4 and 16
+# KiB of every stream at a time -- the granularity of a row kernel whose
+# workgroup owns rows of that size.
+STREAM_SHAPES = ((64, 1, 1), (64, 4, 1), (256, 1, 1), (256, 4, 1), (1024, 1, 1), (1024, 4, 1),
+                 (64, 1, 2), (64, 1, 3), (64, 1, 4), (64, 1, 16))
+STREAM_GRANULES = (1024, 2048, 3072, 4096, 16384)
+
+
 def time_streams(nbytes: int, steps: int, warmup: int):
     """HBM rate of the streaming probe for each mix of read and written
-    streams (the attainable ceilings of the row kernels' access pattern)."""
+    streams (the attainable ceilings of the row kernels' access pattern),
+    and the best rate at each XCD granularity."""
     import torch
 
     from transformer_residual_add_amd import _lib as L
@@ -273,31 +286,39 @@ def time_streams(nbytes: int, steps: int, warmup: int):
 
             moved = (reads + writes) * nbytes
             shapes = []
-            for block in (64, 256, 1024):
-                for per_lane in (1, 4):
-                    def launch():
-                        L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, s),
-                                "skipln_stream")
+            for block, per_lane, granule in STREAM_SHAPES:
+                def launch():
+                    L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, granule, s),
+                            "skipln_stream")
 
-                    for _ in range(warmup):
-                        launch()
-                    torch.cuda.synchronize()
-                    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    ev0.record()
-                    for _ in range(steps):
-                        launch()
-                    ev1.record()
-                    torch.cuda.synchronize()
-                    dt = ev0.elapsed_time(ev1) * 1e-3 / steps
-                    shapes.append({"block": block, "chunks_per_lane": per_lane, "launch_us": round(dt * 1e6, 2),
-                                   "gb_per_s": round(moved / dt / 1e9, 1)})
+                for _ in range(warmup):
+                    launch()
+                torch.cuda.synchronize()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for _ in range(steps):
+                    launch()
+                ev1.record()
+                torch.cuda.synchronize()
+                dt = ev0.elapsed_time(ev1) * 1e-3 / steps
+                shapes.append({"block": block, "chunks_per_lane": per_lane, "xcd_granule": granule,
+                               "xcd_granule_bytes": block * per_lane * 16 * granule,
+                               "launch_us": round(dt * 1e6, 2), "gb_per_s": round(moved / dt / 1e9, 1)})
             best = max(shapes, key=lambda r: r["gb_per_s"])
+            # Best rate among shapes whose XCDs share the streams at this
+            # granularity or coarser: the ceiling of a row kernel with rows
+            # of that many bytes per stream.
+            at_granule = {str(g): max(r["gb_per_s"] for r in shapes if r["xcd_granule_bytes"] >= g)
+                          for g in STREAM_GRANULES}
             out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "best_gb_per_s": best["gb_per_s"],
                         "best_frac_of_peak": round(best["gb_per_s"] / HBM_PEAK_GBS, 4),
-                        "best_shape": [best["block"], best["chunks_per_lane"]], "shapes": shapes})
+                        "best_shape": [best["block"], best["chunks_per_lane"], best["xcd_granule"]],
+                        "best_at_xcd_granule_bytes": at_granule, "shapes": shapes})
             log(f"stream {reads}R{writes}W: best {best['gb_per_s']:.0f} GB/s (block {best['block']}, "
-                f"{best['chunks_per_lane']} chunk(s)/lane); " +
-                ", ".join(f"{r['block']}x{r['chunks_per_lane']}: {r['gb_per_s']:.0f}" for r in shapes))
+                f"{best['chunks_per_lane']} chunk(s)/lane, granule {best['xcd_granule']}); " +
+                ", ".join(f"{r['block']}x{r['chunks_per_lane']}g{r['xcd_granule']}: {r['gb_per_s']:.0f}"
+                          for r in shapes) +
+                "; by XCD granule: " + ", ".join(f"{g}B {v:.0f}" for g, v in at_granule.items()))
     return out
 
 

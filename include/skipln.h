@@ -97,10 +97,11 @@ enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 
 
 /* Kernel families, for skipln_forward_variant / skipln_select.  The automatic
  * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
- * kernel for longer rows of the reducing operations, then -- for calls that
- * bring a workspace (skipln_forward_ws) -- the split-row kernels; rows that
- * are not whole chunks, or tensors not 16-byte aligned, take element-wise
- * row tiles up to 16384 values, and the generic kernel anything else. */
+ * kernel for longer rows of the reducing operations, the register-resident
+ * kernel for BiasSoftmax rows beyond it, then -- for calls that bring a
+ * workspace (skipln_forward_ws) -- the split-row kernels; rows that are not
+ * whole chunks, or tensors not 16-byte aligned, take element-wise row tiles
+ * up to 16384 values, and the generic kernel anything else. */
 enum {
     SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
     SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
@@ -130,6 +131,14 @@ enum {
                                      tensors aligned to their element size
                                      (what the automatic choice takes for rows
                                      that are not whole 16-byte chunks) */
+    SKIPLN_VARIANT_REGROW = 7,    /* long rows of BiasSoftmax: one 1024-lane
+                                     block per row, the row's raw data in
+                                     registers (up to 16 chunks per lane:
+                                     131072 float16 / 65536 float32 values),
+                                     z = data + bias formed again in each of
+                                     two passes from the bias rows re-read
+                                     through the caches; 16-byte chunks,
+                                     aligned pointers; no workspace */
     SKIPLN_VARIANT_GEOMETRY = 64, /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_rowtile_geometries(), for
                                      tests and tuning */
@@ -211,9 +220,12 @@ int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, 
  * workspace / workspace_bytes: NULL / 0, or a workspace as for
  * skipln_forward_ws (size from skipln_workspace_bytes with
  * SKIPLN_OP_BIAS_SOFTMAX, rows = batch_count, hidden = block_size and the
- * skip form above), which lets rows longer than 40896 values split across
- * workgroups (the manifest's long-row variants); without one they take the
- * generic kernel.  Ownership, streams and errors as for skipln_forward.
+ * skip form above).  Rows of 16-byte chunks up to 40896 values stay in one
+ * workgroup's LDS and up to 131072 float16 / 65536 float32 values in one
+ * workgroup's registers (the manifest's long-row variants split them across
+ * workgroups); longer ones split across workgroups through the workspace, or
+ * without one take the generic kernel.  Ownership, streams and errors as for
+ * skipln_forward.
  */
 int skipln_bias_softmax(const void* data, const void* bias, void* out, int64_t batch_count, int64_t block_size,
                         int64_t bias_batch_count, int is_inner_broadcast, int dtype, void* workspace,
@@ -308,18 +320,23 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 
 /* Streaming probe with the access pattern of the row kernels (16-byte
  * non-temporal accesses, one tile of `block` lanes x `chunks_per_lane`
- * chunks per stream and workgroup, in address order; block 64, 256 or 1024,
- * chunks_per_lane 1 or 4): reads 0-2 input streams (src0, then src1; NULL =
- * not read) and writes 0-2 output streams (dst0, then dst1) of `bytes` bytes
- * each.  It measures the HBM rate a kernel of that pattern attains for each
- * mix of reads and writes, the ceiling the row kernels are compared with.
+ * chunks per stream and workgroup; block 64, 256 or 1024, chunks_per_lane 1
+ * or 4): reads 0-2 input streams (src0, then src1; NULL = not read) and
+ * writes 0-2 output streams (dst0, then dst1) of `bytes` bytes each.  It
+ * measures the HBM rate a kernel of that pattern attains for each mix of
+ * reads and writes, the ceiling the row kernels are compared with.
+ * xcd_granule (1 .. 65536): tiles in address order (1), or each XCD handed
+ * xcd_granule consecutive tiles per round of 8 x xcd_granule (the dispatcher
+ * deals workgroup b to XCD b mod 8): the address granularity at which the
+ * eight XCDs share the streams, which for a row kernel is one row.
  * Outputs: dst0 = src0 XOR src1 (a chunk's index when nothing is read),
- * dst1 = dst0 + 1 per 32-bit word.  Device memory, 16-byte aligned, bytes %
- * 16 == 0, outputs overlapping nothing.  Returns SKIPLN_OK, SKIPLN_ERR_NULL
- * (no stream, or src1/dst1 without src0/dst0), SKIPLN_ERR_SHAPE,
- * SKIPLN_ERR_ALIAS, SKIPLN_ERR_VARIANT (tile shape) or SKIPLN_ERR_LAUNCH. */
+ * dst1 = dst0 + 1 per 32-bit word, whatever the tile order.  Device memory,
+ * 16-byte aligned, bytes % 16 == 0, outputs overlapping nothing.  Returns
+ * SKIPLN_OK, SKIPLN_ERR_NULL (no stream, or src1/dst1 without src0/dst0),
+ * SKIPLN_ERR_SHAPE, SKIPLN_ERR_ALIAS, SKIPLN_ERR_VARIANT (tile shape or
+ * granule) or SKIPLN_ERR_LAUNCH. */
 int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
-                  int chunks_per_lane, skipln_stream_t stream);
+                  int chunks_per_lane, int64_t xcd_granule, skipln_stream_t stream);
 
 /* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
 int skipln_rowtile_geometries(void);

@@ -10,8 +10,12 @@ BiasSoftmax (SOFTMAX_TOL): the kernels form the same binary32 z = data + bias
 and maximum M as the oracle; each exponential 2^t, t = (z - M) log2 e, has a
 relative error of about |t| 9.2e-8 (three binary32 roundings in t) plus
 1.2e-7 (the exp2 instruction), the binary32 sum at most depth x 6e-8 (about
-4e-6 for the longest per-lane chains here), the scaling 1.2e-7.  For every
-y >= 1e-20 (|t| <= 67) that stays below 1.1e-5: float32 uses rtol 2e-5 and
+4e-6 for the longest per-lane chains here), the scaling 1.2e-7.  The
+register-resident long-row kernel sums relative to a running per-lane
+maximum and rescales its partial sum when the maximum grows: at most 16
+rescales per lane, each an exp2 and a product (about 1.8e-7 each), adding
+at most 2.9e-6 to the sum's error.  For every y >= 1e-20 (|t| <= 67) the
+total stays below 1.3e-5: float32 uses rtol 2e-5 and
 atol 1e-20 (smaller values, and results flushed below the binary32 normal
 range).  float16 adds one rounding to nearest (2^-11 relative, at most 2^-25
 absolute among subnormals): rtol 1e-3, atol 2^-24.

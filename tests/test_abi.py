@@ -46,7 +46,8 @@ def test_header_enums_match_binding():
         "SKIPLN_VARIANT_AUTO": L.VARIANT_AUTO, "SKIPLN_VARIANT_GENERIC": L.VARIANT_GENERIC,
         "SKIPLN_VARIANT_ROWTILE": L.VARIANT_ROWTILE, "SKIPLN_VARIANT_MULTIWAVE": L.VARIANT_MULTIWAVE,
         "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW, "SKIPLN_VARIANT_SPLITROW": L.VARIANT_SPLITROW,
-        "SKIPLN_VARIANT_ELEMENT": L.VARIANT_ELEMENT, "SKIPLN_VARIANT_ELEMENT_GEOMETRY": L.VARIANT_ELEMENT_GEOMETRY,
+        "SKIPLN_VARIANT_ELEMENT": L.VARIANT_ELEMENT,
+        "SKIPLN_VARIANT_REGROW": L.VARIANT_REGROW, "SKIPLN_VARIANT_ELEMENT_GEOMETRY": L.VARIANT_ELEMENT_GEOMETRY,
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
@@ -321,12 +322,15 @@ def test_workspace_sizes_and_split_selection():
     assert wb(L.OP_BIAS_ADD, 64, 65536, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
     assert wb(L.OP_LAYER_NORM, 64, 65536, 9) == -L.ERR_DTYPE
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32, L.SKIP_BROADCAST, 3) == -L.ERR_SHAPE
-    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == ws(64, 16)
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 0     # held in registers
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4, L.VARIANT_SPLITROW) == ws(64, 16)
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 131080, L.F16) == ws(64, 17)                     # beyond the registers
     # the automatic choice: split rows only where a workspace is at hand
     assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
     assert name_ws(L.OP_LAYER_NORM, 65536, L.F32) == "splitrow_f32"
     assert name_ws(L.OP_SIMPLIFIED, 65536, L.F16) == "rms_splitrow_f16"
-    assert name_ws(L.OP_BIAS_SOFTMAX, 128256, L.F16) == "softmax_splitrow_f16"
+    assert name_ws(L.OP_BIAS_SOFTMAX, 128256, L.F16) == "softmax_regrow_f16"
+    assert name_ws(L.OP_BIAS_SOFTMAX, 131080, L.F16) == "softmax_splitrow_f16"
     assert name_ws(L.OP_LAYER_NORM, 20000, L.F32) == "ldsrow_f32"
     assert name_ws(L.OP_LAYER_NORM, 4096, L.F32) == "rowtile_f32_g256_c4"
     assert name_ws(L.OP_LAYER_NORM, 64 * 4096, L.F32) == "splitrow_f32"        # 64 slices
@@ -335,6 +339,37 @@ def test_workspace_sizes_and_split_selection():
     assert name(L.OP_LAYER_NORM, 64, L.F32, v=L.VARIANT_SPLITROW) == "splitrow_f32"
     assert lib.skipln_select(L.OP_BIAS_ADD, 64, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
     assert lib.skipln_select(L.OP_LAYER_NORM, 66, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+
+
+def test_register_resident_softmax_selection():
+    """BiasSoftmax rows beyond the LDS capacity and up to 16 chunks per lane
+    of a 1024-lane block are held in registers, with or without a
+    workspace; the family takes only 16-byte chunks of BiasSoftmax."""
+    lib = L.load()
+    name = lambda h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT, op=L.OP_BIAS_SOFTMAX, al=1: \
+        L.kernel_name(lib.skipln_select(op, h, dt, mode, al, v))
+    name_ws = lambda h, dt, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select_ws(L.OP_BIAS_SOFTMAX, h, dt, mode, 1, 0))
+    for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST, L.SKIP_BROADCAST_INNER):
+        assert name(40896, L.F32, mode=mode) == "softmax_ldsrow_f32"
+        assert name(40900, L.F32, mode=mode) == "softmax_regrow_f32"
+        assert name(65536, L.F32, mode=mode) == "softmax_regrow_f32"
+        assert name(65540, L.F32, mode=mode) == "softmax_generic_f32"
+        assert name_ws(65540, L.F32, mode) == "softmax_splitrow_f32"
+        assert name(40960, L.F16, mode=mode) == "softmax_regrow_f16"
+        assert name(131072, L.F16, mode=mode) == "softmax_regrow_f16"
+        assert name_ws(131072, L.F16, mode) == "softmax_regrow_f16"
+        assert name(131080, L.F16, mode=mode) == "softmax_generic_f16"
+    # forced: any row of whole chunks up to the capacity
+    assert name(8, L.F32, v=L.VARIANT_REGROW) == "softmax_regrow_f32"
+    assert name(4096, L.F16, v=L.VARIANT_REGROW) == "softmax_regrow_f16"
+    unsupported = -L.ERR_UNSUPPORTED
+    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 65540, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported
+    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 77, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported    # not chunks
+    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 4096, L.F32, 0, 0, L.VARIANT_REGROW) == unsupported  # misaligned
+    for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED, L.OP_BIAS_ADD):
+        assert lib.skipln_select(op, 65536, L.F16, 0, 1, L.VARIANT_REGROW) == unsupported
+    # misaligned long rows take the generic kernel
+    assert name(65536, L.F16, al=0) == "softmax_generic_f16"
 
 
 def FW(ws, nbytes, hidden=65536, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM):
@@ -365,8 +400,8 @@ def test_forward_ws_workspace_checks():
 
 def test_stream_probe_argument_checks():
     """skipln_stream returns these statuses before any HIP call."""
-    st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4: L.load().skipln_stream(s0, s1, d0, d1, n, b, u,
-                                                                                            None)
+    st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load().skipln_stream(s0, s1, d0, d1, n, b,
+                                                                                                 u, g, None)
     assert st(s0=None, d0=None) == L.ERR_NULL
     assert st(s0=None, s1=SK) == L.ERR_NULL
     assert st(d0=None, d1=RES) == L.ERR_NULL
@@ -377,3 +412,5 @@ def test_stream_probe_argument_checks():
     assert st(d0=OUT, d1=OUT + 2048) == L.ERR_ALIAS
     assert st(n=0) == L.OK
     assert st(b=128) == L.ERR_VARIANT and st(u=2) == L.ERR_VARIANT
+    assert st(g=0) == L.ERR_VARIANT and st(g=-3) == L.ERR_VARIANT and st(g=65537) == L.ERR_VARIANT
+    assert st(n=0, g=65536) == L.OK

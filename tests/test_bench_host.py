@@ -57,8 +57,9 @@ def _write_run(root, name, counter, rows):
 
 def test_counter_summary(tmp_path, monkeypatch):
     """Copy calibration (FETCH_SIZE reads half), medians for one kernel per
-    step, sums over dispatches / steps for a split-row step, other kernels
-    (runtime copies) ignored."""
+    step, sums over dispatches / steps for a step of several dispatches (the
+    split-row pair, per batch of rows), other kernels (runtime copies)
+    ignored; the kernel named is the automatic choice."""
     root = str(tmp_path)
     gib_kib = (1 << 30) / 1024
     _write_run(root, "copy1g", "FETCH_SIZE", [("skipln::copy_kernel", gib_kib / 2)] * 12)
@@ -82,7 +83,7 @@ def test_counter_summary(tmp_path, monkeypatch):
     e = {x["workload"]: x for x in data["entries"]}
     assert e[w.name]["traffic_over_algorithmic"] == pytest.approx(1.0, abs=2e-4)  # median, not the outlier
     assert e[v.name]["traffic_over_algorithmic"] == pytest.approx(1.0, abs=2e-4)
-    assert e[v.name]["kernel"].startswith("softmax_splitrow_")
+    assert e[v.name]["kernel"] == "softmax_regrow_f16"
     # a stored entry is used only while the kernel's sources are unchanged
     monkeypatch.setattr(bench, "COUNTERS", out)
     assert bench.counter_traffic(e[w.name]["kernel"], w.name) == e[w.name]["fetch_bytes"] + e[w.name]["write_bytes"]

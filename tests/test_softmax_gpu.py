@@ -81,7 +81,7 @@ def test_hidden_sizes(dt, hidden, mode):
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("variant", [L.VARIANT_GENERIC, L.VARIANT_ROWTILE, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW,
-                                     L.VARIANT_ELEMENT])
+                                     L.VARIANT_ELEMENT, L.VARIANT_REGROW])
 @pytest.mark.parametrize("hidden", [8, 64, 1024, 4096])
 @pytest.mark.parametrize("mode", MODES)
 def test_forced_variants(dt, variant, hidden, mode):
@@ -136,9 +136,55 @@ def test_misaligned_pointers(dt):
         U.check_case(w, offset_elems=1)
 
 
+# --------------------------------------------- register-resident rows --
+
+REGROW_HIDDEN = {"f32": [4100, 16384, 40960, 49152, 65536], "f16": [8200, 40960, 65536, 100000, 128256, 131072]}
+
+
+@pytest.mark.parametrize("dt,hidden", [(d, h) for d in ("f32", "f16") for h in REGROW_HIDDEN[d]])
+@pytest.mark.parametrize("mode,bias_rows", [("exact", None), ("outer", 1), ("outer", 3), ("inner", 4), ("inner", 1)])
+def test_regrow_long_rows(dt, hidden, mode, bias_rows):
+    """Rows held in the registers of one 1024-lane block: partial last
+    chunks per lane (ragged), the largest rows it holds, more rows than
+    resident blocks (the persistent loop and its next-row loads), every bias
+    form -- one bias row for all rows (parked in LDS) or several; the
+    automatic choice beyond the LDS capacity."""
+    rows = 300 if hidden <= 65536 else 264
+    w = case(rows, hidden, dt, mode, bias_rows=bias_rows, seed=hidden + MODES.index(mode) + 7 * (bias_rows or 0))
+    code = L.F32 if dt == "f32" else L.F16
+    auto = T.select_kernel(hidden, code, op=L.OP_BIAS_SOFTMAX, skip_mode=U.skip_mode(w))
+    # row tiles up to 2048 chunks, the LDS up to 40896 values, then registers
+    assert (auto == f"softmax_regrow_{dt}") == (hidden > 40896), auto
+    U.note(f"softmax regrow {dt} H={hidden} {mode} bias rows={bias_rows} rows={rows}")
+    U.check_case(w, variant=L.VARIANT_REGROW)
+    if hidden > 40896 and mode == "outer":
+        U.check_case(w)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+def test_regrow_few_rows_and_in_place(dt):
+    """Fewer rows than blocks; output over the data and over an exact bias."""
+    hidden = 65536
+    for rows, mode, bias_rows in ((1, "outer", 1), (3, "outer", 1), (1, "exact", None), (2, "exact", None),
+                                  (5, "inner", 1)):
+        w = case(rows, hidden, dt, mode, bias_rows=bias_rows, seed=rows)
+        U.note(f"softmax regrow few rows {dt} rows={rows} {mode}")
+        U.check_case(w, variant=L.VARIANT_REGROW)
+    for over in ("data", "bias"):
+        w = case(70, hidden, dt, "exact", seed=7)
+        inputs = W.make_inputs(w)
+        ref = U.oracle_rows(w, inputs)
+        dc = U.DeviceCase(w, inputs, residual=False)
+        U.note(f"softmax regrow in place over {over} {dt}")
+        target = dc.x if over == "data" else dc.skip
+        dc.run(L.VARIANT_REGROW, out=target)
+        U.assert_out_close(dc.host(target), ref["y"], dt, tol=U.SOFTMAX_TOL)
+
+
 # ------------------------------------------------------ special values --
 
-SPECIAL_VARIANTS = [L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW, L.VARIANT_ELEMENT]
+SPECIAL_VARIANTS = [L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW, L.VARIANT_ELEMENT,
+                    L.VARIANT_REGROW]
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
@@ -189,7 +235,7 @@ def test_fully_masked_wavefronts_with_broadcast_mask():
         b = np.zeros((4, hidden))
         for j, keep in enumerate((1, 100, 257, 4095)):
             b[j, keep:] = -np.inf
-        for variant in (L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW):
+        for variant in (L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW, L.VARIANT_REGROW):
             U.note(f"softmax masked wavefronts {dt} variant={variant}")
             dc, _ = run_manual(w, x, b, variant)
             assert not np.isnan(dc.host(dc.out)).any()
@@ -249,7 +295,7 @@ def test_forced_variant_through_wrapper_matches_auto():
     x = torch.from_numpy(rng.standard_normal((64, 1024)).astype(np.float32)).cuda()
     b = torch.from_numpy(rng.standard_normal((8, 1024)).astype(np.float32)).cuda()
     outs = [T.bias_softmax(x, b, True, axis=1, variant=v)
-            for v in (L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW)]
+            for v in (L.VARIANT_AUTO, L.VARIANT_GENERIC, L.VARIANT_MULTIWAVE, L.VARIANT_LDSROW, L.VARIANT_REGROW)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.allclose(o, outs[0], rtol=4e-5, atol=1e-20)

@@ -15,8 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskipln.so")
 # (source, extra flags): the row tiles compile once per operation (kOp* = 0..3).
-SOURCES = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_stream.hip",
-                                                    "skipln_api.cpp")] + [
+SOURCES = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_regrow.hip",
+                                                    "skipln_stream.hip", "skipln_api.cpp")] + [
     (os.path.join(CSRC, "skipln_rowtile_op.hip"), [f"-DSKIPLN_ROWTILE_OP={op}"]) for op in range(4)]
 ARCH = "gfx950"
 

@@ -164,12 +164,16 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
     }
     const bool lds_ok = vec_ok && skipln::ldsrow_holds(op, hidden, dtype);
     const bool split_ok = vec_ok && skipln::split_holds(op, hidden, dtype);
+    const bool reg_ok = vec_ok && skipln::regrow_holds(op, hidden, dtype);
     if (variant == SKIPLN_VARIANT_LDSROW) return lds_ok ? base + skipln::kLdsRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     if (variant == SKIPLN_VARIANT_SPLITROW) return split_ok ? base + skipln::kSplitRowIndex : -SKIPLN_ERR_UNSUPPORTED;
+    if (variant == SKIPLN_VARIANT_REGROW) return reg_ok ? base + skipln::kRegRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     // Long rows of the reducing operations: staged in LDS; beyond its
-    // capacity split across workgroups when a workspace is at hand.
+    // capacity held in registers (softmax), or split across workgroups when
+    // a workspace is at hand.
     if (variant == SKIPLN_VARIANT_AUTO && hidden / v > skipln::kRowtileMaxAutoChunks) {
         if (lds_ok) return base + skipln::kLdsRowIndex;
+        if (reg_ok) return base + skipln::kRegRowIndex;
         if (split_ok && with_workspace) return base + skipln::kSplitRowIndex;
     }
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
@@ -278,6 +282,10 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
         return status_of(skipln::launch_split(a, c.op, c.dtype, ws->ptr, s));
     }
     if (index == skipln::kGenericIndex) return status_of(skipln::launch_generic(a, c.op, c.dtype, s));
+    if (index == skipln::kRegRowIndex) {
+        if (tiling) return SKIPLN_ERR_UNSUPPORTED;
+        return status_of(skipln::launch_regrow(a, c.op, c.dtype, s));
+    }
     if (index == skipln::kLdsRowIndex) {
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
         return status_of(skipln::launch_ldsrow(a, c.op, c.dtype, s));
@@ -426,8 +434,9 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 }
 
 int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
-                  int chunks_per_lane, skipln_stream_t stream) {
+                  int chunks_per_lane, int64_t xcd_granule, skipln_stream_t stream) {
     if (!skipln::stream_shape_ok(block, chunks_per_lane)) return SKIPLN_ERR_VARIANT;
+    if (xcd_granule < 1 || xcd_granule > skipln::kMaxStreamGranule) return SKIPLN_ERR_VARIANT;
     if (bytes < 0 || bytes % 16 != 0) return SKIPLN_ERR_SHAPE;
     if (src1 && !src0) return SKIPLN_ERR_NULL;   // inputs fill src0 first
     if (dst1 && !dst0) return SKIPLN_ERR_NULL;   // outputs fill dst0 first
@@ -442,8 +451,8 @@ int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, in
     for (int o = 2; o < 4; ++o)
         for (int i = 0; i < 4; ++i)
             if (i != o && overlap(r[o], r[i])) return SKIPLN_ERR_ALIAS;
-    return status_of(skipln::launch_stream(reads, writes, block, chunks_per_lane, src0, src1, dst0, dst1, bytes / 16,
-                                           reinterpret_cast<hipStream_t>(stream)));
+    return status_of(skipln::launch_stream(reads, writes, block, chunks_per_lane, xcd_granule, src0, src1, dst0, dst1,
+                                           bytes / 16, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int skipln_rowtile_geometries(void) { return skipln::rowtile_count(); }

@@ -49,12 +49,14 @@ constexpr int kNumOps = 4;
 
 // Kernel ids: (op * 2 + dtype) * kIdsPerType + index, index 0 = generic,
 // kRowtileFirst.. = row tiles of 16-byte chunks, kElemFirst.. = row tiles of
-// single elements, kSplitRowIndex = the split-row kernel pair, kLdsRowIndex =
-// the LDS-staged long-row kernel.
+// single elements, kRegRowIndex = the register-resident long-row softmax,
+// kSplitRowIndex = the split-row kernel pair, kLdsRowIndex = the LDS-staged
+// long-row kernel.
 constexpr int kIdsPerType = 128;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
 constexpr int kElemFirst = 64;
+constexpr int kRegRowIndex = 125;
 constexpr int kSplitRowIndex = 126;
 constexpr int kLdsRowIndex = 127;
 
@@ -89,6 +91,10 @@ hipError_t launch_ldsrow(const Args& a, int op, int dtype, hipStream_t stream);
 // Whether the long-row kernel runs this operation and row (16-byte chunks,
 // row of binary32 values within kLdsRowBytes).
 bool ldsrow_holds(int op, int64_t hidden, int dtype);
+// Register-resident long rows (BiasSoftmax): whether the kernel holds the row
+// (16-byte chunks, at most 16 per lane of a 1024-lane block), and the launch.
+bool regrow_holds(int op, int64_t hidden, int dtype);
+hipError_t launch_regrow(const Args& a, int op, int dtype, hipStream_t stream);
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 hipError_t launch_elem(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 // One operation's row tiles (chunks / elements), instantiated per operation
@@ -107,9 +113,11 @@ hipError_t launch_split(const Args& a, int op, int dtype, void* workspace, hipSt
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 // Streaming probe: `reads` (0-2) input streams s0, s1 to `writes` (0-2)
 // output streams d0, d1 of `chunks` 16-byte chunks each, in tiles of `block`
-// lanes x `per_lane` chunks (shapes stream_shape_ok accepts).
+// lanes x `per_lane` chunks (shapes stream_shape_ok accepts), `granule`
+// consecutive tiles per XCD (1 = address order).
 bool stream_shape_ok(int block, int per_lane);
-hipError_t launch_stream(int reads, int writes, int block, int per_lane, const void* s0, const void* s1, void* d0,
-                         void* d1, int64_t chunks, hipStream_t stream);
+constexpr int64_t kMaxStreamGranule = 1 << 16;
+hipError_t launch_stream(int reads, int writes, int block, int per_lane, int64_t granule, const void* s0,
+                         const void* s1, void* d0, void* d1, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln

@@ -469,7 +469,7 @@ hipError_t launch_generic_t(const Args& a, hipStream_t st) {
     return launch_grid(generic_kernel<T, OP>, kGenericBlock, blocks < 1 ? 1 : blocks, a, st);
 }
 
-// Kernel names: "<op>generic_<t>", "<op>ldsrow_<t>", "<op>splitrow_<t>",
+// Kernel names: "<op>generic_<t>", "<op>ldsrow_<t>", "<op>splitrow_<t>", "<op>regrow_<t>",
 // "<op>rowtile_<t>_g<G>_c<CH>" and "<op>rowelem_<t>_g<G>_c<CH>" (element-wise
 // row tiles), with "_b<block>" when the block is not the default max(256,
 // G); <op> is empty
@@ -498,6 +498,8 @@ struct NameTable {
                         snprintf(dst, 48, "%sldsrow_%s", op_prefix[op], tn[t]);
                     } else if (i == kSplitRowIndex) {
                         snprintf(dst, 48, "%ssplitrow_%s", op_prefix[op], tn[t]);
+                    } else if (i == kRegRowIndex) {
+                        snprintf(dst, 48, "%sregrow_%s", op_prefix[op], tn[t]);
                     } else if (gi >= 0 && gi < kNumGeoms) {
                         geom_name(dst, op_prefix[op], "rowtile", tn[t], kGeoms[gi]);
                     } else if (i >= kElemFirst && i < kElemFirst + kNumElemGeoms) {

@@ -452,7 +452,7 @@ constexpr Geom kElemGeoms[] = {
     {64, 8, 256},  {256, 8, 256}, {512, 8, 512},  {1024, 16, 1024},
 };
 constexpr int kNumElemGeoms = sizeof(kElemGeoms) / sizeof(kElemGeoms[0]);
-static_assert(kElemFirst + kNumElemGeoms <= kSplitRowIndex, "kernel index ranges are disjoint");
+static_assert(kElemFirst + kNumElemGeoms <= kRegRowIndex, "kernel index ranges are disjoint");
 
 inline hipError_t cu_count(int* out) {
     int dev = 0;

@@ -1,9 +1,15 @@
 // Streaming probe: 0-2 input streams to 0-2 output streams with the access
 // pattern of the row kernels (16-byte non-temporal vector accesses, one tile
-// of BLOCK lanes x U chunks per workgroup, dispatched in address order).  It
-// measures the HBM rates a kernel of that pattern can reach for each mix of
-// reads and writes -- the attainable ceilings the row kernels are compared
-// with.
+// of BLOCK lanes x U chunks per workgroup).  It measures the HBM rates a
+// kernel of that pattern can reach for each mix of reads and writes -- the
+// attainable ceilings the row kernels are compared with.
+//
+// Tile order.  The dispatcher deals workgroups round-robin over the eight
+// XCDs (workgroup b runs on XCD b mod 8), so in address order consecutive
+// tiles land on different XCDs.  With a granule of g tiles the mapping
+// instead hands each XCD g consecutive tiles per round of 8g: the address
+// granularity at which the XCDs share the streams becomes g tiles -- what a
+// row kernel has when one workgroup owns whole rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,10 +23,23 @@ using device::u32x4;
 template <int NR, int NW, int BLOCK, int kStreamCh>
 __global__ void __launch_bounds__(BLOCK)
     stream_kernel(const u32x4* __restrict__ s0, const u32x4* __restrict__ s1, u32x4* __restrict__ d0,
-                  u32x4* __restrict__ d1, int64_t chunks) {
+                  u32x4* __restrict__ d1, int64_t chunks, int64_t granule) {
     constexpr int kStreamBlock = BLOCK;
     constexpr int kStreamTile = BLOCK * kStreamCh;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kStreamTile + threadIdx.x;
+    const int64_t b = blockIdx.x;
+    int64_t tile = b;
+    if (granule > 1) {
+        // Position q of block b in its round of 8g blocks goes to XCD q mod 8
+        // as that XCD's (q div 8)-th block of the round: tile (q mod 8) g +
+        // q div 8 of the round.  A last, partial round keeps address order.
+        const int64_t per_round = 8 * granule;
+        const int64_t round = b / per_round;
+        if ((round + 1) * per_round <= static_cast<int64_t>(gridDim.x)) {
+            const int64_t q = b - round * per_round;
+            tile = round * per_round + (q % 8) * granule + q / 8;
+        }
+    }
+    const int64_t base = tile * kStreamTile + threadIdx.x;
     u32x4 v[kStreamCh];
 #pragma unroll
     for (int k = 0; k < kStreamCh; ++k) {
@@ -52,12 +71,13 @@ __global__ void __launch_bounds__(BLOCK)
 }
 
 template <int NR, int NW, int BLOCK, int U>
-hipError_t launch_stream_t(const void* s0, const void* s1, void* d0, void* d1, int64_t chunks, hipStream_t st) {
+hipError_t launch_stream_t(const void* s0, const void* s1, void* d0, void* d1, int64_t chunks, int64_t granule,
+                           hipStream_t st) {
     const u32x4* a = static_cast<const u32x4*>(s0);
     const u32x4* b = static_cast<const u32x4*>(s1);
     u32x4* c = static_cast<u32x4*>(d0);
     u32x4* d = static_cast<u32x4*>(d1);
-    void* params[] = {&a, &b, &c, &d, &chunks};
+    void* params[] = {&a, &b, &c, &d, &chunks, &granule};
     const int64_t blocks = (chunks + BLOCK * U - 1) / (BLOCK * U);
     // A dispatch counts its work-items in 32 bits.
     if (blocks > 0x7FFFFFFF || blocks * BLOCK > 0xFFFFFFFFll) return hipErrorInvalidValue;
@@ -67,14 +87,14 @@ hipError_t launch_stream_t(const void* s0, const void* s1, void* d0, void* d1, i
 
 template <int NR, int NW>
 hipError_t launch_stream_mix(int block, int per_lane, const void* s0, const void* s1, void* d0, void* d1,
-                             int64_t chunks, hipStream_t st) {
+                             int64_t chunks, int64_t granule, hipStream_t st) {
     switch (block * 8 + per_lane) {
-        case 64 * 8 + 1: return launch_stream_t<NR, NW, 64, 1>(s0, s1, d0, d1, chunks, st);
-        case 64 * 8 + 4: return launch_stream_t<NR, NW, 64, 4>(s0, s1, d0, d1, chunks, st);
-        case 256 * 8 + 1: return launch_stream_t<NR, NW, 256, 1>(s0, s1, d0, d1, chunks, st);
-        case 256 * 8 + 4: return launch_stream_t<NR, NW, 256, 4>(s0, s1, d0, d1, chunks, st);
-        case 1024 * 8 + 1: return launch_stream_t<NR, NW, 1024, 1>(s0, s1, d0, d1, chunks, st);
-        case 1024 * 8 + 4: return launch_stream_t<NR, NW, 1024, 4>(s0, s1, d0, d1, chunks, st);
+        case 64 * 8 + 1: return launch_stream_t<NR, NW, 64, 1>(s0, s1, d0, d1, chunks, granule, st);
+        case 64 * 8 + 4: return launch_stream_t<NR, NW, 64, 4>(s0, s1, d0, d1, chunks, granule, st);
+        case 256 * 8 + 1: return launch_stream_t<NR, NW, 256, 1>(s0, s1, d0, d1, chunks, granule, st);
+        case 256 * 8 + 4: return launch_stream_t<NR, NW, 256, 4>(s0, s1, d0, d1, chunks, granule, st);
+        case 1024 * 8 + 1: return launch_stream_t<NR, NW, 1024, 1>(s0, s1, d0, d1, chunks, granule, st);
+        case 1024 * 8 + 4: return launch_stream_t<NR, NW, 1024, 4>(s0, s1, d0, d1, chunks, granule, st);
         default: return hipErrorInvalidValue;
     }
 }
@@ -85,17 +105,17 @@ bool stream_shape_ok(int block, int per_lane) {
     return (block == 64 || block == 256 || block == 1024) && (per_lane == 1 || per_lane == 4);
 }
 
-hipError_t launch_stream(int reads, int writes, int block, int per_lane, const void* s0, const void* s1, void* d0,
-                         void* d1, int64_t chunks, hipStream_t st) {
+hipError_t launch_stream(int reads, int writes, int block, int per_lane, int64_t granule, const void* s0,
+                         const void* s1, void* d0, void* d1, int64_t chunks, hipStream_t st) {
     switch (reads * 3 + writes) {
-        case 1: return launch_stream_mix<0, 1>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 2: return launch_stream_mix<0, 2>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 3: return launch_stream_mix<1, 0>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 4: return launch_stream_mix<1, 1>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 5: return launch_stream_mix<1, 2>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 6: return launch_stream_mix<2, 0>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 7: return launch_stream_mix<2, 1>(block, per_lane, s0, s1, d0, d1, chunks, st);
-        case 8: return launch_stream_mix<2, 2>(block, per_lane, s0, s1, d0, d1, chunks, st);
+        case 1: return launch_stream_mix<0, 1>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 2: return launch_stream_mix<0, 2>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 3: return launch_stream_mix<1, 0>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 4: return launch_stream_mix<1, 1>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 5: return launch_stream_mix<1, 2>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 6: return launch_stream_mix<2, 0>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 7: return launch_stream_mix<2, 1>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
+        case 8: return launch_stream_mix<2, 2>(block, per_lane, s0, s1, d0, d1, chunks, granule, st);
         default: return hipErrorInvalidValue;
     }
 }
