@@ -229,6 +229,9 @@ skipln::Args make_args(const Call& c) {
     a.eps = c.eps;
     a.tiles_per_block = 1;
     a.tiling = skipln::kTileStrided;
+    // Bytes the launch writes: the output, and the residual when emitted.
+    const int64_t written = c.rows * c.hidden * (c.dtype == SKIPLN_F32 ? 4 : 2) * (c.residual ? 2 : 1);
+    a.store_through = written >= skipln::kStoreThroughBytes ? 1 : 0;
     return a;
 }
 

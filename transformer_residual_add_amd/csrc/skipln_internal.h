@@ -26,7 +26,13 @@ struct Args {
     // walks them (kTile*).  Set by the launcher.
     int64_t tiles_per_block;
     int32_t tiling;
+    // Row-tile and register-resident kernels: write outputs with the
+    // system-scope store policy (set for launches writing at least
+    // kStoreThroughBytes, where it was measured faster).
+    int32_t store_through;
 };
+
+constexpr int64_t kStoreThroughBytes = int64_t(512) << 20;
 
 // Tiling modes of the row-tile kernel (values of Args::tiling and of the
 // C ABI's tiling argument).

@@ -42,14 +42,12 @@ constexpr int kLdsSlabs = 9;       // bias slabs a block parks in LDS (144 KiB)
 // scalar offset.  No branch surrounds the memory accesses, so the compiler
 // can wait for each load on its own (loads complete in issue order) rather
 // than for all of them.
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kNonTemporal = 2;         // cache policy bit of the access
+constexpr int kNonTemporal = 2;         // cache policy of the data loads
 constexpr int kSlabBytes = kRegRowBlock * 16;
 constexpr int kPastRow = 0x40000000;    // lane offset beyond every row
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row_base, int row_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row_base), static_cast<short>(0), row_bytes,
-                                             kRsrcWord3);
+    return buffer_rsrc(row_base, row_bytes);
 }
 
 // CH: slabs of the row (chunks per lane); the launch picks the smallest
@@ -83,6 +81,7 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
     u32x4* O = static_cast<u32x4*>(a.out);
     const int row_bytes = hv * 16;
     const int lane_off = tid * 16;
+    const bool through = a.store_through != 0;
 
     // Slabs holding a chunk of this lane: chunk k exists for k < nk.
     const int nk_lane = (hv - tid + kRegRowBlock - 1) / kRegRowBlock;
@@ -210,7 +209,7 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
             E::widen(bk, bf);
 #pragma unroll
             for (int e = 0; e < V; ++e) y[e] = __builtin_amdgcn_exp2f(((df[e] + bf[e]) - M) * kLog2e) * scale;
-            __builtin_amdgcn_raw_buffer_store_b128(E::narrow(y), orow, lo(k), k * kSlabBytes, kNonTemporal);
+            E::store(E::narrow(y), orow, lo(k), k * kSlabBytes, through);
             if (reload) d[k] = __builtin_amdgcn_raw_buffer_load_b128(nrow, lo(k), k * kSlabBytes, kNonTemporal);
             __builtin_amdgcn_sched_barrier(0);
         };

@@ -62,6 +62,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     const bool has_beta = a.beta != nullptr;
     const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
     const bool small_rows = a.rows <= 0xFFFFFFFFll;
+    const bool through = a.store_through != 0;
 
     bool ok[CH];
 #pragma unroll
@@ -166,6 +167,17 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     for (; tile < t_end; tile += stride) {
         const int64_t row = tile * RPB + slot;
         const bool live = row < a.rows;
+        // Outputs go through buffer resources over this tile's rows (base
+        // and size uniform, in scalar registers): a lane's element offset in
+        // the tile in one register, chunk k's offset k * G as a scalar.
+        const int64_t row0 = tile * RPB;
+        const int tile_bytes =
+            static_cast<int>((a.rows - row0 < RPB ? a.rows - row0 : RPB) * hv * static_cast<int>(sizeof(Raw)));
+        const int voff = (slot * hv + lt) * static_cast<int>(sizeof(Raw));
+        auto put = [&](Raw* base, int k, const Raw& v) {
+            E::store(v, buffer_rsrc(base + row0 * hv, tile_bytes), voff, k * G * static_cast<int>(sizeof(Raw)),
+                     through);
+        };
         if constexpr (V == 8 && kParams) {
             // Keep gamma/beta/bias packed (2 fp16 per VGPR): without this the
             // compiler hoists their widening out of the loop and triples
@@ -266,14 +278,13 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                 parity ^= 1;
             }
             if (live) {
-                Raw* op = O + row * hv + lt;
 #pragma unroll
                 for (int k = 0; k < CH; ++k) {
                     if (ok[k]) {
                         float y[V];
 #pragma unroll
                         for (int e = 0; e < V; ++e) y[e] = s[k][e] * scale;
-                        __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                        put(O, k, E::narrow(y));
                     }
                 }
             }
@@ -283,19 +294,17 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         if constexpr (OP == kOpBiasAdd) {
             // BiasAdd ends here: the sum is the output.
             if (live) {
-                Raw* op = O + row * hv + lt;
 #pragma unroll
                 for (int k = 0; k < CH; ++k)
-                    if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), op + k * G);
+                    if (ok[k]) put(O, k, E::narrow(s[k]));
             }
             continue;
         }
 
         if (R != nullptr && live) {
-            Raw* rp = R + row * hv + lt;
 #pragma unroll
             for (int k = 0; k < CH; ++k)
-                if (ok[k]) __builtin_nontemporal_store(E::narrow(s[k]), rp + k * G);
+                if (ok[k]) put(R, k, E::narrow(s[k]));
         }
 
         // Statistics are taken relative to a value of the row itself (lane
@@ -404,7 +413,6 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         const float rstd = rsqrtf(var + a.eps);
 
         if (live) {
-            Raw* op = O + row * hv + lt;
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 if (ok[k]) {
@@ -413,7 +421,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
                     E::widen(bet[k], bf);
 #pragma unroll
                     for (int e = 0; e < V; ++e) y[e] = (s[k][e] - off) * rstd * gf[e] + bf[e];
-                    __builtin_nontemporal_store(E::narrow(y), op + k * G);
+                    put(O, k, E::narrow(y));
                 }
             }
         }
