@@ -255,7 +255,8 @@ def time_copy(nbytes: int, steps: int, warmup: int):
 
 
 # Tile shapes of the streaming probe: (lanes, chunks per lane, XCD granule in
-# tiles).  Granule 1 is address order: consecutive tiles on different XCDs.
+# tiles), each timed with both store policies of the row kernels (when the mix
+# writes).  Granule 1 is address order: consecutive tiles on different XCDs.
 # The 64 x 1 tile at granules 2, 3, 4 and 16 hands each XCD 2, 3, 4 and 16
 # KiB of every stream at a time -- the granularity of a row kernel whose
 # workgroup owns rows of that size.
@@ -286,10 +287,11 @@ def time_streams(nbytes: int, steps: int, warmup: int):
 
             moved = (reads + writes) * nbytes
             shapes = []
-            for block, per_lane, granule in STREAM_SHAPES:
+            for (block, per_lane, granule), through in [(sh, t) for sh in STREAM_SHAPES for t in (0, 1)
+                                                        if writes or not t]:
                 def launch():
-                    L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, granule, s),
-                            "skipln_stream")
+                    L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, granule,
+                                              through, s), "skipln_stream")
 
                 for _ in range(warmup):
                     launch()
@@ -302,7 +304,7 @@ def time_streams(nbytes: int, steps: int, warmup: int):
                 torch.cuda.synchronize()
                 dt = ev0.elapsed_time(ev1) * 1e-3 / steps
                 shapes.append({"block": block, "chunks_per_lane": per_lane, "xcd_granule": granule,
-                               "xcd_granule_bytes": block * per_lane * 16 * granule,
+                               "store_through": through, "xcd_granule_bytes": block * per_lane * 16 * granule,
                                "launch_us": round(dt * 1e6, 2), "gb_per_s": round(moved / dt / 1e9, 1)})
             best = max(shapes, key=lambda r: r["gb_per_s"])
             # Best rate among shapes whose XCDs share the streams at this
@@ -312,12 +314,14 @@ def time_streams(nbytes: int, steps: int, warmup: int):
                           for g in STREAM_GRANULES}
             out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "best_gb_per_s": best["gb_per_s"],
                         "best_frac_of_peak": round(best["gb_per_s"] / HBM_PEAK_GBS, 4),
-                        "best_shape": [best["block"], best["chunks_per_lane"], best["xcd_granule"]],
+                        "best_shape": [best["block"], best["chunks_per_lane"], best["xcd_granule"],
+                                       best["store_through"]],
                         "best_at_xcd_granule_bytes": at_granule, "shapes": shapes})
             log(f"stream {reads}R{writes}W: best {best['gb_per_s']:.0f} GB/s (block {best['block']}, "
-                f"{best['chunks_per_lane']} chunk(s)/lane, granule {best['xcd_granule']}); " +
-                ", ".join(f"{r['block']}x{r['chunks_per_lane']}g{r['xcd_granule']}: {r['gb_per_s']:.0f}"
-                          for r in shapes) +
+                f"{best['chunks_per_lane']} chunk(s)/lane, granule {best['xcd_granule']}, "
+                f"through {best['store_through']}); " +
+                ", ".join(f"{r['block']}x{r['chunks_per_lane']}g{r['xcd_granule']}t{r['store_through']}: "
+                          f"{r['gb_per_s']:.0f}" for r in shapes) +
                 "; by XCD granule: " + ", ".join(f"{g}B {v:.0f}" for g, v in at_granule.items()))
     return out
 

@@ -329,6 +329,9 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
  * xcd_granule consecutive tiles per round of 8 x xcd_granule (the dispatcher
  * deals workgroup b to XCD b mod 8): the address granularity at which the
  * eight XCDs share the streams, which for a row kernel is one row.
+ * store_through: 0 = non-temporal stores; 1 = non-temporal stores with
+ * system-scope coherence (the policy the row kernels use for launches that
+ * write 512 MiB or more).
  * Outputs: dst0 = src0 XOR src1 (a chunk's index when nothing is read),
  * dst1 = dst0 + 1 per 32-bit word, whatever the tile order.  Device memory,
  * 16-byte aligned, bytes % 16 == 0, outputs overlapping nothing.  Returns
@@ -336,7 +339,7 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
  * SKIPLN_ERR_SHAPE, SKIPLN_ERR_ALIAS, SKIPLN_ERR_VARIANT (tile shape or
  * granule) or SKIPLN_ERR_LAUNCH. */
 int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
-                  int chunks_per_lane, int64_t xcd_granule, skipln_stream_t stream);
+                  int chunks_per_lane, int64_t xcd_granule, int store_through, skipln_stream_t stream);
 
 /* Number of row-tile geometries (for SKIPLN_VARIANT_GEOMETRY + g). */
 int skipln_rowtile_geometries(void);

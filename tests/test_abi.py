@@ -401,7 +401,7 @@ def test_forward_ws_workspace_checks():
 def test_stream_probe_argument_checks():
     """skipln_stream returns these statuses before any HIP call."""
     st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load().skipln_stream(s0, s1, d0, d1, n, b,
-                                                                                                 u, g, None)
+                                                                                                 u, g, 0, None)
     assert st(s0=None, d0=None) == L.ERR_NULL
     assert st(s0=None, s1=SK) == L.ERR_NULL
     assert st(d0=None, d1=RES) == L.ERR_NULL

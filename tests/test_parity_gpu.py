@@ -304,7 +304,7 @@ def test_stream_probe_outputs():
     """The streaming probe's outputs: a copy, the XOR of two inputs, the copy
     plus one, and the chunk index when nothing is read -- in address order and
     with tiles dealt to the XCDs in granules (a permutation of the tiles, with
-    a ragged last tile and a partial last round)."""
+    a ragged last tile and a partial last round), with either store policy."""
     import torch
 
     lib = L.load()
@@ -312,27 +312,27 @@ def test_stream_probe_outputs():
     a = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     b = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     c, d = torch.zeros_like(a), torch.zeros_like(a)
-    for blk, u, g in ((64, 1, 1), (256, 4, 1), (1024, 1, 1), (1024, 4, 1), (64, 1, 2), (64, 1, 3), (64, 4, 16),
-                      (256, 1, 5)):
+    for blk, u, g, t in ((64, 1, 1, 0), (256, 4, 1, 1), (1024, 1, 1, 0), (1024, 4, 1, 1), (64, 1, 2, 0), (64, 1, 3, 1),
+                         (64, 4, 16, 0), (256, 1, 5, 1)):
         c.zero_(), d.zero_()
-        L.check(lib.skipln_stream(a.data_ptr(), None, c.data_ptr(), d.data_ptr(), n, blk, u, g, None),
+        L.check(lib.skipln_stream(a.data_ptr(), None, c.data_ptr(), d.data_ptr(), n, blk, u, g, t, None),
                 "skipln_stream")
         torch.cuda.synchronize()
-        assert torch.equal(c, a) and torch.equal(d, a + 1), (blk, u, g)
-    for g in (1, 4):
+        assert torch.equal(c, a) and torch.equal(d, a + 1), (blk, u, g, t)
+    for g, t in ((1, 0), (4, 1)):
         c.zero_()
-        L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, n, 256, 1, g, None),
+        L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, n, 256, 1, g, t, None),
                 "skipln_stream")
         torch.cuda.synchronize()
         assert torch.equal(c, a ^ b)
     idx = torch.arange(n // 16, dtype=torch.int32, device="cuda")
-    for g in (1, 7):
+    for g, t in ((1, 1), (7, 0)):
         c.fill_(-1)
-        L.check(lib.skipln_stream(None, None, c.data_ptr(), None, n, 64, 4, g, None), "skipln_stream")
+        L.check(lib.skipln_stream(None, None, c.data_ptr(), None, n, 64, 4, g, t, None), "skipln_stream")
         torch.cuda.synchronize()
         assert torch.equal(c.view(-1, 4)[:, 0], idx) and not c.view(-1, 4)[:, 1:].any()
     before = c.clone()
-    L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), None, None, n, 1024, 4, 2, None), "skipln_stream")
+    L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), None, None, n, 1024, 4, 2, 0, None), "skipln_stream")
     torch.cuda.synchronize()
     assert torch.equal(c, before)
 

@@ -43,7 +43,7 @@ SIGNATURES = {
     "skipln_validate": (_i32, [_i32, _vp, _vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _i32]),
     "skipln_select": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "skipln_copy": (_i32, [_vp, _vp, _i64, _vp]),
-    "skipln_stream": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _vp]),
+    "skipln_stream": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _i32, _vp]),
     "skipln_rowtile_geometries": (_i32, []),
     "skipln_element_geometries": (_i32, []),
     "skipln_kernel_name": (C.c_char_p, [_i32]),

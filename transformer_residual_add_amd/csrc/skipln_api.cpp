@@ -437,7 +437,7 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
 }
 
 int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, int64_t bytes, int block,
-                  int chunks_per_lane, int64_t xcd_granule, skipln_stream_t stream) {
+                  int chunks_per_lane, int64_t xcd_granule, int store_through, skipln_stream_t stream) {
     if (!skipln::stream_shape_ok(block, chunks_per_lane)) return SKIPLN_ERR_VARIANT;
     if (xcd_granule < 1 || xcd_granule > skipln::kMaxStreamGranule) return SKIPLN_ERR_VARIANT;
     if (bytes < 0 || bytes % 16 != 0) return SKIPLN_ERR_SHAPE;
@@ -454,8 +454,8 @@ int skipln_stream(const void* src0, const void* src1, void* dst0, void* dst1, in
     for (int o = 2; o < 4; ++o)
         for (int i = 0; i < 4; ++i)
             if (i != o && overlap(r[o], r[i])) return SKIPLN_ERR_ALIAS;
-    return status_of(skipln::launch_stream(reads, writes, block, chunks_per_lane, xcd_granule, src0, src1, dst0, dst1,
-                                           bytes / 16, reinterpret_cast<hipStream_t>(stream)));
+    return status_of(skipln::launch_stream(reads, writes, block, chunks_per_lane, xcd_granule, store_through != 0, src0,
+                                           src1, dst0, dst1, bytes / 16, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int skipln_rowtile_geometries(void) { return skipln::rowtile_count(); }

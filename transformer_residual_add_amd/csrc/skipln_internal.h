@@ -120,10 +120,11 @@ hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t s
 // Streaming probe: `reads` (0-2) input streams s0, s1 to `writes` (0-2)
 // output streams d0, d1 of `chunks` 16-byte chunks each, in tiles of `block`
 // lanes x `per_lane` chunks (shapes stream_shape_ok accepts), `granule`
-// consecutive tiles per XCD (1 = address order).
+// consecutive tiles per XCD (1 = address order), stores with the
+// system-scope policy when `through` is set.
 bool stream_shape_ok(int block, int per_lane);
 constexpr int64_t kMaxStreamGranule = 1 << 16;
-hipError_t launch_stream(int reads, int writes, int block, int per_lane, int64_t granule, const void* s0,
-                         const void* s1, void* d0, void* d1, int64_t chunks, hipStream_t stream);
+hipError_t launch_stream(int reads, int writes, int block, int per_lane, int64_t granule, int through,
+                         const void* s0, const void* s1, void* d0, void* d1, int64_t chunks, hipStream_t stream);
 
 }  // namespace skipln
