@@ -90,7 +90,11 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
     // asm), so the compiler forms each offset where it is used instead of
     // keeping sixteen of them live across the row loop.
     int lofs = lane_off, nk = nk_lane;
-    auto lo = [&](int k) { return k < nk ? lofs : kPastRow; };
+    // The launch runs the smallest compiled slab count CH >= the row's
+    // slabs, and consecutive counts differ by at most 2 from 4 up, so slabs
+    // below CH - 2 are whole for every lane: no mask there.
+    constexpr int kWhole = CH >= 4 ? CH - 2 : 0;
+    auto lo = [&](int k) { return k < kWhole || k < nk ? lofs : kPastRow; };
     auto refresh = [&]() {
         lofs = lane_off;
         nk = nk_lane;
@@ -152,7 +156,7 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
             float cm = kNegInf;
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                z[e] = k < nk ? df[e] + bf[e] : kNegInf;
+                z[e] = k < kWhole || k < nk ? df[e] + bf[e] : kNegInf;
                 cm = __builtin_fmaxf(cm, z[e]);
             }
             const float mn = __builtin_fmaxf(m, cm);
@@ -263,7 +267,8 @@ hipError_t launch_regrow_sb(const Args& a, int n, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
-// Slab counts compiled: a row of n slabs runs the first count >= n.
+// Slab counts compiled: a row of n slabs runs the first count >= n (for
+// counts of 4 and more, n >= count - 1: the kernel relies on it).
 template <typename T>
 hipError_t launch_regrow_t(const Args& a, hipStream_t st) {
     const int hv = a.hidden / Elem<T>::kPerChunk;
