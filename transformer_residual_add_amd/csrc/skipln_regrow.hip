@@ -6,8 +6,8 @@
 // the row's raw data chunks t, t + 1024, ..., t + 15 * 1024 in VGPRs (64
 // VGPRs: rows of up to 131072 float16 or 65536 float32 values), so the data
 // crosses HBM once, and forms z = fl32(data + bias) afresh in each of the two
-// passes, re-reading the bias row through the caches (one row shared by every
-// data row in the vocabulary case, or a few rows):
+// passes, re-reading the bias row -- from LDS when one bias row serves every
+// data row (a vocabulary's logit bias), else through the caches:
 //   pass 1: per lane, a running maximum m and the sum s of 2^((z - m) log2 e),
 //           rescaled whenever m grows (the single-pass softmax statistics of
 //           Milakov and Gimelshein, "Online normalizer calculation for
