@@ -100,6 +100,43 @@ def test_workload_full_size_sampled(name):
             f"row variances off in rows {r0}:{r1}"
 
 
+STORE_THROUGH_BYTES = 512 << 20  # launches writing this much store with the system-scope policy
+
+
+@pytest.mark.parametrize("dt,hidden,residual,op", [("f16", 1000, True, "layer_norm"), ("f32", 999, True, "layer_norm"),
+                                                    ("f16", 1024, False, "simplified"),
+                                                    ("f32", 1000, False, "bias_add")],
+                         ids=["elem_f16_ln", "elem_f32_ln", "chunk_f16_rms", "elem_f32_biasadd"])
+@pytest.mark.parametrize("side", ["below", "above"])
+def test_store_policies_at_the_threshold(dt, hidden, residual, op, side):
+    """Launches just below and just above the output size where the row
+    tiles switch to system-scope stores, for chunk and element-wise tiles:
+    sampled row blocks against the oracle, every row of the last block."""
+    import torch
+
+    itemsize = 4 if dt == "f32" else 2
+    per_row = hidden * itemsize * (2 if residual else 1)
+    rows = STORE_THROUGH_BYTES // per_row + (1 if side == "above" else -1)
+    assert (rows * per_row >= STORE_THROUGH_BYTES) == (side == "above")
+    w = W.small_case(rows, hidden, dt, beta=op != "bias_add", bias=True, residual=residual, eps=1e-5,
+                     seed=hidden + rows % 97, op=op)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=w.residual)
+    code = L.F32 if dt == "f32" else L.F16
+    U.note(f"store policy {side}: {op} {dt} rows={rows} H={hidden} "
+           f"{T.select_kernel(hidden, code, op=U.OPS[op])}")
+    dc.run()
+    torch.cuda.synchronize()
+    out = dc.out.view(w.rows, w.hidden)
+    res = dc.res.view(w.rows, w.hidden) if dc.res is not None else None
+    n_blocks = -(-w.rows // W.BLOCK_ROWS)
+    for b in sorted({0, n_blocks // 3, n_blocks - 1}):
+        r0, r1 = b * W.BLOCK_ROWS, min(w.rows, (b + 1) * W.BLOCK_ROWS)
+        part = {k: (None if v is None else v[r0:r1] if k in ("input", "skip") else v) for k, v in inputs.items()}
+        ref = U.oracle_rows(w, part, row_offset=r0)
+        U.compare(w, out[r0:r1].cpu().numpy(), None if res is None else res[r0:r1].cpu().numpy(), ref)
+
+
 # ------------------------------------------------------ flags and shapes --
 
 FLAG_SETS = [(bool(m & 1), bool(m & 2), bool(m & 4), bool(m & 8)) for m in range(16)]
