@@ -191,7 +191,10 @@ def test_select_kernels():
     sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT, op=L.OP_LAYER_NORM: lib.skipln_select(op, h, dt, mode, al, v)
     name = lambda kid: L.kernel_name(kid)
     assert name(sel(768, 0)) == "rowtile_f32_g192_c1_b192"
-    assert name(sel(1024, 1)) == "rowtile_f16_g128_c1"
+    assert name(sel(1024, 1)) == "rowtile_f16_g64_c2"                 # one wavefront per row
+    assert name(sel(1024, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g128_c1"
+    assert name(sel(768, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g192_c1_b192"
+    assert name(sel(768, 0, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 0)) == "rowtile_f32_g256_c4"
     assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4"
     assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
