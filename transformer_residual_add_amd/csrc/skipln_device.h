@@ -84,11 +84,13 @@ struct Elem<_Float16> {
     __device__ __forceinline__ static float hi(unsigned w) {
         return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(w >> 16)));
     }
-    // Round to nearest even (the default rounding mode of the conversion).
+    // Round to nearest even: a two-element vector conversion, one packed
+    // conversion instruction (v_cvt_pk_f16_f32, the default rounding mode)
+    // instead of two conversions, a shift and an or.
     __device__ __forceinline__ static unsigned pack(float a, float b) {
-        unsigned short ha = __builtin_bit_cast(unsigned short, static_cast<_Float16>(a));
-        unsigned short hb = __builtin_bit_cast(unsigned short, static_cast<_Float16>(b));
-        return static_cast<unsigned>(ha) | (static_cast<unsigned>(hb) << 16);
+        typedef float F2 __attribute__((ext_vector_type(2)));
+        typedef _Float16 H2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(unsigned, __builtin_convertvector(F2{a, b}, H2));
     }
     __device__ __forceinline__ static void widen(const u32x4& r, float* f) {
         f[0] = lo(r.x); f[1] = hi(r.x);
