@@ -50,6 +50,20 @@ struct Elem<float> {
         f[2] = __uint_as_float(r.z);
         f[3] = __uint_as_float(r.w);
     }
+    // f = a + b and y = t g + b element by element (one rounding each); the
+    // binary16 forms below round the same way.
+    __device__ __forceinline__ static void widen_add(const u32x4& a, const u32x4& b, float* f) {
+        f[0] = __uint_as_float(a.x) + __uint_as_float(b.x);
+        f[1] = __uint_as_float(a.y) + __uint_as_float(b.y);
+        f[2] = __uint_as_float(a.z) + __uint_as_float(b.z);
+        f[3] = __uint_as_float(a.w) + __uint_as_float(b.w);
+    }
+    __device__ __forceinline__ static void widen_fma(const float* t, const u32x4& g, const u32x4& b, float* y) {
+        y[0] = __builtin_fmaf(t[0], __uint_as_float(g.x), __uint_as_float(b.x));
+        y[1] = __builtin_fmaf(t[1], __uint_as_float(g.y), __uint_as_float(b.y));
+        y[2] = __builtin_fmaf(t[2], __uint_as_float(g.z), __uint_as_float(b.z));
+        y[3] = __builtin_fmaf(t[3], __uint_as_float(g.w), __uint_as_float(b.w));
+    }
     __device__ __forceinline__ static u32x4 narrow(const float* f) {
         u32x4 r;
         r.x = __float_as_uint(f[0]);
@@ -98,6 +112,45 @@ struct Elem<_Float16> {
         f[4] = lo(r.z); f[5] = hi(r.z);
         f[6] = lo(r.w); f[7] = hi(r.w);
     }
+    // f = a + b element by element in binary32: one mixed-precision fma
+    // a * 1 + b per element (v_fma_mix_f32 reads either half of a register
+    // as a binary16 operand and widens it exactly), so each sum is rounded
+    // once, as when both halves are widened and then added, in one
+    // instruction instead of three.  The compiler folds a widening fma by 1
+    // into a plain add and does not form this instruction by itself.
+    __device__ __forceinline__ static float add_lo(unsigned a, unsigned b) {
+        float r;
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    }
+    __device__ __forceinline__ static float add_hi(unsigned a, unsigned b) {
+        float r;
+        asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+        return r;
+    }
+    __device__ __forceinline__ static void widen_add(const u32x4& a, const u32x4& b, float* f) {
+        f[0] = add_lo(a.x, b.x); f[1] = add_hi(a.x, b.x);
+        f[2] = add_lo(a.y, b.y); f[3] = add_hi(a.y, b.y);
+        f[4] = add_lo(a.z, b.z); f[5] = add_hi(a.z, b.z);
+        f[6] = add_lo(a.w, b.w); f[7] = add_hi(a.w, b.w);
+    }
+    // y = t g + b: the binary32 t times g's half plus b's half.
+    __device__ __forceinline__ static float fma_lo(float t, unsigned g, unsigned b) {
+        float r;
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,1]" : "=v"(r) : "v"(t), "v"(g), "v"(b));
+        return r;
+    }
+    __device__ __forceinline__ static float fma_hi(float t, unsigned g, unsigned b) {
+        float r;
+        asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,1] op_sel_hi:[0,1,1]" : "=v"(r) : "v"(t), "v"(g), "v"(b));
+        return r;
+    }
+    __device__ __forceinline__ static void widen_fma(const float* t, const u32x4& g, const u32x4& b, float* y) {
+        y[0] = fma_lo(t[0], g.x, b.x); y[1] = fma_hi(t[1], g.x, b.x);
+        y[2] = fma_lo(t[2], g.y, b.y); y[3] = fma_hi(t[3], g.y, b.y);
+        y[4] = fma_lo(t[4], g.z, b.z); y[5] = fma_hi(t[5], g.z, b.z);
+        y[6] = fma_lo(t[6], g.w, b.w); y[7] = fma_hi(t[7], g.w, b.w);
+    }
     __device__ __forceinline__ static u32x4 narrow(const float* f) {
         u32x4 r;
         r.x = pack(f[0], f[1]);
@@ -134,6 +187,12 @@ struct Single<float> {
     __device__ __forceinline__ static Raw zero() { return 0u; }
     __device__ __forceinline__ static void widen(const Raw& r, float* f) { f[0] = __uint_as_float(r); }
     __device__ __forceinline__ static Raw narrow(const float* f) { return __float_as_uint(f[0]); }
+    __device__ __forceinline__ static void widen_fma(const float* t, const Raw& g, const Raw& b, float* y) {
+        float u, v;
+        widen(g, &u);
+        widen(b, &v);
+        y[0] = __builtin_fmaf(t[0], u, v);
+    }
     __device__ __forceinline__ static void store(const Raw& v, __amdgpu_buffer_rsrc_t r, int voff, int soff,
                                                  bool through) {
         if (through)
@@ -150,6 +209,12 @@ struct Single<_Float16> {
     __device__ __forceinline__ static Raw zero() { return 0; }
     __device__ __forceinline__ static void widen(const Raw& r, float* f) {
         f[0] = static_cast<float>(__builtin_bit_cast(_Float16, r));
+    }
+    __device__ __forceinline__ static void widen_fma(const float* t, const Raw& g, const Raw& b, float* y) {
+        float u, v;
+        widen(g, &u);
+        widen(b, &v);
+        y[0] = __builtin_fmaf(t[0], u, v);
     }
     // Round to nearest even.
     __device__ __forceinline__ static Raw narrow(const float* f) {

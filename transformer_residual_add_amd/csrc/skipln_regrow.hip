@@ -150,13 +150,12 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
             const u32x4 bk = bias_of(k);
-            float df[V], bf[V], z[V];
-            E::widen(d[k], df);
-            E::widen(bk, bf);
+            float z[V];
+            E::widen_add(d[k], bk, z);
             float cm = kNegInf;
 #pragma unroll
             for (int e = 0; e < V; ++e) {
-                z[e] = k < kWhole || k < nk ? df[e] + bf[e] : kNegInf;
+                z[e] = k < kWhole || k < nk ? z[e] : kNegInf;
                 cm = __builtin_fmaxf(cm, z[e]);
             }
             const float mn = __builtin_fmaxf(m, cm);
@@ -191,6 +190,11 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
         // M = -inf (no finite value) gives (z - M) = NaN below, as the
         // definition has it; a NaN S makes the row NaN.
         const float scale = 1.0f / S;
+        // binary16 outputs take 1/S into the exponent, 2^(t - log2 S): one fma
+        // instead of two products per element.  The added error (about
+        // |log2 S| 2^-24 relative, S <= the row's length) is far below the
+        // output's own rounding; binary32 outputs keep the product.
+        const float lsc = -log2f(S);
 
         // Pass 2: outputs, and the next row's data into the freed registers
         // (an empty range when there is no next row: no memory access).  The
@@ -205,14 +209,18 @@ __global__ void __launch_bounds__(kRegRowBlock) regrow_softmax_kernel(const Args
         ring_start();
         auto emit = [&](int k, bool reload) {
             const u32x4 bk = bias_of(k);
-            float df[V], bf[V], y[V];
+            float y[V];
             // Widen the raw chunk again rather than keep pass 1's binary32
             // copy of the whole row alive (it would not fit in registers).
             asm volatile("" : "+v"(d[k]));
-            E::widen(d[k], df);
-            E::widen(bk, bf);
+            E::widen_add(d[k], bk, y);
 #pragma unroll
-            for (int e = 0; e < V; ++e) y[e] = __builtin_amdgcn_exp2f(((df[e] + bf[e]) - M) * kLog2e) * scale;
+            for (int e = 0; e < V; ++e) {
+                if constexpr (sizeof(T) == 2)
+                    y[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[e] - M, kLog2e, lsc));
+                else
+                    y[e] = __builtin_amdgcn_exp2f((y[e] - M) * kLog2e) * scale;
+            }
             E::store(E::narrow(y), orow, lo(k), k * kSlabBytes, through);
             if (reload) d[k] = __builtin_amdgcn_raw_buffer_load_b128(nrow, lo(k), k * kSlabBytes, kNonTemporal);
             __builtin_amdgcn_sched_barrier(0);

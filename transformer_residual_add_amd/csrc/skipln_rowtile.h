@@ -416,11 +416,10 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
                 if (ok[k]) {
-                    float gf[V], bf[V], y[V];
-                    E::widen(gam[k], gf);
-                    E::widen(bet[k], bf);
+                    float t[V], y[V];
 #pragma unroll
-                    for (int e = 0; e < V; ++e) y[e] = (s[k][e] - off) * rstd * gf[e] + bf[e];
+                    for (int e = 0; e < V; ++e) t[e] = (s[k][e] - off) * rstd;
+                    E::widen_fma(t, gam[k], bet[k], y);
                     put(O, k, E::narrow(y));
                 }
             }
