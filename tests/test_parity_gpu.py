@@ -762,3 +762,54 @@ def test_python_wrapper_rejects_bad_inputs():
         T.skip_layer_norm(x, x, g, epsilon=-1.0)
     with pytest.raises(TypeError):
         T.skip_layer_norm(x.double(), x.double(), g.double())
+
+
+def _subnormal_rows(w, seed):
+    """float16 inputs whose rows 0..5 hold subnormal values (multiples of
+    2^-24 below 2^-14, exact in binary16): rows 0-1 all of x, skip and bias
+    subnormal; rows 2-3 subnormal x with normal skip; rows 4-5 subnormal x
+    and bias with a zero skip."""
+    rng = np.random.default_rng(seed)
+    inputs = W.make_inputs(w)
+    h = w.hidden
+
+    def sub(n):
+        m = rng.integers(-1023, 1024, size=n)
+        m[m == 0] = 1
+        return (m.astype(np.float64) * 2.0 ** -24).astype(np.float16)
+
+    x, s = inputs["input"], inputs["skip"]
+    for r in range(6):
+        x[r] = sub(h)
+    s[0], s[1] = sub(h), sub(h)
+    s[4] = 0
+    s[5] = 0
+    if inputs.get("bias") is not None:
+        inputs["bias"][:] = sub(h)
+    assert np.all(np.abs(x[:6].astype(np.float64)) < 2.0 ** -14)
+    return inputs
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add"])
+@pytest.mark.parametrize("variant_hidden", [(L.VARIANT_AUTO, 1000), (L.VARIANT_GENERIC, 1000),
+                                            (L.VARIANT_MULTIWAVE, 1000), (L.VARIANT_ROWTILE, 1000),
+                                            (L.VARIANT_ELEMENT, 1000), (L.VARIANT_ROWTILE, 8192),
+                                            (L.VARIANT_LDSROW, 20000), (L.VARIANT_SPLITROW, 20000)],
+                         ids=lambda t: f"v{t[0]}_h{t[1]}")
+def test_float16_subnormals(op, variant_hidden):
+    """binary16 subnormal data, skip and bias are widened exactly: the
+    residual (and BiasAdd's output) is bit-exact, and with eps = 0 rows made
+    only of subnormals normalize to O(1) values (a kernel that flushed them
+    would see a zero row, zero variance and NaN)."""
+    variant, hidden = variant_hidden
+    if op == "bias_add" and variant in (L.VARIANT_LDSROW, L.VARIANT_SPLITROW):
+        pytest.skip("BiasAdd has no row statistics, so no LDS-staged or split-row kernel")
+    w = W.small_case(24, hidden, "f16", beta=True, bias=True, residual=op != "bias_add", eps=0.0,
+                     seed=hidden + 3, op=op)
+    inputs = _subnormal_rows(w, seed=hidden)
+    U.note(f"float16 subnormals {op} variant {variant} H={hidden}")
+    dc, ref = U.check_case(w, variant=variant, inputs=inputs, workspace=variant == L.VARIANT_SPLITROW or None)
+    out = dc.host(dc.out).astype(np.float64)
+    assert np.isfinite(out).all()
+    if op != "bias_add":
+        assert np.abs(out[:6]).max() > 0.5
