@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 #include <utility>
 
 #include "skipln_device.h"
@@ -33,7 +34,11 @@ __device__ __forceinline__ float wave_elems(int hv, int w) {
     return static_cast<float>(n * V);
 }
 
-template <typename E, int OP, int G, int CH, int BLOCK>
+// SS (stream skip): the first tile's exact skip is read with non-temporal
+// loads (the launcher's choice for one wave of resident blocks with one tile
+// each); otherwise, and for every later tile, the skip goes through the
+// caches.
+template <typename E, int OP, int G, int CH, int BLOCK, bool SS>
 __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd || OP == kOpBiasSoftmax,
                   "operation");
@@ -108,7 +113,9 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     //                    tiles p + n*P.  Its skip rows are loaded once.
     const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
     int64_t t_first, stride, t_end;
-    const bool stationary = a.tiling == kTileSkipStationary;
+    // (Never launched stationary with SS: left out, so that its first loads
+    // cannot be merged with the streaming ones.)
+    const bool stationary = !SS && a.tiling == kTileSkipStationary;
     if (a.tiling == kTileContiguous) {
         t_first = blockIdx.x * a.tiles_per_block;
         stride = 1;
@@ -133,7 +140,8 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         xr[k] = E::zero();
         sr[k] = E::zero();
     }
-    auto issue_loads = [&](int64_t tile, bool with_skip) {
+    // `stream`: std::true_type for a block's first tile in an SS kernel.
+    auto issue_loads = [&](int64_t tile, bool with_skip, auto stream) {
         const int64_t row = tile * RPB + slot;
         if (row < a.rows) {
             const int64_t srow = skip_row_of(row, a, small_rows);
@@ -143,8 +151,17 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             for (int k = 0; k < CH; ++k) {
                 if (ok[k]) {
                     xr[k] = __builtin_nontemporal_load(xp + k * G);
-                    // The broadcast skip is re-read by every batch: keep it cached.
-                    if (with_skip) sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
+                    // The broadcast skip is re-read by every batch: keep it
+                    // cached.  (The compiler merges the two loads of one
+                    // address below into one and drops the non-temporal hint,
+                    // so an exact skip is a cached load too; the streaming
+                    // form is a separate instantiation of this body.)
+                    if (with_skip) {
+                        if constexpr (decltype(stream)::value)
+                            sr[k] = __builtin_nontemporal_load(sp + k * G);
+                        else
+                            sr[k] = bcast ? sp[k * G] : __builtin_nontemporal_load(sp + k * G);
+                    }
                 }
             }
         }
@@ -155,11 +172,11 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     // long-lived skip-stationary block gets its first tile moving first.
     int64_t tile = t_first;
     if (stationary) {
-        if (tile < t_end) issue_loads(tile, true);
+        if (tile < t_end) issue_loads(tile, true, std::false_type{});
         load_params();
     } else {
         load_params();
-        if (tile < t_end) issue_loads(tile, true);
+        if (tile < t_end) issue_loads(tile, true, std::integral_constant<bool, SS>{});
     }
 
     int parity = 0;
@@ -212,7 +229,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
 
         // Registers of x/skip are free again: start the next tile's loads.
-        if (tile + stride < t_end) issue_loads(tile + stride, !stationary);
+        if (tile + stride < t_end) issue_loads(tile + stride, !stationary, std::false_type{});
 
         if constexpr (OP == kOpBiasSoftmax) {
             // Softmax over the row: exponentials relative to a reference
@@ -516,7 +533,7 @@ template <typename E, int OP, int GG, int CH, int BLOCK>
 hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     constexpr Geom g = {GG, CH, BLOCK};
     static int occ = 0;
-    auto kernel = rowtile_kernel<E, OP, g.g, g.ch, g.block>;
+    auto kernel = rowtile_kernel<E, OP, g.g, g.ch, g.block, false>;
     const int64_t rpb = g.block / g.g;
     const int64_t tiles = (a0.rows + rpb - 1) / rpb;
     Args a = a0;
@@ -556,6 +573,23 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     }
     a.tiles_per_block = per;
     a.tiling = mode;
+    // An exact skip streams its first tile (the SS kernel) when the launch is
+    // one wave of resident blocks with one tile each: measured 4.15 against
+    // 4.28 us on 1024 rows of 768 float32 values, 3.7 against 3.8 us on 1024
+    // rows of 768 float16 values.  Launches whose blocks walk several tiles,
+    // or whose grid runs in several waves, measured slower with it (25
+    // against 23 us on 16384 rows of 1024 float16 values).  Element-wise
+    // kernels (odd row lengths) keep one form.
+    if constexpr (E::kPerChunk > 1) {
+        if (mode != kTileSkipStationary && a.skip_rows <= 0 && a.skip_group <= 0 && per <= 1) {
+            static int occ_ss = 0;
+            auto kernel_ss = rowtile_kernel<E, OP, g.g, g.ch, g.block, true>;
+            int64_t resident_ss = 0;
+            const hipError_t e = resident_blocks(kernel_ss, g.block, &occ_ss, &resident_ss);
+            if (e != hipSuccess) return e;
+            if (blocks <= resident_ss) return launch_grid(kernel_ss, g.block, blocks < 1 ? 1 : blocks, a, st);
+        }
+    }
     return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);
 }
 
