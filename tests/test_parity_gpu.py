@@ -813,3 +813,33 @@ def test_float16_subnormals(op, variant_hidden):
     assert np.isfinite(out).all()
     if op != "bias_add":
         assert np.abs(out[:6]).max() > 0.5
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add"])
+@pytest.mark.parametrize("dt,rows,hidden", [("f32", 1024, 768), ("f16", 1024, 768), ("f16", 5, 1024),
+                                            ("f32", 37, 4096), ("f16", 300, 8192)],
+                         ids=lambda v: str(v))
+def test_streamed_first_tile_matches_cached(op, dt, rows, hidden):
+    """A launch of one wave of resident blocks with one tile each reads an
+    exact skip with non-temporal loads (a kernel instantiation of its own);
+    launches whose blocks walk two tiles read it through the caches.  The
+    arithmetic is the same, so the outputs agree bit for bit, and with the
+    oracle."""
+    w = W.small_case(rows, hidden, dt, beta=True, bias=True, residual=op != "bias_add", eps=1e-5,
+                     seed=rows + hidden, op=op)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=w.residual)
+    U.note(f"streamed first tile {op} {dt} {rows}x{hidden}")
+    dc.run()
+    out_auto = dc.host(dc.out).copy()
+    res_auto = dc.host(dc.res).copy() if w.residual else None
+    ref = U.oracle_rows(w, inputs)
+    U.compare(w, out_auto, res_auto, ref)
+    for tpb, strided in [(2, 1), (2, 0)]:
+        dc.out.fill_(float("nan"))
+        if w.residual:
+            dc.res.fill_(float("nan"))
+        dc.run_config(-1, tpb, strided)
+        U.assert_bits_equal(dc.host(dc.out), out_auto, f"out, {tpb} tiles per block")
+        if w.residual:
+            U.assert_bits_equal(dc.host(dc.res), res_auto, f"residual, {tpb} tiles per block")
