@@ -311,7 +311,8 @@ int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int align
 
 /* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte
  * aligned, bytes % 16 == 0, no overlap), with the access pattern of the
- * row-tile kernel (16-byte non-temporal loads and stores, persistent grid).
+ * row-tile kernel's streamed input and outputs (16-byte non-temporal loads
+ * and stores, persistent grid).
  * It is the reference for the bandwidth one kernel can reach on the device
  * and for calibrating hardware byte counters against a known byte count.
  * Returns SKIPLN_OK, SKIPLN_ERR_NULL, SKIPLN_ERR_SHAPE (bytes < 0 or not a
@@ -330,8 +331,9 @@ int skipln_copy(void* dst, const void* src, int64_t bytes, skipln_stream_t strea
  * deals workgroup b to XCD b mod 8): the address granularity at which the
  * eight XCDs share the streams, which for a row kernel is one row.
  * store_through: 0 = non-temporal stores; 1 = non-temporal stores with
- * system-scope coherence (the policy the row kernels use for launches that
- * write 512 MiB or more).
+ * system-scope coherence (the policy the row-tile kernels use for launches
+ * that write 512 MiB or more, and the register-resident softmax for such
+ * launches whose rows are whole 16 KiB slabs).
  * Outputs: dst0 = src0 XOR src1 (a chunk's index when nothing is read),
  * dst1 = dst0 + 1 per 32-bit word, whatever the tile order.  Device memory,
  * 16-byte aligned, bytes % 16 == 0, outputs overlapping nothing.  Returns
