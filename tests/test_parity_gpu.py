@@ -843,3 +843,31 @@ def test_streamed_first_tile_matches_cached(op, dt, rows, hidden):
         U.assert_bits_equal(dc.host(dc.out), out_auto, f"out, {tpb} tiles per block")
         if w.residual:
             U.assert_bits_equal(dc.host(dc.res), res_auto, f"residual, {tpb} tiles per block")
+
+
+@pytest.mark.parametrize("hidden", [131072, 128256], ids=["whole_slabs", "ragged_last_slab"])
+def test_register_resident_store_policies(hidden):
+    """The register-resident softmax above the store threshold, one bias row:
+    system-scope stores for rows of whole 16 KiB slabs (131072 float16
+    values), non-temporal ones for rows with a ragged last slab; sampled row
+    blocks against the oracle."""
+    import torch
+
+    rows = STORE_THROUGH_BYTES // (hidden * 2) + 1
+    w = W.small_case(rows, hidden, "f16", skip_rows=1, seed=hidden % 1000, input_dist=W.normal(0, 2),
+                     skip_dist=W.normal(0, 1), op="bias_softmax")
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=False)
+    name = T.select_kernel(hidden, L.F16, op=U.OPS["bias_softmax"], skip_mode=L.SKIP_BROADCAST)
+    assert name.startswith("softmax_regrow_"), name
+    U.note(f"register-resident store policy: rows={rows} H={hidden} {name}")
+    dc.run()
+    torch.cuda.synchronize()
+    out = dc.out.view(w.rows, w.hidden)
+    n_blocks = -(-w.rows // W.BLOCK_ROWS)
+    for b in sorted({0, n_blocks // 2, n_blocks - 1}):
+        r0, r1 = b * W.BLOCK_ROWS, min(w.rows, (b + 1) * W.BLOCK_ROWS)
+        part = dict(inputs)
+        part["input"] = inputs["input"][r0:r1]
+        ref = U.oracle_rows(w, part, row_offset=r0)
+        U.compare(w, out[r0:r1].cpu().numpy(), None, ref)
