@@ -871,3 +871,49 @@ def test_register_resident_store_policies(hidden):
         part["input"] = inputs["input"][r0:r1]
         ref = U.oracle_rows(w, part, row_offset=r0)
         U.compare(w, out[r0:r1].cpu().numpy(), None, ref)
+
+
+def _random_case(rng):
+    """One random workload: operation, type, rows, hidden size (ragged,
+    chunk-multiple, power of two, long), optional tensors, skip form."""
+    op = str(rng.choice(["layer_norm", "simplified", "bias_add", "bias_softmax"], p=[0.4, 0.2, 0.2, 0.2]))
+    dt = str(rng.choice(["f32", "f16"]))
+    kind = int(rng.integers(0, 4))
+    if kind == 0:
+        hidden = int(rng.integers(1, 300))
+    elif kind == 1:
+        hidden = int(rng.integers(1, 600)) * (4 if dt == "f32" else 8)
+    elif kind == 2:
+        hidden = 1 << int(rng.integers(4, 14))
+    else:
+        hidden = int(rng.integers(8000, 40000))
+    rows = int(rng.integers(1, 200 if hidden < 8000 else 40))
+    skip_rows = None
+    if rng.random() < 0.3 and op != "bias_add":  # BiasAdd's skip has X's shape
+        divisors = [d for d in range(1, rows + 1) if rows % d == 0 and d < rows]
+        if divisors:
+            skip_rows = int(rng.choice(divisors))
+    inner = op == "bias_softmax" and skip_rows is not None and bool(rng.random() < 0.5)
+    w = W.small_case(rows, hidden, dt, skip_rows=skip_rows, beta=bool(rng.random() < 0.7),
+                     bias=bool(rng.random() < 0.6), residual=bool(rng.random() < 0.6) and op != "bias_add",
+                     eps=float(rng.choice([1e-5, 1e-12, 1e-3])), seed=int(rng.integers(1, 1 << 30)), op=op,
+                     inner=inner)
+    offset = int(rng.choice([0, 0, 0, 1, 3]))
+    return w, offset
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_shapes(seed):
+    """Twenty-five random workloads per seed (operation, type, rows, hidden size,
+    optional tensors, skip form, misaligned pointers), each through the
+    automatic kernel choice and compared with the oracle row by row."""
+    rng = np.random.default_rng(20_000 + seed)
+    for i in range(25):
+        w, offset = _random_case(rng)
+        U.note(f"random seed={seed} case={i}: {w.op} {w.dtype} shape={w.shape} skip={w.skip_shape} "
+               f"residual={w.residual} offset={offset}")
+        inputs = W.make_inputs(w)
+        dc = U.DeviceCase(w, inputs, residual=w.residual, offset_elems=offset)
+        dc.run()
+        ref = U.oracle_rows(w, inputs)
+        U.compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, ref)
