@@ -133,8 +133,8 @@ enum {
                                      that are not whole 16-byte chunks) */
     SKIPLN_VARIANT_REGROW = 7,    /* long rows of BiasSoftmax: one 1024-lane
                                      block per row, the row's raw data in
-                                     registers (up to 16 chunks per lane:
-                                     131072 float16 / 65536 float32 values),
+                                     registers (up to 20 chunks per lane:
+                                     163840 float16 / 81920 float32 values),
                                      z = data + bias formed again in each of
                                      two passes from the bias rows re-read
                                      through the caches; 16-byte chunks,
@@ -221,7 +221,7 @@ int skipln_bias_add(const void* x, const void* bias, const void* skip, void* y, 
  * skipln_forward_ws (size from skipln_workspace_bytes with
  * SKIPLN_OP_BIAS_SOFTMAX, rows = batch_count, hidden = block_size and the
  * skip form above).  Rows of 16-byte chunks up to 40896 values stay in one
- * workgroup's LDS and up to 131072 float16 / 65536 float32 values in one
+ * workgroup's LDS and up to 163840 float16 / 81920 float32 values in one
  * workgroup's registers (the manifest's long-row variants split them across
  * workgroups); longer ones split across workgroups through the workspace, or
  * without one take the generic kernel.  Ownership, streams and errors as for

@@ -327,13 +327,13 @@ def test_workspace_sizes_and_split_selection():
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32, L.SKIP_BROADCAST, 3) == -L.ERR_SHAPE
     assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 0     # held in registers
     assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4, L.VARIANT_SPLITROW) == ws(64, 16)
-    assert wb(L.OP_BIAS_SOFTMAX, 64, 131080, L.F16) == ws(64, 17)                     # beyond the registers
+    assert wb(L.OP_BIAS_SOFTMAX, 64, 163848, L.F16) == ws(64, 21)                     # beyond the registers
     # the automatic choice: split rows only where a workspace is at hand
     assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
     assert name_ws(L.OP_LAYER_NORM, 65536, L.F32) == "splitrow_f32"
     assert name_ws(L.OP_SIMPLIFIED, 65536, L.F16) == "rms_splitrow_f16"
     assert name_ws(L.OP_BIAS_SOFTMAX, 128256, L.F16) == "softmax_regrow_f16"
-    assert name_ws(L.OP_BIAS_SOFTMAX, 131080, L.F16) == "softmax_splitrow_f16"
+    assert name_ws(L.OP_BIAS_SOFTMAX, 163848, L.F16) == "softmax_splitrow_f16"
     assert name_ws(L.OP_LAYER_NORM, 20000, L.F32) == "ldsrow_f32"
     assert name_ws(L.OP_LAYER_NORM, 4096, L.F32) == "rowtile_f32_g256_c4"
     assert name_ws(L.OP_LAYER_NORM, 64 * 4096, L.F32) == "splitrow_f32"        # 64 slices
@@ -345,7 +345,7 @@ def test_workspace_sizes_and_split_selection():
 
 
 def test_register_resident_softmax_selection():
-    """BiasSoftmax rows beyond the LDS capacity and up to 16 chunks per lane
+    """BiasSoftmax rows beyond the LDS capacity and up to 20 chunks per lane
     of a 1024-lane block are held in registers, with or without a
     workspace; the family takes only 16-byte chunks of BiasSoftmax."""
     lib = L.load()
@@ -356,17 +356,19 @@ def test_register_resident_softmax_selection():
         assert name(40896, L.F32, mode=mode) == "softmax_ldsrow_f32"
         assert name(40900, L.F32, mode=mode) == "softmax_regrow_f32"
         assert name(65536, L.F32, mode=mode) == "softmax_regrow_f32"
-        assert name(65540, L.F32, mode=mode) == "softmax_generic_f32"
-        assert name_ws(65540, L.F32, mode) == "softmax_splitrow_f32"
+        assert name(81920, L.F32, mode=mode) == "softmax_regrow_f32"
+        assert name(81924, L.F32, mode=mode) == "softmax_generic_f32"
+        assert name_ws(81924, L.F32, mode) == "softmax_splitrow_f32"
         assert name(40960, L.F16, mode=mode) == "softmax_regrow_f16"
         assert name(131072, L.F16, mode=mode) == "softmax_regrow_f16"
         assert name_ws(131072, L.F16, mode) == "softmax_regrow_f16"
-        assert name(131080, L.F16, mode=mode) == "softmax_generic_f16"
+        assert name(163840, L.F16, mode=mode) == "softmax_regrow_f16"
+        assert name(163848, L.F16, mode=mode) == "softmax_generic_f16"
     # forced: any row of whole chunks up to the capacity
     assert name(8, L.F32, v=L.VARIANT_REGROW) == "softmax_regrow_f32"
     assert name(4096, L.F16, v=L.VARIANT_REGROW) == "softmax_regrow_f16"
     unsupported = -L.ERR_UNSUPPORTED
-    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 65540, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported
+    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 81924, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported
     assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 77, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported    # not chunks
     assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 4096, L.F32, 0, 0, L.VARIANT_REGROW) == unsupported  # misaligned
     for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED, L.OP_BIAS_ADD):

@@ -138,7 +138,8 @@ def test_misaligned_pointers(dt):
 
 # --------------------------------------------- register-resident rows --
 
-REGROW_HIDDEN = {"f32": [4100, 16384, 40960, 49152, 65536], "f16": [8200, 40960, 65536, 100000, 128256, 131072]}
+REGROW_HIDDEN = {"f32": [4100, 16384, 40960, 49152, 65536, 70000, 81920],
+                 "f16": [8200, 40960, 65536, 100000, 128256, 131072, 140000, 151936, 163840]}
 
 
 @pytest.mark.parametrize("dt,hidden", [(d, h) for d in ("f32", "f16") for h in REGROW_HIDDEN[d]])

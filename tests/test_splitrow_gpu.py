@@ -69,7 +69,7 @@ def test_split_softmax(dt_hidden, mode):
 
 
 @pytest.mark.parametrize("dt,hidden,op", [("f32", 65536, "layer_norm"), ("f16", 131072, "simplified"),
-                                          ("f32", 98304, "bias_softmax"), ("f16", 131080, "bias_softmax"),
+                                          ("f32", 98304, "bias_softmax"), ("f16", 163848, "bias_softmax"),
                                           ("f32", 262144, "layer_norm")])
 def test_split_auto_with_workspace(dt, hidden, op):
     """Rows beyond the LDS capacity (for BiasSoftmax, beyond the registers of

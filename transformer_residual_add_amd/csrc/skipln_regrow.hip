@@ -3,8 +3,9 @@
 // long-row variants for blocks too large for one workgroup's shared memory).
 //
 // One 1024-lane block per row at a time, persistent over rows.  Lane t keeps
-// the row's raw data chunks t, t + 1024, ..., t + 15 * 1024 in VGPRs (64
-// VGPRs: rows of up to 131072 float16 or 65536 float32 values), so the data
+// the row's raw data chunks t, t + 1024, ..., t + 19 * 1024 in VGPRs (80
+// VGPRs: rows of up to 163840 float16 or 81920 float32 values; 126 VGPRs in
+// all, no spills), so the data
 // crosses HBM once, and forms z = fl32(data + bias) afresh in each of the two
 // passes, re-reading the bias row -- from LDS when one bias row serves every
 // data row (a vocabulary's logit bias), else through the caches:
@@ -29,7 +30,7 @@ namespace {
 using namespace device;
 
 constexpr int kRegRowBlock = 1024;
-constexpr int kRegRowChunks = 16;  // chunks of data per lane
+constexpr int kRegRowChunks = 20;  // chunks of data per lane
 constexpr int kBiasAhead = 2;      // bias chunks loaded ahead of use
 constexpr int kLdsSlabs = 9;       // bias slabs a block parks in LDS (144 KiB)
 
@@ -277,6 +278,8 @@ hipError_t launch_regrow_sb(const Args& a, int n, hipStream_t st) {
     if (n <= 10) return launch_regrow_ch<T, 10, SB>(a, st);
     if (n <= 12) return launch_regrow_ch<T, 12, SB>(a, st);
     if (n <= 14) return launch_regrow_ch<T, 14, SB>(a, st);
+    if (n <= 16) return launch_regrow_ch<T, 16, SB>(a, st);
+    if (n <= 18) return launch_regrow_ch<T, 18, SB>(a, st);
     if (n <= kRegRowChunks) return launch_regrow_ch<T, kRegRowChunks, SB>(a, st);
     return hipErrorInvalidValue;
 }
