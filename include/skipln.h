@@ -105,7 +105,9 @@ enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 
 enum {
     SKIPLN_VARIANT_AUTO = 0,      /* what skipln_forward picks */
     SKIPLN_VARIANT_GENERIC = 1,   /* one workgroup per row, any hidden size and
-                                     alignment, three passes over the row */
+                                     alignment: aligned rows of whole 16-byte
+                                     chunks read twice with 16-byte accesses,
+                                     others in three element-wise passes */
     SKIPLN_VARIANT_ROWTILE = 2,   /* row held in registers, 16-byte accesses:
                                      needs hidden*sizeof(T) % 16 == 0, 16-byte
                                      aligned pointers, hidden <= 4096*16/sizeof(T) */

@@ -406,6 +406,28 @@ def test_new_ops_forced_variants(op, variant, dt):
     U.check_case(w, variant=variant)
 
 
+@pytest.mark.parametrize("misalign", [0, 1], ids=["aligned", "misaligned"])
+@pytest.mark.parametrize("rows_hidden", [(600, 64), (40, 8200), (12, 40000), (6, 65536), (6, 65537)],
+                         ids=lambda t: f"{t[0]}x{t[1]}")
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])
+def test_generic_both_forms(op, dt, rows_hidden, misalign):
+    """The generic kernel in its 16-byte-chunk form (aligned rows of whole
+    chunks) and its element form (misaligned tensors, or a row that ends
+    inside a chunk), forced, for every operation: more rows than resident
+    blocks (a block's reduction slots reused), rows with fewer chunks than
+    lanes, ragged batches of chunks, long rows far from zero mean."""
+    rows, hidden = rows_hidden
+    kw = dict(input_dist=W.normal(100.0, 1)) if op in ("layer_norm", "simplified") else {}
+    if op == "bias_softmax":
+        w = W.small_case(rows, hidden, dt, skip_rows=2, op=op, seed=rows + hidden + misalign)
+    else:
+        w = W.small_case(rows, hidden, dt, skip_rows=None if op == "bias_add" else 2, beta=True, bias=True,
+                         residual=True, eps=1e-5, seed=rows + hidden + misalign, op=op, **kw)
+    U.note(f"generic {op} {dt} {rows}x{hidden} misalign={misalign}")
+    U.check_case(w, variant=L.VARIANT_GENERIC, offset_elems=misalign)
+
+
 @pytest.mark.parametrize("op", ["simplified", "bias_add"])
 def test_new_ops_misaligned(op):
     w = W.small_case(20, 1024, "f16", beta=True, bias=True, residual=True, eps=1e-5, seed=9, op=op)

@@ -30,8 +30,11 @@
 //     they do not displace the broadcast skip and the parameters in L2.
 //   * ldsrow_kernel: rows too long for registers, staged in LDS (160 KiB per
 //     workgroup on gfx950), one 1024-lane block per row.
+//   * generic_chunk_kernel: aligned rows of whole 16-byte chunks beyond the
+//     other families' reach when no workspace is given, one 1024-lane block
+//     per row, two reads of the row (statistics, then output).
 //   * generic_kernel: any H and any alignment, one 256-lane block per row,
-//     several passes over the row.
+//     several passes over the row with element accesses.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -487,8 +490,265 @@ constexpr AutoEntry kAutoElem[] = {
     {512, 7},  {1024, 12}, {2048, 19}, {4096, 20}, {8192, 16}, {16384, 21},
 };
 
+// Generic kernel, chunked form: rows of whole 16-byte chunks with every
+// tensor 16-byte aligned (the automatic choice sends such rows here only
+// when they are too long for the other families and no workspace came with
+// the call).  One 1024-lane block per row (persistent), chunk c of the row
+// on lane c mod 1024 in every pass, kGenChunkBatch chunks loaded per lane
+// before they are used.  The normalizations read the row twice: pass 1
+// forms the sums and their statistics relative to the row's first sum
+// (per lane: count, mean and M2 of each chunk merged with Chan's update;
+// then across the block), pass 2 forms the sums again, writes the residual
+// and the output.  BiasSoftmax keeps a running maximum and rescaled sum per
+// lane in pass 1 (at most one rescale per batch of 4 chunks), merged across
+// the block before pass 2 writes the scaled exponentials.  BiasAdd is one
+// pass.
+// Every chunk is read and written by one lane, data before output, so an
+// output may alias its input exactly.
+constexpr int kGenChunkBlock = 1024;
+constexpr int kGenChunkBatch = 4;
+
+struct Moments {  // count, mean and M2 of values relative to the row's shift
+    float n, mean, m2;
+};
+__device__ __forceinline__ Moments merge_moments(Moments a, Moments b) {
+    if (b.n == 0.0f) return a;
+    if (a.n == 0.0f) return b;
+    const float n = a.n + b.n;
+    const float d = b.mean - a.mean;
+    const float f = b.n / n;
+    return Moments{n, a.mean + d * f, a.m2 + b.m2 + d * d * a.n * f};
+}
+
+template <typename T, int OP>
+__global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Args a) {
+    using E = Elem<T>;
+    using Raw = typename E::Raw;
+    constexpr int V = E::kPerChunk;
+    constexpr int W = kGenChunkBlock / 64;
+    constexpr int B = kGenChunkBatch;
+    constexpr float kLog2e = 1.4426950408889634f;
+    constexpr float kNegInf = -__builtin_inff();
+    __shared__ float4 red[2][W];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int hv = a.hidden / V;
+    const float h = static_cast<float>(a.hidden);
+    const bool small_rows = a.rows <= 0xFFFFFFFFll;
+    const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
+    const bool has_bias = a.bias != nullptr;
+    const bool has_beta = a.beta != nullptr;
+    const Raw* X = static_cast<const Raw*>(a.input);
+    const Raw* S = static_cast<const Raw*>(a.skip);
+    const Raw* Bz = static_cast<const Raw*>(a.bias);
+    const Raw* Gm = static_cast<const Raw*>(a.gamma);
+    const Raw* Bt = static_cast<const Raw*>(a.beta);
+    Raw* O = static_cast<Raw*>(a.out);
+    Raw* R = static_cast<Raw*>(a.residual);
+    int buf = 0;
+
+    for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
+        const int64_t srow = skip_row_of(row, a, small_rows);
+        const Raw* xp = X + row * hv;
+        const Raw* sp = S + srow * hv;
+        // The binary32 sums of chunk c, by the same operations in each pass.
+        auto sums = [&](const Raw& xr, const Raw& sr, int c, float* v) {
+            float xf[V], sf[V];
+            E::widen(xr, xf);
+            E::widen(sr, sf);
+            if constexpr (OP == kOpBiasAdd) {
+                float bf[V];
+                E::widen(Bz[c], bf);
+#pragma unroll
+                for (int e = 0; e < V; ++e) v[e] = (xf[e] + bf[e]) + sf[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) v[e] = xf[e] + sf[e];
+                if (OP != kOpBiasSoftmax && has_bias) {
+                    float bf[V];
+                    E::widen(Bz[c], bf);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) v[e] = v[e] + bf[e];
+                }
+            }
+        };
+        // Visit the lane's chunks in batches of B (chunks c0 + b * 1024):
+        // every load of a batch is issued before the first is used.
+        auto for_batches = [&](auto&& body) {
+            for (int c0 = tid; c0 < hv; c0 += kGenChunkBlock * B) {
+                Raw xr[B], sr[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int c = c0 + b * kGenChunkBlock;
+                    xr[b] = sr[b] = E::zero();
+                    if (c < hv) {
+                        xr[b] = __builtin_nontemporal_load(xp + c);
+                        sr[b] = bcast ? sp[c] : __builtin_nontemporal_load(sp + c);
+                    }
+                }
+                float v[B][V];
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (c0 + b * kGenChunkBlock < hv) sums(xr[b], sr[b], c0 + b * kGenChunkBlock, v[b]);
+                body(c0, v);
+            }
+        };
+        auto for_chunks = [&](auto&& body) {
+            for_batches([&](int c0, float (&v)[B][V]) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (c0 + b * kGenChunkBlock < hv) body(c0 + b * kGenChunkBlock, v[b]);
+            });
+        };
+
+        if constexpr (OP == kOpBiasAdd) {
+            for_chunks([&](int c, const float* v) { __builtin_nontemporal_store(E::narrow(v), O + row * hv + c); });
+            continue;
+        }
+
+        if constexpr (OP == kOpBiasSoftmax) {
+            // Per lane: the running maximum m of its batches and the sum of
+            // 2^((z - m) log2 e), rescaled once per batch that raises m.
+            float m = kNegInf, sm = 0.0f;
+            for_batches([&](int c0, float (&v)[B][V]) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (c0 + b * kGenChunkBlock >= hv)
+#pragma unroll
+                        for (int e = 0; e < V; ++e) v[b][e] = kNegInf;
+                float bm = kNegInf;
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) bm = __builtin_fmaxf(bm, v[b][e]);
+                if (bm > m) {
+                    sm = sm * __builtin_amdgcn_exp2f((m - bm) * kLog2e);
+                    m = bm;
+                }
+                const float r = m != kNegInf ? m : 0.0f;
+                float cs = 0.0f;
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) cs += __builtin_amdgcn_exp2f((v[b][e] - r) * kLog2e);
+                sm += cs;
+            });
+            const float mw = wave_max(m);
+            const float sw = wave_sum(sm * (m != kNegInf ? __builtin_amdgcn_exp2f((m - mw) * kLog2e) : 0.0f));
+            if ((tid & 63) == 0) red[buf][wave] = make_float4(mw, sw, 0.0f, 0.0f);
+            __syncthreads();
+            float M = kNegInf;
+#pragma unroll
+            for (int w = 0; w < W; ++w) M = __builtin_fmaxf(M, red[buf][w].x);
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float4 p = red[buf][w];
+                tot += p.y * (p.x != kNegInf ? __builtin_amdgcn_exp2f((p.x - M) * kLog2e) : 0.0f);
+            }
+            buf ^= 1;
+            const float scale = 1.0f / tot;
+            for_chunks([&](int c, const float* v) {
+                float y[V];
+#pragma unroll
+                for (int e = 0; e < V; ++e) y[e] = __builtin_amdgcn_exp2f((v[e] - M) * kLog2e) * scale;
+                __builtin_nontemporal_store(E::narrow(y), O + row * hv + c);
+            });
+            continue;
+        }
+
+        // Normalizations.  Layer norm takes its statistics relative to the
+        // row's first sum, read by every lane before the block's first
+        // barrier (which precedes every store of the row).
+        float shift = 0.0f;
+        if constexpr (OP == kOpLayerNorm) {
+            shift = E::load1(a.input, row * a.hidden) + E::load1(a.skip, srow * a.hidden);
+            if (has_bias) shift = shift + E::load1(a.bias, 0);
+        }
+        float mean_rel = 0.0f, var;
+        if constexpr (OP == kOpSimplified) {
+            float sq = 0.0f;
+            for_chunks([&](int, const float* v) {
+#pragma unroll
+                for (int e = 0; e < V; ++e) sq += v[e] * v[e];
+            });
+            const float ws = wave_sum(sq);
+            if ((tid & 63) == 0) red[buf][wave] = make_float4(ws, 0.0f, 0.0f, 0.0f);
+            __syncthreads();
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) tot += red[buf][w].x;
+            buf ^= 1;
+            var = tot / h;
+        } else {
+            Moments mo{0.0f, 0.0f, 0.0f};
+            for_chunks([&](int, const float* v) {
+                float cm = 0.0f;
+#pragma unroll
+                for (int e = 0; e < V; ++e) cm += v[e] - shift;
+                cm *= 1.0f / V;
+                float cq = 0.0f;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float d = (v[e] - shift) - cm;
+                    cq += d * d;
+                }
+                mo = merge_moments(mo, Moments{static_cast<float>(V), cm, cq});
+            });
+            // Across the wavefront (butterfly), then across the block.
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const Moments o{__shfl_xor(mo.n, off), __shfl_xor(mo.mean, off), __shfl_xor(mo.m2, off)};
+                mo = merge_moments(mo, o);
+            }
+            if ((tid & 63) == 0) red[buf][wave] = make_float4(mo.n, mo.mean, mo.m2, 0.0f);
+            __syncthreads();
+            Moments t{0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float4 p = red[buf][w];
+                t = merge_moments(t, Moments{p.x, p.y, p.z});
+            }
+            buf ^= 1;
+            mean_rel = t.mean;
+            var = t.m2 / h;
+        }
+        const float rstd = rsqrtf(var + a.eps);
+        // Pass 2: the sums again, the residual and the output (writes only
+        // after the row's statistics, i.e. after every read of pass 1).
+        for_chunks([&](int c, const float* v) {
+            if (R != nullptr) __builtin_nontemporal_store(E::narrow(v), R + row * hv + c);
+            float gf[V], bf[V], y[V];
+            E::widen(Gm[c], gf);
+            if (has_beta) {
+                E::widen(Bt[c], bf);
+            } else {
+#pragma unroll
+                for (int e = 0; e < V; ++e) bf[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const float t = OP == kOpLayerNorm ? ((v[e] - shift) - mean_rel) * rstd : v[e] * rstd;
+                y[e] = t * gf[e] + bf[e];
+            }
+            __builtin_nontemporal_store(E::narrow(y), O + row * hv + c);
+        });
+    }
+}
+
 template <typename T, int OP>
 hipError_t launch_generic_t(const Args& a, hipStream_t st) {
+    // Rows of whole 16-byte chunks with every tensor aligned: the chunked form.
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    if (a.hidden % Elem<T>::kPerChunk == 0 && al(a.input) && al(a.skip) && al(a.out) && al(a.residual) &&
+        al(a.gamma) && al(a.beta) && al(a.bias)) {
+        static int occ_c = 0;
+        int64_t resident = 0;
+        const hipError_t e = resident_blocks(generic_chunk_kernel<T, OP>, kGenChunkBlock, &occ_c, &resident);
+        if (e != hipSuccess) return e;
+        const int64_t blocks = a.rows < resident ? a.rows : resident;
+        return launch_grid(generic_chunk_kernel<T, OP>, kGenChunkBlock, blocks < 1 ? 1 : blocks, a, st);
+    }
     static int occ = 0;
     int64_t resident = 0;
     const hipError_t e = resident_blocks(generic_kernel<T, OP>, kGenericBlock, &occ, &resident);
