@@ -32,7 +32,8 @@
 //     workgroup on gfx950), one 1024-lane block per row.
 //   * generic_chunk_kernel: aligned rows of whole 16-byte chunks beyond the
 //     other families' reach when no workspace is given, one 1024-lane block
-//     per row, two reads of the row (statistics, then output).
+//     per row, two passes (statistics, then output), the second taking the
+//     row's first 40,832 sums from LDS and re-reading only the rest.
 //   * generic_kernel: any H and any alignment, one 256-lane block per row,
 //     several passes over the row with element accesses.
 #include <hip/hip_runtime.h>
@@ -503,10 +504,20 @@ constexpr AutoEntry kAutoElem[] = {
 // lane in pass 1 (at most one rescale per batch of 4 chunks), merged across
 // the block before pass 2 writes the scaled exponentials.  BiasAdd is one
 // pass.
-// Every chunk is read and written by one lane, data before output, so an
-// output may alias its input exactly.
+// Pass 1 also parks the binary32 sums of the row's first chunks in LDS (as
+// many as fit beside the reduction slots: 40,832 values), so pass 2 re-reads
+// from HBM only the chunks beyond them.  Every chunk is read, parked and
+// written by one lane, data before output, so an output may alias its input
+// exactly and the parked sums need no barrier.
 constexpr int kGenChunkBlock = 1024;
 constexpr int kGenChunkBatch = 4;
+constexpr int kGenParkBytes = 160 * 1024 - 2 * (kGenChunkBlock / 64) * 16;  // LDS beside `red`
+// Chunks of a row whose sums the block parks: the row's, at most the LDS's.
+template <typename T>
+constexpr int gen_park_chunks(int hv) {
+    constexpr int cap = kGenParkBytes / (4 * Elem<T>::kPerChunk);
+    return hv < cap ? hv : cap;
+}
 
 struct Moments {  // count, mean and M2 of values relative to the row's shift
     float n, mean, m2;
@@ -529,10 +540,13 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
     constexpr int B = kGenChunkBatch;
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr float kNegInf = -__builtin_inff();
+    constexpr int Q = V / 4;  // float4 words of binary32 sums per chunk
     __shared__ float4 red[2][W];
+    extern __shared__ float4 park[];  // Q planes of lc chunks' sums
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int hv = a.hidden / V;
+    const int lc = OP == kOpBiasAdd ? 0 : gen_park_chunks<T>(hv);
     const float h = static_cast<float>(a.hidden);
     const bool small_rows = a.rows <= 0xFFFFFFFFll;
     const bool bcast = a.skip_rows > 0 || a.skip_group > 0;
@@ -546,6 +560,12 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
     Raw* O = static_cast<Raw*>(a.out);
     Raw* R = static_cast<Raw*>(a.residual);
     int buf = 0;
+    auto put = [&](int c, const float* v) {
+        if (c < lc) {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) park[q * lc + c] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+    };
 
     for (int64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
         const int64_t srow = skip_row_of(row, a, small_rows);
@@ -574,8 +594,9 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
         };
         // Visit the lane's chunks in batches of B (chunks c0 + b * 1024):
         // every load of a batch is issued before the first is used.
-        auto for_batches = [&](auto&& body) {
-            for (int c0 = tid; c0 < hv; c0 += kGenChunkBlock * B) {
+        auto for_batches = [&](int start, auto&& body) {
+#pragma unroll 1
+            for (int c0 = start; c0 < hv; c0 += kGenChunkBlock * B) {
                 Raw xr[B], sr[B];
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
@@ -594,7 +615,30 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
             }
         };
         auto for_chunks = [&](auto&& body) {
-            for_batches([&](int c0, float (&v)[B][V]) {
+            for_batches(tid, [&](int c0, float (&v)[B][V]) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+                    if (c0 + b * kGenChunkBlock < hv) body(c0 + b * kGenChunkBlock, v[b]);
+            });
+        };
+        // Pass 2: parked sums from LDS, then the rest formed again from HBM
+        // in batches from the lane's first chunk past the parked ones.
+        auto for_chunks_again = [&](auto&& body) {
+#pragma unroll 1
+            for (int c = tid; c < lc; c += kGenChunkBlock) {
+                float v[V];
+#pragma unroll
+                for (int q = 0; q < Q; ++q) {
+                    const float4 p = park[q * lc + c];
+                    v[4 * q] = p.x;
+                    v[4 * q + 1] = p.y;
+                    v[4 * q + 2] = p.z;
+                    v[4 * q + 3] = p.w;
+                }
+                body(c, v);
+            }
+            const int first = tid >= lc ? tid : tid + (lc - tid + kGenChunkBlock - 1) / kGenChunkBlock * kGenChunkBlock;
+            for_batches(first, [&](int c0, float (&v)[B][V]) {
 #pragma unroll
                 for (int b = 0; b < B; ++b)
                     if (c0 + b * kGenChunkBlock < hv) body(c0 + b * kGenChunkBlock, v[b]);
@@ -610,12 +654,17 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
             // Per lane: the running maximum m of its batches and the sum of
             // 2^((z - m) log2 e), rescaled once per batch that raises m.
             float m = kNegInf, sm = 0.0f;
-            for_batches([&](int c0, float (&v)[B][V]) {
+            for_batches(tid, [&](int c0, float (&v)[B][V]) {
 #pragma unroll
-                for (int b = 0; b < B; ++b)
-                    if (c0 + b * kGenChunkBlock >= hv)
+                for (int b = 0; b < B; ++b) {
+                    const int c = c0 + b * kGenChunkBlock;
+                    if (c < hv) {
+                        put(c, v[b]);
+                    } else {
 #pragma unroll
                         for (int e = 0; e < V; ++e) v[b][e] = kNegInf;
+                    }
+                }
                 float bm = kNegInf;
 #pragma unroll
                 for (int b = 0; b < B; ++b)
@@ -648,7 +697,7 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
             }
             buf ^= 1;
             const float scale = 1.0f / tot;
-            for_chunks([&](int c, const float* v) {
+            for_chunks_again([&](int c, const float* v) {
                 float y[V];
 #pragma unroll
                 for (int e = 0; e < V; ++e) y[e] = __builtin_amdgcn_exp2f((v[e] - M) * kLog2e) * scale;
@@ -668,7 +717,8 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
         float mean_rel = 0.0f, var;
         if constexpr (OP == kOpSimplified) {
             float sq = 0.0f;
-            for_chunks([&](int, const float* v) {
+            for_chunks([&](int c, const float* v) {
+                put(c, v);
 #pragma unroll
                 for (int e = 0; e < V; ++e) sq += v[e] * v[e];
             });
@@ -682,7 +732,8 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
             var = tot / h;
         } else {
             Moments mo{0.0f, 0.0f, 0.0f};
-            for_chunks([&](int, const float* v) {
+            for_chunks([&](int c, const float* v) {
+                put(c, v);
                 float cm = 0.0f;
 #pragma unroll
                 for (int e = 0; e < V; ++e) cm += v[e] - shift;
@@ -716,7 +767,7 @@ __global__ void __launch_bounds__(kGenChunkBlock) generic_chunk_kernel(const Arg
         const float rstd = rsqrtf(var + a.eps);
         // Pass 2: the sums again, the residual and the output (writes only
         // after the row's statistics, i.e. after every read of pass 1).
-        for_chunks([&](int c, const float* v) {
+        for_chunks_again([&](int c, const float* v) {
             if (R != nullptr) __builtin_nontemporal_store(E::narrow(v), R + row * hv + c);
             float gf[V], bf[V], y[V];
             E::widen(Gm[c], gf);
@@ -742,12 +793,22 @@ hipError_t launch_generic_t(const Args& a, hipStream_t st) {
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
     if (a.hidden % Elem<T>::kPerChunk == 0 && al(a.input) && al(a.skip) && al(a.out) && al(a.residual) &&
         al(a.gamma) && al(a.beta) && al(a.bias)) {
-        static int occ_c = 0;
-        int64_t resident = 0;
-        const hipError_t e = resident_blocks(generic_chunk_kernel<T, OP>, kGenChunkBlock, &occ_c, &resident);
+        auto kernel = generic_chunk_kernel<T, OP>;
+        const int lc = OP == kOpBiasAdd ? 0 : gen_park_chunks<T>(a.hidden / Elem<T>::kPerChunk);
+        const size_t lds = static_cast<size_t>(lc) * Elem<T>::kPerChunk * sizeof(float);
+        int cus = 0;
+        hipError_t e = cu_count(&cus);
         if (e != hipSuccess) return e;
-        const int64_t blocks = a.rows < resident ? a.rows : resident;
-        return launch_grid(generic_chunk_kernel<T, OP>, kGenChunkBlock, blocks < 1 ? 1 : blocks, a, st);
+        int occ = 0;  // depends on the row's LDS footprint, so it is not cached
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kGenChunkBlock, lds);
+        if (e != hipSuccess) return e;
+        if (occ < 1) return hipErrorInvalidConfiguration;
+        int64_t blocks = static_cast<int64_t>(cus) * occ;
+        if (a.rows < blocks) blocks = a.rows;
+        Args arg = a;
+        void* params[] = {&arg};
+        return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks)),
+                               dim3(kGenChunkBlock), params, lds, st);
     }
     static int occ = 0;
     int64_t resident = 0;
