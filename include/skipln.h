@@ -99,7 +99,9 @@ enum { SKIPLN_OP_LAYER_NORM = 0, SKIPLN_OP_SIMPLIFIED = 1, SKIPLN_OP_BIAS_ADD = 
  * choice: row tiles up to 2048 chunks of 16 bytes per row, the LDS-staged
  * kernel for longer rows of the reducing operations, the register-resident
  * kernel for BiasSoftmax rows beyond it, then -- for calls that bring a
- * workspace (skipln_forward_ws) -- the split-row kernels; rows that are not
+ * workspace (skipln_forward_ws) -- the split-row kernels, except for 256 or
+ * more rows of RMS, or of float32 layer norm up to 65536 values, which the
+ * generic kernel runs faster without a workspace; rows that are not
  * whole chunks, or tensors not 16-byte aligned, take element-wise row tiles
  * up to 16384 values, and the generic kernel anything else. */
 enum {
@@ -252,7 +254,8 @@ int skipln_forward_ws(int op, const void* input, const void* skip, int skip_mode
                       skipln_stream_t stream);
 
 /* Workspace bytes skipln_forward_ws needs for these arguments (0: none), or a
- * negative status code.  Host code only. */
+ * negative status code.  The kernel choice depends on the row count (see
+ * skipln_select_ws).  Host code only. */
 int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode, int64_t skip_rows,
                                int variant);
 
@@ -308,7 +311,11 @@ int skipln_validate(int op, const void* input, const void* skip, int skip_mode, 
  * is 16-byte aligned. */
 int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
 
-/* The same for skipln_forward_ws given a sufficient workspace. */
+/* The same for skipln_forward_ws given a sufficient workspace, for a call of
+ * fewer than 256 rows.  With 256 rows or more, RMS rows and float32 layer
+ * norm rows of up to 65536 values that would split across workgroups take
+ * the generic kernel instead, which needs no workspace (measured faster
+ * there); skipln_workspace_bytes, which knows the row count, then returns 0. */
 int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int aligned16, int variant);
 
 /* Streaming copy of `bytes` bytes from src to dst (device memory, 16-byte

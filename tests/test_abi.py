@@ -315,8 +315,19 @@ def test_workspace_sizes_and_split_selection():
     # 128 MiB of inputs (x, and skip when it is not broadcast)
     ws = lambda rows, slices: rows * slices * 16
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == ws(64, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32) == ws(256, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == ws(512, 16)
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, v=L.VARIANT_SPLITROW) == ws(256, 16)
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8, L.VARIANT_SPLITROW) == ws(512, 16)
+    # 256 rows or more (a row for every CU): RMS, and float32 layer norm up to
+    # 65536 values, take the generic kernel, which needs no workspace
+    assert wb(L.OP_LAYER_NORM, 255, 65536, L.F32) == ws(255, 16)
+    assert wb(L.OP_LAYER_NORM, 256, 65536, L.F32) == 0
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 0
+    assert wb(L.OP_LAYER_NORM, 256, 65540, L.F32) > 0                    # split rows beyond 65536
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F16) == ws(512, 8)
+    assert wb(L.OP_SIMPLIFIED, 255, 262144, L.F32) == ws(64, 64)
+    assert wb(L.OP_SIMPLIFIED, 256, 262144, L.F32) == 0
+    assert wb(L.OP_SIMPLIFIED, 4096, 65536, L.F16) == 0
+    assert wb(L.OP_BIAS_SOFTMAX, 1024, 163848, L.F16) > 0
     assert wb(L.OP_LAYER_NORM, 201, 65540, L.F32) == ws(201, 17)
     assert wb(L.OP_LAYER_NORM, 0, 65536, L.F32) == 0
     assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32) == 0                       # row tiles need none

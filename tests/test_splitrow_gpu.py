@@ -89,7 +89,35 @@ def test_split_many_rows(dt, hidden):
     rows = 519
     w = norm_case(rows, hidden, dt, "layer_norm", seed=11)
     U.note(f"split many rows {dt} H={hidden} rows={rows}")
-    U.check_case(w, workspace=True)
+    U.check_case(w, variant=SPLIT, workspace=True)
+
+
+@pytest.mark.parametrize("dt,hidden,op", [("f32", 65536, "layer_norm"), ("f16", 65536, "simplified"),
+                                          ("f32", 262144, "simplified")])
+def test_many_rows_auto_takes_generic(dt, hidden, op):
+    """With a row for every CU, RMS rows and float32 layer norm rows of up
+    to 65536 values take the generic kernel even when a workspace is at hand:
+    the workspace size is 0, and the call through skipln_forward_ws (with an
+    empty workspace) and through the allocating wrapper match the oracle."""
+    import torch
+
+    rows = 256
+    w = norm_case(rows, hidden, dt, op, seed=13, mu=100.0 if op == "layer_norm" else 0.0)
+    code = L.F32 if dt == "f32" else L.F16
+    assert T.workspace_bytes(U.OPS[op], rows, hidden, code) == 0
+    assert T.workspace_bytes(U.OPS[op], rows - 1, hidden, code) > 0
+    inputs = W.make_inputs(w)
+    ref = U.oracle_rows(w, inputs)
+    U.note(f"auto many rows {op} {dt} H={hidden} rows={rows}")
+    dc = U.DeviceCase(w, inputs, residual=True)
+    dc.run(L.VARIANT_AUTO, workspace=True)
+    U.compare(w, dc.host(dc.out), dc.host(dc.res), ref)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out, res = T.skip_layer_norm(tt(inputs["input"]), tt(inputs["skip"]), tt(inputs["gamma"]), tt(inputs["beta"]),
+                                 tt(inputs["bias"]), epsilon=float(w.eps), return_residual=True,
+                                 simplified=op == "simplified")
+    torch.cuda.synchronize()
+    U.compare(w, out.cpu().numpy().reshape(rows, hidden), res.cpu().numpy().reshape(rows, hidden), ref)
 
 
 def test_split_workspace_errors_enqueue_nothing():

@@ -144,11 +144,26 @@ bool all_element_aligned(const Call& c) {
     return true;
 }
 
+// Many long rows of a normalization: the generic kernel's chunk form (one
+// 1024-lane workgroup per row, the row's first 40,832 sums parked in LDS, no
+// workspace) outruns the split-row kernels once there is a row for every CU
+// (MI355X: 256).  Measured, generic / split-row time: RMS 0.80-0.93 for 256
+// to 2048 rows of 65,536 to 262,144 values (either type; 0.99 at 128 rows);
+// float32 layer norm 0.85-0.91 for 256-2048 rows of 65,536 values, 1.29 at
+// 128 rows, 0.92-1.00 at 131,072 values; float16 layer norm 0.97-1.08.
+constexpr int64_t kGenericManyRows = 256;
+bool generic_outruns_split(int op, int64_t hidden, int dtype, int64_t rows) {
+    if (rows < kGenericManyRows) return false;
+    return op == SKIPLN_OP_SIMPLIFIED || (op == SKIPLN_OP_LAYER_NORM && dtype == SKIPLN_F32 && hidden <= 65536);
+}
+
 // Kernel id (>= 0) for this variant, or -status.  vec_ok: tensors 16-byte
 // aligned; elem_ok: aligned to their element size.  with_workspace: the call
-// brings a workspace, so the automatic choice may take the split-row kernels.
+// brings a workspace, so the automatic choice may take the split-row kernels
+// (unless it has `rows` rows that the generic kernel runs faster; rows < 0:
+// not known).
 int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool elem_ok, int variant,
-           bool with_workspace) {
+           bool with_workspace, int64_t rows) {
     const int base = (op * 2 + dtype) * skipln::kIdsPerType;
     const int v = dtype == SKIPLN_F32 ? 4 : 8;  // elements per 16-byte chunk
     const bool chunked = vec_ok && hidden % v == 0;
@@ -174,7 +189,8 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
     if (variant == SKIPLN_VARIANT_AUTO && hidden / v > skipln::kRowtileMaxAutoChunks) {
         if (lds_ok) return base + skipln::kLdsRowIndex;
         if (reg_ok) return base + skipln::kRegRowIndex;
-        if (split_ok && with_workspace) return base + skipln::kSplitRowIndex;
+        if (split_ok && with_workspace && !generic_outruns_split(op, hidden, dtype, rows))
+            return base + skipln::kSplitRowIndex;
     }
     if (variant == SKIPLN_VARIANT_AUTO || variant == SKIPLN_VARIANT_ROWTILE ||
         variant == SKIPLN_VARIANT_MULTIWAVE) {
@@ -257,7 +273,7 @@ int run(const Call& c, int variant, const skipln::Tiling* tiling, skipln_stream_
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
     const int id = select(c.op, c.hidden, c.dtype, c.skip_mode != SKIPLN_SKIP_EXACT, all_aligned16(c),
-                          all_element_aligned(c), variant, ws != nullptr);
+                          all_element_aligned(c), variant, ws != nullptr, c.rows);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
     const skipln::Args a = make_args(c);
@@ -317,7 +333,7 @@ int skipln_select(int op, int64_t hidden, int dtype, int skip_mode, int aligned,
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, false);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, false, -1);
 }
 
 int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int aligned, int variant) {
@@ -325,7 +341,7 @@ int skipln_select_ws(int op, int64_t hidden, int dtype, int skip_mode, int align
     if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
-    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, true);
+    return select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, aligned != 0, true, variant, true, -1);
 }
 
 int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode, int64_t skip_rows,
@@ -335,7 +351,7 @@ int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, 
     if (!mode_ok(op, skip_mode)) return -SKIPLN_ERR_MODE;
     if (rows < 0 || hidden <= 0 || hidden > INT32_MAX) return -SKIPLN_ERR_SHAPE;
     if (skip_mode != SKIPLN_SKIP_EXACT && (skip_rows <= 0 || rows % skip_rows != 0)) return -SKIPLN_ERR_SHAPE;
-    const int id = select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, true, true, variant, true);
+    const int id = select(op, hidden, dtype, skip_mode != SKIPLN_SKIP_EXACT, true, true, variant, true, rows);
     if (id < 0) return id;
     if (id % skipln::kIdsPerType != skipln::kSplitRowIndex || rows == 0) return 0;
     Call c = make_call(op, nullptr, nullptr, skip_mode, skip_rows, nullptr, nullptr, nullptr, nullptr, nullptr, rows,
