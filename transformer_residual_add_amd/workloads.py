@@ -281,6 +281,34 @@ EXTRA: Dict[str, Workload] = {
             seed=1013,
             op="simplified",
         ),
+        # Rows beyond one workgroup's LDS (65536 values): the generic kernel's
+        # chunk form (part of each row parked in LDS) against the split-row
+        # kernels, 512 rows so that every CU holds a row.
+        Workload(
+            name="longrow_512x65536_f32",
+            shape=(512, 65536),
+            dtype="f32",
+            skip_shape=(512, 65536),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 1),
+            bias_dist=normal(0, 0.1),
+            residual=True,
+            eps=1e-5,
+            seed=1031,
+        ),
+        Workload(
+            name="rms_longrow_512x65536_f16",
+            shape=(512, 65536),
+            dtype="f16",
+            skip_shape=(512, 65536),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 1),
+            bias_dist=normal(0, 0.1),
+            residual=True,
+            eps=1e-5,
+            seed=1032,
+            op="simplified",
+        ),
         # BiasSoftmax on attention scores: (batch, heads, queries, keys) data,
         # softmax over the keys.  A per-sequence key-padding mask (B, 1, 1, K)
         # is shared by the heads x queries rows of each sequence (inner
