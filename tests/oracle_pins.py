@@ -368,10 +368,23 @@ def check_bias_add():
         assert np.array_equal(y.view(np.uint8), want.view(np.uint8)), f"bias_add {dt.__name__}"
         exact = x.astype(np.float64) + bias.astype(np.float64) + skip.astype(np.float64)
         _close(ye, exact, 1e-15, 1e-15, "bias_add exact")
-    # hand row: X = [1, 2], bias = [10, 20], skip = [100, 200]
-    y, _ = O.bias_add(np.array([[1, 2]], np.float32), np.array([10, 20], np.float32),
-                      np.array([[100, 200]], np.float32))
-    assert y.tolist() == [[111.0, 222.0]], "bias_add hand row"
+
+
+def check_bias_add_hand_rows():
+    """Hand-derived BiasAdd rows (tests/golden/bias_add_rows.json), among them
+    rows whose binary32 result depends on the grouping: X + bias first, then
+    the skip (com.microsoft BiasAdd manifest, `description`)."""
+    with open(os.path.join(GOLDEN, "bias_add_rows.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        dt = NP[c["dtype"]]
+        y, _ = O.bias_add(_arr(c["x"], dt), _arr(c["bias"], dt), _arr(c["skip"], dt))
+        if "y" in c:
+            assert np.array_equal(y.astype(np.float64), np.asarray(c["y"], np.float64)), \
+                f"{c['name']}: Y {y.tolist()} != {c['y']}"
+        if "y_bits" in c:
+            want = np.array([[int(b, 16) for b in row] for row in c["y_bits"]], np.uint16)
+            assert np.array_equal(y.view(np.uint16), want), f"{c['name']}: Y bits {y.view(np.uint16)} != {want}"
 
 
 # ------------------------------------------------------------ BiasSoftmax --
@@ -462,6 +475,7 @@ ALL_CHECKS = [
     check_invariants,
     check_cancellation_rows,
     check_simplified,
+    check_bias_add_hand_rows,
     check_bias_add,
     check_bias_softmax_closed_forms,
     check_bias_softmax_libraries,

@@ -39,6 +39,12 @@ MUTANTS = [
     ("f16_flushes_subnormals", "if (shift > 24)", "if (shift > 0)"),
     ("f16_decode_subnormal_scale", "ldexpf((float)m, -24)", "ldexpf((float)m, -23)"),
     ("bias_add_skip_first", "float a = xv + bv;\n            a = a + sv;", "float a = xv + sv;\n            a = a + bv;"),
+    ("skipln_bias_joins_skip_first",
+     "            float a = load_t(J->input, i * H + c, J->dtype) + load_t(J->skip, j * H + c, J->dtype);\n"
+     "            if (J->bias)\n                a = a + load_t(J->bias, c, J->dtype);",
+     "            float a = load_t(J->skip, j * H + c, J->dtype);\n"
+     "            if (J->bias)\n                a = a + load_t(J->bias, c, J->dtype);\n"
+     "            a = load_t(J->input, i * H + c, J->dtype) + a;"),
     ("rms_keeps_mean", "if (!J->simplified) {", "if (1) {"),
     ("softmax_inner_outer_swapped", "const int64_t j = inner ? r / repeat : r % bias_rows;",
      "const int64_t j = inner ? r % bias_rows : r / repeat;"),
@@ -81,3 +87,25 @@ def test_planted_mistake_is_caught(mutant_dir, name, old, new):
     finally:
         O.use(None)
     assert caught, f"no pin catches the planted mistake {name}"
+
+
+# Mistakes in the grouping of the binary32 adds must be caught by the
+# hand-derived golden rows themselves, not only by checks whose expected sum
+# is formed in numpy in the oracle's own order.
+GOLDEN_CATCHES = {
+    "bias_add_skip_first": P.check_bias_add_hand_rows,
+    "skipln_bias_joins_skip_first": P.check_hand_rows,
+    "residual_stored_before_bias": P.check_hand_rows,
+}
+
+
+@pytest.mark.parametrize("name", sorted(GOLDEN_CATCHES))
+def test_add_order_mistake_fails_a_golden_row(mutant_dir, name):
+    old, new = next((o, n) for m, o, n in MUTANTS if m == name)
+    lib = _build_mutant(mutant_dir, name + "_golden", old, new)
+    O.use(lib)
+    try:
+        with pytest.raises(AssertionError):
+            GOLDEN_CATCHES[name]()
+    finally:
+        O.use(None)
