@@ -33,18 +33,15 @@ def test_workload_all_rows(name):
     U.check_case(w)
 
 
-def _sample_rows(w, n_blocks, rng):
-    blocks = {0, w.rows // W.BLOCK_ROWS - 1}
-    blocks.update(int(b) for b in rng.choice(w.rows // W.BLOCK_ROWS, size=n_blocks, replace=False))
-    return sorted(blocks)
+ORACLE_BLOCK = 4096  # rows per oracle call in the full-size comparison
 
 
 @pytest.mark.parametrize("name", W.ORDER[3:])
-def test_workload_full_size_sampled(name):
-    """Full-size run in the benchmark's launch configuration; whole row blocks
-    sampled across the tensor checked against the oracle, plus properties
-    over every row: the residual equals numpy's binary32 sum rounded to T, and
-    (out - beta) / gamma has per-row mean ~0 and variance ~var/(var+eps)."""
+def test_workload_full_size_every_row(name):
+    """Full-size run in the benchmark's launch configuration, every row
+    compared with the oracle: the normalized output within tolerance, the
+    residual (when emitted) bit for bit.  The oracle runs in blocks of rows on
+    the host's cores while the device result is copied back block by block."""
     import torch
 
     w = W.WORKLOADS[name]
@@ -55,49 +52,20 @@ def test_workload_full_size_sampled(name):
     U.note(f"workload {name}: launching {T.select_kernel(w.hidden, L.F32 if w.dtype == 'f32' else L.F16, skip_mode=mode)}")
     dc.run()
     torch.cuda.synchronize()
-    U.note(f"workload {name}: comparing sampled rows")
-    rng = np.random.default_rng(w.seed)
+    U.note(f"workload {name}: comparing all {w.rows} rows with the oracle")
     out = dc.out.view(w.rows, w.hidden)
     res = dc.res.view(w.rows, w.hidden) if dc.res is not None else None
-    for b in _sample_rows(w, 6, rng):
-        r0, r1 = b * W.BLOCK_ROWS, min(w.rows, (b + 1) * W.BLOCK_ROWS)
-        part = W.make_rows(w, r0, r1)
-        assert np.array_equal(part["input"], inputs["input"][r0:r1])
-        ref = U.oracle_rows(w, part, row_offset=r0)
+    threads = W.default_threads()
+    for r0 in range(0, w.rows, ORACLE_BLOCK):
+        r1 = min(w.rows, r0 + ORACLE_BLOCK)
+        part = dict(inputs)
+        part["input"] = inputs["input"][r0:r1]
+        if not w.broadcast:
+            part["skip"] = inputs["skip"][r0:r1]
+        ref = U.oracle_rows(w, part, row_offset=r0, threads=threads)
         U.assert_out_close(out[r0:r1].cpu().numpy(), ref["y"], w.dtype, f"out rows {r0}:{r1}")
         if res is not None:
             U.assert_bits_equal(res[r0:r1].cpu().numpy(), ref["residual"], f"residual rows {r0}:{r1}")
-
-    # Properties over all rows, on the device in float64 (test-side arithmetic).
-    g = torch.from_numpy(inputs["gamma"].astype(np.float64)).cuda()
-    b = torch.from_numpy(inputs["beta"].astype(np.float64)).cuda()
-    eps = float(np.float32(w.eps))
-    step = 4096
-    x_all = torch.from_numpy(inputs["input"])
-    s_all = torch.from_numpy(inputs["skip"])
-    for r0 in range(0, w.rows, step):
-        r1 = min(w.rows, r0 + step)
-        x = x_all[r0:r1].cuda().float()
-        if w.broadcast:
-            idx = torch.arange(r0, r1) % w.skip_rows
-            sk = s_all[idx].cuda().float()
-        else:
-            sk = s_all[r0:r1].cuda().float()
-        s32 = x + sk
-        if inputs["bias"] is not None:
-            s32 = s32 + torch.from_numpy(inputs["bias"]).cuda().float()
-        if res is not None:
-            want = s32.to(res.dtype)
-            assert torch.equal(res[r0:r1].view(torch.int16 if res.dtype == torch.float16 else torch.int32),
-                               want.view(torch.int16 if res.dtype == torch.float16 else torch.int32)), \
-                f"residual bits differ in rows {r0}:{r1}"
-        s64 = s32.double()
-        var = s64.var(dim=1, unbiased=False)
-        z = (out[r0:r1].double() - b) / g
-        atol = 2e-2 if w.dtype == "f16" else 1e-4
-        assert torch.all(z.mean(dim=1).abs() < atol), f"row means off in rows {r0}:{r1}"
-        assert torch.all((z.var(dim=1, unbiased=False) - var / (var + eps)).abs() < 2 * atol), \
-            f"row variances off in rows {r0}:{r1}"
 
 
 STORE_THROUGH_BYTES = 512 << 20  # launches writing this much store with the system-scope policy
