@@ -68,14 +68,18 @@ __global__ void __launch_bounds__(BLOCK)
         const int bytes = static_cast<int>((left < kStreamTile ? left : kStreamTile) * 16);
         const __amdgpu_buffer_rsrc_t r0 = device::buffer_rsrc(d0 + t0, bytes);
         const __amdgpu_buffer_rsrc_t r1 = device::buffer_rsrc(NW == 2 ? d1 + t0 : d0 + t0, bytes);
+        // The whole offset in the vector offset, the scalar offset zero: the
+        // compiler then keeps the data registers of each 16-byte store from
+        // being overwritten by the next instruction (it does not when the
+        // scalar offset is a register).
         const int voff = static_cast<int>(threadIdx.x) * 16;
 #pragma unroll
         for (int k = 0; k < kStreamCh; ++k) {
             const int64_t c = base + k * kStreamBlock;
             if (c < chunks) {
-                device::Elem<float>::store(v[k], r0, voff, k * kStreamBlock * 16, through != 0);
+                device::Elem<float>::store(v[k], r0, voff + k * kStreamBlock * 16, 0, through != 0);
                 if constexpr (NW == 2)
-                    device::Elem<float>::store(v[k] + u32x4{1u, 1u, 1u, 1u}, r1, voff, k * kStreamBlock * 16,
+                    device::Elem<float>::store(v[k] + u32x4{1u, 1u, 1u, 1u}, r1, voff + k * kStreamBlock * 16, 0,
                                                through != 0);
             }
         }
