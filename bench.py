@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "SkipLayerNorm rows/s and achieved HBM GB/s (% of MI355X peak) at H=768..8192"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published peak
 CACHE_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
+MI355X_CUS = 256  # compute units, for naming kernels offline (--summarize-counters)
 HEADLINE = "rows65536_h8192_f16_mean100"
 # Workloads that also get an oracle baseline when they run in the sweep.
 CPU_BASELINE_SWEEP = ("bcast_64x512x4096_f32",)
@@ -75,7 +76,7 @@ def parse_args(argv=None):
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the operator, time the streaming copy of this many bytes")
     p.add_argument("--stream-ceilings", type=int, default=0, metavar="BYTES",
-                   help="instead of the operator, time the streaming probe (skipln_stream) for every mix of "
+                   help="instead of the operator, time the streaming probe (skipln_tune_stream) for every mix of "
                         "0-2 read and 0-2 written streams of BYTES each")
     p.add_argument("--summarize-counters", metavar="DIR", default=None,
                    help="no GPU work: turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs under DIR "
@@ -149,7 +150,7 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     # Rows too long for one workgroup split across workgroups through a
     # workspace (one suffices: the steps run in order on one stream).
     ws_bytes = T.workspace_bytes(op, w.rows, w.hidden, code, mode, w.skip_rows if w.broadcast else 0, variant)
-    kernel = T.select_kernel(w.hidden, code, True, variant, mode, op, workspace=ws_bytes > 0)
+    kernel = T.select_kernel(w.hidden, code, True, variant, mode, op, workspace=ws_bytes > 0, rows=w.rows)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
     # how many buffer copies keep the working set above the cache.
@@ -249,15 +250,15 @@ def time_copy(nbytes: int, steps: int, warmup: int):
     nbytes -= nbytes % 16
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255)
     dst = torch.empty_like(src)
-    lib = L.load()
+    lib = L.load_tune()
     s = torch.cuda.current_stream().cuda_stream
     for _ in range(warmup):
-        L.check(lib.skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_copy")
+        L.check(lib.skipln_tune_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_tune_copy")
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for _ in range(steps):
-        L.check(lib.skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_copy")
+        L.check(lib.skipln_tune_copy(dst.data_ptr(), src.data_ptr(), nbytes, s), "skipln_tune_copy")
     ev1.record()
     torch.cuda.synchronize()
     assert torch.equal(src, dst), "copy mismatch"
@@ -285,7 +286,7 @@ def time_streams(nbytes: int, steps: int, warmup: int):
     from transformer_residual_add_amd import _lib as L
 
     nbytes -= nbytes % 16
-    lib = L.load()
+    lib = L.load_tune()
     bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
     s = torch.cuda.current_stream().cuda_stream
     out = []
@@ -301,8 +302,8 @@ def time_streams(nbytes: int, steps: int, warmup: int):
             for (block, per_lane, granule), through in [(sh, t) for sh in STREAM_SHAPES for t in (0, 1)
                                                         if writes or not t]:
                 def launch():
-                    L.check(lib.skipln_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane, granule,
-                                              through, s), "skipln_stream")
+                    L.check(lib.skipln_tune_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane,
+                                                   granule, through, s), "skipln_tune_stream")
 
                 for _ in range(warmup):
                     launch()
@@ -463,7 +464,8 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
         w = W.get(name)
         code = L.F32 if w.dtype == "f32" else L.F16
         ws = T.workspace_bytes(OPS[w.op], w.rows, w.hidden, code, skip_mode(w, L), w.skip_rows if w.broadcast else 0)
-        kernel = T.select_kernel(w.hidden, code, True, 0, skip_mode(w, L), OPS[w.op], workspace=ws > 0)
+        kernel = T.select_kernel(w.hidden, code, True, 0, skip_mode(w, L), OPS[w.op], workspace=ws > 0,
+                                 rows=w.rows, cus=MI355X_CUS)
         f, n = lib_median(name, "FETCH_SIZE")
         wr, _ = lib_median(name, "WRITE_SIZE")
         fb, wb = int(round(f * 1024 * fetch_scale)), int(round(wr * 1024 * write_scale))
@@ -476,7 +478,7 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
         print(f"| {name} | {kernel} | {f:,.1f} | {wr:,.1f} | {fb:,} | {wb:,} | {(fb + wb) / alg:.3f} |")
     data = {
         "about": "HBM bytes per dispatch from rocprofv3 FETCH_SIZE and WRITE_SIZE (separate --pmc runs), each "
-                 "scaled by what the same counter reads for the streaming copy of 1 GiB (skipln_copy: 1 GiB "
+                 "scaled by what the same counter reads for the streaming copy of 1 GiB (skipln_tune_copy: 1 GiB "
                  "read, 1 GiB written). source_sha256 hashes the sources that define the kernel (`sources`) as they "
                  "were when the counters were taken.",
         "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
@@ -508,6 +510,7 @@ def main(argv=None) -> int:
         print("bench.py needs a HIP GPU", file=sys.stderr)
         return 1
     L.load()
+    L.load_tune()
     torch.cuda.set_device(0)
 
     if args.copy_bytes:

@@ -53,6 +53,13 @@ def torch_dtype(dt: str):
     return {"f32": torch.float32, "f16": torch.float16}[dt]
 
 
+def select(op: int, hidden: int, code: int, mode: int = L.SKIP_EXACT, aligned: int = 1,
+           variant: int = L.VARIANT_AUTO, workspace: int = 0, rows: int = -1) -> int:
+    """Kernel id the tuning library's choice gives for a call on the current
+    device (negative: a status)."""
+    return L.load_tune().skipln_tune_select(op, rows, hidden, code, mode, aligned, variant, workspace, 0)
+
+
 def note(msg: str) -> None:
     """Name the case on stdout before a GPU step (flushed)."""
     print(msg, flush=True)
@@ -122,14 +129,15 @@ class DeviceCase:
                       w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
                       stream, variant, OPS[w.op], workspace=workspace)
 
-    def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0):
+    def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0,
+                   store: int = L.STORE_AUTO):
         w = self.w
         p = lambda t: None if t is None else t.data_ptr()
-        st = L.load().skipln_forward_config(
-            OPS[w.op], p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(self.out), p(self.res),
-            w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16, geometry,
-            tiles_per_block, strided, stream or None)
-        L.check(st, "skipln_forward_config")
+        st = L.load_tune().skipln_tune_forward_config(
+            OPS[w.op], p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma),
+            p(self.beta), p(self.bias), p(self.out), p(self.res), w.rows, w.hidden, float(np.float32(w.eps)),
+            L.F32 if w.dtype == "f32" else L.F16, geometry, tiles_per_block, strided, store, stream or None)
+        L.check(st, "skipln_tune_forward_config")
 
     def host(self, t):
         import torch

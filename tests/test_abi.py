@@ -1,10 +1,12 @@
-"""The C ABI on the CPU: libskipln.so loads, exports every function that
-include/skipln.h declares, its enums match the Python binding, and every
-argument check is reachable from the host (skipln_validate / skipln_select
-make no HIP call)."""
+"""The C ABIs on the CPU: libskipln.so and libskipln_tune.so load, export
+exactly the functions their headers declare (include/skipln.h,
+include/skipln_tune.h), their enums match the Python binding, and every
+argument check is reachable from the host (the validate, select and
+workspace-size entry points make no HIP call)."""
 import math
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -12,26 +14,63 @@ from transformer_residual_add_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "skipln.h")
+TUNE_HEADER = os.path.join(ROOT, "include", "skipln_tune.h")
 
 
-def _header():
-    with open(HEADER) as fh:
+def _read(path):
+    with open(path) as fh:
         return fh.read()
 
 
-def test_header_functions_are_exported_and_bound():
-    text = _header()
-    declared = set(re.findall(r"^(?:int|int64_t|const char\*)\s+(skipln_\w+)\s*\(", text, re.M))
+def _declared(text):
+    return set(re.findall(r"^SKIPLN_API\s+(?:int|int64_t|const char\*)\s+(skipln_\w+)\s*\(", text, re.M))
+
+
+def _exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+@pytest.mark.parametrize("header,signatures,loader,path", [
+    (HEADER, L.SIGNATURES, L.load, L.LIB_PATH),
+    (TUNE_HEADER, L.TUNE_SIGNATURES, L.load_tune, L.TUNE_LIB_PATH),
+], ids=["operator", "tune"])
+def test_header_functions_are_the_only_exports(header, signatures, loader, path):
+    declared = _declared(_read(header))
     assert declared, "no declarations found"
-    assert declared == set(L.SIGNATURES), f"binding and header differ: {declared ^ set(L.SIGNATURES)}"
-    lib = L.load()
+    assert declared == set(signatures), f"binding and header differ: {declared ^ set(signatures)}"
+    lib = loader()
     for name in declared:
         assert hasattr(lib, name), f"{name} not exported"
-    assert lib.skipln_version() == 1
+    assert _exported(path) == declared, f"exports differ from the header: {_exported(path) ^ declared}"
+
+
+def test_operator_surface():
+    """The operator library's surface: the operator, its argument checks,
+    the three operations beside it, the workspace form, status strings."""
+    assert set(L.SIGNATURES) == {
+        "skipln_forward", "skipln_validate", "skipln_status_string", "skipln_version",
+        "skipln_forward_simplified", "skipln_bias_add", "skipln_bias_softmax",
+        "skipln_forward_ws", "skipln_workspace_bytes"}
+    assert L.load().skipln_version() == 2
+
+
+def test_validate_takes_the_forward_arguments():
+    """skipln_validate takes skipln_forward's arguments, the stream aside."""
+    text = _read(HEADER)
+
+    def params(name):
+        m = re.search(r"SKIPLN_API int " + name + r"\((.*?)\);", text, re.S)
+        return [p.strip() for p in " ".join(m.group(1).split()).split(",")]
+
+    fwd, val = params("skipln_forward"), params("skipln_validate")
+    assert fwd[-1] == "skipln_stream_t stream"
+    norm = lambda ps: [p.replace("const ", "") for p in ps]
+    assert norm(val) == norm(fwd[:-1])
 
 
 def test_header_enums_match_binding():
-    vals = {k: int(v) for k, v in re.findall(r"(SKIPLN_\w+)\s*=\s*(\d+)", _header())}
+    vals = {k: int(v) for k, v in re.findall(r"(SKIPLN_\w+)\s*=\s*(-?\d+)", _read(HEADER) + _read(TUNE_HEADER))}
     expect = {
         "SKIPLN_F32": L.F32, "SKIPLN_F16": L.F16,
         "SKIPLN_SKIP_EXACT": L.SKIP_EXACT, "SKIPLN_SKIP_BROADCAST": L.SKIP_BROADCAST,
@@ -51,6 +90,8 @@ def test_header_enums_match_binding():
         "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
+        "SKIPLN_STORE_AUTO": L.STORE_AUTO, "SKIPLN_STORE_STREAM": L.STORE_STREAM,
+        "SKIPLN_STORE_THROUGH": L.STORE_THROUGH,
     }
     assert vals == expect
 
@@ -67,8 +108,16 @@ IN, SK, GA, BE, BI, OUT, RES = (0x100000 * k for k in range(1, 8))
 
 def V(input=IN, skip=SK, mode=0, skip_rows=0, gamma=GA, beta=BE, bias=BI, out=OUT, res=RES, rows=4, hidden=8,
       eps=1e-5, dtype=0, op=L.OP_LAYER_NORM):
-    return L.load().skipln_validate(op, input, skip, mode, skip_rows, gamma, beta, bias, out, res, rows, hidden, eps,
-                                    dtype)
+    """The layer norm's checks through the operator library's skipln_validate;
+    the other operations' through the tuning library's op-aware validate
+    (the two must agree on the layer norm)."""
+    args = (input, skip, mode, skip_rows, gamma, beta, bias, out, res, rows, hidden, eps, dtype)
+    tuned = L.load_tune().skipln_tune_validate(op, *args)
+    if op == L.OP_LAYER_NORM:
+        st = L.load().skipln_validate(*args)
+        assert st == tuned
+        return st
+    return tuned
 
 
 def test_validate_accepts_good_arguments():
@@ -186,9 +235,16 @@ def test_validate_allows_exact_aliasing():
     assert V(beta=None, out=BE) == L.OK      # an absent beta occupies no memory
 
 
+CUS = 256  # MI355X compute units, given explicitly: select then makes no HIP call
+
+
+def SEL(op, h, dt, mode=L.SKIP_EXACT, al=1, v=L.VARIANT_AUTO, ws=0, rows=-1, cus=CUS):
+    return L.load_tune().skipln_tune_select(op, rows, h, dt, mode, al, v, ws, cus)
+
+
 def test_select_kernels():
-    lib = L.load()
-    sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT, op=L.OP_LAYER_NORM: lib.skipln_select(op, h, dt, mode, al, v)
+    lib = L.load_tune()
+    sel = lambda h, dt, al=1, v=0, mode=L.SKIP_EXACT, op=L.OP_LAYER_NORM: SEL(op, h, dt, mode, al, v)
     name = lambda kid: L.kernel_name(kid)
     assert name(sel(768, 0)) == "rowtile_f32_g192_c1_b192"
     assert name(sel(1024, 1)) == "rowtile_f16_g64_c2"                 # one wavefront per row
@@ -211,8 +267,8 @@ def test_select_kernels():
     assert name(sel(1000, 0, v=L.VARIANT_ELEMENT)) == "rowelem_f32_g128_c8"
     assert sel(1000, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED   # 4 elements
     assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0)) == "rowelem_f32_g4_c1"
-    ne = lib.skipln_element_geometries()
-    assert ne >= 13
+    ne = lib.skipln_tune_element_geometries()
+    assert ne == 13
     assert sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + ne) == -L.ERR_VARIANT
     for g in range(ne):
         assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + g)).startswith("rowelem_f32_g")
@@ -221,8 +277,8 @@ def test_select_kernels():
     assert name(sel(8, 1, v=1)) == "generic_f16"
     assert sel(1001, 0, v=L.VARIANT_ROWTILE) == -L.ERR_UNSUPPORTED
     assert name(sel(64, 0, v=L.VARIANT_MULTIWAVE)).startswith("rowtile_f32_g128")
-    ng = lib.skipln_rowtile_geometries()
-    assert ng >= 13
+    ng = lib.skipln_tune_rowtile_geometries()
+    assert ng == 23
     for g in range(ng):
         kid = sel(16, 0, v=L.VARIANT_GEOMETRY + g)   # 4 chunks: every geometry holds them
         assert kid >= 0 and name(kid).startswith("rowtile_f32_g")
@@ -262,27 +318,52 @@ def test_select_kernels():
     assert L.kernel_name(-1) == "unknown" and L.kernel_name(10 ** 6) == "unknown"
 
 
+def test_every_geometry_is_an_automatic_choice():
+    """Each row-tile and element-wise geometry is what the automatic choice
+    takes for some operation, type, skip form and row length."""
+    lib = L.load_tune()
+    used, used_elem = set(), set()
+    for op in (L.OP_LAYER_NORM, L.OP_BIAS_ADD, L.OP_BIAS_SOFTMAX):
+        for dt, v in ((0, 4), (1, 8)):
+            for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST):
+                if op == L.OP_BIAS_ADD and mode != L.SKIP_EXACT:
+                    continue
+                for hv in range(1, 4097):
+                    used.add(L.kernel_name(SEL(op, hv * v, dt, mode)).split("_", 1)[-1].replace("rowtile_", "")
+                             .split("_", 1)[-1])
+            for h in range(1, 16385):
+                n = L.kernel_name(SEL(op, h, dt, al=0))
+                if "rowelem_" in n:
+                    used_elem.add(n.split("rowelem_")[1].split("_", 1)[1])
+    names = {L.kernel_name(SEL(L.OP_LAYER_NORM, 4, 0, v=L.VARIANT_GEOMETRY + g)).split("rowtile_f32_")[1]
+             for g in range(lib.skipln_tune_rowtile_geometries())}
+    assert names <= used, f"geometries no automatic choice takes: {names - used}"
+    elems = {L.kernel_name(SEL(L.OP_LAYER_NORM, 1, 0, al=0, v=L.VARIANT_ELEMENT_GEOMETRY + g)).split("rowelem_f32_")[1]
+             for g in range(lib.skipln_tune_element_geometries())}
+    assert elems <= used_elem, f"element geometries no automatic choice takes: {elems - used_elem}"
+
+
 def test_auto_choice_holds_every_hidden_size():
     """The automatic choice exists for every chunked hidden size up to the
     row-tile limit, holds the row, and is monotone in capacity."""
-    lib = L.load()
+    lib = L.load_tune()
     for dt, v in ((0, 4), (1, 8)):
         for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST):
             for hv in range(1, 2049):
-                kid = lib.skipln_select(L.OP_LAYER_NORM, hv * v, dt, mode, 1, 0)
+                kid = SEL(L.OP_LAYER_NORM, hv * v, dt, mode)
                 assert kid >= 0 and L.kernel_name(kid).startswith("rowtile_"), (dt, mode, hv)
                 n = L.kernel_name(kid)
                 g = int(n.split("_g")[1].split("_")[0])
                 c = int(n.split("_c")[1].split("_")[0])
                 assert g * c >= hv
             for hv in range(2049, 4097):
-                kid = lib.skipln_select(L.OP_BIAS_ADD, hv * v, dt, mode and 0, 1, 0)
+                kid = SEL(L.OP_BIAS_ADD, hv * v, dt)
                 n = L.kernel_name(kid)
                 assert n.startswith("biasadd_rowtile_"), (dt, hv, n)
-            assert L.kernel_name(lib.skipln_select(L.OP_BIAS_ADD, 4097 * v, dt, 0, 1, 0)).startswith("biasadd_generic_")
+            assert L.kernel_name(SEL(L.OP_BIAS_ADD, 4097 * v, dt)).startswith("biasadd_generic_")
         for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST, L.SKIP_BROADCAST_INNER):
             for hv in range(1, 2049):
-                n = L.kernel_name(lib.skipln_select(L.OP_BIAS_SOFTMAX, hv * v, dt, mode, 1, 0))
+                n = L.kernel_name(SEL(L.OP_BIAS_SOFTMAX, hv * v, dt, mode))
                 assert n.startswith("softmax_rowtile_"), (dt, mode, hv, n)
                 g = int(n.split("_g")[1].split("_")[0])
                 c = int(n.split("_c")[1].split("_")[0])
@@ -303,66 +384,71 @@ def test_no_cpu_fallback_in_product_path():
 # ------------------------------------------------------------- workspace --
 
 def test_workspace_sizes_and_split_selection():
-    lib = L.load()
-    wb = lambda op, rows, h, dt, mode=L.SKIP_EXACT, srows=0, v=L.VARIANT_AUTO: \
-        lib.skipln_workspace_bytes(op, rows, h, dt, mode, srows, v)
-    name_ws = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: \
-        L.kernel_name(lib.skipln_select_ws(op, h, dt, mode, 1, v))
-    name = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select(op, h, dt, mode, 1, v))
-    # header (16 B) + one arrival counter per row (padded to 16 B) + one float4
-    # partial per slice; 65536 float32 = 16 slices of 4096
+    lib, tune = L.load(), L.load_tune()
+    wb = lambda op, rows, h, dt, mode=L.SKIP_EXACT, srows=0: lib.skipln_workspace_bytes(op, rows, h, dt, mode, srows)
+    wbv = lambda op, rows, h, dt, mode=L.SKIP_EXACT, srows=0, v=L.VARIANT_AUTO: \
+        tune.skipln_tune_workspace_bytes(op, rows, h, dt, mode, srows, v)
+    name = lambda op, h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT, ws=0, rows=-1, cus=CUS: \
+        L.kernel_name(SEL(op, h, dt, mode, 1, v, ws, rows, cus))
     # one float4 partial per slice of a batch of rows; a batch streams at most
     # 128 MiB of inputs (x, and skip when it is not broadcast)
     ws = lambda rows, slices: rows * slices * 16
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == ws(64, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, v=L.VARIANT_SPLITROW) == ws(256, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8, L.VARIANT_SPLITROW) == ws(512, 16)
-    # 256 rows or more (a row for every CU): RMS, and float32 layer norm up to
-    # 65536 values, take the generic kernel, which needs no workspace
+    assert wbv(L.OP_LAYER_NORM, 1000, 65536, L.F32, v=L.VARIANT_SPLITROW) == ws(256, 16)
+    assert wbv(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8, L.VARIANT_SPLITROW) == ws(512, 16)
+    # the operator library's size does not depend on the device: whatever the
+    # row count, a call that may split its rows gets the split-row size
     assert wb(L.OP_LAYER_NORM, 255, 65536, L.F32) == ws(255, 16)
-    assert wb(L.OP_LAYER_NORM, 256, 65536, L.F32) == 0
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == 0
-    assert wb(L.OP_LAYER_NORM, 256, 65540, L.F32) > 0                    # split rows beyond 65536
+    assert wb(L.OP_LAYER_NORM, 256, 65536, L.F32) == ws(256, 16)
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == ws(512, 16)
     assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F16) == ws(512, 8)
     assert wb(L.OP_SIMPLIFIED, 255, 262144, L.F32) == ws(64, 64)
-    assert wb(L.OP_SIMPLIFIED, 256, 262144, L.F32) == 0
-    assert wb(L.OP_SIMPLIFIED, 4096, 65536, L.F16) == 0
     assert wb(L.OP_BIAS_SOFTMAX, 1024, 163848, L.F16) > 0
     assert wb(L.OP_LAYER_NORM, 201, 65540, L.F32) == ws(201, 17)
     assert wb(L.OP_LAYER_NORM, 0, 65536, L.F32) == 0
     assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32) == 0                       # row tiles need none
     assert wb(L.OP_LAYER_NORM, 64, 20000, L.F32) == 0                      # LDS-staged
-    assert wb(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_SPLITROW) == ws(64, 1)
-    assert wb(L.OP_BIAS_ADD, 64, 65536, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert wbv(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_SPLITROW) == ws(64, 1)
+    assert wbv(L.OP_BIAS_ADD, 64, 65536, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert wbv(L.OP_LAYER_NORM, 64, 4096, L.F32, v=L.VARIANT_GENERIC) == 0
     assert wb(L.OP_LAYER_NORM, 64, 65536, 9) == -L.ERR_DTYPE
     assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32, L.SKIP_BROADCAST, 3) == -L.ERR_SHAPE
+    assert wb(7, 64, 65536, L.F32) == -L.ERR_OP
     assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 0     # held in registers
-    assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4, L.VARIANT_SPLITROW) == ws(64, 16)
+    assert wbv(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4, L.VARIANT_SPLITROW) == ws(64, 16)
     assert wb(L.OP_BIAS_SOFTMAX, 64, 163848, L.F16) == ws(64, 21)                     # beyond the registers
-    # the automatic choice: split rows only where a workspace is at hand
+    # the automatic choice: split rows only where a workspace is at hand ...
     assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
-    assert name_ws(L.OP_LAYER_NORM, 65536, L.F32) == "splitrow_f32"
-    assert name_ws(L.OP_SIMPLIFIED, 65536, L.F16) == "rms_splitrow_f16"
-    assert name_ws(L.OP_BIAS_SOFTMAX, 128256, L.F16) == "softmax_regrow_f16"
-    assert name_ws(L.OP_BIAS_SOFTMAX, 163848, L.F16) == "softmax_splitrow_f16"
-    assert name_ws(L.OP_LAYER_NORM, 20000, L.F32) == "ldsrow_f32"
-    assert name_ws(L.OP_LAYER_NORM, 4096, L.F32) == "rowtile_f32_g256_c4"
-    assert name_ws(L.OP_LAYER_NORM, 64 * 4096, L.F32) == "splitrow_f32"        # 64 slices
-    assert name_ws(L.OP_LAYER_NORM, 64 * 4096 + 4, L.F32) == "generic_f32"     # 65 slices
-    assert name_ws(L.OP_BIAS_ADD, 65536, L.F32) == "biasadd_generic_f32"
+    assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1) == "splitrow_f32"
+    assert name(L.OP_SIMPLIFIED, 65536, L.F16, ws=1) == "rms_splitrow_f16"
+    # ... and with fewer rows than the device has compute units: from one row
+    # per CU, RMS and float32 layer norm up to 65536 values run generic
+    for cus in (256, 80):
+        assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1, rows=cus - 1, cus=cus) == "splitrow_f32"
+        assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1, rows=cus, cus=cus) == "generic_f32"
+        assert name(L.OP_SIMPLIFIED, 262144, L.F32, ws=1, rows=cus, cus=cus) == "rms_generic_f32"
+        assert name(L.OP_SIMPLIFIED, 262144, L.F32, ws=1, rows=cus - 1, cus=cus) == "rms_splitrow_f32"
+    assert name(L.OP_LAYER_NORM, 65540, L.F32, ws=1, rows=1000) == "splitrow_f32"       # beyond 65536
+    assert name(L.OP_LAYER_NORM, 65536, L.F16, ws=1, rows=1000) == "splitrow_f16"       # float16 keeps it
+    assert name(L.OP_BIAS_SOFTMAX, 128256, L.F16, ws=1) == "softmax_regrow_f16"
+    assert name(L.OP_BIAS_SOFTMAX, 163848, L.F16, ws=1) == "softmax_splitrow_f16"
+    assert name(L.OP_LAYER_NORM, 20000, L.F32, ws=1) == "ldsrow_f32"
+    assert name(L.OP_LAYER_NORM, 4096, L.F32, ws=1) == "rowtile_f32_g256_c4"
+    assert name(L.OP_LAYER_NORM, 64 * 4096, L.F32, ws=1) == "splitrow_f32"        # 64 slices
+    assert name(L.OP_LAYER_NORM, 64 * 4096 + 4, L.F32, ws=1) == "generic_f32"     # 65 slices
+    assert name(L.OP_BIAS_ADD, 65536, L.F32, ws=1) == "biasadd_generic_f32"
     assert name(L.OP_LAYER_NORM, 64, L.F32, v=L.VARIANT_SPLITROW) == "splitrow_f32"
-    assert lib.skipln_select(L.OP_BIAS_ADD, 64, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
-    assert lib.skipln_select(L.OP_LAYER_NORM, 66, L.F32, 0, 1, L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert SEL(L.OP_BIAS_ADD, 64, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
+    assert SEL(L.OP_LAYER_NORM, 66, L.F32, v=L.VARIANT_SPLITROW) == -L.ERR_UNSUPPORTED
 
 
 def test_register_resident_softmax_selection():
     """BiasSoftmax rows beyond the LDS capacity and up to 20 chunks per lane
     of a 1024-lane block are held in registers, with or without a
     workspace; the family takes only 16-byte chunks of BiasSoftmax."""
-    lib = L.load()
     name = lambda h, dt, v=L.VARIANT_AUTO, mode=L.SKIP_EXACT, op=L.OP_BIAS_SOFTMAX, al=1: \
-        L.kernel_name(lib.skipln_select(op, h, dt, mode, al, v))
-    name_ws = lambda h, dt, mode=L.SKIP_EXACT: L.kernel_name(lib.skipln_select_ws(L.OP_BIAS_SOFTMAX, h, dt, mode, 1, 0))
+        L.kernel_name(SEL(op, h, dt, mode, al, v))
+    name_ws = lambda h, dt, mode=L.SKIP_EXACT: L.kernel_name(SEL(L.OP_BIAS_SOFTMAX, h, dt, mode, ws=1))
     for mode in (L.SKIP_EXACT, L.SKIP_BROADCAST, L.SKIP_BROADCAST_INNER):
         assert name(40896, L.F32, mode=mode) == "softmax_ldsrow_f32"
         assert name(40900, L.F32, mode=mode) == "softmax_regrow_f32"
@@ -379,26 +465,29 @@ def test_register_resident_softmax_selection():
     assert name(8, L.F32, v=L.VARIANT_REGROW) == "softmax_regrow_f32"
     assert name(4096, L.F16, v=L.VARIANT_REGROW) == "softmax_regrow_f16"
     unsupported = -L.ERR_UNSUPPORTED
-    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 81924, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported
-    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 77, L.F32, 0, 1, L.VARIANT_REGROW) == unsupported    # not chunks
-    assert lib.skipln_select(L.OP_BIAS_SOFTMAX, 4096, L.F32, 0, 0, L.VARIANT_REGROW) == unsupported  # misaligned
+    assert SEL(L.OP_BIAS_SOFTMAX, 81924, L.F32, v=L.VARIANT_REGROW) == unsupported
+    assert SEL(L.OP_BIAS_SOFTMAX, 77, L.F32, v=L.VARIANT_REGROW) == unsupported    # not chunks
+    assert SEL(L.OP_BIAS_SOFTMAX, 4096, L.F32, al=0, v=L.VARIANT_REGROW) == unsupported  # misaligned
     for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED, L.OP_BIAS_ADD):
-        assert lib.skipln_select(op, 65536, L.F16, 0, 1, L.VARIANT_REGROW) == unsupported
+        assert SEL(op, 65536, L.F16, v=L.VARIANT_REGROW) == unsupported
     # misaligned long rows take the generic kernel
     assert name(65536, L.F16, al=0) == "softmax_generic_f16"
 
 
-def FW(ws, nbytes, hidden=65536, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM):
-    return L.load().skipln_forward_ws(op, IN, SK, 0, 0, GA, BE, BI, OUT, RES, 4, hidden, 1e-5, L.F32, variant, ws,
-                                      nbytes, None)
+def FW(ws, nbytes, hidden=65536, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM, res=RES):
+    """skipln_forward_ws (automatic choice) or the tuning library's forced
+    family, on fake pointers: every status here returns before any HIP call."""
+    args = (IN, SK, 0, 0, GA, BE, BI, OUT, res, 4, hidden, 1e-5, L.F32)
+    if variant == L.VARIANT_AUTO:
+        return L.load().skipln_forward_ws(op, *args, ws, nbytes, None)
+    return L.load_tune().skipln_tune_forward(op, *args, variant, ws, nbytes, None)
 
 
 WS = 0x10000000  # beyond every fake tensor (4 rows of 65536 float32 = 1 MiB each)
 
 
 def test_forward_ws_workspace_checks():
-    """Each status here returns before any HIP call."""
-    need = L.load().skipln_workspace_bytes(L.OP_LAYER_NORM, 4, 65536, L.F32, 0, 0, 0)
+    need = L.load().skipln_workspace_bytes(L.OP_LAYER_NORM, 4, 65536, L.F32, 0, 0)
     assert need == 4 * 16 * 16
     assert FW(None, 0) == L.ERR_WORKSPACE
     assert FW(WS, need - 1) == L.ERR_WORKSPACE
@@ -409,14 +498,29 @@ def test_forward_ws_workspace_checks():
     assert FW(WS, need, variant=L.VARIANT_LDSROW) == L.ERR_UNSUPPORTED
     assert FW(None, 0, hidden=64, variant=L.VARIANT_SPLITROW) == L.ERR_WORKSPACE
     assert FW(WS, need, op=L.OP_BIAS_ADD, variant=L.VARIANT_SPLITROW) == L.ERR_UNSUPPORTED
+    assert FW(WS, need, variant=99) == L.ERR_VARIANT
     # a residual over the input cannot take the split-row kernels (they read x twice)
-    assert L.load().skipln_forward_ws(L.OP_LAYER_NORM, IN, SK, 0, 0, GA, BE, BI, OUT, IN, 4, 65536, 1e-5, L.F32,
-                                      L.VARIANT_SPLITROW, WS, need, None) == L.ERR_UNSUPPORTED
+    assert FW(WS, need, variant=L.VARIANT_SPLITROW, res=IN) == L.ERR_UNSUPPORTED
+    assert L.load().skipln_forward_ws(9, IN, SK, 0, 0, GA, BE, BI, OUT, RES, 4, 8, 1e-5, L.F32, WS, need, None) \
+        == L.ERR_OP
+
+
+def test_forward_config_argument_checks():
+    """skipln_tune_forward_config rejects these before any HIP call."""
+    cfg = lambda geom=0, tpb=1, tiling=0, store=L.STORE_AUTO: L.load_tune().skipln_tune_forward_config(
+        L.OP_LAYER_NORM, IN, SK, 0, 0, GA, BE, BI, OUT, RES, 4, 64, 1e-5, L.F32, geom, tpb, tiling, store, None)
+    assert cfg(tpb=-1) == L.ERR_SHAPE
+    assert cfg(tiling=3) == L.ERR_VARIANT
+    assert cfg(store=2) == L.ERR_VARIANT and cfg(store=-2) == L.ERR_VARIANT
+    assert cfg(geom=-2) == L.ERR_VARIANT
+    assert cfg(geom=L.load_tune().skipln_tune_rowtile_geometries()) == L.ERR_VARIANT
+    assert cfg(geom=L.VARIANT_ELEMENT_GEOMETRY + L.load_tune().skipln_tune_element_geometries()) == L.ERR_VARIANT
 
 
 def test_stream_probe_argument_checks():
-    """skipln_stream returns these statuses before any HIP call."""
-    st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load().skipln_stream(s0, s1, d0, d1, n, b,
+    """skipln_tune_stream returns these statuses before any HIP call."""
+    st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load_tune().skipln_tune_stream(s0, s1, d0,
+                                                                                                 d1, n, b,
                                                                                                  u, g, 0, None)
     assert st(s0=None, d0=None) == L.ERR_NULL
     assert st(s0=None, s1=SK) == L.ERR_NULL

@@ -133,27 +133,28 @@ def test_hidden_sizes(dt, hidden):
     U.check_case(w)
 
 
+ROWTILE_GEOMETRIES = range(L.load_tune().skipln_tune_rowtile_geometries())
+ELEMENT_GEOMETRIES = range(L.load_tune().skipln_tune_element_geometries())
+
+
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("geom", list(range(48)))
+@pytest.mark.parametrize("geom", ROWTILE_GEOMETRIES)
 @pytest.mark.parametrize("ragged", [False, True])
 @pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])
 def test_every_geometry(dt, geom, ragged, op):
     """Each row-tile geometry, for each operation, at its full capacity and
     one chunk short of it, with a ragged last tile of rows."""
     op_code = U.OPS[op]
-    lib = L.load()
-    if geom >= lib.skipln_rowtile_geometries():
-        pytest.skip("geometry not present")
     v = 4 if dt == "f32" else 8
     code = L.F32 if dt == "f32" else L.F16
     # capacity in chunks: the largest hidden size the geometry accepts
     cap = 0
     for hv in range(1, 4097):
-        if lib.skipln_select(L.OP_LAYER_NORM, hv * v, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom) < 0:
+        if U.select(L.OP_LAYER_NORM, hv * v, code, variant=L.VARIANT_GEOMETRY + geom) < 0:
             break
         cap = hv
     hidden = (cap - 1 if ragged and cap > 1 else cap) * v
-    name = L.kernel_name(lib.skipln_select(op_code, hidden, code, L.SKIP_EXACT, 1, L.VARIANT_GEOMETRY + geom))
+    name = L.kernel_name(U.select(op_code, hidden, code, variant=L.VARIANT_GEOMETRY + geom))
     g = int(name.split("_g")[1].split("_")[0])
     block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
     rpb = block // g
@@ -165,25 +166,22 @@ def test_every_geometry(dt, geom, ragged, op):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("geom", list(range(24)))
+@pytest.mark.parametrize("geom", ELEMENT_GEOMETRIES)
 @pytest.mark.parametrize("shape", ["full", "odd", "short"])
 @pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])
 def test_every_element_geometry(dt, geom, shape, op):
     """Each element-wise row-tile geometry, for each operation: at its full
     capacity, at an odd length just below, and at a quarter (idle lanes),
     with a ragged last tile of rows and a broadcast skip."""
-    lib = L.load()
-    if geom >= lib.skipln_element_geometries():
-        pytest.skip("geometry not present")
     code = L.F32 if dt == "f32" else L.F16
     cap = 0
     for h in (16384, 8192, 4096, 2048, 1024, 512, 256, 128, 64, 32, 16, 8, 4, 2, 1):
-        if lib.skipln_select(L.OP_LAYER_NORM, h, code, L.SKIP_EXACT, 1, L.VARIANT_ELEMENT_GEOMETRY + geom) >= 0:
+        if U.select(L.OP_LAYER_NORM, h, code, variant=L.VARIANT_ELEMENT_GEOMETRY + geom) >= 0:
             cap = h
             break
     hidden = {"full": cap, "odd": max(1, cap - 1), "short": max(1, cap // 4 + 1)}[shape]
     variant = L.VARIANT_ELEMENT_GEOMETRY + geom
-    name = L.kernel_name(lib.skipln_select(U.OPS[op], hidden, code, L.SKIP_EXACT, 1, variant))
+    name = L.kernel_name(U.select(U.OPS[op], hidden, code, variant=variant))
     g = int(name.split("_g")[1].split("_")[0])
     block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
     rows = 3 * (block // g) + 1 if hidden <= 4096 else 9
@@ -196,7 +194,7 @@ def test_every_element_geometry(dt, geom, shape, op):
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (3, 1), (0, 2), (2, 2)], ids=lambda t: f"tpb{t[0]}_m{t[1]}")
-@pytest.mark.parametrize("geom_hidden", [(0, 3), (5, 77), (8, 1000), (13, 63)], ids=lambda g: f"e{g[0]}_h{g[1]}")
+@pytest.mark.parametrize("geom_hidden", [(0, 3), (5, 77), (8, 1000), (4, 63)], ids=lambda g: f"e{g[0]}_h{g[1]}")
 def test_element_launch_configs(dt, tiling, geom_hidden):
     geom, hidden = geom_hidden
     w = W.small_case(203, hidden, dt, skip_rows=7, beta=True, bias=True, residual=True, eps=1e-5, seed=31)
@@ -238,7 +236,7 @@ def test_many_rows_small_hidden(dt):
 @pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (1, 1), (3, 0), (3, 1), (7, 0), (1000, 1), (0, 0), (0, 2),
                                     (1, 2), (2, 2), (5, 2), (1000, 2)],
                          ids=lambda t: f"tpb{t[0]}_m{t[1]}")
-@pytest.mark.parametrize("geom_hidden", [(-1, 1024), (0, 48), (8, 4000), (14, 768)],
+@pytest.mark.parametrize("geom_hidden", [(-1, 1024), (0, 48), (7, 4000), (13, 768)],
                          ids=lambda g: f"g{g[0]}_h{g[1]}")
 def test_launch_configs(dt, tiling, geom_hidden):
     """Every tiling (persistent, contiguous, strided, more tiles per block
@@ -257,8 +255,8 @@ def test_launch_configs(dt, tiling, geom_hidden):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
-@pytest.mark.parametrize("geom,hidden,S,batches", [(18, 4096, 8, 13), (13, 512, 6, 5), (0, 64, 32, 5), (0, 64, 24, 3),
-                                                    (8, 2048, 1, 9), (22, 768, 5, 4)])
+@pytest.mark.parametrize("geom,hidden,S,batches", [(7, 4096, 8, 13), (12, 512, 6, 5), (0, 64, 32, 5), (0, 64, 24, 3),
+                                                    (7, 2048, 1, 9), (15, 768, 5, 4)])
 @pytest.mark.parametrize("tpb", [0, 1, 3])
 def test_skip_stationary_tiles(dt, geom, hidden, S, batches, tpb):
     """Broadcast skip with blocks that keep their skip rows across batches,
@@ -282,7 +280,7 @@ def test_launch_config_errors():
         dc.run_config(0, -1, 0)
     assert e.value.status == L.ERR_SHAPE
     with pytest.raises(T.SkiplnError) as e:
-        dc.run_config(L.load().skipln_rowtile_geometries(), 1, 0)
+        dc.run_config(L.load_tune().skipln_tune_rowtile_geometries(), 1, 0)
     assert e.value.status == L.ERR_VARIANT
     with pytest.raises(T.SkiplnError) as e:
         dc.run_config(-2, 1, 0)
@@ -298,11 +296,11 @@ def test_streaming_copy(nbytes):
 
     src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
     dst = torch.zeros_like(src)
-    L.check(L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), nbytes, None), "skipln_copy")
+    L.check(L.load_tune().skipln_tune_copy(dst.data_ptr(), src.data_ptr(), nbytes, None), "skipln_tune_copy")
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
-    assert L.load().skipln_copy(dst.data_ptr() + 8, src.data_ptr(), 16, None) == L.ERR_SHAPE
-    assert L.load().skipln_copy(dst.data_ptr(), src.data_ptr(), 24, None) == L.ERR_SHAPE
+    assert L.load_tune().skipln_tune_copy(dst.data_ptr() + 8, src.data_ptr(), 16, None) == L.ERR_SHAPE
+    assert L.load_tune().skipln_tune_copy(dst.data_ptr(), src.data_ptr(), 24, None) == L.ERR_SHAPE
 
 
 def test_stream_probe_outputs():
@@ -312,7 +310,7 @@ def test_stream_probe_outputs():
     a ragged last tile and a partial last round), with either store policy."""
     import torch
 
-    lib = L.load()
+    lib = L.load_tune()
     n = (1 << 20) + 48
     a = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
     b = torch.randint(0, 2 ** 31 - 1, (n // 4,), dtype=torch.int32, device="cuda")
@@ -320,24 +318,24 @@ def test_stream_probe_outputs():
     for blk, u, g, t in ((64, 1, 1, 0), (256, 4, 1, 1), (1024, 1, 1, 0), (1024, 4, 1, 1), (64, 1, 2, 0), (64, 1, 3, 1),
                          (64, 4, 16, 0), (256, 1, 5, 1)):
         c.zero_(), d.zero_()
-        L.check(lib.skipln_stream(a.data_ptr(), None, c.data_ptr(), d.data_ptr(), n, blk, u, g, t, None),
-                "skipln_stream")
+        L.check(lib.skipln_tune_stream(a.data_ptr(), None, c.data_ptr(), d.data_ptr(), n, blk, u, g, t, None),
+                "skipln_tune_stream")
         torch.cuda.synchronize()
         assert torch.equal(c, a) and torch.equal(d, a + 1), (blk, u, g, t)
     for g, t in ((1, 0), (4, 1)):
         c.zero_()
-        L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, n, 256, 1, g, t, None),
-                "skipln_stream")
+        L.check(lib.skipln_tune_stream(a.data_ptr(), b.data_ptr(), c.data_ptr(), None, n, 256, 1, g, t, None),
+                "skipln_tune_stream")
         torch.cuda.synchronize()
         assert torch.equal(c, a ^ b)
     idx = torch.arange(n // 16, dtype=torch.int32, device="cuda")
     for g, t in ((1, 1), (7, 0)):
         c.fill_(-1)
-        L.check(lib.skipln_stream(None, None, c.data_ptr(), None, n, 64, 4, g, t, None), "skipln_stream")
+        L.check(lib.skipln_tune_stream(None, None, c.data_ptr(), None, n, 64, 4, g, t, None), "skipln_tune_stream")
         torch.cuda.synchronize()
         assert torch.equal(c.view(-1, 4)[:, 0], idx) and not c.view(-1, 4)[:, 1:].any()
     before = c.clone()
-    L.check(lib.skipln_stream(a.data_ptr(), b.data_ptr(), None, None, n, 1024, 4, 2, 0, None), "skipln_stream")
+    L.check(lib.skipln_tune_stream(a.data_ptr(), b.data_ptr(), None, None, n, 1024, 4, 2, 0, None), "skipln_tune_stream")
     torch.cuda.synchronize()
     assert torch.equal(c, before)
 
@@ -488,9 +486,8 @@ def test_long_rows_auto(dt, hidden):
 def test_large_offset_rows(dt, mu, hidden, variant):
     """Rows whose mean is far from zero (variance cancellation) in every
     kernel family, within the binary32 tolerance."""
-    lib = L.load()
     code = L.F32 if dt == "f32" else L.F16
-    if lib.skipln_select(L.OP_LAYER_NORM, hidden, code, L.SKIP_EXACT, 1, variant) < 0:
+    if U.select(L.OP_LAYER_NORM, hidden, code, variant=variant) < 0:
         pytest.skip("family does not take this shape")
     w = W.small_case(40, hidden, dt, skip_rows=8, beta=True, bias=True, residual=True, eps=1e-5, seed=int(mu) + hidden,
                      input_dist=W.normal(mu, 1))
@@ -501,7 +498,7 @@ def test_large_offset_rows(dt, mu, hidden, variant):
 def test_long_rows_reject_tiling():
     w = W.small_case(4, 20000, "f32", residual=True)
     dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
-    assert L.load().skipln_select(L.OP_LAYER_NORM, 20000, L.F32, L.SKIP_EXACT, 1, L.VARIANT_LDSROW) >= 0
+    assert U.select(L.OP_LAYER_NORM, 20000, L.F32, variant=L.VARIANT_LDSROW) >= 0
     with pytest.raises(T.SkiplnError) as e:
         dc.run_config(-1, 1, 1)  # no row-tile geometry holds 5000 chunks
     assert e.value.status == L.ERR_UNSUPPORTED

@@ -104,13 +104,13 @@ def test_bias_reuse(dt, rows, bias_rows, hidden, mode):
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("tiling", [(0, 1), (1, 0), (3, 1), (0, 2), (2, 2)], ids=lambda t: f"tpb{t[0]}_m{t[1]}")
-@pytest.mark.parametrize("geom", [-1, 0, 13, 28, 29])
+@pytest.mark.parametrize("geom", [-1, 0, 12, 17, 18])
 @pytest.mark.parametrize("mode", MODES)
 def test_launch_configs(dt, tiling, geom, mode):
     w = case(203 if mode == "exact" else 210, 32 if dt == "f32" else 64, dt, mode, bias_rows=7,
              seed=geom + 100)
-    if geom >= 0 and L.load().skipln_select(L.OP_BIAS_SOFTMAX, w.hidden, L.F32 if dt == "f32" else L.F16,
-                                            U.skip_mode(w), 1, L.VARIANT_GEOMETRY + geom) < 0:
+    if geom >= 0 and U.select(L.OP_BIAS_SOFTMAX, w.hidden, L.F32 if dt == "f32" else L.F16, U.skip_mode(w),
+                              variant=L.VARIANT_GEOMETRY + geom) < 0:
         pytest.skip("geometry does not hold the row")
     inputs = W.make_inputs(w)
     dc = U.DeviceCase(w, inputs, residual=False)
@@ -196,9 +196,8 @@ def test_special_rows(dt, hidden, variant):
     except one column; a row of -inf only (NaN); a NaN (NaN row); a +inf
     (NaN row); a masked suffix covering whole wavefronts; huge spread
     (underflowing terms); a large common offset; equal values."""
-    lib = L.load()
     code = L.F32 if dt == "f32" else L.F16
-    if lib.skipln_select(L.OP_BIAS_SOFTMAX, hidden, code, L.SKIP_EXACT, 1, variant) < 0:
+    if U.select(L.OP_BIAS_SOFTMAX, hidden, code, variant=variant) < 0:
         pytest.skip("family does not take this shape")
     rng = np.random.default_rng(hidden + variant)
     rows = 12

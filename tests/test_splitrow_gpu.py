@@ -97,15 +97,16 @@ def test_split_many_rows(dt, hidden):
 def test_many_rows_auto_takes_generic(dt, hidden, op):
     """With a row for every CU, RMS rows and float32 layer norm rows of up
     to 65536 values take the generic kernel even when a workspace is at hand:
-    the workspace size is 0, and the call through skipln_forward_ws (with an
-    empty workspace) and through the allocating wrapper match the oracle."""
+    the kernel choice for the call's row count on this device says so, and
+    the call through skipln_forward_ws (with the workspace the size query
+    asks for, unused) and through the allocating wrapper match the oracle."""
     import torch
 
-    rows = 256
+    rows = torch.cuda.get_device_properties(0).multi_processor_count  # a row for every CU
     w = norm_case(rows, hidden, dt, op, seed=13, mu=100.0 if op == "layer_norm" else 0.0)
     code = L.F32 if dt == "f32" else L.F16
-    assert T.workspace_bytes(U.OPS[op], rows, hidden, code) == 0
-    assert T.workspace_bytes(U.OPS[op], rows - 1, hidden, code) > 0
+    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows).split("_")[-2] == "generic"
+    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows - 1).split("_")[-2] == "splitrow"
     inputs = W.make_inputs(w)
     ref = U.oracle_rows(w, inputs)
     U.note(f"auto many rows {op} {dt} H={hidden} rows={rows}")

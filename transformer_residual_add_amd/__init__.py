@@ -29,26 +29,49 @@ def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, g
                 rows: int, hidden: int, eps: float, dtype: int, stream: int = 0,
                 variant: int = _lib.VARIANT_AUTO, op: int = _lib.OP_LAYER_NORM,
                 workspace: Optional[tuple] = None) -> None:
-    """``skipln_forward_variant`` on raw device pointers, or
-    ``skipln_forward_ws`` when ``workspace`` = (pointer, bytes) is given;
-    raises SkiplnError."""
+    """Operation ``op`` on raw device pointers; raises SkiplnError.
+
+    The automatic kernel choice goes through the operator library: the
+    operation's own entry point, or ``skipln_forward_ws`` when ``workspace`` =
+    (pointer, bytes) is given.  A forced kernel family (``variant``) goes
+    through the tuning library's ``skipln_tune_forward``."""
+    ws_ptr, ws_bytes = workspace if workspace is not None else (None, 0)
+    args = (input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
+            out_ptr, residual_ptr or None, rows, hidden, eps, dtype)
+    if variant != _lib.VARIANT_AUTO:
+        st = _lib.load_tune().skipln_tune_forward(op, *args, variant, ws_ptr or None, ws_bytes, stream or None)
+        _lib.check(st, "skipln_tune_forward")
+        return
     lib = _lib.load()
-    if workspace is None:
-        st = lib.skipln_forward_variant(
-            op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
-            out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, stream or None)
+    if workspace is not None:
+        st = lib.skipln_forward_ws(op, *args, ws_ptr or None, ws_bytes, stream or None)
+    elif op == _lib.OP_LAYER_NORM:
+        st = lib.skipln_forward(*args, stream or None)
+    elif op == _lib.OP_SIMPLIFIED:
+        st = lib.skipln_forward_simplified(*args, stream or None)
+    elif op == _lib.OP_BIAS_ADD:
+        if skip_mode != _lib.SKIP_EXACT:
+            raise SkiplnError(_lib.ERR_MODE, "skipln_bias_add")
+        st = lib.skipln_bias_add(input_ptr, bias_ptr or None, skip_ptr, out_ptr, rows, hidden, dtype, stream or None)
+    elif op == _lib.OP_BIAS_SOFTMAX:
+        bias_rows = rows if skip_mode == _lib.SKIP_EXACT else skip_rows
+        st = lib.skipln_bias_softmax(input_ptr, skip_ptr, out_ptr, rows, hidden, bias_rows,
+                                     1 if skip_mode == _lib.SKIP_BROADCAST_INNER else 0, dtype, None, 0,
+                                     stream or None)
     else:
-        st = lib.skipln_forward_ws(
-            op, input_ptr, skip_ptr, skip_mode, skip_rows, gamma_ptr or None, beta_ptr or None, bias_ptr or None,
-            out_ptr, residual_ptr or None, rows, hidden, eps, dtype, variant, workspace[0] or None, workspace[1],
-            stream or None)
+        raise SkiplnError(_lib.ERR_OP, "forward_raw")
     _lib.check(st, "skipln_forward")
 
 
 def workspace_bytes(op: int, rows: int, hidden: int, dtype: int, skip_mode: int = _lib.SKIP_EXACT,
                     skip_rows: int = 0, variant: int = _lib.VARIANT_AUTO) -> int:
-    """Device workspace ``skipln_forward_ws`` needs for these arguments (0: none)."""
-    n = _lib.load().skipln_workspace_bytes(op, rows, hidden, dtype, skip_mode, skip_rows, variant)
+    """Device workspace a call with these arguments may need (0: none): the
+    operator library's ``skipln_workspace_bytes`` for the automatic choice,
+    the tuning library's for a forced kernel family."""
+    if variant == _lib.VARIANT_AUTO:
+        n = _lib.load().skipln_workspace_bytes(op, rows, hidden, dtype, skip_mode, skip_rows)
+    else:
+        n = _lib.load_tune().skipln_tune_workspace_bytes(op, rows, hidden, dtype, skip_mode, skip_rows, variant)
     if n < 0:
         raise SkiplnError(-n, "skipln_workspace_bytes")
     return int(n)
@@ -87,14 +110,16 @@ def bias_softmax_raw(data_ptr: int, bias_ptr: int, out_ptr: int, batch_count: in
 
 
 def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int = _lib.VARIANT_AUTO,
-                  skip_mode: int = _lib.SKIP_EXACT, op: int = _lib.OP_LAYER_NORM, workspace: bool = False) -> str:
-    """Name of the kernel a call with this operation, hidden size and skip form
-    would launch (``workspace``: a call that brings a workspace)."""
-    lib = _lib.load()
-    fn = lib.skipln_select_ws if workspace else lib.skipln_select
-    kid = fn(op, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant)
+                  skip_mode: int = _lib.SKIP_EXACT, op: int = _lib.OP_LAYER_NORM, workspace: bool = False,
+                  rows: int = -1, cus: int = 0) -> str:
+    """Name of the kernel a call with this operation, row count (-1: fewer than
+    the device's compute units), hidden size and skip form would launch
+    (``workspace``: a call that brings one; ``cus`` <= 0: the current
+    device's compute units)."""
+    kid = _lib.load_tune().skipln_tune_select(op, rows, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant,
+                                              1 if workspace else 0, cus)
     if kid < 0:
-        raise SkiplnError(-kid, "skipln_select")
+        raise SkiplnError(-kid, "skipln_tune_select")
     return _lib.kernel_name(kid)
 
 

@@ -462,33 +462,33 @@ struct AutoEntry {
 // 192 chunks the same change was 2.7 % faster on one box and 3.5 % slower on
 // another for BERT-base (1024 x 768 float32), so 192-lane groups stay.
 constexpr AutoEntry kAutoNorm[] = {
-    {4, 28}, {8, 29}, {16, 0}, {32, 1}, {64, 2}, {128, 3}, {192, 22}, {256, 14}, {512, 27},
-    {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+    {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 3}, {192, 15}, {256, 13}, {512, 16},
+    {768, 6}, {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 // BiasAdd (no reduction) keeps the wider groups: one wavefront per row was
 // slower at 192 chunks (1024 x 768 float32: 3.74 against 3.54 us).
 constexpr AutoEntry kAutoExact[] = {
-    {4, 28}, {8, 29}, {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
-    {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+    {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 12}, {192, 15}, {256, 13}, {512, 16},
+    {768, 6}, {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 constexpr AutoEntry kAutoBroadcast[] = {
-    {4, 28}, {8, 29}, {16, 0}, {32, 1}, {64, 2}, {128, 13}, {192, 22}, {256, 14}, {512, 27},
-    {768, 7}, {1024, 8}, {1536, 9}, {2048, 10}, {3072, 11}, {4096, 12},
+    {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 12}, {192, 15}, {256, 13}, {512, 16},
+    {768, 6}, {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 // BiasSoftmax streams one tensor in and one out and has no per-column
 // parameters; on MI355X it runs fastest with two to four chunks per lane
 // (more independent loads in flight per lane, fewer lanes per reduction)
 // until a row needs several wavefronts (measured over 2..2048 chunks).
 constexpr AutoEntry kAutoSoftmax[] = {
-    {4, 28},   {8, 29},   {16, 31},  {32, 33},   {64, 35},   {128, 37},  {256, 5},
-    {512, 6},  {1024, 15}, {2048, 10}, {3072, 11}, {4096, 12},
+    {4, 17},   {8, 18},   {16, 19},  {32, 20},   {64, 21},   {128, 22},  {256, 4},
+    {512, 5},  {1024, 14}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 
 // Automatic choice by elements per row (measured on MI355X: four elements
 // per lane up to 512 per row, eight beyond).
 constexpr AutoEntry kAutoElem[] = {
     {4, 0},    {8, 1},     {16, 2},    {32, 3},    {64, 4},    {128, 5},   {256, 6},
-    {512, 7},  {1024, 12}, {2048, 19}, {4096, 20}, {8192, 16}, {16384, 21},
+    {512, 7},  {1024, 8}, {2048, 9}, {4096, 10}, {8192, 11}, {16384, 12},
 };
 
 // Generic kernel, chunked form: rows of whole 16-byte chunks with every

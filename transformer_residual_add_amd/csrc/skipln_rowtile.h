@@ -451,29 +451,27 @@ struct Geom {
     int g, ch, block;
 };
 
-// Auto order (increasing capacity G*CH chunks) first, then geometries only
-// reachable through the multi-wavefront variant.
+// Every geometry is the automatic choice of some row length, operation or
+// skip form (the tables in skipln_kernels.hip), measured fastest there on
+// MI355X in sweeps over a wider set: 16-1024-lane groups, 1-8 chunks per
+// lane, 64-1024-lane blocks.  The forced-variant and tuning entry points
+// reach the same kernels.
 constexpr Geom kGeoms[] = {
-    {16, 1, 256},  {32, 1, 256},  {64, 1, 256},   {64, 2, 256},   {64, 3, 256},
-    {64, 4, 256},  {128, 4, 256}, {256, 3, 256},  {256, 4, 256},  {512, 3, 512},
-    {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256}, {256, 1, 256},
-    {512, 2, 512}, {128, 8, 256},  {256, 2, 512},  {256, 4, 512},  {64, 2, 64},
-    {64, 3, 64},   {32, 6, 256},  {192, 1, 192},  {192, 2, 192},  {512, 1, 512},
-    {1024, 1, 1024}, {1024, 2, 1024}, {256, 2, 256}, {4, 1, 256},   {8, 1, 256},
-    {4, 2, 256},   {8, 2, 256},   {8, 4, 256},    {16, 2, 256},   {16, 4, 256},
-    {32, 2, 256},  {128, 2, 256}, {32, 4, 256},   {16, 8, 256},
+    {16, 1, 256}, {32, 1, 256}, {64, 1, 256}, {64, 2, 256}, {64, 4, 256}, {128, 4, 256}, {256, 3, 256},
+    {256, 4, 256}, {512, 3, 512}, {512, 4, 512}, {1024, 3, 1024}, {1024, 4, 1024}, {128, 1, 256},
+    {256, 1, 256}, {512, 2, 512}, {192, 1, 192}, {256, 2, 256}, {4, 1, 256}, {8, 1, 256}, {8, 2, 256},
+    {16, 2, 256}, {32, 2, 256}, {32, 4, 256},
 };
 constexpr int kNumGeoms = sizeof(kGeoms) / sizeof(kGeoms[0]);
 static_assert(kRowtileFirst + kNumGeoms <= kElemFirst, "kernel index ranges are disjoint");
 
 // Element-wise row tiles (one element per access): rows that are not whole
-// 16-byte chunks, or tensors aligned to their element size only.  Two to
-// sixteen elements per lane keep several loads in flight per lane.
+// 16-byte chunks, or tensors aligned to their element size only.  Four to
+// sixteen elements per lane keep several loads in flight per lane; each is
+// the automatic choice for some row length.
 constexpr Geom kElemGeoms[] = {
-    {4, 1, 256},   {4, 2, 256},   {8, 2, 256},    {8, 4, 256},    {16, 4, 256},   {32, 4, 256},
-    {64, 4, 256},  {128, 4, 256}, {256, 4, 256},  {512, 4, 512},  {1024, 4, 1024}, {16, 8, 256},
-    {128, 8, 256}, {32, 2, 256},  {64, 2, 256},   {256, 2, 256},  {1024, 8, 1024}, {16, 2, 256},
-    {64, 8, 256},  {256, 8, 256}, {512, 8, 512},  {1024, 16, 1024},
+    {4, 1, 256}, {4, 2, 256}, {8, 2, 256}, {8, 4, 256}, {16, 4, 256}, {32, 4, 256}, {64, 4, 256},
+    {128, 4, 256}, {128, 8, 256}, {256, 8, 256}, {512, 8, 512}, {1024, 8, 1024}, {1024, 16, 1024},
 };
 constexpr int kNumElemGeoms = sizeof(kElemGeoms) / sizeof(kElemGeoms[0]);
 static_assert(kElemFirst + kNumElemGeoms <= kRegRowIndex, "kernel index ranges are disjoint");
