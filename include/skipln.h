@@ -222,6 +222,21 @@ SKIPLN_API int64_t skipln_workspace_bytes(int op, int64_t rows, int64_t hidden, 
                                           int64_t skip_rows);
 
 /*
+ * skipln_forward_ws without the workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the split-row kernels use the library's own
+ * scratch, a device array of 256 KiB per GPU held until the process ends.  It
+ * allocates nothing.  Calls whose kernels would need more scratch than that
+ * return SKIPLN_ERR_WORKSPACE (the automatic choice needs less than 154 KiB).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (other streams or host threads) race and must be
+ * serialized by the caller.  Otherwise as skipln_forward_ws.
+ */
+SKIPLN_API int skipln_forward_ws_static(int op, const void* input, const void* skip, int skip_mode,
+                                        int64_t skip_rows, const void* gamma, const void* beta, const void* bias,
+                                        void* out, void* residual_out, int64_t rows, int64_t hidden,
+                                        float eps, int dtype, skipln_stream_t stream);
+
+/*
  * The argument checks of skipln_forward alone, with the same arguments (the
  * stream aside): host code only, no HIP call, no pointer dereferenced.
  * Returns the status skipln_forward would return before enqueueing anything.

@@ -51,7 +51,7 @@ def test_operator_surface():
     assert set(L.SIGNATURES) == {
         "skipln_forward", "skipln_validate", "skipln_status_string", "skipln_version",
         "skipln_forward_simplified", "skipln_bias_add", "skipln_bias_softmax",
-        "skipln_forward_ws", "skipln_workspace_bytes"}
+        "skipln_forward_ws", "skipln_workspace_bytes", "skipln_forward_ws_static"}
     assert L.load().skipln_version() == 2
 
 
@@ -534,3 +534,31 @@ def test_stream_probe_argument_checks():
     assert st(b=128) == L.ERR_VARIANT and st(u=2) == L.ERR_VARIANT
     assert st(g=0) == L.ERR_VARIANT and st(g=-3) == L.ERR_VARIANT and st(g=65537) == L.ERR_VARIANT
     assert st(n=0, g=65536) == L.OK
+
+
+def test_static_scratch_covers_every_automatic_split():
+    """The automatic choice never needs more workspace than the static
+    scratch of skipln_forward_ws_static holds (256 KiB)."""
+    lib = L.load()
+    worst = 0
+    for dt, v in ((L.F32, 4), (L.F16, 8)):
+        for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED, L.OP_BIAS_SOFTMAX):
+            for mode, srows in ((L.SKIP_EXACT, 0), (L.SKIP_BROADCAST, 1)):
+                for h in list(range(40904, 530000, v * 389)) + [65536, 81924, 163848, 262144, 524288]:
+                    if h % v:
+                        continue
+                    worst = max(worst, lib.skipln_workspace_bytes(op, 10 ** 7, h, dt, mode, srows))
+    assert 0 < worst < 154 * 1024
+
+
+def test_static_entry_argument_checks():
+    """skipln_forward_ws_static returns these before any HIP call."""
+    st = lambda op=L.OP_LAYER_NORM, hidden=65536, rows=4, out=OUT, eps=1e-5, dtype=L.F32: \
+        L.load().skipln_forward_ws_static(op, IN, SK, 0, 0, GA, BE, BI, out, RES, rows, hidden, eps, dtype, None)
+    assert st(op=9) == L.ERR_OP
+    assert st(dtype=5) == L.ERR_DTYPE
+    assert st(eps=-1.0) == L.ERR_EPS
+    assert st(hidden=0) == L.ERR_SHAPE
+    assert st(out=None) == L.ERR_NULL
+    assert st(out=IN + 4) == L.ERR_ALIAS
+    assert st(rows=0) == L.OK

@@ -38,6 +38,7 @@ SIGNATURES = {
     "skipln_bias_add": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _i32, _vp]),
     "skipln_bias_softmax": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _i64, _vp]),
     "skipln_forward_ws": (_i32, [_i32] + _FWD + [_vp, _i64, _vp]),
+    "skipln_forward_ws_static": (_i32, [_i32] + _FWD + [_vp]),
     "skipln_workspace_bytes": (_i64, [_i32, _i64, _i64, _i32, _i32, _i64]),
     "skipln_validate": (_i32, _FWD),
     "skipln_status_string": (C.c_char_p, [_i32]),

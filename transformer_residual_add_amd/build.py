@@ -23,7 +23,7 @@ TUNE_LIB = os.path.join(PKG, "libskipln_tune.so")
 KERNELS = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_regrow.hip")] + [
     (os.path.join(CSRC, "skipln_rowtile_op.hip"), [f"-DSKIPLN_ROWTILE_OP={op}"]) for op in range(4)]
 CORE = [(os.path.join(CSRC, "skipln_core.cpp"), [])]
-API = [(os.path.join(CSRC, "skipln_api.cpp"), [])]
+API = [(os.path.join(CSRC, "skipln_api.cpp"), []), (os.path.join(CSRC, "skipln_static.hip"), [])]
 TUNE = [(os.path.join(CSRC, "skipln_stream.hip"), []), (os.path.join(CSRC, "skipln_tune_api.cpp"), [])]
 SOURCES = KERNELS + CORE + API + TUNE
 # The objects each library links.
