@@ -86,6 +86,9 @@ def parse_args(argv=None):
                    "profiles/counters.json); run it on the tree the counters were taken on")
     p.add_argument("--counter-steps", type=int, default=12,
                    help="steps (warm-up included) each counter run made, for --summarize-counters")
+    p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"), default=None,
+                   help="no GPU work: per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench.py run "
+                        "against the HIP-event launch times that run printed (its JSON line), as a markdown table")
     return p.parse_args(argv)
 
 
@@ -433,11 +436,7 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
     from transformer_residual_add_amd import _lib as L
     from transformer_residual_add_amd import workloads as W
 
-    def lib_median(name, counter):
-        """Counter per step and library dispatches seen.  One kernel per
-        step: the median over its dispatches.  Several (the split-row pair,
-        per batch of rows): the sum over all of them divided by the steps run
-        (``steps``)."""
+    def lib_dispatches(name, counter):
         path = os.path.join(root, f"{name}_{counter}", "run_counter_collection.csv")
         by = {}
         for k, v in _counter_rows(path, counter):
@@ -445,8 +444,19 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
                 by.setdefault(k, []).append(v)
         if not by:
             raise SystemExit(f"no library dispatch in {path}")
+        return by
+
+    def lib_median(name, counter):
+        """Counter per step and library dispatches seen.  A step of one
+        kernel (one library kernel in both counter runs): the median over its
+        dispatches (however many launches the run made: the timed launches
+        cycle every buffer set).  A step of several (the split-row pair, per
+        batch of rows): the sum over all of them divided by the steps run
+        (``steps``)."""
+        by = lib_dispatches(name, counter)
+        kernels = set(lib_dispatches(name, "FETCH_SIZE")) | set(lib_dispatches(name, "WRITE_SIZE"))
         n = sum(len(v) for v in by.values())
-        if len(by) == 1 and n == steps:
+        if len(kernels) == 1:
             return _median(next(iter(by.values()))), n
         return sum(sum(v) for v in by.values()) / steps, n
 
@@ -493,8 +503,57 @@ def summarize_counters(root: str, out_path: str, steps: int) -> int:
     return 0
 
 
+def summarize_trace(trace_csv: str, bench_json: str) -> int:
+    """Per-workload kernel durations from a kernel trace of one bench.py run:
+    every dispatch of the workload's kernel, and its timed dispatches (the
+    last ``launches`` of them: the graph replay the run brackets with HIP
+    events), beside the event average the run reported."""
+    import csv
+
+    with open(bench_json) as fh:
+        line = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    head = {"workload": line["config"]["workload"], "kernel": line["config"]["kernel"],
+            "launches": line["config"]["launches_timed"], "launch_us": line["config"]["launch_us"],
+            "algorithmic_bytes": None}
+    runs = [head] + [{"workload": r["workload"], "kernel": r["kernel"], "launches": r["launches"],
+                      "launch_us": r["launch_us"]} for r in line.get("sweep", [])]
+    by_kernel = {}
+    with open(trace_csv, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if "skipln" not in row["Kernel_Name"]:
+                continue
+            ns = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+            by_kernel.setdefault(row["Kernel_Name"], []).append((float(row["Start_Timestamp"]), ns))
+    from transformer_residual_add_amd import workloads as W
+
+    print("| workload | kernel (library name) | dispatches | avg all us | avg timed us | median timed us | "
+          "bench.py events us | trace / events | % of 8 TB/s (trace) |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    used = set()
+    for r in runs:
+        # the trace names kernels by their template arguments: take the kernel
+        # whose dispatch count and order match this workload (first unused
+        # kernel with at least `launches` dispatches, in the run's order)
+        cands = [k for k in by_kernel if k not in used and len(by_kernel[k]) >= r["launches"]]
+        if not cands:
+            continue
+        k = min(cands, key=lambda k: by_kernel[k][0][0])
+        used.add(k)
+        d = sorted(by_kernel[k])
+        timed = [ns / 1e3 for _, ns in d[-r["launches"]:]]
+        allv = [ns / 1e3 for _, ns in d]
+        avg_t = sum(timed) / len(timed)
+        alg = W.get(r["workload"]).algorithmic_bytes()
+        print(f"| {r['workload']} | {r['kernel']} | {len(d)} | {sum(allv) / len(allv):.2f} | {avg_t:.2f} | "
+              f"{_median(timed):.2f} | {r['launch_us']:.2f} | {avg_t / r['launch_us']:.3f} | "
+              f"{alg / (avg_t * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} |")
+    return 0
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
+    if args.summarize_trace:
+        return summarize_trace(*args.summarize_trace)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.counters_out or COUNTERS, args.counter_steps)
     if args.gpus != 1:
