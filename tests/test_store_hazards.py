@@ -121,8 +121,13 @@ def device_asm():
 def test_no_unguarded_store_data_overwrite(device_asm):
     assert device_asm
     problems = []
+    kernels = 0
     for name, text in device_asm.items():
+        if ".amdhsa_kernel" not in text:
+            continue  # no kernel in this source (device data only)
+        kernels += 1
         assert "buffer_store_dwordx4" in text or "global_store_dwordx4" in text, name
         for line, store, nxt in scan(text):
             problems.append(f"{name}:{line}: {store} -> {nxt}")
+    assert kernels >= 6
     assert not problems, "\n".join(problems[:20])
