@@ -86,6 +86,21 @@ def parse_args(argv=None):
                    "profiles/counters.json); run it on the tree the counters were taken on")
     p.add_argument("--counter-steps", type=int, default=12,
                    help="steps (warm-up included) each counter run made, for --summarize-counters")
+    p.add_argument("--launch-configs", metavar="WORKLOAD", default=None,
+                   help="instead of the benchmark, time the automatic launch of WORKLOAD beside forced launch "
+                        "configurations (--config; default: the automatic geometry with each tiling that applies "
+                        "and both store policies), graph replays interleaved --reps times")
+    p.add_argument("--config", action="append", default=[], metavar="G:T:TILING:STORE",
+                   help="a launch configuration for --launch-configs: row-tile geometry index (-1: the automatic "
+                        "one), tiles per block (0: sized to the resident grid), SKIPLN_TILE_* and SKIPLN_STORE_* "
+                        "values; repeatable")
+    p.add_argument("--reps", type=int, default=6, help="interleaved replays per configuration (--launch-configs)")
+    p.add_argument("--counter-pass", action="store_true",
+                   help="with --launch-configs: no timing; launch each configuration --steps times eagerly, in "
+                        "order, for a rocprofv3 --pmc run, and print the dispatch plan")
+    p.add_argument("--summarize-config-counters", nargs=2, metavar=("DIR", "PLAN_JSON"), default=None,
+                   help="no GPU work: per-configuration HBM bytes and L2 hits/misses from rocprofv3 --pmc runs "
+                        "of a --counter-pass (DIR/<COUNTER>/run_counter_collection.csv), as a markdown table")
     p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"), default=None,
                    help="no GPU work: per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench.py run "
                         "against the HIP-event launch times that run printed (its JSON line), as a markdown table")
@@ -290,34 +305,40 @@ def time_streams(nbytes: int, steps: int, warmup: int):
 
     nbytes -= nbytes % 16
     lib = L.load_tune()
-    bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
+    # Streams smaller than the last-level cache rotate over enough copies
+    # that each launch reads and writes HBM, as the benchmark's steps do.
+    n_sets = max(1, -(-CACHE_BYTES // nbytes))
+    bufs = [[torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 255) for _ in range(4)]
+            for _ in range(n_sets)]
     s = torch.cuda.current_stream().cuda_stream
     out = []
     for reads in (0, 1, 2):
         for writes in (0, 1, 2):
             if reads + writes == 0:
                 continue
-            src = [bufs[i].data_ptr() for i in range(reads)] + [None] * (2 - reads)
-            dst = [bufs[2 + i].data_ptr() for i in range(writes)] + [None] * (2 - writes)
+            srcs = [[b[i].data_ptr() for i in range(reads)] + [None] * (2 - reads) for b in bufs]
+            dsts = [[b[2 + i].data_ptr() for i in range(writes)] + [None] * (2 - writes) for b in bufs]
 
             moved = (reads + writes) * nbytes
             shapes = []
             for (block, per_lane, granule), through in [(sh, t) for sh in STREAM_SHAPES for t in (0, 1)
                                                         if writes or not t]:
-                def launch():
+                def launch(i):
+                    src, dst = srcs[i % n_sets], dsts[i % n_sets]
                     L.check(lib.skipln_tune_stream(src[0], src[1], dst[0], dst[1], nbytes, block, per_lane,
                                                    granule, through, s), "skipln_tune_stream")
 
-                for _ in range(warmup):
-                    launch()
+                for i in range(warmup):
+                    launch(i)
                 torch.cuda.synchronize()
                 ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                n = -(-max(steps, n_sets) // n_sets) * n_sets
                 ev0.record()
-                for _ in range(steps):
-                    launch()
+                for i in range(n):
+                    launch(i)
                 ev1.record()
                 torch.cuda.synchronize()
-                dt = ev0.elapsed_time(ev1) * 1e-3 / steps
+                dt = ev0.elapsed_time(ev1) * 1e-3 / n
                 shapes.append({"block": block, "chunks_per_lane": per_lane, "xcd_granule": granule,
                                "store_through": through, "xcd_granule_bytes": block * per_lane * 16 * granule,
                                "launch_us": round(dt * 1e6, 2), "gb_per_s": round(moved / dt / 1e9, 1)})
@@ -327,7 +348,7 @@ def time_streams(nbytes: int, steps: int, warmup: int):
             # of that many bytes per stream.
             at_granule = {str(g): max(r["gb_per_s"] for r in shapes if r["xcd_granule_bytes"] >= g)
                           for g in STREAM_GRANULES}
-            out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "best_gb_per_s": best["gb_per_s"],
+            out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "buffer_sets": n_sets, "best_gb_per_s": best["gb_per_s"],
                         "best_frac_of_peak": round(best["gb_per_s"] / HBM_PEAK_GBS, 4),
                         "best_shape": [best["block"], best["chunks_per_lane"], best["xcd_granule"],
                                        best["store_through"]],
@@ -339,6 +360,190 @@ def time_streams(nbytes: int, steps: int, warmup: int):
                           f"{r['gb_per_s']:.0f}" for r in shapes) +
                 "; by XCD granule: " + ", ".join(f"{g}B {v:.0f}" for g, v in at_granule.items()))
     return out
+
+
+# Names of the SKIPLN_TILE_* and SKIPLN_STORE_* values, for labels.
+TILING_NAMES = {0: "contiguous", 1: "strided", 2: "skip-stationary"}
+STORE_NAMES = {-1: "auto", 0: "nt", 1: "sc0 sc1 nt"}
+
+
+def default_configs(w):
+    """Launch configurations compared with the automatic one: the automatic
+    geometry with each tiling that applies to the workload (a block per tile;
+    a resident grid walking the tiles; for a cyclic broadcast skip, blocks
+    that keep their skip rows and walk the batches) and both store
+    policies."""
+    shapes = [(1, 1), (0, 1)]
+    if w.broadcast and not w.inner:
+        shapes = [(0, 2)] + shapes
+    return [(-1, per, tiling, store) for per, tiling in shapes for store in (0, 1)]
+
+
+def parse_config(text: str):
+    parts = [int(v) for v in text.split(":")]
+    if len(parts) != 4:
+        raise SystemExit(f"--config wants G:T:TILING:STORE, got {text!r}")
+    return tuple(parts)
+
+
+def config_label(cfg, L) -> str:
+    if cfg is None:
+        return "automatic"
+    g, per, tiling, store = cfg
+    shape = "resident grid" if per == 0 else f"{per} tile(s) per block"
+    geom = "auto geometry" if g < 0 else f"geometry {g}"
+    return f"{geom}, {TILING_NAMES.get(tiling, tiling)}, {shape}, {STORE_NAMES.get(store, store)} stores"
+
+
+def time_configs(w, configs, steps: int, warmup: int, reps: int, counter_pass: bool):
+    """The automatic launch of workload ``w`` and each forced configuration:
+    one graph per configuration (a whole number of rounds over the buffer
+    sets), replayed in turn ``reps`` times; the median replay gives the
+    launch time.  ``counter_pass``: each configuration launched ``steps``
+    times eagerly instead, in order, nothing else from the library."""
+    import torch
+
+    import transformer_residual_add_amd as T
+    from transformer_residual_add_amd import _lib as L
+    from transformer_residual_add_amd import workloads as W
+
+    tune = L.load_tune()
+    code = L.F32 if w.dtype == "f32" else L.F16
+    op = OPS[w.op]
+    mode = skip_mode(w, L)
+    srows = w.skip_rows if w.broadcast else 0
+    alg = w.algorithmic_bytes()
+    if T.workspace_bytes(op, w.rows, w.hidden, code, mode, srows) > 0:
+        raise SystemExit(f"{w.name}: the automatic launch takes the split-row kernels; nothing to compare")
+    n_sets = max(1, min(96, -(-4 * CACHE_BYTES // alg)))
+    inputs = W.make_inputs(w)
+    dev = DeviceSets(w, inputs, n_sets)
+    del inputs
+    ptr = lambda t: None if t is None else t.data_ptr()
+    auto_kernel = T.select_kernel(w.hidden, code, True, 0, mode, op, rows=w.rows)
+
+    def stepper(cfg):
+        def step(i, stream):
+            d = dev.sets[i % n_sets]
+            if cfg is None:
+                T.forward_raw(ptr(d["input"]), ptr(d["skip"]), mode, srows, ptr(d["gamma"]), ptr(d["beta"]),
+                              ptr(d["bias"]), ptr(d["out"]), ptr(d["res"]), w.rows, w.hidden, float(w.eps), code,
+                              stream, 0, op)
+                return
+            g, per, tiling, store = cfg
+            L.check(tune.skipln_tune_forward_config(op, ptr(d["input"]), ptr(d["skip"]), mode, srows,
+                                                    ptr(d["gamma"]), ptr(d["beta"]), ptr(d["bias"]), ptr(d["out"]),
+                                                    ptr(d["res"]), w.rows, w.hidden, float(w.eps), code, g, per,
+                                                    tiling, store, stream), "skipln_tune_forward_config")
+        return step
+
+    def kernel_of(cfg):
+        if cfg is None or cfg[0] < 0:
+            return auto_kernel
+        kid = tune.skipln_tune_select(op, w.rows, w.hidden, code, mode, 1, L.VARIANT_GEOMETRY + cfg[0], 0, 0)
+        return L.kernel_name(kid) if kid >= 0 else "unknown"
+
+    todo = [None] + list(configs)
+    main = torch.cuda.current_stream()
+    if counter_pass:
+        plan = []
+        for cfg in todo:
+            step = stepper(cfg)
+            for i in range(steps):
+                step(i, main.cuda_stream)
+            torch.cuda.synchronize()
+            plan.append({"label": config_label(cfg, L), "config": cfg, "kernel": kernel_of(cfg), "dispatches": steps})
+            log(f"{w.name}: {steps} launches of {plan[-1]['label']}")
+        del dev
+        return {"workload": w.name, "algorithmic_bytes": alg, "plan": plan}
+
+    launches = -(-max(steps, n_sets) // n_sets) * n_sets
+    graphs = []
+    for cfg in todo:
+        step = stepper(cfg)
+        for i in range(warmup):
+            step(i, main.cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(launches):
+                step(i, cap)
+        g.replay()
+        torch.cuda.synchronize()
+        graphs.append(g)
+    times = [[] for _ in todo]
+    for _ in range(reps):
+        for j, g in enumerate(graphs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            g.replay()
+            e1.record(main)
+            torch.cuda.synchronize()
+            times[j].append(e0.elapsed_time(e1) * 1e3 / launches)
+    rows = []
+    for cfg, ts in zip(todo, times):
+        med = _median(ts)
+        rows.append({"label": config_label(cfg, L), "config": cfg, "kernel": kernel_of(cfg),
+                     "launch_us": round(med, 2), "min_us": round(min(ts), 2), "max_us": round(max(ts), 2),
+                     "frac_of_peak": round(alg / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"{w.name}: {rows[-1]['label']} ({rows[-1]['kernel']}): {med:.2f} us "
+            f"({rows[-1]['frac_of_peak']:.1%} of peak)")
+    del graphs, dev
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "algorithmic_bytes": alg, "launches_per_replay": launches, "buffer_sets": n_sets,
+            "reps": reps, "configs": rows}
+
+
+def summarize_config_counters(root: str, plan_json: str) -> int:
+    """HBM bytes (FETCH_SIZE, WRITE_SIZE, scaled by the streaming copy's
+    calibration in profiles/counters.json) and L2 hits and misses per launch
+    configuration of a --counter-pass run: the library's dispatches, in
+    dispatch order, split by the plan that run printed."""
+    import csv
+
+    with open(plan_json) as fh:
+        run = json.loads([ln for ln in fh.read().splitlines() if ln.startswith("{")][-1])
+    run = run.get("launch_configs", run)
+    plan = run["plan"]
+    with open(COUNTERS) as fh:
+        cal = json.load(fh)["copy_calibration"]
+    scale = {"FETCH_SIZE": cal["fetch_scale"] * 1024, "WRITE_SIZE": cal["write_scale"] * 1024}
+    values = {}
+    for sub in sorted(os.listdir(root)):
+        path = os.path.join(root, sub, "run_counter_collection.csv")
+        if not os.path.exists(path):
+            continue
+        per = {}
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if "skipln" in row["Kernel_Name"]:
+                    per.setdefault(row["Counter_Name"], []).append((int(row["Dispatch_Id"]),
+                                                                    float(row["Counter_Value"])))
+        for counter, v in per.items():
+            v.sort()
+            if len(v) != sum(p["dispatches"] for p in plan):
+                raise SystemExit(f"{path}: {len(v)} library dispatches of {counter}, plan has "
+                                 f"{sum(p['dispatches'] for p in plan)}")
+            values[counter] = [x for _, x in v]
+    counters = [c for c in ("FETCH_SIZE", "WRITE_SIZE", "TCC_HIT_sum", "TCC_MISS_sum") if c in values]
+    print("| configuration | kernel | " + " | ".join(
+        {"FETCH_SIZE": "HBM read bytes", "WRITE_SIZE": "HBM written bytes", "TCC_HIT_sum": "L2 hits",
+         "TCC_MISS_sum": "L2 misses"}[c] for c in counters) + " | traffic / algorithmic |")
+    print("|---|---|" + "---|" * len(counters) + "---|")
+    at = 0
+    for p in plan:
+        cells = []
+        med = {}
+        for c in counters:
+            med[c] = _median(values[c][at:at + p["dispatches"]]) * scale.get(c, 1.0)
+            cells.append(f"{med[c]:,.0f}")
+        ratio = ""
+        if "FETCH_SIZE" in med and "WRITE_SIZE" in med:
+            ratio = f"{(med['FETCH_SIZE'] + med['WRITE_SIZE']) / run['algorithmic_bytes']:.3f}"
+        print(f"| {p['label']} | {p['kernel']} | " + " | ".join(cells) + f" | {ratio} |")
+        at += p["dispatches"]
+    return 0
 
 
 def host_threads() -> int:
@@ -554,6 +759,8 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     if args.summarize_trace:
         return summarize_trace(*args.summarize_trace)
+    if args.summarize_config_counters:
+        return summarize_config_counters(*args.summarize_config_counters)
     if args.summarize_counters:
         return summarize_counters(args.summarize_counters, args.counters_out or COUNTERS, args.counter_steps)
     if args.gpus != 1:
@@ -577,6 +784,13 @@ def main(argv=None) -> int:
         return 0
     if args.stream_ceilings:
         print(json.dumps({"stream": time_streams(args.stream_ceilings, args.steps, args.warmup)}), flush=True)
+        return 0
+
+    if args.launch_configs:
+        w = W.get(args.launch_configs)
+        configs = [parse_config(c) for c in args.config] or default_configs(w)
+        print(json.dumps({"launch_configs": time_configs(w, configs, args.steps, args.warmup, args.reps,
+                                                         args.counter_pass)}), flush=True)
         return 0
 
     w = W.get(args.workload)

@@ -91,3 +91,51 @@ def test_counter_summary(tmp_path, monkeypatch):
     json.dump(data, open(out, "w"))
     assert bench.counter_traffic(data["entries"][0]["kernel"], data["entries"][0]["workload"]) is None
     assert bench.counter_traffic("no_such_kernel", w.name) is None
+
+
+def test_launch_config_arguments():
+    a = bench.parse_args(["--launch-configs", "bcast_64x512x4096_f32", "--config=-1:0:2:1", "--config=7:1:1:0"])
+    assert [bench.parse_config(c) for c in a.config] == [(-1, 0, 2, 1), (7, 1, 1, 0)]
+    with pytest.raises(SystemExit):
+        bench.parse_config("1:2:3")
+    # a cyclic broadcast skip adds the skip-stationary tiling; both store policies each
+    c4 = bench.default_configs(W.WORKLOADS["bcast_64x512x4096_f32"])
+    assert (-1, 0, 2, 0) in c4 and (-1, 0, 2, 1) in c4 and len(c4) == 6
+    c5 = bench.default_configs(W.WORKLOADS["rows65536_h8192_f16_mean100"])
+    assert all(t != 2 for _, _, t, _ in c5) and len(c5) == 4
+
+
+def test_config_counter_summary(tmp_path, monkeypatch, capsys):
+    """Library dispatches are split by the plan in dispatch order (other
+    kernels ignored, rows out of order sorted by Dispatch_Id), per-config
+    medians scaled by the stored copy calibration; a plan that does not match
+    the dispatch count is refused."""
+    root = tmp_path / "pmc"
+    cal = tmp_path / "counters.json"
+    json.dump({"copy_calibration": {"fetch_scale": 2.0, "write_scale": 1.0}}, open(cal, "w"))
+    monkeypatch.setattr(bench, "COUNTERS", str(cal))
+    plan = {"workload": "w", "algorithmic_bytes": 3 * 1024 * 100,
+            "plan": [{"label": "first", "config": None, "kernel": "k0", "dispatches": 3},
+                     {"label": "second", "config": [-1, 0, 1, 0], "kernel": "k0", "dispatches": 3}]}
+    plan_path = tmp_path / "plan.json"
+    plan_path.write_text("[bench] log line\n" + json.dumps({"launch_configs": plan}) + "\n")
+    for counter, values in (("FETCH_SIZE", [100, 100, 900, 200, 200, 200]), ("WRITE_SIZE", [100] * 6)):
+        d = root / counter
+        d.mkdir(parents=True)
+        with open(d / "run_counter_collection.csv", "w", newline="") as fh:
+            w = csv.writer(fh)
+            w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writerow([1, "__amd_rocclr_copyBuffer", counter, 5])
+            rows = [(i + 2, "void skipln::rowtile::rowtile_kernel<...>", counter, v) for i, v in enumerate(values)]
+            for r in reversed(rows):
+                w.writerow(r)
+    assert bench.summarize_config_counters(str(root), str(plan_path)) == 0
+    out = capsys.readouterr().out.splitlines()
+    first = [ln for ln in out if ln.startswith("| first")][0]
+    second = [ln for ln in out if ln.startswith("| second")][0]
+    assert "204,800" in first and "102,400" in first and "| 1.000 |" in first   # median 100 KiB x 2, 100 KiB x 1
+    assert "409,600" in second and "| 1.667 |" in second
+    plan["plan"][1]["dispatches"] = 4
+    plan_path.write_text(json.dumps(plan) + "\n")
+    with pytest.raises(SystemExit):
+        bench.summarize_config_counters(str(root), str(plan_path))
