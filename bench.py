@@ -92,7 +92,7 @@ def parse_args(argv=None):
                         "and both store policies), graph replays interleaved --reps times")
     p.add_argument("--config", action="append", default=[], metavar="G:T:TILING:STORE",
                    help="a launch configuration for --launch-configs: row-tile geometry index (-1: the automatic "
-                        "one), tiles per block (0: sized to the resident grid), SKIPLN_TILE_* and SKIPLN_STORE_* "
+                        "one), tiles per block (0: the launcher's default), SKIPLN_TILE_* and SKIPLN_STORE_* "
                         "values; repeatable")
     p.add_argument("--reps", type=int, default=6, help="interleaved replays per configuration (--launch-configs)")
     p.add_argument("--counter-pass", action="store_true",
@@ -371,11 +371,11 @@ def default_configs(w):
     """Launch configurations compared with the automatic one: the automatic
     geometry with each tiling that applies to the workload (a block per tile;
     a resident grid walking the tiles; for a cyclic broadcast skip, blocks
-    that keep their skip rows and walk the batches) and both store
-    policies."""
+    that keep their skip rows and walk 3 batches, or all of them) and both
+    store policies."""
     shapes = [(1, 1), (0, 1)]
     if w.broadcast and not w.inner:
-        shapes = [(0, 2)] + shapes
+        shapes = [(3, 2), (w.rows // w.skip_rows, 2)] + shapes
     return [(-1, per, tiling, store) for per, tiling in shapes for store in (0, 1)]
 
 
@@ -390,7 +390,7 @@ def config_label(cfg, L) -> str:
     if cfg is None:
         return "automatic"
     g, per, tiling, store = cfg
-    shape = "resident grid" if per == 0 else f"{per} tile(s) per block"
+    shape = "default grid" if per == 0 else f"{per} tile(s) per block"
     geom = "auto geometry" if g < 0 else f"geometry {g}"
     return f"{geom}, {TILING_NAMES.get(tiling, tiling)}, {shape}, {STORE_NAMES.get(store, store)} stores"
 

@@ -106,7 +106,8 @@ SKIPLN_API int skipln_tune_forward(int op, const void* input, const void* skip, 
  * (0 <= geometry < skipln_tune_rowtile_geometries()), -1 for the automatic
  * choice, or SKIPLN_VARIANT_ELEMENT_GEOMETRY + g for element-wise geometry g.
  * tiles_per_block (T) > 0: row tiles (batches, for
- * SKIPLN_TILE_SKIP_STATIONARY) per block; 0: sized so the grid matches the
+ * SKIPLN_TILE_SKIP_STATIONARY) per block; 0: the launcher's choice -- three
+ * batches per block for SKIPLN_TILE_SKIP_STATIONARY, otherwise a grid of the
  * blocks the device holds at once (SKIPLN_TILE_CONTIGUOUS then behaves as
  * SKIPLN_TILE_STRIDED).  tiling: SKIPLN_TILE_*.  store: SKIPLN_STORE_*.
  * Returns SKIPLN_ERR_UNSUPPORTED when the geometry cannot hold the row or the

@@ -100,7 +100,7 @@ def test_launch_config_arguments():
         bench.parse_config("1:2:3")
     # a cyclic broadcast skip adds the skip-stationary tiling; both store policies each
     c4 = bench.default_configs(W.WORKLOADS["bcast_64x512x4096_f32"])
-    assert (-1, 0, 2, 0) in c4 and (-1, 0, 2, 1) in c4 and len(c4) == 6
+    assert (-1, 3, 2, 0) in c4 and (-1, 64, 2, 1) in c4 and len(c4) == 8
     c5 = bench.default_configs(W.WORKLOADS["rows65536_h8192_f16_mean100"])
     assert all(t != 2 for _, _, t, _ in c5) and len(c5) == 4
 

@@ -75,8 +75,8 @@ bool generic_outruns_split(int op, int64_t hidden, int dtype, int64_t rows, int 
 // block, so blocks are dispatched in address order and the set of rows in
 // flight stays compact; this reached the 2-read/2-write streaming rate on
 // MI355X.  A cyclic broadcast skip is shared by every batch: each block of a
-// normalization keeps its skip rows (and gamma/beta) in registers and walks
-// the batches.  BiasSoftmax has no parameters to keep and measured faster
+// normalization keeps its skip rows (and gamma/beta) in registers and walks a
+// few batches (the launcher's default).  BiasSoftmax has no parameters to keep and measured faster
 // streaming its rows in address order, its bias rows served by the caches,
 // as is grouped (inner) reuse, whose consecutive rows share a bias row.
 Tiling auto_tiling(int op, int skip_mode) {

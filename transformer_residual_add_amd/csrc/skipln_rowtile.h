@@ -524,6 +524,8 @@ hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipSt
 }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+// Batches a skip-stationary block walks when the launch does not say.
+constexpr int64_t kStationaryBatches = 3;
 // A dispatch counts its work-items in 32 bits: blocks x block stays below 2^32.
 constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
@@ -543,7 +545,7 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
         (a.skip_rows <= 0 || a.skip_rows % rpb != 0 || a.skip_rows / rpb > max_blocks))
         mode = kTileStrided;
     int64_t resident = 0;
-    if (per <= 0) {
+    if (per <= 0 && mode != kTileSkipStationary) {
         const hipError_t e = resident_blocks(kernel, g.block, &occ, &resident);
         if (e != hipSuccess) return e;
     }
@@ -552,9 +554,16 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
         const int64_t P = a.skip_rows / rpb;
         const int64_t batches = a.rows / a.skip_rows;
         if (per <= 0) {
-            // Enough batch chunks per tile column to fill the resident grid.
-            const int64_t chunks = resident > P ? resident / P : 1;
-            per = (batches + chunks - 1) / chunks;
+            // Each block keeps its skip rows for kStationaryBatches batches.
+            // Measured on MI355X over seven broadcast shapes (64-512
+            // batches of 64-2048 skip rows, 768-8192 values, both types,
+            // layer norm and RMS): 3 batches per block was the fastest or
+            // within 2 % of it on every shape, and 8-15 % faster on six of
+            // them than a grid sized to the resident blocks; that grid's
+            // speed also swung with the block count (on 64 batches of 512
+            // float32 rows of 4096: 175 us at 512 blocks, 190-205 us at
+            // 1024-2048, 178 us at 3 batches per block).
+            per = kStationaryBatches < batches ? kStationaryBatches : batches;
         }
         // At most max_blocks / P batch chunks per tile column.
         const int64_t chunks_max = max_blocks / P;
