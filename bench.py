@@ -732,8 +732,8 @@ def summarize_trace(trace_csv: str, bench_json: str) -> int:
     from transformer_residual_add_amd import workloads as W
 
     print("| workload | kernel (library name) | dispatches | avg all us | avg timed us | median timed us | "
-          "bench.py events us | trace / events | % of 8 TB/s (trace) |")
-    print("|---|---|---|---|---|---|---|---|---|")
+          "min timed us | bench.py events us | trace / events | % of 8 TB/s (trace) |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
     used = set()
     for r in runs:
         # the trace names kernels by their template arguments: take the kernel
@@ -750,7 +750,7 @@ def summarize_trace(trace_csv: str, bench_json: str) -> int:
         avg_t = sum(timed) / len(timed)
         alg = W.get(r["workload"]).algorithmic_bytes()
         print(f"| {r['workload']} | {r['kernel']} | {len(d)} | {sum(allv) / len(allv):.2f} | {avg_t:.2f} | "
-              f"{_median(timed):.2f} | {r['launch_us']:.2f} | {avg_t / r['launch_us']:.3f} | "
+              f"{_median(timed):.2f} | {min(timed):.2f} | {r['launch_us']:.2f} | {avg_t / r['launch_us']:.3f} | "
               f"{alg / (avg_t * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} |")
     return 0
 

@@ -1,7 +1,8 @@
 """skipln_forward_ws_static (no allocation, library-held scratch) against
 skipln_forward_ws (caller workspace) through the C ABI: the same kernels on
 the same inputs give the same bits, call after call, the second call of each
-pair smaller than the first; both also within tolerance of the oracle."""
+pair smaller than the first; both also within tolerance of the oracle.  And
+the call such callers make it for: captured in a HIP graph and replayed."""
 import numpy as np
 import pytest
 
@@ -23,16 +24,16 @@ def gpu_ready():
     torch.cuda.synchronize()
 
 
-def _call(entry, w, dc, out, res, ws=None):
+def _call(entry, w, dc, out, res, ws=None, stream=None):
     p = lambda t: None if t is None else t.data_ptr()
     args = (U.OPS[w.op], p(dc.x), p(dc.skip), U.skip_mode(w), w.skip_rows if w.broadcast else 0, p(dc.gamma),
             p(dc.beta), p(dc.bias), p(out), p(res), w.rows, w.hidden, float(np.float32(w.eps)),
             L.F32 if w.dtype == "f32" else L.F16)
     lib = L.load()
     if entry == "static":
-        st = lib.skipln_forward_ws_static(*args, None)
+        st = lib.skipln_forward_ws_static(*args, stream)
     else:
-        st = lib.skipln_forward_ws(*args, ws[0], ws[1], None)
+        st = lib.skipln_forward_ws(*args, ws[0], ws[1], stream)
     L.check(st, f"skipln_forward_ws{'_static' if entry == 'static' else ''}")
 
 
@@ -81,3 +82,43 @@ def test_static_scratch_matches_caller_workspace(name, big, small):
             U.assert_bits_equal(dc.host(dc.res), ref_res.cpu().numpy().reshape(w.rows, w.hidden),
                                 f"{name} residual rows={w.rows}")
         U.compare(w, got, dc.host(dc.res) if w.residual else None, U.oracle_rows(w, inputs))
+
+
+def test_static_scratch_under_graph_capture():
+    """A split-row layer norm through skipln_forward_ws_static, captured in a
+    HIP graph on a side stream and replayed three times; between replays an
+    eager call of another shape goes through the same scratch.  Every replay
+    writes the eager call's bits (the kernels clear nothing with memsets, so
+    the graph holds kernel nodes only)."""
+    import torch
+
+    big, other = _case(16, 65536, "f32", "layer_norm", 11), _case(5, 45056, "f32", "layer_norm", 12)
+    dcs = {}
+    for w in (big, other):
+        dcs[w.name] = U.DeviceCase(w, W.make_inputs(w), residual=True)
+    dc, dco = dcs[big.name], dcs[other.name]
+    U.note(f"no-alloc graph: eager rows={big.rows} H={big.hidden}")
+    _call("static", big, dc, dc.out, dc.res)
+    torch.cuda.synchronize()
+    want_out, want_res = dc.out.clone(), dc.res.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _call("static", big, dc, dc.out, dc.res, stream=s.cuda_stream)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    U.note("no-alloc graph: capture")
+    with torch.cuda.graph(g, stream=s):
+        _call("static", big, dc, dc.out, dc.res, stream=s.cuda_stream)
+    for i in range(3):
+        U.note(f"no-alloc graph: eager call rows={other.rows} H={other.hidden}, then replay {i}")
+        _call("static", other, dco, dco.out, dco.res)
+        dc.out.fill_(float("nan"))
+        dc.res.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dc.out.view(torch.int32), want_out.view(torch.int32)), f"replay {i}: output bits"
+        assert torch.equal(dc.res.view(torch.int32), want_res.view(torch.int32)), f"replay {i}: residual bits"
+    inputs = W.make_inputs(big)
+    U.compare(big, dc.host(dc.out), dc.host(dc.res), U.oracle_rows(big, inputs))
