@@ -117,17 +117,18 @@ class DeviceCase:
         return buf.data_ptr(), n
 
     def run(self, variant: int = L.VARIANT_AUTO, stream: int = 0, out=None, res="default", workspace=None):
-        """``workspace``: None (skipln_forward_variant), True (a fresh one of the
-        size the call needs, through skipln_forward_ws) or (pointer, bytes)."""
+        """``workspace``: None (no workspace: the operation's own entry point,
+        or skipln_tune_forward for a forced family), True (a fresh one of the
+        size the call needs) or (pointer, bytes)."""
         w = self.w
         p = lambda t: None if t is None else t.data_ptr()
         o = self.out if out is None else out
         r = self.res if res == "default" else res
         if workspace is True:
             workspace = self.workspace(variant)
-        T.forward_raw(p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma), p(self.beta), p(self.bias), p(o), p(r),
-                      w.rows, w.hidden, float(np.float32(w.eps)), L.F32 if w.dtype == "f32" else L.F16,
-                      stream, variant, OPS[w.op], workspace=workspace)
+        T.forward_raw(p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma),
+                      p(self.beta), p(self.bias), p(o), p(r), w.rows, w.hidden, float(np.float32(w.eps)),
+                      L.F32 if w.dtype == "f32" else L.F16, stream, variant, OPS[w.op], workspace=workspace)
 
     def run_config(self, geometry: int, tiles_per_block: int, strided: int, stream: int = 0,
                    store: int = L.STORE_AUTO):

@@ -42,7 +42,9 @@ constexpr int kTileSkipStationary = 2;  // broadcast skip: fixed skip rows per b
 
 // How a row-tile launch distributes tiles over blocks.
 struct Tiling {
-    int64_t tiles_per_block;  // 0: sized so the grid matches the resident blocks
+    int64_t tiles_per_block;  // 0: the launcher's choice (skip-stationary:
+                              // 3 batches per block; otherwise a grid of the
+                              // blocks the device holds at once)
     int mode;                 // kTile*
 };
 
