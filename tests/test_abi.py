@@ -562,3 +562,27 @@ def test_static_entry_argument_checks():
     assert st(out=None) == L.ERR_NULL
     assert st(out=IN + 4) == L.ERR_ALIAS
     assert st(rows=0) == L.OK
+
+
+def test_rejected_arguments_raise_value_error():
+    """The binding raises a SkiplnError for every status but SKIPLN_OK; a
+    status that rejects the arguments is also a ValueError naming the
+    status, one that reports the runtime or device is not."""
+    import transformer_residual_add_amd as T
+
+    L.check(L.OK, "ok")
+    for st in (L.ERR_NULL, L.ERR_SHAPE, L.ERR_DTYPE, L.ERR_MODE, L.ERR_EPS, L.ERR_ALIAS, L.ERR_UNSUPPORTED,
+               L.ERR_VARIANT, L.ERR_OP, L.ERR_WORKSPACE):
+        with pytest.raises(ValueError) as e:
+            L.check(st, "call")
+        assert isinstance(e.value, L.SkiplnError) and e.value.status == st
+        assert L.status_string(st) in str(e.value)
+    for st in (L.ERR_LAUNCH, L.ERR_DEVICE):
+        with pytest.raises(L.SkiplnError) as e:
+            L.check(st, "call")
+        assert not isinstance(e.value, ValueError)
+    # host-only paths of the binding: an unknown element type, an unknown operation
+    with pytest.raises(ValueError):
+        T.workspace_bytes(L.OP_LAYER_NORM, 4, 64, 7)
+    with pytest.raises(ValueError):
+        T.workspace_bytes(9, 4, 64, L.F32)

@@ -14,14 +14,14 @@ from __future__ import annotations
 from typing import Optional
 
 from . import _lib
-from ._lib import SkiplnError  # noqa: F401
+from ._lib import SkiplnArgumentError, SkiplnError  # noqa: F401
 
 # The manifest's default epsilon: 1e-12 rounded to binary32
 # (SkipLayerNormalization manifest, `attributes.epsilon`).
 DEFAULT_EPSILON = 9.999999960041972e-13
 
 __all__ = ["skip_layer_norm", "bias_add", "bias_softmax", "bias_softmax_raw", "softmax_shape", "forward_raw",
-           "workspace_bytes", "select_kernel", "SkiplnError", "DEFAULT_EPSILON"]
+           "workspace_bytes", "select_kernel", "SkiplnError", "SkiplnArgumentError", "DEFAULT_EPSILON"]
 
 
 def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, gamma_ptr: Optional[int],
@@ -51,7 +51,7 @@ def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, g
         st = lib.skipln_forward_simplified(*args, stream or None)
     elif op == _lib.OP_BIAS_ADD:
         if skip_mode != _lib.SKIP_EXACT:
-            raise SkiplnError(_lib.ERR_MODE, "skipln_bias_add")
+            _lib.check(_lib.ERR_MODE, "skipln_bias_add")
         st = lib.skipln_bias_add(input_ptr, bias_ptr or None, skip_ptr, out_ptr, rows, hidden, dtype, stream or None)
     elif op == _lib.OP_BIAS_SOFTMAX:
         bias_rows = rows if skip_mode == _lib.SKIP_EXACT else skip_rows
@@ -59,7 +59,7 @@ def forward_raw(input_ptr: int, skip_ptr: int, skip_mode: int, skip_rows: int, g
                                      1 if skip_mode == _lib.SKIP_BROADCAST_INNER else 0, dtype, None, 0,
                                      stream or None)
     else:
-        raise SkiplnError(_lib.ERR_OP, "forward_raw")
+        _lib.check(_lib.ERR_OP, "forward_raw")
     _lib.check(st, "skipln_forward")
 
 
@@ -73,7 +73,7 @@ def workspace_bytes(op: int, rows: int, hidden: int, dtype: int, skip_mode: int 
     else:
         n = _lib.load_tune().skipln_tune_workspace_bytes(op, rows, hidden, dtype, skip_mode, skip_rows, variant)
     if n < 0:
-        raise SkiplnError(-n, "skipln_workspace_bytes")
+        _lib.check(-n, "skipln_workspace_bytes")
     return int(n)
 
 
@@ -119,7 +119,7 @@ def select_kernel(hidden: int, dtype: int, aligned16: bool = True, variant: int 
     kid = _lib.load_tune().skipln_tune_select(op, rows, hidden, dtype, skip_mode, 1 if aligned16 else 0, variant,
                                               1 if workspace else 0, cus)
     if kid < 0:
-        raise SkiplnError(-kid, "skipln_tune_select")
+        _lib.check(-kid, "skipln_tune_select")
     return _lib.kernel_name(kid)
 
 

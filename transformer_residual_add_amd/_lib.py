@@ -62,9 +62,20 @@ _libs = {}
 
 
 class SkiplnError(RuntimeError):
+    """A status other than SKIPLN_OK; ``status`` holds the code."""
+
     def __init__(self, status: int, where: str = "skipln"):
         self.status = status
         super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+class SkiplnArgumentError(SkiplnError, ValueError):
+    """A status that rejects the call's arguments (nothing was enqueued)."""
+
+
+# Statuses that reject arguments; the others report the runtime or device.
+ARGUMENT_STATUSES = frozenset({ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS, ERR_UNSUPPORTED,
+                               ERR_VARIANT, ERR_OP, ERR_WORKSPACE})
 
 
 def _open(path: str, signatures) -> C.CDLL:
@@ -114,5 +125,7 @@ def kernel_name(kernel_id: int) -> str:
 
 
 def check(status: int, where: str) -> None:
+    """Raise for any status but SKIPLN_OK: SkiplnArgumentError (also a
+    ValueError) for rejected arguments, SkiplnError otherwise."""
     if status != OK:
-        raise SkiplnError(status, where)
+        raise (SkiplnArgumentError if status in ARGUMENT_STATUSES else SkiplnError)(status, where)
