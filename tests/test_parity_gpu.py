@@ -36,20 +36,28 @@ def test_workload_all_rows(name):
 ORACLE_BLOCK = 4096  # rows per oracle call in the full-size comparison
 
 
-@pytest.mark.parametrize("name", W.ORDER[3:])
+# The two largest configurations, and the benchmark's full-size root-mean-square
+# and BiasAdd workloads.
+FULL_SIZE = list(W.ORDER[3:]) + ["rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
 def test_workload_full_size_every_row(name):
     """Full-size run in the benchmark's launch configuration, every row
     compared with the oracle: the normalized output within tolerance, the
-    residual (when emitted) bit for bit.  The oracle runs in blocks of rows on
-    the host's cores while the device result is copied back block by block."""
+    residual (when emitted) and BiasAdd's output bit for bit.  The oracle runs
+    in blocks of rows on the host's cores while the device result is copied
+    back block by block."""
     import torch
 
-    w = W.WORKLOADS[name]
+    w = W.get(name)
     U.note(f"workload {name}: generating rows={w.rows} H={w.hidden} {w.dtype}")
     inputs = W.make_inputs(w)
     dc = U.DeviceCase(w, inputs, residual=w.residual)
     mode = L.SKIP_BROADCAST if w.broadcast else L.SKIP_EXACT
-    U.note(f"workload {name}: launching {T.select_kernel(w.hidden, L.F32 if w.dtype == 'f32' else L.F16, skip_mode=mode)}")
+    kernel = T.select_kernel(w.hidden, L.F32 if w.dtype == "f32" else L.F16, skip_mode=mode, op=U.OPS[w.op],
+                             rows=w.rows)
+    U.note(f"workload {name}: launching {kernel}")
     dc.run()
     torch.cuda.synchronize()
     U.note(f"workload {name}: comparing all {w.rows} rows with the oracle")
@@ -63,7 +71,10 @@ def test_workload_full_size_every_row(name):
         if not w.broadcast:
             part["skip"] = inputs["skip"][r0:r1]
         ref = U.oracle_rows(w, part, row_offset=r0, threads=threads)
-        U.assert_out_close(out[r0:r1].cpu().numpy(), ref["y"], w.dtype, f"out rows {r0}:{r1}")
+        if w.op == "bias_add":
+            U.assert_bits_equal(out[r0:r1].cpu().numpy(), ref["y"], f"bias_add out rows {r0}:{r1}")
+        else:
+            U.assert_out_close(out[r0:r1].cpu().numpy(), ref["y"], w.dtype, f"out rows {r0}:{r1}")
         if res is not None:
             U.assert_bits_equal(res[r0:r1].cpu().numpy(), ref["residual"], f"residual rows {r0}:{r1}")
 
