@@ -51,7 +51,7 @@ def kernel_sources(kernel: str):
     elif "splitrow_" in kernel:
         files = ("skipln_device.h", "skipln_split.hip")
     elif "regrow_" in kernel:
-        files = ("skipln_device.h", "skipln_regrow.hip")
+        files = ("skipln_device.h", "skipln_regrow.hip" if kernel.startswith("softmax_") else "skipln_regnorm.hip")
     else:
         files = ("skipln_device.h", "skipln_kernels.hip")
     return [os.path.join(CSRC, f) for f in files]

@@ -273,7 +273,7 @@ def test_select_kernels():
     for g in range(ne):
         assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + g)).startswith("rowelem_f32_g")
     assert name(sel(20000, 0)) == "ldsrow_f32"
-    assert name(sel(50000, 0)) == "generic_f32"
+    assert name(sel(50000, 0)) == "regrow_f32"                      # held in registers
     assert name(sel(8, 1, v=1)) == "generic_f16"
     assert sel(1001, 0, v=L.VARIANT_ROWTILE) == -L.ERR_UNSUPPORTED
     assert name(sel(64, 0, v=L.VARIANT_MULTIWAVE)).startswith("rowtile_f32_g128")
@@ -292,11 +292,14 @@ def test_select_kernels():
     assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
     assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
-    # long rows: LDS-staged up to 163584 bytes of binary32 sums, then generic
+    # long rows: LDS-staged up to 163584 bytes of binary32 sums, then held
+    # in registers up to 65536 values, then generic
     assert name(sel(8192, 0)) == "rowtile_f32_g512_c4"
     assert name(sel(8196, 0)) == "ldsrow_f32"
     assert name(sel(40896, 0)) == "ldsrow_f32"
-    assert name(sel(40900, 0)) == "generic_f32"
+    assert name(sel(40900, 0)) == "regrow_f32"
+    assert name(sel(65536, 1, op=L.OP_SIMPLIFIED)) == "rms_regrow_f16"
+    assert name(sel(65540, 0)) == "generic_f32"
     assert name(sel(16392, 1, op=L.OP_SIMPLIFIED)) == "rms_ldsrow_f16"
     assert name(sel(16392, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g1024_c3"
     assert name(sel(64, 0, v=L.VARIANT_LDSROW)) == "ldsrow_f32"
@@ -393,15 +396,19 @@ def test_workspace_sizes_and_split_selection():
     # one float4 partial per slice of a batch of rows; a batch streams at most
     # 128 MiB of inputs (x, and skip when it is not broadcast)
     ws = lambda rows, slices: rows * slices * 16
-    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == ws(64, 16)
+    assert wb(L.OP_LAYER_NORM, 64, 131072, L.F32) == ws(64, 32)
     assert wbv(L.OP_LAYER_NORM, 1000, 65536, L.F32, v=L.VARIANT_SPLITROW) == ws(256, 16)
     assert wbv(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8, L.VARIANT_SPLITROW) == ws(512, 16)
     # the operator library's size does not depend on the device: whatever the
     # row count, a call that may split its rows gets the split-row size
-    assert wb(L.OP_LAYER_NORM, 255, 65536, L.F32) == ws(255, 16)
-    assert wb(L.OP_LAYER_NORM, 256, 65536, L.F32) == ws(256, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F32, L.SKIP_BROADCAST, 8) == ws(512, 16)
-    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F16) == ws(512, 8)
+    for rows in (255, 256, 1000):
+        assert wb(L.OP_LAYER_NORM, rows, 131072, L.F32) == \
+            wbv(L.OP_LAYER_NORM, rows, 131072, L.F32, v=L.VARIANT_SPLITROW) > 0
+    assert wb(L.OP_LAYER_NORM, 1000, 131072, L.F32, L.SKIP_BROADCAST, 8) == ws(256, 32)
+    assert wb(L.OP_LAYER_NORM, 1000, 131072, L.F16) == ws(256, 16)
+    # rows held in registers need none
+    assert wb(L.OP_LAYER_NORM, 64, 65536, L.F32) == 0
+    assert wb(L.OP_LAYER_NORM, 1000, 65536, L.F16) == 0
     assert wb(L.OP_SIMPLIFIED, 255, 262144, L.F32) == ws(64, 64)
     assert wb(L.OP_BIAS_SOFTMAX, 1024, 163848, L.F16) > 0
     assert wb(L.OP_LAYER_NORM, 201, 65540, L.F32) == ws(201, 17)
@@ -417,19 +424,26 @@ def test_workspace_sizes_and_split_selection():
     assert wb(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4) == 0     # held in registers
     assert wbv(L.OP_BIAS_SOFTMAX, 64, 128256, L.F16, L.SKIP_BROADCAST_INNER, 4, L.VARIANT_SPLITROW) == ws(64, 16)
     assert wb(L.OP_BIAS_SOFTMAX, 64, 163848, L.F16) == ws(64, 21)                     # beyond the registers
-    # the automatic choice: split rows only where a workspace is at hand ...
-    assert name(L.OP_LAYER_NORM, 65536, L.F32) == "generic_f32"
-    assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1) == "splitrow_f32"
-    assert name(L.OP_SIMPLIFIED, 65536, L.F16, ws=1) == "rms_splitrow_f16"
-    # ... and with fewer rows than the device has compute units: from one row
-    # per CU, RMS and float32 layer norm up to 65536 values run generic
+    # the automatic choice: rows up to 65536 values held in registers (float16
+    # always; float32 with at most two rows per compute unit, else generic) ...
+    for ws_ in (0, 1):
+        assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=ws_) == "regrow_f32"
+        assert name(L.OP_SIMPLIFIED, 65536, L.F16, ws=ws_, rows=10 ** 6) == "rms_regrow_f16"
     for cus in (256, 80):
-        assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1, rows=cus - 1, cus=cus) == "splitrow_f32"
-        assert name(L.OP_LAYER_NORM, 65536, L.F32, ws=1, rows=cus, cus=cus) == "generic_f32"
+        for op, pre in ((L.OP_LAYER_NORM, ""), (L.OP_SIMPLIFIED, "rms_")):
+            assert name(op, 65536, L.F32, ws=1, rows=2 * cus, cus=cus) == pre + "regrow_f32"
+            assert name(op, 65536, L.F32, ws=1, rows=2 * cus + 1, cus=cus) == pre + "generic_f32"
+            assert name(op, 65536, L.F16, ws=1, rows=100 * cus, cus=cus) == pre + "regrow_f16"
+    # ... longer rows split only where a workspace is at hand, and with fewer
+    # rows than the device has compute units: from one row per CU, RMS runs
+    # generic
+    assert name(L.OP_LAYER_NORM, 131072, L.F32) == "generic_f32"
+    assert name(L.OP_LAYER_NORM, 131072, L.F32, ws=1) == "splitrow_f32"
+    for cus in (256, 80):
         assert name(L.OP_SIMPLIFIED, 262144, L.F32, ws=1, rows=cus, cus=cus) == "rms_generic_f32"
         assert name(L.OP_SIMPLIFIED, 262144, L.F32, ws=1, rows=cus - 1, cus=cus) == "rms_splitrow_f32"
     assert name(L.OP_LAYER_NORM, 65540, L.F32, ws=1, rows=1000) == "splitrow_f32"       # beyond 65536
-    assert name(L.OP_LAYER_NORM, 65536, L.F16, ws=1, rows=1000) == "splitrow_f16"       # float16 keeps it
+    assert name(L.OP_LAYER_NORM, 131072, L.F16, ws=1, rows=1000) == "splitrow_f16"      # float16 keeps it
     assert name(L.OP_BIAS_SOFTMAX, 128256, L.F16, ws=1) == "softmax_regrow_f16"
     assert name(L.OP_BIAS_SOFTMAX, 163848, L.F16, ws=1) == "softmax_splitrow_f16"
     assert name(L.OP_LAYER_NORM, 20000, L.F32, ws=1) == "ldsrow_f32"
@@ -468,27 +482,36 @@ def test_register_resident_softmax_selection():
     assert SEL(L.OP_BIAS_SOFTMAX, 81924, L.F32, v=L.VARIANT_REGROW) == unsupported
     assert SEL(L.OP_BIAS_SOFTMAX, 77, L.F32, v=L.VARIANT_REGROW) == unsupported    # not chunks
     assert SEL(L.OP_BIAS_SOFTMAX, 4096, L.F32, al=0, v=L.VARIANT_REGROW) == unsupported  # misaligned
-    for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED, L.OP_BIAS_ADD):
-        assert SEL(op, 65536, L.F16, v=L.VARIANT_REGROW) == unsupported
+    assert SEL(L.OP_BIAS_ADD, 65536, L.F16, v=L.VARIANT_REGROW) == unsupported
+    # the normalizations' register-resident rows: 32776-65536 float16,
+    # 36868-65536 float32 values
+    assert name(65536, L.F16, v=L.VARIANT_REGROW, op=L.OP_LAYER_NORM) == "regrow_f16"
+    assert name(32776, L.F16, v=L.VARIANT_REGROW, op=L.OP_SIMPLIFIED) == "rms_regrow_f16"
+    assert name(36868, L.F32, v=L.VARIANT_REGROW, op=L.OP_LAYER_NORM) == "regrow_f32"
+    for op in (L.OP_LAYER_NORM, L.OP_SIMPLIFIED):
+        assert SEL(op, 32768, L.F16, v=L.VARIANT_REGROW) == unsupported
+        assert SEL(op, 36864, L.F32, v=L.VARIANT_REGROW) == unsupported
+        assert SEL(op, 65544, L.F16, v=L.VARIANT_REGROW) == unsupported
+        assert SEL(op, 65540, L.F32, v=L.VARIANT_REGROW) == unsupported
     # misaligned long rows take the generic kernel
     assert name(65536, L.F16, al=0) == "softmax_generic_f16"
 
 
-def FW(ws, nbytes, hidden=65536, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM, res=RES):
+def FW(ws, nbytes, hidden=131072, variant=L.VARIANT_AUTO, op=L.OP_LAYER_NORM, res=RES):
     """skipln_forward_ws (automatic choice) or the tuning library's forced
     family, on fake pointers: every status here returns before any HIP call."""
-    args = (IN, SK, 0, 0, GA, BE, BI, OUT, res, 4, hidden, 1e-5, L.F32)
+    args = (IN, SK, 0, 0, GA, BE, BI, OUT, res, 2, hidden, 1e-5, L.F32)
     if variant == L.VARIANT_AUTO:
         return L.load().skipln_forward_ws(op, *args, ws, nbytes, None)
     return L.load_tune().skipln_tune_forward(op, *args, variant, ws, nbytes, None)
 
 
-WS = 0x10000000  # beyond every fake tensor (4 rows of 65536 float32 = 1 MiB each)
+WS = 0x10000000  # beyond every fake tensor (2 rows of 131072 float32 = 1 MiB each)
 
 
 def test_forward_ws_workspace_checks():
-    need = L.load().skipln_workspace_bytes(L.OP_LAYER_NORM, 4, 65536, L.F32, 0, 0)
-    assert need == 4 * 16 * 16
+    need = L.load().skipln_workspace_bytes(L.OP_LAYER_NORM, 2, 131072, L.F32, 0, 0)
+    assert need == 2 * 32 * 16
     assert FW(None, 0) == L.ERR_WORKSPACE
     assert FW(WS, need - 1) == L.ERR_WORKSPACE
     assert FW(WS + 8, need) == L.ERR_WORKSPACE          # not 16-byte aligned

@@ -34,13 +34,15 @@ def test_header_is_strict_c99_and_the_consumer_links(tmp_path):
 # (rows, hidden, dtype, skip_rows or None, beta, bias, residual, eps): an
 # exact float32 batch with every optional tensor; a float16 broadcast skip
 # without beta; rows that are not whole 16-byte chunks (element-wise tiles);
-# rows beyond one workgroup's LDS (skipln_forward runs the generic kernel,
-# the workspace and no-allocation forms the split-row pair).
+# rows beyond one workgroup's LDS held in registers; rows beyond the
+# registers too (skipln_forward runs the generic kernel, the workspace and
+# no-allocation forms the split-row pair).
 CASES = [
     (37, 768, "f32", None, True, True, True, 1e-12),
     (64, 1024, "f16", 16, False, True, True, 1e-5),
     (29, 1000, "f16", None, True, False, True, 1e-5),
-    (6, 65536, "f32", None, True, True, False, 1e-5),
+    (6, 65536, "f16", None, True, True, True, 1e-5),
+    (6, 100000, "f32", None, True, True, False, 1e-5),
 ]
 
 

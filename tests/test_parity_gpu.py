@@ -479,6 +479,58 @@ def test_long_rows_lds_staged(op, dt_hidden, flags):
     U.check_case(w, variant=L.VARIANT_LDSROW)
 
 
+REGNORM_HIDDEN = {"f32": [36868, 40960, 41000, 45056, 50000, 57344, 61444, 65536],
+                  "f16": [32776, 40960, 41000, 45056, 50000, 57344, 61448, 65536]}
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified"])
+@pytest.mark.parametrize("dt_hidden", [(d, h) for d in ("f32", "f16") for h in REGNORM_HIDDEN[d]],
+                         ids=lambda t: f"{t[0]}_h{t[1]}")
+@pytest.mark.parametrize("flags", ["all", "bare", "bcast"])
+def test_register_resident_normalizations(op, dt_hidden, flags):
+    """Rows held in the registers of one 1024-lane block, forced: every
+    compiled slab count, rows ending inside a slab, with and without beta,
+    bias and residual, exact and broadcast skip."""
+    dt, hidden = dt_hidden
+    rows = 6 if flags == "bcast" else 7
+    w = W.small_case(rows, hidden, dt, skip_rows=3 if flags == "bcast" else None, beta=flags != "bare",
+                     bias=flags != "bare", residual=flags != "bare", eps=1e-5, seed=hidden % 97, op=op)
+    U.note(f"regnorm {op} {dt} H={hidden} {flags}")
+    U.check_case(w, variant=L.VARIANT_REGROW)
+
+
+@pytest.mark.parametrize("dt,hidden,mu", [("f32", 65536, 1000.0), ("f16", 61448, 100.0), ("f32", 45056, 100.0)])
+def test_register_resident_normalizations_many_rows_far_from_zero(dt, hidden, mu):
+    """More rows than resident blocks (the persistent loop and its next-row
+    loads) with a mean far from zero (the statistics' shift), forced."""
+    w = W.small_case(600, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=3,
+                     input_dist=W.normal(mu, 1))
+    U.note(f"regnorm many rows {dt} H={hidden} mu={mu}")
+    U.check_case(w, variant=L.VARIANT_REGROW)
+
+
+def test_register_resident_normalizations_special_values():
+    """A NaN stays in its row; a constant row with eps = 0 is NaN (0/0)."""
+    w = W.small_case(5, 45056, "f32", beta=True, bias=True, residual=True, eps=0.0, seed=4)
+    inputs = W.make_inputs(w)
+    inputs["input"][1, 7] = np.nan
+    inputs["input"][2, :] = 3.0
+    inputs["skip"][2, :] = 0.0
+    inputs["bias"][:] = 0.0
+    U.note("regnorm special values")
+    U.check_case(w, variant=L.VARIANT_REGROW, inputs=inputs)
+
+
+@pytest.mark.parametrize("dt,hidden,rows", [("f16", 65536, 300), ("f32", 49152, 64)])
+def test_register_resident_normalizations_auto(dt, hidden, rows):
+    """The automatic choice takes the register-resident rows where they win."""
+    code = L.F32 if dt == "f32" else L.F16
+    assert T.select_kernel(hidden, code, rows=rows).startswith("regrow_")
+    w = W.small_case(rows, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=hidden + rows)
+    U.note(f"regnorm auto {dt} H={hidden} rows={rows}")
+    U.check_case(w)
+
+
 @pytest.mark.parametrize("dt,hidden", [("f32", 12288), ("f32", 40896), ("f16", 32768)])
 def test_long_rows_auto(dt, hidden):
     w = W.small_case(300 if hidden < 20000 else 64, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5,

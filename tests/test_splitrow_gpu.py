@@ -68,12 +68,12 @@ def test_split_softmax(dt_hidden, mode):
     U.check_case(w, variant=SPLIT, workspace=True)
 
 
-@pytest.mark.parametrize("dt,hidden,op", [("f32", 65536, "layer_norm"), ("f16", 131072, "simplified"),
+@pytest.mark.parametrize("dt,hidden,op", [("f32", 100000, "layer_norm"), ("f16", 131072, "simplified"),
                                           ("f32", 98304, "bias_softmax"), ("f16", 163848, "bias_softmax"),
                                           ("f32", 262144, "layer_norm")])
 def test_split_auto_with_workspace(dt, hidden, op):
-    """Rows beyond the LDS capacity (for BiasSoftmax, beyond the registers of
-    one block as well): the automatic choice with a workspace."""
+    """Rows beyond the LDS capacity and beyond the registers of one block:
+    the automatic choice with a workspace."""
     code = L.F32 if dt == "f32" else L.F16
     assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True).endswith(f"splitrow_{dt}")
     w = (softmax_case(8, hidden, dt, "inner", bias_rows=2) if op == "bias_softmax"
@@ -92,21 +92,25 @@ def test_split_many_rows(dt, hidden):
     U.check_case(w, variant=SPLIT, workspace=True)
 
 
-@pytest.mark.parametrize("dt,hidden,op", [("f32", 65536, "layer_norm"), ("f16", 65536, "simplified"),
-                                          ("f32", 262144, "simplified")])
-def test_many_rows_auto_takes_generic(dt, hidden, op):
-    """With a row for every CU, RMS rows and float32 layer norm rows of up
-    to 65536 values take the generic kernel even when a workspace is at hand:
-    the kernel choice for the call's row count on this device says so, and
-    the call through skipln_forward_ws (with the workspace the size query
-    asks for, unused) and through the allocating wrapper match the oracle."""
+@pytest.mark.parametrize("dt,hidden,op,per_cu,below", [("f32", 65536, "layer_norm", 2, "regrow"),
+                                                       ("f16", 131072, "simplified", 0, "splitrow"),
+                                                       ("f32", 262144, "simplified", 0, "splitrow")])
+def test_many_rows_auto_takes_generic(dt, hidden, op, per_cu, below):
+    """With many rows the generic kernel runs even when a workspace is at
+    hand: RMS rows from one row per CU (below that, the split-row pair);
+    float32 layer norm rows of up to 65536 values beyond two rows per CU
+    (below that, held in registers).  The kernel choice for the call's row
+    count on this device says so, and the call through skipln_forward_ws
+    (with the workspace the size query asks for, unused) and through the
+    allocating wrapper match the oracle."""
     import torch
 
-    rows = torch.cuda.get_device_properties(0).multi_processor_count  # a row for every CU
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rows = per_cu * cus + 1 if per_cu else cus
     w = norm_case(rows, hidden, dt, op, seed=13, mu=100.0 if op == "layer_norm" else 0.0)
     code = L.F32 if dt == "f32" else L.F16
     assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows).split("_")[-2] == "generic"
-    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows - 1).split("_")[-2] == "splitrow"
+    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows - 1).split("_")[-2] == below
     inputs = W.make_inputs(w)
     ref = U.oracle_rows(w, inputs)
     U.note(f"auto many rows {op} {dt} H={hidden} rows={rows}")
@@ -124,7 +128,7 @@ def test_many_rows_auto_takes_generic(dt, hidden, op):
 def test_split_workspace_errors_enqueue_nothing():
     import torch
 
-    w = norm_case(4, 65536, "f32", "layer_norm", seed=2)
+    w = norm_case(4, 100000, "f32", "layer_norm", seed=2)
     dc = U.DeviceCase(w, W.make_inputs(w), residual=True)
     ptr, need = dc.workspace()
     before = dc.out.clone()

@@ -43,10 +43,10 @@ def _case(rows, hidden, dt, op, seed, skip_rows=None):
 
 
 PAIRS = [
-    ("layer_norm_f32", _case(16, 65536, "f32", "layer_norm", 1), _case(5, 45056, "f32", "layer_norm", 2)),
+    ("layer_norm_f32", _case(16, 100000, "f32", "layer_norm", 1), _case(5, 70000, "f32", "layer_norm", 2)),
     ("simplified_f16", _case(12, 131072, "f16", "simplified", 3), _case(3, 49152, "f16", "simplified", 4)),
-    ("layer_norm_f16_bcast", _case(8, 65536, "f16", "layer_norm", 5, skip_rows=2),
-     _case(2, 41984, "f16", "layer_norm", 6)),
+    ("layer_norm_f16_bcast", _case(8, 131072, "f16", "layer_norm", 5, skip_rows=2),
+     _case(2, 81920, "f16", "layer_norm", 6)),
     ("softmax_f32", _case(4, 100000, "f32", "bias_softmax", 7), _case(2, 90000, "f32", "bias_softmax", 8)),
     ("layer_norm_f32_no_split", _case(64, 1024, "f32", "layer_norm", 9), _case(7, 768, "f32", "layer_norm", 10)),
 ]
@@ -92,7 +92,7 @@ def test_static_scratch_under_graph_capture():
     the graph holds kernel nodes only)."""
     import torch
 
-    big, other = _case(16, 65536, "f32", "layer_norm", 11), _case(5, 45056, "f32", "layer_norm", 12)
+    big, other = _case(16, 100000, "f32", "layer_norm", 11), _case(5, 70000, "f32", "layer_norm", 12)
     dcs = {}
     for w in (big, other):
         dcs[w.name] = U.DeviceCase(w, W.make_inputs(w), residual=True)

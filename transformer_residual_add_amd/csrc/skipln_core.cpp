@@ -199,6 +199,19 @@ int validate(const Call& c) {
     return SKIPLN_OK;
 }
 
+// Long normalization rows past the LDS kernel's capacity, held in registers
+// (up to 65,536 values) instead of split across workgroups or read twice by
+// the generic kernel.  Measured on MI355X (256 CUs), against the better of
+// the two: float16 layer norm and RMS 11-27 % faster from 128 to 4096 rows;
+// float32 22 % faster at 256 rows and 8 % at 512, within 1 % at 1024-2048
+// and slower beyond (4096 rows of 49,152 values: 8 % layer norm, 16 % RMS),
+// where the generic kernel's deeper load pipeline wins.  Rows unknown
+// (< 0) count as few.
+bool regnorm_wins(int dtype, int64_t rows, int cus) {
+    if (dtype == SKIPLN_F16) return true;
+    return rows < 0 || cus <= 0 || rows <= 2 * static_cast<int64_t>(cus);
+}
+
 int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool elem_ok, int variant,
            bool with_workspace, int64_t rows, int cus) {
     const int base = (op * 2 + dtype) * kIdsPerType;
@@ -221,11 +234,11 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
     if (variant == kVariantSplitRow) return split_ok ? base + kSplitRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     if (variant == kVariantRegRow) return reg_ok ? base + kRegRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     // Long rows of the reducing operations: staged in LDS; beyond its
-    // capacity held in registers (softmax), or split across workgroups when
-    // a workspace is at hand.
+    // capacity held in registers (softmax; the normalizations where that
+    // wins), or split across workgroups when a workspace is at hand.
     if (variant == kVariantAuto && hidden / v > kRowtileMaxAutoChunks) {
         if (lds_ok) return base + kLdsRowIndex;
-        if (reg_ok) return base + kRegRowIndex;
+        if (reg_ok && (op == SKIPLN_OP_BIAS_SOFTMAX || regnorm_wins(dtype, rows, cus))) return base + kRegRowIndex;
         if (split_ok && with_workspace && !generic_outruns_split(op, hidden, dtype, rows, cus))
             return base + kSplitRowIndex;
     }
@@ -301,22 +314,27 @@ int run(const Call& c, int variant, const Tiling* tiling, skipln_stream_t stream
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
     const bool vec = all_aligned16(c), elem = all_element_aligned(c), bcast = c.skip_mode != SKIPLN_SKIP_EXACT;
-    // First the choice for a device of any size; where that is the split-row
-    // pair the workspace must serve (checked before any HIP call), and the
-    // device's compute units decide between it and the generic kernel.
+    // First the choice for a device of any size (as few rows as it has
+    // compute units).  Where that is the split-row pair the workspace must
+    // serve (checked before any HIP call); there, and for float32 rows held in
+    // registers, the row count against the device's compute units decides
+    // between that choice and the generic kernel.
     int id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, ws != nullptr, -1, 0);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
-    if (id % kIdsPerType == kSplitRowIndex && variant == kVariantAuto) {
+    const int first = id % kIdsPerType;
+    const bool split_first = first == kSplitRowIndex;
+    const bool reg_norm_f32 = first == kRegRowIndex && c.op != SKIPLN_OP_BIAS_SOFTMAX && c.dtype == SKIPLN_F32;
+    if (variant == kVariantAuto && (split_first || reg_norm_f32)) {
         const bool residual_aliases = c.residual && (c.residual == c.input || c.residual == c.skip);
-        if (!residual_aliases) {
+        if (split_first && !residual_aliases) {
             const int w = check_workspace(c, ws, kSplitRowIndex);
             if (w != SKIPLN_OK) return w;
         }
         int cus = 0;
         const hipError_t e = device_cus(&cus);
         if (e != hipSuccess) return status_of(e);
-        id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, true, c.rows, cus);
+        id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, split_first || ws != nullptr, c.rows, cus);
         if (id < 0) return -id;
     }
     const Args a = make_args(c, store);

@@ -118,6 +118,10 @@ hipError_t launch_elem_for(const Args& a, int dtype, int geometry, Tiling tiling
 bool split_holds(int op, int64_t hidden, int dtype);
 int64_t split_workspace_bytes(const Args& a, int dtype);
 hipError_t launch_split(const Args& a, int op, int dtype, void* workspace, hipStream_t stream);
+// Register-resident long rows of the normalizations (layer norm and its
+// root-mean-square form): whether the kernel holds this row, and its launch.
+bool regnorm_holds(int op, int64_t hidden, int dtype);
+hipError_t launch_regnorm(const Args& a, int op, int dtype, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 // Streaming probe: `reads` (0-2) input streams s0, s1 to `writes` (0-2)
 // output streams d0, d1 of `chunks` 16-byte chunks each, in tiles of `block`

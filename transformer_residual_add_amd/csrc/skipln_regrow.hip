@@ -299,12 +299,14 @@ hipError_t launch_regrow_t(const Args& a, hipStream_t st) {
 }  // namespace
 
 bool regrow_holds(int op, int64_t hidden, int dtype) {
+    if (op == kOpLayerNorm || op == kOpSimplified) return regnorm_holds(op, hidden, dtype);
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     return op == kOpBiasSoftmax && hidden > 0 && hidden % v == 0 &&
            hidden / v <= static_cast<int64_t>(kRegRowBlock) * kRegRowChunks;
 }
 
 hipError_t launch_regrow(const Args& a, int op, int dtype, hipStream_t st) {
+    if (op == kOpLayerNorm || op == kOpSimplified) return launch_regnorm(a, op, dtype, st);
     if (op != kOpBiasSoftmax) return hipErrorInvalidValue;
     return dtype == 0 ? launch_regrow_t<float>(a, st) : launch_regrow_t<_Float16>(a, st);
 }
