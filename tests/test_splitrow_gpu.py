@@ -92,25 +92,21 @@ def test_split_many_rows(dt, hidden):
     U.check_case(w, variant=SPLIT, workspace=True)
 
 
-@pytest.mark.parametrize("dt,hidden,op,per_cu,below", [("f32", 65536, "layer_norm", 2, "regrow"),
-                                                       ("f16", 131072, "simplified", 0, "splitrow"),
-                                                       ("f32", 262144, "simplified", 0, "splitrow")])
-def test_many_rows_auto_takes_generic(dt, hidden, op, per_cu, below):
-    """With many rows the generic kernel runs even when a workspace is at
-    hand: RMS rows from one row per CU (below that, the split-row pair);
-    float32 layer norm rows of up to 65536 values beyond two rows per CU
-    (below that, held in registers).  The kernel choice for the call's row
-    count on this device says so, and the call through skipln_forward_ws
-    (with the workspace the size query asks for, unused) and through the
-    allocating wrapper match the oracle."""
+@pytest.mark.parametrize("dt,hidden,op", [("f16", 131072, "simplified"), ("f32", 262144, "simplified")])
+def test_many_rows_auto_takes_generic(dt, hidden, op):
+    """With a row for every CU, RMS rows beyond the registers' 65536 values
+    take the generic kernel even when a workspace is at hand (with fewer
+    rows, the split-row pair): the kernel
+    choice for the call's row count on this device says so, and the call
+    through skipln_forward_ws (with the workspace the size query asks for,
+    unused) and through the allocating wrapper match the oracle."""
     import torch
 
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    rows = per_cu * cus + 1 if per_cu else cus
+    rows = torch.cuda.get_device_properties(0).multi_processor_count  # a row for every CU
     w = norm_case(rows, hidden, dt, op, seed=13, mu=100.0 if op == "layer_norm" else 0.0)
     code = L.F32 if dt == "f32" else L.F16
     assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows).split("_")[-2] == "generic"
-    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows - 1).split("_")[-2] == below
+    assert T.select_kernel(hidden, code, op=U.OPS[op], workspace=True, rows=rows - 1).split("_")[-2] == "splitrow"
     inputs = W.make_inputs(w)
     ref = U.oracle_rows(w, inputs)
     U.note(f"auto many rows {op} {dt} H={hidden} rows={rows}")

@@ -58,17 +58,18 @@ bool all_element_aligned(const Call& c) {
     return true;
 }
 
-// Many long rows of a normalization: the generic kernel's chunk form (one
-// 1024-lane workgroup per row, the row's first 40,832 sums parked in LDS, no
-// workspace) outruns the split-row kernels once there is a row for every
-// compute unit.  Measured on MI355X (256 CUs), generic / split-row time: RMS
-// 0.80-0.93 for 256 to 2048 rows of 65,536 to 262,144 values (either type;
-// 0.99 at 128 rows); float32 layer norm 0.85-0.91 for 256-2048 rows of 65,536
-// values, 1.29 at 128 rows, 0.92-1.00 at 131,072 values; float16 layer norm
-// 0.97-1.08.
+// Many long RMS rows (past the register-resident kernel's 65,536 values):
+// the generic kernel's chunk form (one 1024-lane workgroup per row, the
+// row's first 40,832 sums parked in LDS, no workspace) outruns the split-row
+// kernels once there is a row for every compute unit.  Measured on MI355X
+// (256 CUs), generic / split-row time: RMS 0.80-0.93 for 256 to 2048 rows of
+// 65,536 to 262,144 values (either type; 0.99 at 128 rows); layer norm
+// 0.92-1.08 beyond 65,536 values (the split-row kernels kept).
 bool generic_outruns_split(int op, int64_t hidden, int dtype, int64_t rows, int cus) {
+    (void)hidden;
+    (void)dtype;
     if (rows < 0 || cus <= 0 || rows < cus) return false;
-    return op == SKIPLN_OP_SIMPLIFIED || (op == SKIPLN_OP_LAYER_NORM && dtype == SKIPLN_F32 && hidden <= 65536);
+    return op == SKIPLN_OP_SIMPLIFIED;
 }
 
 // Tiling of the automatic launch.  Streaming rows (exact skip): one tile per
@@ -199,19 +200,6 @@ int validate(const Call& c) {
     return SKIPLN_OK;
 }
 
-// Long normalization rows past the LDS kernel's capacity, held in registers
-// (up to 65,536 values) instead of split across workgroups or read twice by
-// the generic kernel.  Measured on MI355X (256 CUs), against the better of
-// the two: float16 layer norm and RMS 11-27 % faster from 128 to 4096 rows;
-// float32 22 % faster at 256 rows and 8 % at 512, within 1 % at 1024-2048
-// and slower beyond (4096 rows of 49,152 values: 8 % layer norm, 16 % RMS),
-// where the generic kernel's deeper load pipeline wins.  Rows unknown
-// (< 0) count as few.
-bool regnorm_wins(int dtype, int64_t rows, int cus) {
-    if (dtype == SKIPLN_F16) return true;
-    return rows < 0 || cus <= 0 || rows <= 2 * static_cast<int64_t>(cus);
-}
-
 int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool elem_ok, int variant,
            bool with_workspace, int64_t rows, int cus) {
     const int base = (op * 2 + dtype) * kIdsPerType;
@@ -234,11 +222,15 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
     if (variant == kVariantSplitRow) return split_ok ? base + kSplitRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     if (variant == kVariantRegRow) return reg_ok ? base + kRegRowIndex : -SKIPLN_ERR_UNSUPPORTED;
     // Long rows of the reducing operations: staged in LDS; beyond its
-    // capacity held in registers (softmax; the normalizations where that
-    // wins), or split across workgroups when a workspace is at hand.
+    // capacity held in registers, or split across workgroups when a
+    // workspace is at hand.
     if (variant == kVariantAuto && hidden / v > kRowtileMaxAutoChunks) {
         if (lds_ok) return base + kLdsRowIndex;
-        if (reg_ok && (op == SKIPLN_OP_BIAS_SOFTMAX || regnorm_wins(dtype, rows, cus))) return base + kRegRowIndex;
+        // Register-resident rows (measured on MI355X against the generic and
+        // split-row kernels, 65,536-value rows: float16 11-27 % faster from
+        // 128 to 4096 rows; float32 7-19 % faster at 256-512 and 2048-4096
+        // rows, within 5 % at 1024).
+        if (reg_ok) return base + kRegRowIndex;
         if (split_ok && with_workspace && !generic_outruns_split(op, hidden, dtype, rows, cus))
             return base + kSplitRowIndex;
     }
@@ -314,27 +306,22 @@ int run(const Call& c, int variant, const Tiling* tiling, skipln_stream_t stream
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
     const bool vec = all_aligned16(c), elem = all_element_aligned(c), bcast = c.skip_mode != SKIPLN_SKIP_EXACT;
-    // First the choice for a device of any size (as few rows as it has
-    // compute units).  Where that is the split-row pair the workspace must
-    // serve (checked before any HIP call); there, and for float32 rows held in
-    // registers, the row count against the device's compute units decides
-    // between that choice and the generic kernel.
+    // First the choice for a device of any size; where that is the split-row
+    // pair the workspace must serve (checked before any HIP call), and the
+    // device's compute units decide between it and the generic kernel.
     int id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, ws != nullptr, -1, 0);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
-    const int first = id % kIdsPerType;
-    const bool split_first = first == kSplitRowIndex;
-    const bool reg_norm_f32 = first == kRegRowIndex && c.op != SKIPLN_OP_BIAS_SOFTMAX && c.dtype == SKIPLN_F32;
-    if (variant == kVariantAuto && (split_first || reg_norm_f32)) {
+    if (id % kIdsPerType == kSplitRowIndex && variant == kVariantAuto) {
         const bool residual_aliases = c.residual && (c.residual == c.input || c.residual == c.skip);
-        if (split_first && !residual_aliases) {
+        if (!residual_aliases) {
             const int w = check_workspace(c, ws, kSplitRowIndex);
             if (w != SKIPLN_OK) return w;
         }
         int cus = 0;
         const hipError_t e = device_cus(&cus);
         if (e != hipSuccess) return status_of(e);
-        id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, split_first || ws != nullptr, c.rows, cus);
+        id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, true, c.rows, cus);
         if (id < 0) return -id;
     }
     const Args a = make_args(c, store);

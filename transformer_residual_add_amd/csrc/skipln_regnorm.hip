@@ -7,9 +7,11 @@
 // the binary32 sums s = (x + skip) + bias of its chunks t, t + 1024, ... in
 // VGPRs (64 values per lane at 65,536 values per row), so every input crosses
 // HBM once:
-//   pass 1: the row's x loads (and, for float16, its skip loads) are all
-//           issued at once; the float32 skip and the bias go through short
-//           register rings; s is formed slab by slab;
+//   pass 1: every x and skip load of the row is issued at once (float16
+//           skip chunks into registers; float32 ones, twice as wide, mostly
+//           straight into LDS with direct-to-LDS buffer loads, the rest into
+//           registers); the bias goes through a short register ring; s is
+//           formed slab by slab;
 //   statistics from the registers, exactly two-pass: the mean, then the sum
 //           of squared deviations from it (the mean square for the
 //           root-mean-square form), each merged across the block through LDS;
@@ -35,7 +37,7 @@ constexpr int kNormMaxValues = 64;       // binary32 sums per lane
 constexpr int kNormPastRow = 0x40000000; // lane offset beyond every row
 constexpr int kNormNonTemporal = 2;      // cache policy of the streamed loads
 constexpr int kParamAhead = 2;           // bias / gamma / beta slabs loaded ahead
-constexpr int kSkipAhead = 3;            // float32 skip slabs loaded ahead
+constexpr int kLdsSkipSlabs = 9;         // float32 skip slabs loaded straight into LDS (144 KiB)
 
 template <typename T, int OP, int CH>
 __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
@@ -43,12 +45,16 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
     constexpr int V = E::kPerChunk;
     constexpr int W = kNormBlock / 64;
     static_assert(CH * V <= kNormMaxValues, "row held in registers");
-    // float16 skip chunks are as small as the sums they become: all of them
-    // load at once.  float32 ones would double the row's registers: a ring.
-    constexpr int SA = sizeof(T) == 2 ? CH : (kSkipAhead < CH ? kSkipAhead : CH);
+    // Every load of a row is issued at once.  float16 skip chunks are as
+    // small as the sums they become: they load into registers.  float32 ones
+    // would double the row's registers: the first LS slabs load straight
+    // into LDS (16-byte direct-to-LDS buffer loads), the rest into registers.
+    constexpr int LS = sizeof(T) == 4 ? (kLdsSkipSlabs < CH ? kLdsSkipSlabs : CH) : 0;
+    constexpr int SA = CH - LS;  // skip slabs in registers
     // The longest float32 rows leave room for one parameter slab ahead only.
     constexpr int PA = sizeof(T) == 4 && CH >= 16 ? 1 : (kParamAhead < CH ? kParamAhead : CH);
     __shared__ float4 red[2][W];
+    extern __shared__ u32x4 lskip[];  // LS slabs of kNormBlock chunks
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -79,7 +85,7 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
     refresh();
 
     u32x4 xq[CH];
-    u32x4 sq[SA];
+    u32x4 sq[SA > 0 ? SA : 1];
     int64_t row = blockIdx.x;
     int64_t srow = 0;  // skip row of the row whose loads are in flight
     auto issue_row = [&](int64_t r) {
@@ -91,20 +97,34 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
 #pragma unroll
         for (int k = 0; k < CH; ++k)
             xq[k] = __builtin_amdgcn_raw_buffer_load_b128(xr, lo(k), k * kNormSlabBytes, kNormNonTemporal);
+        // Lane t of wavefront w writes its chunk at LDS chunk k * kNormBlock +
+        // 64 w + t: every lane later reads back only its own chunk.
+        // (The direct-to-LDS builtin exists for the device pass only; the
+        // host pass, which emits just the launch stub, must not see it.)
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int k = 0; k < LS; ++k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                sr, (__attribute__((address_space(3))) void*)(lskip + k * kNormBlock + wave * 64), 16, lo(k),
+                k * kNormSlabBytes, 0, kNormNonTemporal);
+#endif
 #pragma unroll
         for (int k = 0; k < SA; ++k)
-            sq[k] = __builtin_amdgcn_raw_buffer_load_b128(sr, lo(k), k * kNormSlabBytes, kNormNonTemporal);
+            sq[k] = __builtin_amdgcn_raw_buffer_load_b128(sr, lo(LS + k), (LS + k) * kNormSlabBytes,
+                                                          kNormNonTemporal);
     };
     issue_row(row);
 
     int buf = 0;
     for (; row < a.rows; row += gridDim.x) {
-        const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(S + srow * hv, row_bytes);
         refresh();
         // Pass 1: s = (x + skip) + bias in binary32.
         u32x4 bq[PA];
 #pragma unroll
         for (int j = 0; j < PA; ++j) bq[j] = __builtin_amdgcn_raw_buffer_load_b128(biasr, lo(j), j * kNormSlabBytes, 0);
+        // The skip slabs in LDS are read back once every load of the row
+        // has landed (all were issued together; the bias just after).
+        if constexpr (LS > 0) __builtin_amdgcn_s_waitcnt(0);
         float s[CH][V];
         // Layer norm sums s - sh, sh = the wavefront's first sum (chunk 0 of
         // its lane 0 always lies in the row), so that rounding scales with
@@ -112,10 +132,7 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
         float acc = 0.0f, sh = 0.0f;
 #pragma unroll
         for (int k = 0; k < CH; ++k) {
-            const u32x4 sk = sq[k % SA];
-            if (SA < CH && k + SA < CH)
-                sq[k % SA] = __builtin_amdgcn_raw_buffer_load_b128(sr, lo(k + SA), (k + SA) * kNormSlabBytes,
-                                                                   kNormNonTemporal);
+            const u32x4 sk = k < LS ? lskip[k * kNormBlock + tid] : sq[k - LS];
             const u32x4 bk = bq[k % PA];
             if (k + PA < CH)
                 bq[k % PA] = __builtin_amdgcn_raw_buffer_load_b128(biasr, lo(k + PA), (k + PA) * kNormSlabBytes, 0);
@@ -123,7 +140,8 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
             E::widen(xq[k], xf);
             E::widen(sk, sf);
             E::widen(bk, bf);
-            // Chunks past the row's end read zeros: s = 0, no contribution.
+            // Chunks past the row's end (whatever their sums) contribute
+            // nothing; their stores are dropped by the range check.
 #pragma unroll
             for (int e = 0; e < V; ++e) s[k][e] = (xf[e] + sf[e]) + bf[e];
             if constexpr (OP != kOpSimplified)
@@ -132,7 +150,7 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
 #pragma unroll
             for (int e = 0; e < V; ++e) {
                 if constexpr (OP == kOpSimplified)
-                    acc += s[k][e] * s[k][e];
+                    acc += valid ? s[k][e] * s[k][e] : 0.0f;
                 else
                     acc += valid ? s[k][e] - sh : 0.0f;
             }
@@ -231,10 +249,12 @@ __global__ void __launch_bounds__(kNormBlock) regnorm_kernel(const Args a) {
 template <typename T, int OP, int CH>
 hipError_t launch_ch(const Args& a, hipStream_t st) {
     auto kernel = regnorm_kernel<T, OP, CH>;
+    constexpr size_t lds = sizeof(T) == 4 ? static_cast<size_t>(kLdsSkipSlabs < CH ? kLdsSkipSlabs : CH) * kNormSlabBytes
+                                          : 0;
     static int occ_cache = 0;
     int occ = __atomic_load_n(&occ_cache, __ATOMIC_RELAXED);
     if (occ <= 0) {
-        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kNormBlock, 0);
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kNormBlock, lds);
         if (e != hipSuccess) return e;
         if (occ < 1) return hipErrorInvalidConfiguration;
         __atomic_store_n(&occ_cache, occ, __ATOMIC_RELAXED);
@@ -247,7 +267,7 @@ hipError_t launch_ch(const Args& a, hipStream_t st) {
     Args arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks < 1 ? 1 : blocks)),
-                           dim3(kNormBlock), params, 0, st);
+                           dim3(kNormBlock), params, lds, st);
 }
 
 // Slab counts compiled: the smallest that covers the row.
