@@ -281,9 +281,10 @@ EXTRA: Dict[str, Workload] = {
             seed=1013,
             op="simplified",
         ),
-        # Rows beyond one workgroup's LDS (65536 values): the generic kernel's
-        # chunk form (part of each row parked in LDS) against the split-row
-        # kernels, 512 rows so that every CU holds a row.
+        # Rows beyond one workgroup's LDS (65536 values): the register-resident
+        # rows against the generic kernel's chunk form (part of each row
+        # parked in LDS) and the split-row kernels; 512 rows, so that every CU
+        # holds a row or two, and 4096 rows, sixteen per CU.
         Workload(
             name="longrow_512x65536_f32",
             shape=(512, 65536),
@@ -295,6 +296,18 @@ EXTRA: Dict[str, Workload] = {
             residual=True,
             eps=1e-5,
             seed=1031,
+        ),
+        Workload(
+            name="longrow_4096x65536_f32",
+            shape=(4096, 65536),
+            dtype="f32",
+            skip_shape=(4096, 65536),
+            input_dist=normal(0, 1),
+            skip_dist=normal(0, 1),
+            bias_dist=normal(0, 0.1),
+            residual=True,
+            eps=1e-5,
+            seed=1033,
         ),
         Workload(
             name="rms_longrow_512x65536_f16",
