@@ -119,6 +119,24 @@ SKIPLN_API int skipln_tune_forward_config(int op, const void* input, const void*
                                           float eps, int dtype, int geometry, int64_t tiles_per_block, int tiling,
                                           int store, skipln_stream_t stream);
 
+/* Operation `op` on the row tiles, one row tile per block, in one of the two
+ * kernel forms such launches can take: form 0 holds gamma, beta and bias in
+ * registers from the start (the form whose blocks may walk several tiles);
+ * form 1 loads gamma and beta only once the tile's sum is formed and has no
+ * next-tile prefetch, so it needs far fewer registers, and a compute unit
+ * holds at most `blocks_per_cu` of its blocks (0: as many as its registers
+ * allow; -1: the operator library's table; the limit is set through the
+ * launch's LDS).  geometry: row-tile geometry, or -1 for the automatic
+ * choice.  store: SKIPLN_STORE_*.  The result is the same operator.
+ * Returns SKIPLN_ERR_UNSUPPORTED when the geometry cannot hold the row or the
+ * tensors are not 16-byte aligned, SKIPLN_ERR_VARIANT for an unknown
+ * geometry, form, store policy, or blocks_per_cu < -1. */
+SKIPLN_API int skipln_tune_forward_form(int op, const void* input, const void* skip, int skip_mode,
+                                        int64_t skip_rows, const void* gamma, const void* beta, const void* bias,
+                                        void* out, void* residual_out, int64_t rows, int64_t hidden,
+                                        float eps, int dtype, int geometry, int form, int blocks_per_cu, int store,
+                                        skipln_stream_t stream);
+
 /* Workspace bytes skipln_tune_forward needs for this variant (0: none), or a
  * negative status code.  Host code only. */
 SKIPLN_API int64_t skipln_tune_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode,

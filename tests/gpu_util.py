@@ -140,6 +140,16 @@ class DeviceCase:
             L.F32 if w.dtype == "f32" else L.F16, geometry, tiles_per_block, strided, store, stream or None)
         L.check(st, "skipln_tune_forward_config")
 
+    def run_form(self, geometry: int, form: int, blocks_per_cu: int, stream: int = 0, store: int = L.STORE_AUTO):
+        """One row tile per block in kernel form ``form`` (skipln_tune_forward_form)."""
+        w = self.w
+        p = lambda t: None if t is None else t.data_ptr()
+        st = L.load_tune().skipln_tune_forward_form(
+            OPS[w.op], p(self.x), p(self.skip), skip_mode(w), w.skip_rows if w.broadcast else 0, p(self.gamma),
+            p(self.beta), p(self.bias), p(self.out), p(self.res), w.rows, w.hidden, float(np.float32(w.eps)),
+            L.F32 if w.dtype == "f32" else L.F16, geometry, form, blocks_per_cu, store, stream or None)
+        L.check(st, "skipln_tune_forward_form")
+
     def host(self, t):
         import torch
 

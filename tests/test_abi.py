@@ -536,6 +536,19 @@ def test_forward_config_argument_checks():
     assert cfg(geom=L.VARIANT_ELEMENT_GEOMETRY + L.load_tune().skipln_tune_element_geometries()) == L.ERR_VARIANT
 
 
+def test_forward_form_argument_checks():
+    """skipln_tune_forward_form rejects these before any HIP call."""
+    frm = lambda geom=0, form=1, cap=0, store=L.STORE_AUTO: L.load_tune().skipln_tune_forward_form(
+        L.OP_LAYER_NORM, IN, SK, 0, 0, GA, BE, BI, OUT, RES, 4, 64, 1e-5, L.F32, geom, form, cap, store, None)
+    assert frm(form=2) == L.ERR_VARIANT and frm(form=-1) == L.ERR_VARIANT
+    assert frm(cap=-2) == L.ERR_VARIANT
+    assert frm(store=2) == L.ERR_VARIANT
+    assert frm(geom=-2) == L.ERR_VARIANT
+    assert frm(geom=L.load_tune().skipln_tune_rowtile_geometries()) == L.ERR_VARIANT
+    # the argument checks of the operator itself still come first for the rest
+    assert frm(geom=L.VARIANT_ELEMENT_GEOMETRY) == L.ERR_VARIANT
+
+
 def test_stream_probe_argument_checks():
     """skipln_tune_stream returns these statuses before any HIP call."""
     st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load_tune().skipln_tune_stream(s0, s1, d0,

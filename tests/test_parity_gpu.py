@@ -36,9 +36,10 @@ def test_workload_all_rows(name):
 ORACLE_BLOCK = 4096  # rows per oracle call in the full-size comparison
 
 
-# The two largest configurations, and the benchmark's full-size root-mean-square
-# and BiasAdd workloads.
-FULL_SIZE = list(W.ORDER[3:]) + ["rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16"]
+# The two largest configurations, the benchmark's full-size root-mean-square
+# and BiasAdd workloads, and 2 GiB layer norms that take the single-tile form.
+FULL_SIZE = list(W.ORDER[3:]) + ["rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "rows65536_h4096_f16",
+                                   "rows131072_h2048_f16", "rows16384_h16384_f16"]
 
 
 @pytest.mark.parametrize("name", FULL_SIZE)
@@ -174,6 +175,38 @@ def test_every_geometry(dt, geom, ragged, op):
                      op=op)
     U.note(f"geometry {geom} ({name}) H={hidden} rows={rows}")
     U.check_case(w, variant=L.VARIANT_GEOMETRY + geom)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("geom", ROWTILE_GEOMETRIES)
+@pytest.mark.parametrize("form_cap", [(1, 0), (1, 3), (0, -1)], ids=lambda f: f"form{f[0]}_cap{f[1]}")
+@pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])
+def test_kernel_forms(dt, geom, form_cap, op):
+    """Both kernel forms of one-tile-per-block launches at every geometry
+    (the single-tile form with and without a blocks-per-CU limit), one chunk
+    short of capacity, a ragged last tile of rows, a broadcast skip on the
+    normalizations."""
+    form, cap = form_cap
+    v = 4 if dt == "f32" else 8
+    code = L.F32 if dt == "f32" else L.F16
+    chunks = 0
+    for hv in range(1, 4097):
+        if U.select(L.OP_LAYER_NORM, hv * v, code, variant=L.VARIANT_GEOMETRY + geom) < 0:
+            break
+        chunks = hv
+    hidden = max(1, chunks - 1) * v
+    name = L.kernel_name(U.select(U.OPS[op], hidden, code, variant=L.VARIANT_GEOMETRY + geom))
+    g = int(name.split("_g")[1].split("_")[0])
+    block = int(name.split("_b")[1]) if "_b" in name else max(256, g)
+    rows = 3 * (block // g) + 1
+    bcast = op in ("layer_norm", "simplified")
+    w = W.small_case(rows, hidden, dt, skip_rows=1 if bcast else None, beta=True, bias=True, residual=True,
+                     eps=1e-5, seed=geom * 11 + form * 3 + cap + 1, op=op)
+    inputs = W.make_inputs(w)
+    U.note(f"form {form} cap {cap} geometry {geom} ({name}) {op} H={hidden} rows={rows}")
+    dc = U.DeviceCase(w, inputs, residual=w.residual)
+    dc.run_form(geom, form, cap)
+    U.compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, U.oracle_rows(w, inputs))
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
@@ -581,7 +614,8 @@ def test_rows_zero_is_noop():
 
 @pytest.mark.parametrize("variant_hidden", [(L.VARIANT_AUTO, 1024), (L.VARIANT_GENERIC, 1024),
                                             (L.VARIANT_MULTIWAVE, 1024), (L.VARIANT_LDSROW, 12288),
-                                            (L.VARIANT_ELEMENT, 1000), (L.VARIANT_AUTO, 1000)],
+                                            (L.VARIANT_ELEMENT, 1000), (L.VARIANT_AUTO, 1000),
+                                            (L.VARIANT_REGROW, 65536), (L.VARIANT_AUTO, 49152)],
                          ids=lambda t: f"v{t[0]}_h{t[1]}")
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("op", ["layer_norm", "simplified"])

@@ -65,9 +65,7 @@ bool all_element_aligned(const Call& c) {
 // (256 CUs), generic / split-row time: RMS 0.80-0.93 for 256 to 2048 rows of
 // 65,536 to 262,144 values (either type; 0.99 at 128 rows); layer norm
 // 0.92-1.08 beyond 65,536 values (the split-row kernels kept).
-bool generic_outruns_split(int op, int64_t hidden, int dtype, int64_t rows, int cus) {
-    (void)hidden;
-    (void)dtype;
+bool generic_outruns_split(int op, int64_t rows, int cus) {
     if (rows < 0 || cus <= 0 || rows < cus) return false;
     return op == SKIPLN_OP_SIMPLIFIED;
 }
@@ -231,7 +229,7 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         // 128 to 4096 rows; float32 7-19 % faster at 256-512 and 2048-4096
         // rows, within 5 % at 1024).
         if (reg_ok) return base + kRegRowIndex;
-        if (split_ok && with_workspace && !generic_outruns_split(op, hidden, dtype, rows, cus))
+        if (split_ok && with_workspace && !generic_outruns_split(op, rows, cus))
             return base + kSplitRowIndex;
     }
     if (variant == kVariantAuto || variant == kVariantRowtile || variant == kVariantMultiwave) {

@@ -40,12 +40,30 @@ constexpr int kTileContiguous = 0;      // block b: tiles b*T .. b*T + T - 1
 constexpr int kTileStrided = 1;         // block b: tiles b, b + grid, ...
 constexpr int kTileSkipStationary = 2;  // broadcast skip: fixed skip rows per block
 
+// Kernel forms of the row tiles: blocks that may walk several tiles (the
+// next tile's loads issued while the current one finishes; parameters held
+// in registers throughout), blocks of exactly one tile (no prefetch, gamma
+// and beta loaded once the sum is formed: far fewer registers), and the
+// latter with a streamed first skip tile (small launches).
+constexpr int kFormAuto = -1;
+constexpr int kFormWalk = 0;
+constexpr int kFormOneTile = 1;
+constexpr int kFormStreamSkip = 2;
+// Blocks per compute unit of a single-tile launch: the launcher's table.
+constexpr int kBlocksAuto = -1;
+
 // How a row-tile launch distributes tiles over blocks.
 struct Tiling {
     int64_t tiles_per_block;  // 0: the launcher's choice (skip-stationary:
                               // 3 batches per block; otherwise a grid of the
                               // blocks the device holds at once)
     int mode;                 // kTile*
+    // Launches of one tile per block (not skip-stationary): the kernel form
+    // (kFormAuto: the launcher's table) and, for kFormOneTile, the blocks a
+    // compute unit may hold (kBlocksAuto: the table's; 0: as many as the
+    // kernel's registers allow).
+    int form = kFormAuto;
+    int blocks_per_cu = kBlocksAuto;
 };
 
 // Operations sharing the row kernels.

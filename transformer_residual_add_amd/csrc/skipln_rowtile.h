@@ -34,11 +34,22 @@ __device__ __forceinline__ float wave_elems(int hv, int w) {
     return static_cast<float>(n * V);
 }
 
-// SS (stream skip): the first tile's exact skip is read with non-temporal
-// loads (the launcher's choice for one wave of resident blocks with one tile
-// each); otherwise, and for every later tile, the skip goes through the
-// caches.
-template <typename E, int OP, int G, int CH, int BLOCK, bool SS>
+// Static LDS of a row-tile kernel: the cross-wavefront partials, double
+// buffered.
+template <int G, int BLOCK>
+constexpr int partial_bytes() {
+    return 2 * (BLOCK / G) * (G > 64 ? G / 64 : 1) * 16;
+}
+
+// FORM (kForm* in skipln_internal.h): kFormWalk blocks walk the tiles the
+// launch gives them, each tile's loads issued while the previous tile
+// finishes, gamma/beta/bias held in registers throughout; kFormOneTile
+// blocks take exactly tile blockIdx.x (the launcher's guarantee) and load
+// gamma and beta only once the sum is formed, so far fewer registers are
+// live; kFormStreamSkip is kFormOneTile with the exact skip read by
+// non-temporal loads (the launcher's choice for one wave of resident blocks).
+// Otherwise the skip goes through the caches.
+template <typename E, int OP, int G, int CH, int BLOCK, int FORM>
 __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     static_assert(OP == kOpLayerNorm || OP == kOpSimplified || OP == kOpBiasAdd || OP == kOpBiasSoftmax,
                   "operation");
@@ -49,7 +60,14 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     constexpr int RPB = BLOCK / G;                  // rows per block per tile
     constexpr int WPR = G > 64 ? G / 64 : 1;        // wavefronts per row
     static_assert(BLOCK % G == 0 && BLOCK % 64 == 0, "block of whole groups and wavefronts");
+    static_assert(FORM >= kFormWalk && FORM <= kFormStreamSkip, "kernel form");
+    constexpr bool SS = FORM == kFormStreamSkip;
+    constexpr bool ONE = FORM != kFormWalk;
+    // One tile per block: gamma and beta are loaded after the sum is formed
+    // (their registers are not held through the loads of x and skip).
+    constexpr bool LP = kNorm && ONE;
     __shared__ float4 partial[2][RPB][WPR];
+    static_assert(sizeof(partial) == partial_bytes<G, BLOCK>(), "static LDS of the kernel");
 
     const int tid = threadIdx.x;
     // Row of the tile handled by this group; wave-uniform when G >= 64, and
@@ -86,7 +104,7 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         for (int k = 0; k < CH; ++k) {
             const int c = k * G + lt;
             if (ok[k]) {
-                if constexpr (kNorm) {
+                if constexpr (kNorm && !LP) {
                     gam[k] = static_cast<const Raw*>(a.gamma)[c];
                     if (has_beta) bet[k] = static_cast<const Raw*>(a.beta)[c];
                 }
@@ -113,10 +131,15 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
     //                    tiles p + n*P.  Its skip rows are loaded once.
     const int64_t n_tiles = (a.rows + RPB - 1) / RPB;
     int64_t t_first, stride, t_end;
-    // (Never launched stationary with SS: left out, so that its first loads
-    // cannot be merged with the streaming ones.)
-    const bool stationary = !SS && a.tiling == kTileSkipStationary;
-    if (a.tiling == kTileContiguous) {
+    // (The single-tile forms are never launched skip-stationary: left out, so
+    // that the streamed first loads cannot be merged with cached ones.)
+    const bool stationary = !ONE && a.tiling == kTileSkipStationary;
+    if constexpr (ONE) {
+        // One tile per block (the launcher's guarantee for these forms).
+        t_first = blockIdx.x;
+        stride = 1;
+        t_end = t_first + 1;
+    } else if (a.tiling == kTileContiguous) {
         t_first = blockIdx.x * a.tiles_per_block;
         stride = 1;
         t_end = t_first + a.tiles_per_block < n_tiles ? t_first + a.tiles_per_block : n_tiles;
@@ -201,7 +224,10 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
             // their register footprint, which costs occupancy.
 #pragma unroll
             for (int k = 0; k < CH; ++k) {
-                asm volatile("" : "+v"(gam[k]), "+v"(bet[k]), "+v"(bia[k]));
+                if constexpr (LP)
+                    asm volatile("" : "+v"(bia[k]));
+                else
+                    asm volatile("" : "+v"(gam[k]), "+v"(bet[k]), "+v"(bia[k]));
             }
         }
 
@@ -229,7 +255,8 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
         }
 
         // Registers of x/skip are free again: start the next tile's loads.
-        if (tile + stride < t_end) issue_loads(tile + stride, !stationary, std::false_type{});
+        if constexpr (!ONE)
+            if (tile + stride < t_end) issue_loads(tile + stride, !stationary, std::false_type{});
 
         if constexpr (OP == kOpBiasSoftmax) {
             // Softmax over the row: exponentials relative to a reference
@@ -322,6 +349,16 @@ __global__ void __launch_bounds__(BLOCK) rowtile_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < CH; ++k)
                 if (ok[k]) put(R, k, E::narrow(s[k]));
+        }
+        if constexpr (LP) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const int c = k * G + lt;
+                if (ok[k]) {
+                    gam[k] = static_cast<const Raw*>(a.gamma)[c];
+                    if (has_beta) bet[k] = static_cast<const Raw*>(a.beta)[c];
+                }
+            }
         }
 
         // Statistics are taken relative to a value of the row itself (lane
@@ -516,11 +553,108 @@ hipError_t resident_blocks(K kernel, int block, int* occupancy_cache, int64_t* o
 }
 
 template <typename K>
-hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipStream_t st) {
+hipError_t launch_grid(K kernel, int block, int64_t blocks, const Args& a, hipStream_t st, size_t lds = 0) {
     Args arg = a;
     void* params[] = {&arg};
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(blocks)),
-                           dim3(block), params, 0, st);
+                           dim3(block), params, lds, st);
+}
+
+// LDS of a compute unit (160 KiB on gfx950), cached per device.
+inline hipError_t lds_per_cu(int* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::atomic<int> cache[64];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && n > 0) cache[dev].store(n, std::memory_order_relaxed);
+    *out = n;
+    return hipSuccess;
+}
+
+// Largest number of blocks per compute unit a launch can be held to.
+constexpr int kMaxBlocksCap = 16;
+
+// Dynamic LDS that holds a compute unit to at most `cap` resident blocks of
+// `kernel` (0: no limit): the least LDS for which the runtime's occupancy
+// calculation (which knows the LDS allocation granule) gives `cap` or fewer,
+// found by bisection once per kernel and cap (`cache`: kMaxBlocksCap + 1
+// entries, LDS + 1, 0 = not computed) and assumed alike on every device.
+template <typename K>
+hipError_t cap_lds(K kernel, int block, int cap, int static_bytes, std::atomic<int>* cache, size_t* out) {
+    *out = 0;
+    if (cap <= 0) return hipSuccess;
+    if (cap > kMaxBlocksCap) cap = kMaxBlocksCap;
+    const int known = cache[cap].load(std::memory_order_relaxed);
+    if (known > 0) {
+        *out = static_cast<size_t>(known - 1);
+        return hipSuccess;
+    }
+    int lds = 0;
+    hipError_t e = lds_per_cu(&lds);
+    if (e != hipSuccess) return e;
+    if (lds <= static_bytes + 1) return hipSuccess;
+    auto occupancy = [&](int dyn, int* occ) {
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, reinterpret_cast<const void*>(kernel), block,
+                                                           static_cast<size_t>(dyn));
+    };
+    int occ = 0;
+    e = occupancy(0, &occ);
+    if (e != hipSuccess) return e;
+    int lo = 0, hi = lds - static_bytes;  // occupancy(lo) > cap, occupancy(hi) <= cap
+    if (occ > cap) {
+        while (hi - lo > 1) {
+            const int mid = lo + (hi - lo) / 2;
+            e = occupancy(mid, &occ);
+            if (e != hipSuccess) return e;
+            (occ > cap ? lo : hi) = mid;
+        }
+    } else {
+        hi = 0;
+    }
+    cache[cap].store(hi + 1, std::memory_order_relaxed);
+    *out = static_cast<size_t>(hi);
+    return hipSuccess;
+}
+
+// Launches of one tile per block that move at least this many bytes take
+// the single-tile form where single_tile_blocks() says so.  Measured on
+// MI355X, one block per tile, graph replay: at 2 GiB per launch (eight times
+// the 256 MiB last-level cache) the single-tile form was 4-12 % faster on
+// the geometries below; at 1 GiB within -7..+3 %, and on launches of
+// 134-268 MB the walking form was as fast or faster (16384 rows of 1024
+// float16 values: 23.1 against 23.2-23.6 us).
+constexpr int64_t kSingleTileMinBytes = int64_t(2) << 30;
+
+// Blocks per compute unit of the single-tile form for the normalizations
+// (0: as many as the registers allow), or -1 where the walking form stays.
+// Measured at 2 GiB per launch, layer norm, walking form against the best
+// cap: float16 rows of 1024 (64-lane groups, 2 chunks) 350.6 -> 337.0 us at
+// 4 blocks; 2048 (256 x 1) 390.1 -> 362.2 at 6; 4096 (256 x 2) 358.2 ->
+// 344.2 at 4; 16384 (512 x 4; the walking form holds one block per CU)
+// 404.3 -> 356.4 with no cap; float32 rows of 512 361.1 -> 339.6 at 3, 1024
+// 386.8 -> 358.5 at 5, 2048 360.5 -> 340.1 at 4; RMS alike (float16 2048:
+// 386.6 -> 362.0, 4096: 359.7 -> 347.0).  Rows of 1536, 3072-6144 and 8192
+// float16 values (and 768, 3072-5120, 4096 and 8192 float32) gained under 3 %
+// or lost, as did BiasAdd and BiasSoftmax: those keep the walking form.
+template <typename E, int OP, int G, int CH>
+constexpr int single_tile_blocks() {
+    if constexpr (OP != kOpLayerNorm && OP != kOpSimplified) return -1;
+    constexpr bool half = E::kPerChunk == 8;
+    if constexpr (G == 64 && CH == 2) return half ? 4 : 3;
+    if constexpr (G == 256 && CH == 1) return half ? 6 : 5;
+    if constexpr (G == 256 && CH == 2) return 4;
+    if constexpr (G == 512 && CH == 4) return half ? 0 : -1;
+    return -1;
 }
 
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;
@@ -533,7 +667,7 @@ template <typename E, int OP, int GG, int CH, int BLOCK>
 hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     constexpr Geom g = {GG, CH, BLOCK};
     static int occ = 0;
-    auto kernel = rowtile_kernel<E, OP, g.g, g.ch, g.block, false>;
+    auto kernel = rowtile_kernel<E, OP, g.g, g.ch, g.block, kFormWalk>;
     const int64_t rpb = g.block / g.g;
     const int64_t tiles = (a0.rows + rpb - 1) / rpb;
     Args a = a0;
@@ -588,13 +722,37 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     // against 23 us on 16384 rows of 1024 float16 values).  Element-wise
     // kernels (odd row lengths) keep one form.
     if constexpr (E::kPerChunk > 1) {
-        if (mode != kTileSkipStationary && a.skip_rows <= 0 && a.skip_group <= 0 && per <= 1) {
+        if (tiling.form == kFormAuto && mode != kTileSkipStationary && a.skip_rows <= 0 && a.skip_group <= 0 &&
+            per <= 1) {
             static int occ_ss = 0;
-            auto kernel_ss = rowtile_kernel<E, OP, g.g, g.ch, g.block, true>;
+            auto kernel_ss = rowtile_kernel<E, OP, g.g, g.ch, g.block, kFormStreamSkip>;
             int64_t resident_ss = 0;
             const hipError_t e = resident_blocks(kernel_ss, g.block, &occ_ss, &resident_ss);
             if (e != hipSuccess) return e;
             if (blocks <= resident_ss) return launch_grid(kernel_ss, g.block, blocks < 1 ? 1 : blocks, a, st);
+        }
+    }
+    if constexpr (E::kPerChunk > 1) {
+        if (mode != kTileSkipStationary && per <= 1) {
+            // cap: blocks per CU of the single-tile form (0: no limit), or
+            // -1 for the walking form.
+            int cap = -1;
+            if (tiling.form == kFormOneTile) {
+                constexpr int table = single_tile_blocks<E, OP, g.g, g.ch>();
+                cap = tiling.blocks_per_cu >= 0 ? tiling.blocks_per_cu : (table > 0 ? table : 0);
+            } else if (tiling.form == kFormAuto) {
+                const int64_t streams = 3 + (a.residual != nullptr ? 1 : 0);
+                const int64_t bytes = streams * a.rows * (a.hidden / E::kPerChunk) * 16;  // 16-byte chunks
+                if (bytes >= kSingleTileMinBytes) cap = single_tile_blocks<E, OP, g.g, g.ch>();
+            }
+            if (cap >= 0) {
+                static std::atomic<int> lds_cache[kMaxBlocksCap + 1];
+                auto kernel_one = rowtile_kernel<E, OP, g.g, g.ch, g.block, kFormOneTile>;
+                size_t lds = 0;
+                const hipError_t e = cap_lds(kernel_one, g.block, cap, partial_bytes<g.g, g.block>(), lds_cache, &lds);
+                if (e != hipSuccess) return e;
+                return launch_grid(kernel_one, g.block, blocks < 1 ? 1 : blocks, a, st, lds);
+            }
         }
     }
     return launch_grid(kernel, g.block, blocks < 1 ? 1 : blocks, a, st);

@@ -80,6 +80,26 @@ SKIPLN_API int skipln_tune_forward_config(int op, const void* input, const void*
                variant, &t, stream, nullptr, store);
 }
 
+SKIPLN_API int skipln_tune_forward_form(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
+                                        const void* gamma, const void* beta, const void* bias, void* out,
+                                        void* residual_out, int64_t rows, int64_t hidden, float eps, int dtype,
+                                        int geometry, int form, int blocks_per_cu, int store, skipln_stream_t stream) {
+    if (form != skipln::kFormWalk && form != skipln::kFormOneTile) return SKIPLN_ERR_VARIANT;
+    if (blocks_per_cu < skipln::kBlocksAuto) return SKIPLN_ERR_VARIANT;
+    if (store != SKIPLN_STORE_AUTO && store != SKIPLN_STORE_STREAM && store != SKIPLN_STORE_THROUGH)
+        return SKIPLN_ERR_VARIANT;
+    if (geometry < -1 || geometry >= skipln::rowtile_count()) return SKIPLN_ERR_VARIANT;
+    skipln::Tiling t;
+    t.tiles_per_block = 1;
+    t.mode = skipln::kTileStrided;
+    t.form = form;
+    t.blocks_per_cu = blocks_per_cu;
+    const int variant = geometry < 0 ? SKIPLN_VARIANT_ROWTILE : SKIPLN_VARIANT_GEOMETRY + geometry;
+    return run(make_call(op, input, skip, skip_mode, skip_rows, gamma, beta, bias, out, residual_out, rows, hidden, eps,
+                         dtype),
+               variant, &t, stream, nullptr, store);
+}
+
 SKIPLN_API int64_t skipln_tune_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode,
                                                int64_t skip_rows, int variant) {
     if (variant == SKIPLN_VARIANT_AUTO)

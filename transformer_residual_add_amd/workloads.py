@@ -281,6 +281,12 @@ EXTRA: Dict[str, Workload] = {
             seed=1013,
             op="simplified",
         ),
+        # 2 GiB layer norms of common hidden sizes (one block per row tile, the
+        # single-tile kernel form).
+        *[Workload(name=f"rows{rows}_h{h}_f16", shape=(rows, h), dtype="f16", skip_shape=(rows, h),
+                   input_dist=normal(0, 1), skip_dist=normal(0, 1), bias_dist=normal(0, 0.1), residual=True,
+                   eps=1e-5, seed=1040 + i)
+          for i, (rows, h) in enumerate(((65536, 4096), (131072, 2048), (16384, 16384)))],
         # Rows beyond one workgroup's LDS (65536 values): the register-resident
         # rows against the generic kernel's chunk form (part of each row
         # parked in LDS) and the split-row kernels; 512 rows, so that every CU
