@@ -536,6 +536,26 @@ def test_forward_config_argument_checks():
     assert cfg(geom=L.VARIANT_ELEMENT_GEOMETRY + L.load_tune().skipln_tune_element_geometries()) == L.ERR_VARIANT
 
 
+def test_large_launches_take_1024_lane_row_tiles():
+    """Normalization rows of 2049-3072 chunks (float16: 2689-3072) of whole
+    128-byte lines leave the LDS-staged kernel for 1024-lane row tiles once
+    input, skip and output each span 512 MiB; broadcast skips, BiasSoftmax and
+    other lengths do not."""
+    sel = lambda h, dt, rows, op=L.OP_LAYER_NORM, mode=L.SKIP_EXACT: L.kernel_name(L.load_tune().skipln_tune_select(
+        op, rows, h, dt, mode, 1, L.VARIANT_AUTO, 0, 256))
+    big = lambda h, dt: -(-(512 << 20) // (h * (4 if dt == L.F32 else 2)))
+    for h, dt in ((8224, L.F32), (10240, L.F32), (12288, L.F32), (21568, L.F16), (24576, L.F16)):
+        n = big(h, dt)
+        for op, prefix in ((L.OP_LAYER_NORM, ""), (L.OP_SIMPLIFIED, "rms_")):
+            assert sel(h, dt, n, op) == f"{prefix}rowtile_{'f32' if dt == L.F32 else 'f16'}_g1024_c3"
+            assert sel(h, dt, n - 1, op).startswith(f"{prefix}ldsrow_")
+        assert sel(h, dt, n, mode=L.SKIP_BROADCAST).startswith("ldsrow_")
+        assert sel(h, dt, n, L.OP_BIAS_SOFTMAX).startswith("softmax_")
+    # too short, too long, or rows that end inside a 128-byte line
+    for h, dt in ((8192, L.F32), (12320, L.F32), (21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
+        assert "g1024_c3" not in sel(h, dt, big(h, dt))
+
+
 def test_forward_form_argument_checks():
     """skipln_tune_forward_form rejects these before any HIP call."""
     frm = lambda geom=0, form=1, cap=0, store=L.STORE_AUTO: L.load_tune().skipln_tune_forward_form(

@@ -223,6 +223,21 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
     // capacity held in registers, or split across workgroups when a
     // workspace is at hand.
     if (variant == kVariantAuto && hidden / v > kRowtileMaxAutoChunks) {
+        // Large launches of normalization rows of up to 3072 chunks (whole
+        // cache lines): 1024-lane row tiles in the single-tile form outrun
+        // the LDS-staged kernel.  Measured on MI355X, 2 GiB launches (rows x
+        // (input, skip, residual, output)): float32 rows of 8224 / 8448 /
+        // 10240 / 11264 / 12288 values 447.9 / 439.0 / 413.2 / 405.3 / 397.9
+        // -> 373.3 / 371.5 / 363.2 / 373.7 / 376.1 us; float16 rows of 22528
+        // / 24576 values 427.1 / 418.2 -> 413.6 / 404.0; float16 rows of
+        // 20480 values 431.3 against 436.2 (below 2689 chunks float16 stays
+        // on the LDS kernel).
+        const int64_t hv = hidden / v;
+        if (chunked && !broadcast && (op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED) && hv <= 3072 &&
+            (dtype == SKIPLN_F32 || hv > 2688) && single_tile_launch(rows, hidden, dtype == SKIPLN_F32 ? 4 : 2)) {
+            const int g = rowtile_pick(op, hidden, dtype, false, false);
+            if (g >= 0) return base + kRowtileFirst + g;
+        }
         if (lds_ok) return base + kLdsRowIndex;
         // Register-resident rows (measured on MI355X against the generic and
         // split-row kernels, 65,536-value rows: float16 11-27 % faster from
@@ -304,10 +319,11 @@ int run(const Call& c, int variant, const Tiling* tiling, skipln_stream_t stream
     const int st = validate(c);
     if (st != SKIPLN_OK) return st;
     const bool vec = all_aligned16(c), elem = all_element_aligned(c), bcast = c.skip_mode != SKIPLN_SKIP_EXACT;
-    // First the choice for a device of any size; where that is the split-row
-    // pair the workspace must serve (checked before any HIP call), and the
-    // device's compute units decide between it and the generic kernel.
-    int id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, ws != nullptr, -1, 0);
+    // First the choice for a device of any size (the row count decides only
+    // the large-launch rule); where that is the split-row pair the workspace
+    // must serve (checked before any HIP call), and the device's compute
+    // units decide between it and the generic kernel.
+    int id = select(c.op, c.hidden, c.dtype, bcast, vec, elem, variant, ws != nullptr, c.rows, 0);
     if (id < 0) return -id;
     if (c.rows == 0) return SKIPLN_OK;
     if (id % kIdsPerType == kSplitRowIndex && variant == kVariantAuto) {

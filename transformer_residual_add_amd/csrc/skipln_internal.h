@@ -52,6 +52,23 @@ constexpr int kFormStreamSkip = 2;
 // Blocks per compute unit of a single-tile launch: the launcher's table.
 constexpr int kBlocksAuto = -1;
 
+// Launches that favour the single-tile form (the row-tile launcher's table)
+// and, for the longest rows, 1024-lane row tiles in that form: the input
+// (and so skip and output) spans at least kLargeLaunchStreamBytes (2 GiB
+// moved with the residual, eight times the 256 MiB last-level cache) and
+// every row is whole 128-byte cache lines.  Rows that end inside a line
+// share it with the next row, which another block writes; there the
+// single-tile form measured 4-20 % slower than the walking form or the
+// LDS-staged kernel (2 GiB launches: float16 rows of 2056 values 555 against
+// 502 us, float32 rows of 1028 values 531 against 511, float16 rows of 22600
+// values 560 against 467 on the LDS kernel).
+constexpr int64_t kLargeLaunchStreamBytes = int64_t(512) << 20;
+inline bool single_tile_launch(int64_t rows, int64_t hidden, int elem_bytes) {
+    if (rows <= 0 || hidden <= 0) return false;
+    const int64_t row_bytes = hidden * elem_bytes;
+    return row_bytes % 128 == 0 && rows >= (kLargeLaunchStreamBytes + row_bytes - 1) / row_bytes;
+}
+
 // How a row-tile launch distributes tiles over blocks.
 struct Tiling {
     int64_t tiles_per_block;  // 0: the launcher's choice (skip-stationary:

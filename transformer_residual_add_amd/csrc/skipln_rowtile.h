@@ -626,15 +626,13 @@ hipError_t cap_lds(K kernel, int block, int cap, int static_bytes, std::atomic<i
     return hipSuccess;
 }
 
-// Launches of one tile per block that move at least this many bytes take
-// the single-tile form where single_tile_blocks() says so.  Measured on
-// MI355X, one block per tile, graph replay: at 2 GiB per launch (eight times
-// the 256 MiB last-level cache) the single-tile form was 4-12 % faster on
-// the geometries below; at 1 GiB within -7..+3 %, and on launches of
-// 134-268 MB the walking form was as fast or faster (16384 rows of 1024
+// Large launches of cache-line rows (single_tile_launch()) of one tile per
+// block take the single-tile form where single_tile_blocks() says so.  Measured on MI355X, one block
+// per tile, graph replay: at 2 GiB per launch the single-tile form was 4-12 %
+// faster on the geometries below; at 1 GiB within -7..+3 %, and on launches
+// of 134-268 MB the walking form was as fast or faster (16384 rows of 1024
 // float16 values: 23.1 against 23.2-23.6 us).
-constexpr int64_t kSingleTileMinBytes = int64_t(2) << 30;
-
+//
 // Blocks per compute unit of the single-tile form for the normalizations
 // (0: as many as the registers allow), or -1 where the walking form stays.
 // Measured at 2 GiB per launch, layer norm, walking form against the best
@@ -646,6 +644,10 @@ constexpr int64_t kSingleTileMinBytes = int64_t(2) << 30;
 // 386.6 -> 362.0, 4096: 359.7 -> 347.0).  Rows of 1536, 3072-6144 and 8192
 // float16 values (and 768, 3072-5120, 4096 and 8192 float32) gained under 3 %
 // or lost, as did BiasAdd and BiasSoftmax: those keep the walking form.
+// 1024-lane tiles of 3 chunks per lane (rows of up to 3072 chunks, which the
+// automatic choice gives them only in large launches) hold one block per CU
+// in either form; the single form was faster (float16 20480: 446.6 -> 436.2
+// us; float32 12288: 403.8 -> 376.1).
 template <typename E, int OP, int G, int CH>
 constexpr int single_tile_blocks() {
     if constexpr (OP != kOpLayerNorm && OP != kOpSimplified) return -1;
@@ -654,6 +656,7 @@ constexpr int single_tile_blocks() {
     if constexpr (G == 256 && CH == 1) return half ? 6 : 5;
     if constexpr (G == 256 && CH == 2) return 4;
     if constexpr (G == 512 && CH == 4) return half ? 0 : -1;
+    if constexpr (G == 1024 && CH == 3) return 0;
     return -1;
 }
 
@@ -740,10 +743,9 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
             if (tiling.form == kFormOneTile) {
                 constexpr int table = single_tile_blocks<E, OP, g.g, g.ch>();
                 cap = tiling.blocks_per_cu >= 0 ? tiling.blocks_per_cu : (table > 0 ? table : 0);
-            } else if (tiling.form == kFormAuto) {
-                const int64_t streams = 3 + (a.residual != nullptr ? 1 : 0);
-                const int64_t bytes = streams * a.rows * (a.hidden / E::kPerChunk) * 16;  // 16-byte chunks
-                if (bytes >= kSingleTileMinBytes) cap = single_tile_blocks<E, OP, g.g, g.ch>();
+            } else if (tiling.form == kFormAuto &&
+                       single_tile_launch(a.rows, a.hidden, static_cast<int>(16 / E::kPerChunk))) {
+                cap = single_tile_blocks<E, OP, g.g, g.ch>();
             }
             if (cap >= 0) {
                 static std::atomic<int> lds_cache[kMaxBlocksCap + 1];

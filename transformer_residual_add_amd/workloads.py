@@ -287,6 +287,11 @@ EXTRA: Dict[str, Workload] = {
                    input_dist=normal(0, 1), skip_dist=normal(0, 1), bias_dist=normal(0, 0.1), residual=True,
                    eps=1e-5, seed=1040 + i)
           for i, (rows, h) in enumerate(((65536, 4096), (131072, 2048), (16384, 16384)))],
+        # A large launch of float32 rows past the LDS-staged kernel's switch
+        # point (3072 chunks per row: 1024-lane single-tile row tiles).
+        Workload(name="rows16384_h12288_f32", shape=(16384, 12288), dtype="f32", skip_shape=(16384, 12288),
+                 input_dist=normal(0, 1), skip_dist=normal(0, 1), bias_dist=normal(0, 0.1), residual=True, eps=1e-5,
+                 seed=1044),
         # Rows beyond one workgroup's LDS (65536 values): the register-resident
         # rows against the generic kernel's chunk form (part of each row
         # parked in LDS) and the split-row kernels; 512 rows, so that every CU
