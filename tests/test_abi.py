@@ -554,6 +554,10 @@ def test_large_launches_take_1024_lane_row_tiles():
     # too short, too long, or rows that end inside a 128-byte line
     for h, dt in ((8192, L.F32), (12320, L.F32), (21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
         assert "g1024_c3" not in sel(h, dt, big(h, dt))
+    # float16 RMS from 2304 chunks
+    assert sel(18432, L.F16, big(18432, L.F16), L.OP_SIMPLIFIED) == "rms_rowtile_f16_g1024_c3"
+    assert sel(18368, L.F16, big(18368, L.F16), L.OP_SIMPLIFIED) == "rms_ldsrow_f16"
+    assert sel(18432, L.F16, big(18432, L.F16)) == "ldsrow_f16"
 
 
 def test_forward_form_argument_checks():

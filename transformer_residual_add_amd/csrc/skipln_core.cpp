@@ -230,11 +230,15 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         // 10240 / 11264 / 12288 values 447.9 / 439.0 / 413.2 / 405.3 / 397.9
         // -> 373.3 / 371.5 / 363.2 / 373.7 / 376.1 us; float16 rows of 22528
         // / 24576 values 427.1 / 418.2 -> 413.6 / 404.0; float16 rows of
-        // 20480 values 431.3 against 436.2 (below 2689 chunks float16 stays
-        // on the LDS kernel).
+        // 20480 values 431.3 against 436.2, so float16 layer norm stays on
+        // the LDS kernel below 2689 chunks.  float16 RMS (58 VGPRs, two
+        // blocks per CU where layer norm holds one) gains from 2304 chunks:
+        // rows of 18432 / 20480 values 436.9 / 465.4 -> 422.0 / 437.9 us at
+        // 16384 rows.
         const int64_t hv = hidden / v;
-        if (chunked && !broadcast && (op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED) && hv <= 3072 &&
-            (dtype == SKIPLN_F32 || hv > 2688) && single_tile_launch(rows, hidden, dtype == SKIPLN_F32 ? 4 : 2)) {
+        const int64_t hv_min = dtype == SKIPLN_F32 ? 2049 : op == SKIPLN_OP_SIMPLIFIED ? 2304 : 2689;
+        if (chunked && !broadcast && (op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED) && hv >= hv_min &&
+            hv <= 3072 && single_tile_launch(rows, hidden, dtype == SKIPLN_F32 ? 4 : 2)) {
             const int g = rowtile_pick(op, hidden, dtype, false, false);
             if (g >= 0) return base + kRowtileFirst + g;
         }
