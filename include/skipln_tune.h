@@ -137,6 +137,16 @@ SKIPLN_API int skipln_tune_forward_form(int op, const void* input, const void* s
                                         float eps, int dtype, int geometry, int form, int blocks_per_cu, int store,
                                         skipln_stream_t stream);
 
+/* Blocks of row-tile geometry `geometry` (0 <= geometry <
+ * skipln_tune_rowtile_geometries()) a compute unit of the current device holds
+ * at once for operation `op` and `dtype`, in kernel form `form` (0 or 1, as
+ * in skipln_tune_forward_form) with form 1 held to `blocks_per_cu` (0: no
+ * limit; -1: the operator library's table) exactly as
+ * skipln_tune_forward_form launches it: a count >= 1, or a negative status
+ * code (SKIPLN_ERR_OP, SKIPLN_ERR_DTYPE, SKIPLN_ERR_VARIANT for an unknown
+ * geometry or form or blocks_per_cu < -1, checked before any HIP call). */
+SKIPLN_API int skipln_tune_blocks_per_cu(int op, int dtype, int geometry, int form, int blocks_per_cu);
+
 /* Workspace bytes skipln_tune_forward needs for this variant (0: none), or a
  * negative status code.  Host code only. */
 SKIPLN_API int64_t skipln_tune_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode,

@@ -573,6 +573,18 @@ def test_forward_form_argument_checks():
     assert frm(geom=L.VARIANT_ELEMENT_GEOMETRY) == L.ERR_VARIANT
 
 
+def test_blocks_per_cu_argument_checks():
+    """skipln_tune_blocks_per_cu rejects these before any HIP call."""
+    bpc = lambda op=L.OP_LAYER_NORM, dt=L.F16, geom=0, form=1, cap=0: L.load_tune().skipln_tune_blocks_per_cu(
+        op, dt, geom, form, cap)
+    assert bpc(op=9) == -L.ERR_OP
+    assert bpc(dt=5) == -L.ERR_DTYPE
+    assert bpc(geom=-1) == -L.ERR_VARIANT
+    assert bpc(geom=L.load_tune().skipln_tune_rowtile_geometries()) == -L.ERR_VARIANT
+    assert bpc(form=2) == -L.ERR_VARIANT and bpc(form=-1) == -L.ERR_VARIANT
+    assert bpc(cap=-2) == -L.ERR_VARIANT
+
+
 def test_stream_probe_argument_checks():
     """skipln_tune_stream returns these statuses before any HIP call."""
     st = lambda s0=IN, s1=None, d0=OUT, d1=None, n=4096, b=256, u=4, g=1: L.load_tune().skipln_tune_stream(s0, s1, d0,

@@ -210,6 +210,24 @@ def test_kernel_forms(dt, geom, form_cap, op):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("geom", ROWTILE_GEOMETRIES)
+@pytest.mark.parametrize("op", ["layer_norm", "bias_softmax"])
+def test_single_tile_blocks_per_cu(dt, geom, op):
+    """The single-tile form's blocks-per-CU limit (set through the launch's
+    LDS) holds a compute unit to exactly min(limit, what its registers allow)
+    for every limit from 1 to 8; the table's limit never exceeds the
+    registers' count."""
+    tune = L.load_tune()
+    code = L.F32 if dt == "f32" else L.F16
+    bpc = lambda form, cap: tune.skipln_tune_blocks_per_cu(U.OPS[op], code, geom, form, cap)
+    free = bpc(1, 0)
+    assert free >= 1 and bpc(0, -1) >= 1
+    for cap in range(1, 9):
+        assert bpc(1, cap) == min(cap, free), (cap, free)
+    assert 1 <= bpc(1, -1) <= free
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("geom", ELEMENT_GEOMETRIES)
 @pytest.mark.parametrize("shape", ["full", "odd", "short"])
 @pytest.mark.parametrize("op", ["layer_norm", "simplified", "bias_add", "bias_softmax"])

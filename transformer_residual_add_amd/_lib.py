@@ -48,6 +48,7 @@ TUNE_SIGNATURES = {
     "skipln_tune_forward": (_i32, [_i32] + _FWD + [_i32, _vp, _i64, _vp]),
     "skipln_tune_forward_config": (_i32, [_i32] + _FWD + [_i32, _i64, _i32, _i32, _vp]),
     "skipln_tune_forward_form": (_i32, [_i32] + _FWD + [_i32, _i32, _i32, _i32, _vp]),
+    "skipln_tune_blocks_per_cu": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "skipln_tune_workspace_bytes": (_i64, [_i32, _i64, _i64, _i32, _i32, _i64, _i32]),
     "skipln_tune_select": (_i32, [_i32, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32]),
     "skipln_tune_kernel_name": (C.c_char_p, [_i32]),

@@ -146,6 +146,12 @@ template <int OP>
 hipError_t launch_rowtile_for(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
 template <int OP>
 hipError_t launch_elem_for(const Args& a, int dtype, int geometry, Tiling tiling, hipStream_t stream);
+// Blocks of row-tile geometry g's kernel a compute unit holds at once, in
+// kernel form kFormWalk or kFormOneTile (held to blocks_per_cu as a launch of
+// that form is; kBlocksAuto: the launcher's table).
+hipError_t rowtile_occupancy(int op, int dtype, int geometry, int form, int blocks_per_cu, int* out);
+template <int OP>
+hipError_t rowtile_occupancy_for(int dtype, int geometry, int form, int blocks_per_cu, int* out);
 // Split-row kernels (rows cut into slices of 1024 chunks, one workgroup per
 // slice, partials through a caller-provided workspace): whether they run
 // this operation and row (16-byte chunks, at most 64 slices), the workspace

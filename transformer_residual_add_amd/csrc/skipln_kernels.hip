@@ -1007,6 +1007,16 @@ hipError_t launch_elem(const Args& a, int op, int dtype, int geometry, Tiling ti
     }
 }
 
+hipError_t rowtile_occupancy(int op, int dtype, int geometry, int form, int blocks_per_cu, int* out) {
+    switch (op) {
+        case kOpLayerNorm: return rowtile_occupancy_for<kOpLayerNorm>(dtype, geometry, form, blocks_per_cu, out);
+        case kOpSimplified: return rowtile_occupancy_for<kOpSimplified>(dtype, geometry, form, blocks_per_cu, out);
+        case kOpBiasAdd: return rowtile_occupancy_for<kOpBiasAdd>(dtype, geometry, form, blocks_per_cu, out);
+        case kOpBiasSoftmax: return rowtile_occupancy_for<kOpBiasSoftmax>(dtype, geometry, form, blocks_per_cu, out);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_rowtile(const Args& a, int op, int dtype, int geometry, Tiling tiling, hipStream_t st) {
     switch (op) {
         case kOpLayerNorm: return launch_rowtile_for<kOpLayerNorm>(a, dtype, geometry, tiling, st);

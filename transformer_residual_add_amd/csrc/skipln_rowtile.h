@@ -666,6 +666,33 @@ constexpr int64_t kStationaryBatches = 3;
 // A dispatch counts its work-items in 32 bits: blocks x block stays below 2^32.
 constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 
+// The single-tile form's blocks per CU for a launch that asks for `cap`
+// (kBlocksAuto: the table's, or no limit where the table keeps the walking
+// form), and the dynamic LDS that enforces it.
+template <typename E, int OP, int GG, int CH, int BLOCK>
+hipError_t one_tile_lds(int cap, size_t* lds) {
+    static std::atomic<int> cache[kMaxBlocksCap + 1];
+    constexpr int table = single_tile_blocks<E, OP, GG, CH>();
+    if (cap < 0) cap = table > 0 ? table : 0;
+    return cap_lds(rowtile_kernel<E, OP, GG, CH, BLOCK, kFormOneTile>, BLOCK, cap, partial_bytes<GG, BLOCK>(), cache,
+                   lds);
+}
+
+// Blocks of a geometry's kernel a compute unit holds at once in kernel form
+// `form` (kFormWalk, or kFormOneTile held to `blocks_per_cu` as a launch of
+// that form is).
+template <typename E, int OP, int GG, int CH, int BLOCK>
+hipError_t occupancy_geom(int form, int blocks_per_cu, int* out) {
+    if (form == kFormWalk)
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            out, reinterpret_cast<const void*>(rowtile_kernel<E, OP, GG, CH, BLOCK, kFormWalk>), BLOCK, 0);
+    size_t lds = 0;
+    const hipError_t e = one_tile_lds<E, OP, GG, CH, BLOCK>(blocks_per_cu, &lds);
+    if (e != hipSuccess) return e;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        out, reinterpret_cast<const void*>(rowtile_kernel<E, OP, GG, CH, BLOCK, kFormOneTile>), BLOCK, lds);
+}
+
 template <typename E, int OP, int GG, int CH, int BLOCK>
 hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     constexpr Geom g = {GG, CH, BLOCK};
@@ -737,23 +764,24 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     }
     if constexpr (E::kPerChunk > 1) {
         if (mode != kTileSkipStationary && per <= 1) {
-            // cap: blocks per CU of the single-tile form (0: no limit), or
-            // -1 for the walking form.
-            int cap = -1;
+            // The single-tile form when forced, or for a large launch where
+            // the table gives it blocks per CU (>= 0).
+            bool single = false;
+            int cap = kBlocksAuto;
             if (tiling.form == kFormOneTile) {
-                constexpr int table = single_tile_blocks<E, OP, g.g, g.ch>();
-                cap = tiling.blocks_per_cu >= 0 ? tiling.blocks_per_cu : (table > 0 ? table : 0);
+                single = true;
+                cap = tiling.blocks_per_cu;
             } else if (tiling.form == kFormAuto &&
                        single_tile_launch(a.rows, a.hidden, static_cast<int>(16 / E::kPerChunk))) {
                 cap = single_tile_blocks<E, OP, g.g, g.ch>();
+                single = cap >= 0;
             }
-            if (cap >= 0) {
-                static std::atomic<int> lds_cache[kMaxBlocksCap + 1];
-                auto kernel_one = rowtile_kernel<E, OP, g.g, g.ch, g.block, kFormOneTile>;
+            if (single) {
                 size_t lds = 0;
-                const hipError_t e = cap_lds(kernel_one, g.block, cap, partial_bytes<g.g, g.block>(), lds_cache, &lds);
+                const hipError_t e = one_tile_lds<E, OP, g.g, g.ch, g.block>(cap, &lds);
                 if (e != hipSuccess) return e;
-                return launch_grid(kernel_one, g.block, blocks < 1 ? 1 : blocks, a, st, lds);
+                return launch_grid(rowtile_kernel<E, OP, g.g, g.ch, g.block, kFormOneTile>, g.block,
+                                   blocks < 1 ? 1 : blocks, a, st, lds);
             }
         }
     }
@@ -764,6 +792,16 @@ template <typename T, int OP, int... I>
 hipError_t launch_geom_dispatch(int idx, const Args& a, Tiling t, hipStream_t st, std::integer_sequence<int, I...>) {
     hipError_t r = hipErrorInvalidValue;
     ((idx == I ? (r = launch_geom<Elem<T>, OP, kGeoms[I].g, kGeoms[I].ch, kGeoms[I].block>(a, t, st), 0) : 0), ...);
+    return r;
+}
+
+template <typename T, int OP, int... I>
+hipError_t occupancy_geom_dispatch(int idx, int form, int blocks_per_cu, int* out, std::integer_sequence<int, I...>) {
+    hipError_t r = hipErrorInvalidValue;
+    ((idx == I ? (r = occupancy_geom<Elem<T>, OP, kGeoms[I].g, kGeoms[I].ch, kGeoms[I].block>(form, blocks_per_cu, out),
+                  0)
+               : 0),
+     ...);
     return r;
 }
 

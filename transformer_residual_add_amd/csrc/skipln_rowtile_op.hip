@@ -27,7 +27,17 @@ hipError_t launch_elem_for(const Args& a, int dtype, int geometry, Tiling tiling
                       : launch_elem_dispatch<_Float16, OP>(geometry, a, tiling, st, seq);
 }
 
+template <int OP>
+hipError_t rowtile_occupancy_for(int dtype, int geometry, int form, int blocks_per_cu, int* out) {
+    using namespace rowtile;
+    if (geometry < 0 || geometry >= kNumGeoms) return hipErrorInvalidValue;
+    auto seq = std::make_integer_sequence<int, kNumGeoms>{};
+    return dtype == 0 ? occupancy_geom_dispatch<float, OP>(geometry, form, blocks_per_cu, out, seq)
+                      : occupancy_geom_dispatch<_Float16, OP>(geometry, form, blocks_per_cu, out, seq);
+}
+
 template hipError_t launch_rowtile_for<SKIPLN_ROWTILE_OP>(const Args&, int, int, Tiling, hipStream_t);
+template hipError_t rowtile_occupancy_for<SKIPLN_ROWTILE_OP>(int, int, int, int, int*);
 template hipError_t launch_elem_for<SKIPLN_ROWTILE_OP>(const Args&, int, int, Tiling, hipStream_t);
 
 }  // namespace skipln

@@ -100,6 +100,18 @@ SKIPLN_API int skipln_tune_forward_form(int op, const void* input, const void* s
                variant, &t, stream, nullptr, store);
 }
 
+SKIPLN_API int skipln_tune_blocks_per_cu(int op, int dtype, int geometry, int form, int blocks_per_cu) {
+    if (!skipln::core::known_op(op)) return -SKIPLN_ERR_OP;
+    if (dtype != SKIPLN_F32 && dtype != SKIPLN_F16) return -SKIPLN_ERR_DTYPE;
+    if (geometry < 0 || geometry >= skipln::rowtile_count()) return -SKIPLN_ERR_VARIANT;
+    if (form != skipln::kFormWalk && form != skipln::kFormOneTile) return -SKIPLN_ERR_VARIANT;
+    if (blocks_per_cu < skipln::kBlocksAuto) return -SKIPLN_ERR_VARIANT;
+    int occ = 0;
+    const hipError_t e = skipln::rowtile_occupancy(op, dtype, geometry, form, blocks_per_cu, &occ);
+    if (e != hipSuccess) return -status_of(e);
+    return occ;
+}
+
 SKIPLN_API int64_t skipln_tune_workspace_bytes(int op, int64_t rows, int64_t hidden, int dtype, int skip_mode,
                                                int64_t skip_rows, int variant) {
     if (variant == SKIPLN_VARIANT_AUTO)
