@@ -288,12 +288,17 @@ def time_copy(nbytes: int, steps: int, warmup: int):
 # Tile shapes of the streaming probe: (lanes, chunks per lane, XCD granule in
 # tiles), each timed with both store policies of the row kernels (when the mix
 # writes).  Granule 1 is address order: consecutive tiles on different XCDs.
-# The 64 x 1 tile at granules 2, 3, 4 and 16 hands each XCD 2, 3, 4 and 16
-# KiB of every stream at a time -- the granularity of a row kernel whose
-# workgroup owns rows of that size.
+# The 64 x 1 tile at granules 2-64 hands each XCD 2-64 KiB of every stream at
+# a time, spread over as many one-wavefront workgroups; the 256 x 4 and
+# 1024 x 1 tiles at granules 2 and 4 hand 32-64 KiB to one XCD in 16 KiB
+# workgroup tiles.  A row kernel whose workgroup owns a row has both an XCD
+# granule and a workgroup tile of at least one row.
 STREAM_SHAPES = ((64, 1, 1), (64, 4, 1), (256, 1, 1), (256, 4, 1), (1024, 1, 1), (1024, 4, 1),
-                 (64, 1, 2), (64, 1, 3), (64, 1, 4), (64, 1, 16))
-STREAM_GRANULES = (1024, 2048, 3072, 4096, 16384)
+                 (64, 1, 2), (64, 1, 3), (64, 1, 4), (64, 1, 16), (64, 1, 32), (64, 1, 64), (256, 4, 2),
+                 (256, 4, 4), (1024, 1, 2))
+STREAM_GRANULES = (1024, 2048, 3072, 4096, 16384, 65536)
+# Workgroup tile sizes (bytes of each stream one workgroup moves) reported.
+STREAM_TILES = (1024, 4096, 16384, 65536)
 
 
 def time_streams(nbytes: int, steps: int, warmup: int):
@@ -349,17 +354,24 @@ def time_streams(nbytes: int, steps: int, warmup: int):
             # of that many bytes per stream.
             at_granule = {str(g): max(r["gb_per_s"] for r in shapes if r["xcd_granule_bytes"] >= g)
                           for g in STREAM_GRANULES}
+            # Best rate among shapes whose workgroups each move at least this
+            # many bytes of every stream: the ceiling of a row kernel whose
+            # workgroup owns rows of that size.
+            at_tile = {str(b): max(r["gb_per_s"] for r in shapes if r["block"] * r["chunks_per_lane"] * 16 >= b)
+                       for b in STREAM_TILES}
             out.append({"reads": reads, "writes": writes, "bytes_moved": moved, "buffer_sets": n_sets, "best_gb_per_s": best["gb_per_s"],
                         "best_frac_of_peak": round(best["gb_per_s"] / HBM_PEAK_GBS, 4),
                         "best_shape": [best["block"], best["chunks_per_lane"], best["xcd_granule"],
                                        best["store_through"]],
-                        "best_at_xcd_granule_bytes": at_granule, "shapes": shapes})
+                        "best_at_xcd_granule_bytes": at_granule, "best_at_tile_bytes": at_tile,
+                        "shapes": shapes})
             log(f"stream {reads}R{writes}W: best {best['gb_per_s']:.0f} GB/s (block {best['block']}, "
                 f"{best['chunks_per_lane']} chunk(s)/lane, granule {best['xcd_granule']}, "
                 f"through {best['store_through']}); " +
                 ", ".join(f"{r['block']}x{r['chunks_per_lane']}g{r['xcd_granule']}t{r['store_through']}: "
                           f"{r['gb_per_s']:.0f}" for r in shapes) +
-                "; by XCD granule: " + ", ".join(f"{g}B {v:.0f}" for g, v in at_granule.items()))
+                "; by XCD granule: " + ", ".join(f"{g}B {v:.0f}" for g, v in at_granule.items()) +
+                "; by workgroup tile: " + ", ".join(f"{b}B {v:.0f}" for b, v in at_tile.items()))
     return out
 
 
