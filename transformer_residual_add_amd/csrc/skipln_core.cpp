@@ -103,8 +103,17 @@ Args make_args(const Call& c, int store) {
     a.tiles_per_block = 1;
     a.tiling = kTileStrided;
     // Bytes the launch writes: the output, and the residual when emitted.
-    const int64_t written = c.rows * c.hidden * (c.dtype == SKIPLN_F32 ? 4 : 2) * (c.residual ? 2 : 1);
-    a.store_through = store == kStoreAuto ? (written >= kStoreThroughBytes ? 1 : 0) : (store == kStoreThrough);
+    // The system-scope store policy serves large launches of rows of whole
+    // 128-byte lines only: where rows end inside a line (so every row's
+    // first and last line are written partly), it measured 14-19 % slower
+    // than non-temporal stores on MI355X (2 GiB launches: float16 rows of
+    // 2056 / 4104 / 8200 values 500 / 489 / 485 against 431 / 417 / 391 us,
+    // float32 rows of 1028 values 511 against 420), while on whole-line rows
+    // it is the faster one (float16 rows of 2048 values: 367 against 375).
+    const int64_t row_bytes = c.hidden * (c.dtype == SKIPLN_F32 ? 4 : 2);
+    const int64_t written = c.rows * row_bytes * (c.residual ? 2 : 1);
+    a.store_through = store == kStoreAuto ? (written >= kStoreThroughBytes && row_bytes % 128 == 0 ? 1 : 0)
+                                          : (store == kStoreThrough);
     return a;
 }
 

@@ -28,7 +28,8 @@ struct Args {
     int32_t tiling;
     // Row-tile and register-resident kernels: write outputs with the
     // system-scope store policy (set for launches writing at least
-    // kStoreThroughBytes, where it was measured faster).
+    // kStoreThroughBytes of rows of whole 128-byte lines, where it was
+    // measured faster).
     int32_t store_through;
 };
 
