@@ -49,6 +49,8 @@ def kernel_sources(kernel: str):
     taken on other versions of them are stale."""
     if "rowtile_" in kernel or "rowelem_" in kernel:
         files = ("skipln_device.h", "skipln_rowtile.h", "skipln_rowtile_op.hip")
+    elif "span_" in kernel:
+        files = ("skipln_device.h", "skipln_rowtile.h", "skipln_span.hip")
     elif "splitrow_" in kernel:
         files = ("skipln_device.h", "skipln_split.hip")
     elif "regrow_" in kernel:

@@ -68,11 +68,21 @@ enum {
                                      two passes from the bias rows re-read
                                      through the caches; 16-byte chunks,
                                      aligned pointers; no workspace */
+    SKIPLN_VARIANT_SPAN = 8,      /* span row tiles: a row of any length read
+                                     as the aligned 16-byte chunks its bytes
+                                     touch, elements of neighbouring rows
+                                     masked; every tensor 16-byte aligned at
+                                     its base; rows spanning up to 2048
+                                     chunks (what the automatic choice takes
+                                     for rows that are not whole 16-byte
+                                     chunks) */
     SKIPLN_VARIANT_GEOMETRY = 64, /* + g: ROWTILE with row-tile geometry g,
                                      0 <= g < skipln_tune_rowtile_geometries(), for
                                      tests and tuning */
-    SKIPLN_VARIANT_ELEMENT_GEOMETRY = 128 /* + g: ELEMENT with geometry g,
+    SKIPLN_VARIANT_ELEMENT_GEOMETRY = 128, /* + g: ELEMENT with geometry g,
                                      0 <= g < skipln_tune_element_geometries() */
+    SKIPLN_VARIANT_SPAN_GEOMETRY = 192 /* + g: SPAN with geometry g,
+                                     0 <= g < skipln_tune_span_geometries() */
 };
 
 /* How the row-tile kernel distributes row tiles over workgroups (see
@@ -166,10 +176,12 @@ SKIPLN_API int skipln_tune_select(int op, int64_t rows, int64_t hidden, int dtyp
  * "softmax_rowtile_f16_g8_c1", ...); "unknown" for an invalid id. */
 SKIPLN_API const char* skipln_tune_kernel_name(int kernel_id);
 
-/* Number of row-tile geometries (SKIPLN_VARIANT_GEOMETRY + g) and of
- * element-wise ones (SKIPLN_VARIANT_ELEMENT_GEOMETRY + g). */
+/* Number of row-tile geometries (SKIPLN_VARIANT_GEOMETRY + g), of
+ * element-wise ones (SKIPLN_VARIANT_ELEMENT_GEOMETRY + g) and of span ones
+ * (SKIPLN_VARIANT_SPAN_GEOMETRY + g). */
 SKIPLN_API int skipln_tune_rowtile_geometries(void);
 SKIPLN_API int skipln_tune_element_geometries(void);
+SKIPLN_API int skipln_tune_span_geometries(void);
 
 /* The argument checks of operation `op` (the rules of skipln_forward_ws):
  * host code only, no HIP call, no pointer dereferenced. */

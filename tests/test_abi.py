@@ -87,7 +87,8 @@ def test_header_enums_match_binding():
         "SKIPLN_VARIANT_LDSROW": L.VARIANT_LDSROW, "SKIPLN_VARIANT_SPLITROW": L.VARIANT_SPLITROW,
         "SKIPLN_VARIANT_ELEMENT": L.VARIANT_ELEMENT,
         "SKIPLN_VARIANT_REGROW": L.VARIANT_REGROW, "SKIPLN_VARIANT_ELEMENT_GEOMETRY": L.VARIANT_ELEMENT_GEOMETRY,
-        "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY,
+        "SKIPLN_VARIANT_GEOMETRY": L.VARIANT_GEOMETRY, "SKIPLN_VARIANT_SPAN": L.VARIANT_SPAN,
+        "SKIPLN_VARIANT_SPAN_GEOMETRY": L.VARIANT_SPAN_GEOMETRY,
         "SKIPLN_TILE_CONTIGUOUS": L.TILE_CONTIGUOUS, "SKIPLN_TILE_STRIDED": L.TILE_STRIDED,
         "SKIPLN_TILE_SKIP_STATIONARY": L.TILE_SKIP_STATIONARY,
         "SKIPLN_STORE_AUTO": L.STORE_AUTO, "SKIPLN_STORE_STREAM": L.STORE_STREAM,
@@ -255,18 +256,37 @@ def test_select_kernels():
     assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4"
     assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
     assert name(sel(64, 0)) == "rowtile_f32_g16_c1"
-    # not a multiple of a 16-byte chunk, or misaligned: element-wise row tiles;
-    # too long for every family: generic
-    assert name(sel(1001, 0)) == "rowelem_f32_g128_c8"
+    # not a multiple of a 16-byte chunk with 16-byte aligned tensors: span row
+    # tiles (up to 2048 chunks touched); misaligned tensors or longer rows:
+    # element-wise row tiles; too long for every family: generic
+    assert name(sel(1001, 0)) == "span_f32_g64_c4"
+    assert name(sel(77, 1)) == "span_f16_g8_c2"
+    assert name(sel(3, 1)) == "span_f16_g8_c2"
+    assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g64_c4"
+    assert name(sel(2039, 1)) == "span_f16_g64_c4"           # 256 chunks touched
+    assert name(sel(2041, 1)) == "rowelem_f16_g256_c8"       # layer norm beyond one wavefront
+    assert name(sel(16366, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g512_c4"    # 2047 chunks touched
+    assert name(sel(16378, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f16_g1024_c16"
+    assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowelem_f16_g256_c8"
+    assert name(sel(1001, 0, mode=L.SKIP_BROADCAST)) == "rowelem_f32_g128_c8"
+    assert name(sel(1001, 0, al=0)) == "rowelem_f32_g128_c8"
     assert name(sel(1024, 0, al=0)) == "rowelem_f32_g128_c8"
-    assert name(sel(77, 1)) == "rowelem_f16_g32_c4"
-    assert name(sel(3, 1)) == "rowelem_f16_g4_c1"
+    assert name(sel(77, 1, al=0)) == "rowelem_f16_g32_c4"
+    assert name(sel(3, 1, al=0)) == "rowelem_f16_g4_c1"
     assert name(sel(16384, 1, al=0)) == "rowelem_f16_g1024_c16"
     assert name(sel(16385, 1, al=0)) == "generic_f16"
     assert sel(16385, 1, v=L.VARIANT_ELEMENT) == -L.ERR_UNSUPPORTED
     assert name(sel(1000, 0, v=L.VARIANT_ELEMENT)) == "rowelem_f32_g128_c8"
     assert sel(1000, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED   # 4 elements
     assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0)) == "rowelem_f32_g4_c1"
+    ns = lib.skipln_tune_span_geometries()
+    assert ns == 8
+    assert sel(4, 0, v=L.VARIANT_SPAN_GEOMETRY + ns) == -L.ERR_VARIANT
+    assert sel(4, 0, al=0, v=L.VARIANT_SPAN) == -L.ERR_UNSUPPORTED              # needs 16-byte aligned tensors
+    assert sel(4001, 0, v=L.VARIANT_SPAN_GEOMETRY + 0) == -L.ERR_UNSUPPORTED    # too long for 8 x 2
+    assert name(sel(1024, 0, v=L.VARIANT_SPAN)) == "span_f32_g128_c4"           # any length when forced
+    for g in range(ns):
+        assert name(sel(5, 1, v=L.VARIANT_SPAN_GEOMETRY + g)).startswith("span_f16_g")
     ne = lib.skipln_tune_element_geometries()
     assert ne == 13
     assert sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + ne) == -L.ERR_VARIANT
@@ -291,7 +311,8 @@ def test_select_kernels():
     assert sel(64, 0, op=7) == -L.ERR_OP
     assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
-    assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
+    assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_span_f16_g64_c2"
+    assert name(sel(1001, 1, al=0, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
     # long rows: LDS-staged up to 163584 bytes of binary32 sums, then held
     # in registers up to 65536 values, then generic
     assert name(sel(8192, 0)) == "rowtile_f32_g512_c4"
@@ -314,7 +335,8 @@ def test_select_kernels():
     assert name(sel(8, 0, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowtile_f32_g4_c1"
     assert name(sel(4096, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowtile_f16_g128_c4"
     assert name(sel(20000, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_ldsrow_f32"
-    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f32_g4_c2"
+    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f32_g8_c2"
+    assert name(sel(7, 0, al=0, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f32_g4_c2"
     assert name(sel(64, 1, op=L.OP_BIAS_SOFTMAX, v=L.VARIANT_LDSROW)) == "softmax_ldsrow_f16"
     assert sel(64, 0, mode=L.SKIP_BROADCAST_INNER) == -L.ERR_MODE
     assert sel(66, 0, v=L.VARIANT_LDSROW) == -L.ERR_UNSUPPORTED
@@ -322,8 +344,8 @@ def test_select_kernels():
 
 
 def test_every_geometry_is_an_automatic_choice():
-    """Each row-tile and element-wise geometry is what the automatic choice
-    takes for some operation, type, skip form and row length."""
+    """Each row-tile, element-wise and span geometry is what the automatic
+    choice takes for some operation, type, skip form and row length."""
     lib = L.load_tune()
     used, used_elem = set(), set()
     for op in (L.OP_LAYER_NORM, L.OP_BIAS_ADD, L.OP_BIAS_SOFTMAX):
@@ -344,6 +366,12 @@ def test_every_geometry_is_an_automatic_choice():
     elems = {L.kernel_name(SEL(L.OP_LAYER_NORM, 1, 0, al=0, v=L.VARIANT_ELEMENT_GEOMETRY + g)).split("rowelem_f32_")[1]
              for g in range(lib.skipln_tune_element_geometries())}
     assert elems <= used_elem, f"element geometries no automatic choice takes: {elems - used_elem}"
+    used_span = {L.kernel_name(SEL(op, h, dt)).split("span_")[1].split("_", 1)[1]
+                 for op in (L.OP_LAYER_NORM, L.OP_BIAS_SOFTMAX) for dt in (0, 1) for h in range(1, 16385, 3)
+                 if "span_" in L.kernel_name(SEL(op, h, dt))}
+    spans = {L.kernel_name(SEL(L.OP_LAYER_NORM, 1, 0, v=L.VARIANT_SPAN_GEOMETRY + g)).split("span_f32_")[1]
+             for g in range(lib.skipln_tune_span_geometries())}
+    assert spans <= used_span, f"span geometries no automatic choice takes: {spans - used_span}"
 
 
 def test_auto_choice_holds_every_hidden_size():

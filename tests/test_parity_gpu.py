@@ -597,7 +597,7 @@ def test_long_rows_auto(dt, hidden):
 @pytest.mark.parametrize("mu", [100.0, 1000.0])
 @pytest.mark.parametrize("hidden", [64, 768, 4096, 12288])
 @pytest.mark.parametrize("variant", [L.VARIANT_AUTO, L.VARIANT_MULTIWAVE, L.VARIANT_GENERIC, L.VARIANT_LDSROW,
-                                     L.VARIANT_ELEMENT])
+                                     L.VARIANT_ELEMENT, L.VARIANT_SPAN])
 def test_large_offset_rows(dt, mu, hidden, variant):
     """Rows whose mean is far from zero (variance cancellation) in every
     kernel family, within the binary32 tolerance."""

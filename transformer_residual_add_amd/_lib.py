@@ -24,8 +24,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_MODE, ERR_EPS, ERR_ALIAS = 0, 1, 2, 3, 4
 ERR_UNSUPPORTED, ERR_LAUNCH, ERR_DEVICE, ERR_VARIANT, ERR_OP, ERR_WORKSPACE = 7, 8, 9, 10, 11, 12
 OP_LAYER_NORM, OP_SIMPLIFIED, OP_BIAS_ADD, OP_BIAS_SOFTMAX = 0, 1, 2, 3
 VARIANT_AUTO, VARIANT_GENERIC, VARIANT_ROWTILE, VARIANT_MULTIWAVE, VARIANT_LDSROW, VARIANT_SPLITROW = 0, 1, 2, 3, 4, 5
-VARIANT_ELEMENT, VARIANT_REGROW = 6, 7
-VARIANT_GEOMETRY, VARIANT_ELEMENT_GEOMETRY = 64, 128
+VARIANT_ELEMENT, VARIANT_REGROW, VARIANT_SPAN = 6, 7, 8
+VARIANT_GEOMETRY, VARIANT_ELEMENT_GEOMETRY, VARIANT_SPAN_GEOMETRY = 64, 128, 192
 TILE_CONTIGUOUS, TILE_STRIDED, TILE_SKIP_STATIONARY = 0, 1, 2
 STORE_AUTO, STORE_STREAM, STORE_THROUGH = -1, 0, 1
 
@@ -54,6 +54,7 @@ TUNE_SIGNATURES = {
     "skipln_tune_kernel_name": (C.c_char_p, [_i32]),
     "skipln_tune_rowtile_geometries": (_i32, []),
     "skipln_tune_element_geometries": (_i32, []),
+    "skipln_tune_span_geometries": (_i32, []),
     "skipln_tune_validate": (_i32, [_i32] + _FWD),
     "skipln_tune_copy": (_i32, [_vp, _vp, _i64, _vp]),
     "skipln_tune_stream": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _i32, _vp]),

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libskipln.so")
 TUNE_LIB = os.path.join(PKG, "libskipln_tune.so")
 # (source, extra flags): the row tiles compile once per operation (kOp* = 0..3).
-KERNELS = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_regrow.hip", "skipln_regnorm.hip")] + [
+KERNELS = [(os.path.join(CSRC, f), []) for f in ("skipln_kernels.hip", "skipln_split.hip", "skipln_regrow.hip", "skipln_regnorm.hip",
+                                                    "skipln_span.hip")] + [
     (os.path.join(CSRC, "skipln_rowtile_op.hip"), [f"-DSKIPLN_ROWTILE_OP={op}"]) for op in range(4)]
 CORE = [(os.path.join(CSRC, "skipln_core.cpp"), [])]
 API = [(os.path.join(CSRC, "skipln_api.cpp"), []), (os.path.join(CSRC, "skipln_static.hip"), [])]

@@ -217,6 +217,17 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         const int g = elem_ok ? elem_pick(op, hidden) : -1;
         return g >= 0 ? base + kElemFirst + g : -SKIPLN_ERR_UNSUPPORTED;
     }
+    if (variant == kVariantSpan) {
+        int g = -1;  // the smallest geometry that holds the row
+        for (int i = 0; vec_ok && g < 0 && i < span_count(); ++i)
+            if (span_holds(i, hidden, dtype)) g = i;
+        return g >= 0 ? base + kSpanFirst + g : -SKIPLN_ERR_UNSUPPORTED;
+    }
+    if (variant >= kVariantSpanGeometry && variant < kVariantSpanGeometry + span_count()) {
+        const int g = variant - kVariantSpanGeometry;
+        if (!vec_ok || !span_holds(g, hidden, dtype)) return -SKIPLN_ERR_UNSUPPORTED;
+        return base + kSpanFirst + g;
+    }
     if (variant >= kVariantElementGeometry && variant < kVariantElementGeometry + elem_count()) {
         const int g = variant - kVariantElementGeometry;
         if (!elem_ok || !elem_holds(g, hidden)) return -SKIPLN_ERR_UNSUPPORTED;
@@ -264,8 +275,10 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         const int g = chunked ? rowtile_pick(op, hidden, dtype, broadcast, variant == kVariantMultiwave) : -1;
         if (g >= 0) return base + kRowtileFirst + g;
         if (variant != kVariantAuto) return -SKIPLN_ERR_UNSUPPORTED;
-        // Rows that are not whole chunks (or tensors not 16-byte aligned):
-        // element-wise row tiles, then the generic kernel.
+        // Rows that are not whole chunks: span row tiles (16-byte aligned
+        // tensors), else element-wise row tiles, then the generic kernel.
+        const int sp = vec_ok && !chunked ? span_pick(op, hidden, dtype, broadcast) : -1;
+        if (sp >= 0) return base + kSpanFirst + sp;
         const int e = elem_ok && !chunked ? elem_pick(op, hidden) : -1;
         if (e >= 0) return base + kElemFirst + e;
         return base + kGenericIndex;
@@ -374,6 +387,10 @@ int run(const Call& c, int variant, const Tiling* tiling, skipln_stream_t stream
     if (index == kLdsRowIndex) {
         if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // the long-row kernel has no tiling
         return status_of(launch_ldsrow(a, c.op, c.dtype, s));
+    }
+    if (index >= kSpanFirst && index < kSpanFirst + span_count()) {
+        if (tiling) return SKIPLN_ERR_UNSUPPORTED;  // one tile of rows per block
+        return status_of(launch_span(a, c.op, c.dtype, index - kSpanFirst, s));
     }
     if (index >= kElemFirst) {
         const int g = index - kElemFirst;

@@ -21,8 +21,10 @@ constexpr int kVariantLdsRow = 4;
 constexpr int kVariantSplitRow = 5;
 constexpr int kVariantElement = 6;
 constexpr int kVariantRegRow = 7;
+constexpr int kVariantSpan = 8;
 constexpr int kVariantGeometry = 64;
 constexpr int kVariantElementGeometry = 128;
+constexpr int kVariantSpanGeometry = 192;
 
 // One call's arguments after the operation's own rules: BiasAdd has no
 // gamma, beta, residual output or epsilon; BiasSoftmax has none of these and

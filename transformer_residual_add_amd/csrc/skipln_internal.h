@@ -95,11 +95,13 @@ constexpr int kNumOps = 4;
 // kRowtileFirst.. = row tiles of 16-byte chunks, kElemFirst.. = row tiles of
 // single elements, kRegRowIndex = the register-resident long-row softmax,
 // kSplitRowIndex = the split-row kernel pair, kLdsRowIndex = the LDS-staged
-// long-row kernel.
+// long-row kernel, kSpanFirst.. = span row tiles (rows that are not whole
+// chunks, read as aligned 16-byte chunks).
 constexpr int kIdsPerType = 128;
 constexpr int kGenericIndex = 0;
 constexpr int kRowtileFirst = 1;
 constexpr int kElemFirst = 64;
+constexpr int kSpanFirst = 96;
 constexpr int kRegRowIndex = 125;
 constexpr int kSplitRowIndex = 126;
 constexpr int kLdsRowIndex = 127;
@@ -164,6 +166,15 @@ hipError_t launch_split(const Args& a, int op, int dtype, void* workspace, hipSt
 // root-mean-square form): whether the kernel holds this row, and its launch.
 bool regnorm_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_regnorm(const Args& a, int op, int dtype, hipStream_t stream);
+// Span row tiles (rows of any length, every tensor 16-byte aligned): the
+// number of geometries, geometry g's group, chunks per lane and block,
+// whether it holds a row of `hidden` values, the automatic choice (or -1),
+// and the launch (one row per group, one tile of rows per block).
+int span_count();
+bool span_geometry(int geometry, int* g, int* ch, int* block);
+bool span_holds(int geometry, int64_t hidden, int dtype);
+int span_pick(int op, int64_t hidden, int dtype, bool broadcast);
+hipError_t launch_span(const Args& a, int op, int dtype, int geometry, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);
 // Streaming probe: `reads` (0-2) input streams s0, s1 to `writes` (0-2)
 // output streams d0, d1 of `chunks` 16-byte chunks each, in tiles of `block`

@@ -853,6 +853,9 @@ struct NameTable {
                         geom_name(dst, op_prefix[op], "rowtile", tn[t], kGeoms[gi]);
                     } else if (i >= kElemFirst && i < kElemFirst + kNumElemGeoms) {
                         geom_name(dst, op_prefix[op], "rowelem", tn[t], kElemGeoms[i - kElemFirst]);
+                    } else if (Geom sg; i >= kSpanFirst &&
+                               span_geometry(i - kSpanFirst, &sg.g, &sg.ch, &sg.block)) {
+                        geom_name(dst, op_prefix[op], "span", tn[t], sg);
                     } else {
                         snprintf(dst, 48, "unknown");
                     }

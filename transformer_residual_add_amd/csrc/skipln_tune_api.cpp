@@ -16,6 +16,8 @@ static_assert(SKIPLN_VARIANT_AUTO == skipln::core::kVariantAuto &&
                   SKIPLN_VARIANT_SPLITROW == skipln::core::kVariantSplitRow &&
                   SKIPLN_VARIANT_ELEMENT == skipln::core::kVariantElement &&
                   SKIPLN_VARIANT_REGROW == skipln::core::kVariantRegRow &&
+                  SKIPLN_VARIANT_SPAN == skipln::core::kVariantSpan &&
+                  SKIPLN_VARIANT_SPAN_GEOMETRY == skipln::core::kVariantSpanGeometry &&
                   SKIPLN_VARIANT_GEOMETRY == skipln::core::kVariantGeometry &&
                   SKIPLN_VARIANT_ELEMENT_GEOMETRY == skipln::core::kVariantElementGeometry,
               "kernel families of the ABI and the host logic agree");
@@ -149,6 +151,8 @@ SKIPLN_API const char* skipln_tune_kernel_name(int kernel_id) { return skipln::k
 SKIPLN_API int skipln_tune_rowtile_geometries(void) { return skipln::rowtile_count(); }
 
 SKIPLN_API int skipln_tune_element_geometries(void) { return skipln::elem_count(); }
+
+SKIPLN_API int skipln_tune_span_geometries(void) { return skipln::span_count(); }
 
 SKIPLN_API int skipln_tune_validate(int op, const void* input, const void* skip, int skip_mode, int64_t skip_rows,
                                     const void* gamma, const void* beta, const void* bias, const void* out,
