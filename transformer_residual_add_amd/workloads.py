@@ -363,6 +363,22 @@ EXTRA: Dict[str, Workload] = {
             seed=1022,
             op="bias_softmax",
         ),
+        # Attention over 1500 keys (an audio encoder's frames), with an
+        # additive bias as large as the scores (one bias row per data row):
+        # rows of 3000 bytes, not whole 16-byte chunks, so each row starts at
+        # its own offset within a chunk.
+        Workload(
+            name="softmax_frames_8x8x1500x1500_f16_fullbias",
+            shape=(8 * 8 * 1500, 1500),
+            dtype="f16",
+            skip_shape=(8 * 8 * 1500, 1500),
+            input_dist=normal(0, 2),
+            skip_dist=normal(0, 1),
+            gamma_dist=None,
+            beta_dist=None,
+            seed=1024,
+            op="bias_softmax",
+        ),
         # Softmax over a vocabulary (sampling from language-model logits): rows
         # of 128256 values, beyond one workgroup's LDS, so they split across
         # workgroups; one bias row (a logit bias) shared by every row.
