@@ -121,6 +121,21 @@ def test_span_in_place(dt, hidden):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("hidden", [77, 121, 197])
+def test_span_softmax_in_place(dt, hidden):
+    """Softmax written over its data: on rows of 8 and 16 lanes the chunk two
+    rows share is spliced from both rows' results and stored whole by the
+    later row, after both rows have read it."""
+    w = W.small_case(8 * 64 + 5, hidden, dt, op="bias_softmax", seed=hidden + 2)
+    inputs = W.make_inputs(w)
+    ref = U.oracle_rows(w, inputs)
+    dc = U.DeviceCase(w, inputs, residual=False)
+    U.note(f"span softmax in place {dt} H={hidden}")
+    dc.run(L.VARIANT_SPAN, out=dc.x)
+    U.assert_out_close(dc.host(dc.x), ref["y"], dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_span_softmax_special_values(dt):
     """-inf keys (a padding mask), a row of -inf only (NaN), a NaN and a +inf
     (their rows NaN), and every other row finite, in rows of 197 keys."""

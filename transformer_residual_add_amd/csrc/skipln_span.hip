@@ -77,6 +77,20 @@ __device__ __forceinline__ u32x4 realign(const u32x4& lo, const u32x4& hi, int s
     return r;
 }
 
+// Bytes 0 .. dx-1 of `head` followed by bytes dx .. 15 of `rest`.
+__device__ __forceinline__ u32x4 splice(const u32x4& head, const u32x4& rest, int dx) {
+    const unsigned h[4] = {head.x, head.y, head.z, head.w};
+    const unsigned r[4] = {rest.x, rest.y, rest.z, rest.w};
+    unsigned o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int cut = dx - 4 * q;  // bytes of dword q taken from head
+        const unsigned m = cut >= 4 ? 0xFFFFFFFFu : cut <= 0 ? 0u : (1u << (cut * 8)) - 1u;
+        o[q] = (h[q] & m) | (r[q] & ~m);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
 // A vector of `chunks` whole or partial 16-byte chunks seen from a row:
 // chunk i of the row's span needs the vector's chunks q0 + i and q0 + i + 1,
 // shifted by `sig` bytes; chunks outside the vector read as zeros.  A partial
@@ -114,6 +128,23 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
     constexpr int WPR = G > 64 ? G / 64 : 1;           // wavefronts per row
     static_assert(BLOCK % G == 0 && BLOCK % 64 == 0 && G >= 8, "block of whole groups and wavefronts");
     __shared__ float4 partial[2][RPB][WPR];
+    // Seams: the chunk that holds the end of one row and the start of the
+    // next.  Where both rows lie in one wavefront (all but every (64/G)th
+    // row), the two rows' lanes park their copies of it here and the later
+    // row's first lane stores the spliced chunk whole, instead of both
+    // storing their elements one by one.  One wavefront writes and reads each
+    // entry, so no barrier is needed: its LDS operations complete in order.
+    // Taken for softmax rows of 8 and 16 lanes: over 77 / 197 float16 keys
+    // 127-136 / 64-66 against 151 / 70-71 us, 121 float32 keys 138-139
+    // against 142-143.  Elsewhere the few registers it holds cost more than
+    // the stores save (32-lane softmax rows over 255 keys, the
+    // normalizations and BiasAdd: 2-7 % slower; some lost a wavefront of
+    // occupancy).  Outputs: out, and the normalizations' residual.
+    constexpr int NOUT = kNorm ? 2 : 1;
+    constexpr bool kSeams = OP == kOpBiasSoftmax && G <= 16;
+    constexpr int kSeamRows = kSeams ? RPB : 1;
+    __shared__ u32x4 seam_head[NOUT][kSeamRows];  // from the earlier row
+    __shared__ u32x4 seam_rest[NOUT][kSeamRows];  // from the later row
 
     const int tid = threadIdx.x;
     const int slot = G >= 64 ? __builtin_amdgcn_readfirstlane(tid / G) : tid / G;
@@ -211,7 +242,13 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
         const int tile_bytes = static_cast<int>((t1 - t0) * 16);
         const int lane_base = static_cast<int>(c0 - t0);
         const bool through = a.store_through != 0;
-        auto put = [&](void* base, int k, const u32x4& v) {
+        // Rows longer than one chunk have distinct first and last chunks, so
+        // a seam holds the ends of exactly two rows.  Seam j (the start of
+        // slot j) joins two rows of one wavefront unless slot j starts one.
+        const bool seams = kSeams && H * SZ > 16;
+        auto joined = [&](int j) { return j % (64 / G) != 0; };
+        const int tail_bytes = static_cast<int>((rb + H * SZ) & 15);  // of the row in its last chunk; 0: whole
+        auto put = [&](void* base, int o, int k, const u32x4& v) {
             const __amdgpu_buffer_rsrc_t r = buffer_rsrc(static_cast<char*>(base) + t0 * 16, tile_bytes);
             const int i = k * G + lt;
             const int voff = (lane_base + i) * 16;
@@ -219,6 +256,16 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
             if (first >= 0 && first + V <= hid) {
                 E::store(v, r, voff, 0, through);
                 return;
+            }
+            if (seams) {
+                if (i == 0 && dx != 0 && joined(slot)) {
+                    seam_rest[o][slot] = v;
+                    return;
+                }
+                if (i == n - 1 && tail_bytes != 0 && slot + 1 < rows_in && joined(slot + 1)) {
+                    seam_head[o][slot + 1] = v;
+                    return;
+                }
             }
             // End chunks: the neighbouring row writes the chunk's other
             // elements, so these stores take the default (write-back) policy,
@@ -236,6 +283,24 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
                 } else {
                     const unsigned short hv = static_cast<unsigned short>(w[e >> 1] >> ((e & 1) * 16));
                     __builtin_amdgcn_raw_buffer_store_b16(hv, r, voff + e * 2, 0, 0);
+                }
+            }
+        };
+
+        // The joined seams, once the wavefront's rows have parked their ends:
+        // the later row's first lane stores each.
+        auto flush_seams = [&]() {
+            if (!seams) return;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lt == 0 && live && dx != 0 && joined(slot)) {
+#pragma unroll
+                for (int o = 0; o < NOUT; ++o) {
+                    void* base = o == 0 ? a.out : a.residual;
+                    if (base == nullptr) continue;
+                    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(static_cast<char*>(base) + t0 * 16, tile_bytes);
+                    E::store(splice(seam_head[o][slot], seam_rest[o][slot], dx), r, lane_base * 16, 0, through);
                 }
             }
         };
@@ -266,7 +331,8 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
         if constexpr (OP == kOpBiasAdd) {
 #pragma unroll
             for (int k = 0; k < CH; ++k)
-                if (k * G + lt < n) put(a.out, k, E::narrow(s[k]));
+                if (k * G + lt < n) put(a.out, 0, k, E::narrow(s[k]));
+            flush_seams();
             return;
         }
 
@@ -330,16 +396,17 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
                     float y[V];
 #pragma unroll
                     for (int e = 0; e < V; ++e) y[e] = s[k][e] * scale;
-                    put(a.out, k, E::narrow(y));
+                    put(a.out, 0, k, E::narrow(y));
                 }
             }
+            flush_seams();
             return;
         }
 
         if (a.residual != nullptr) {
 #pragma unroll
             for (int k = 0; k < CH; ++k)
-                if (k * G + lt < n) put(a.residual, k, E::narrow(s[k]));
+                if (k * G + lt < n) put(a.residual, 1, k, E::narrow(s[k]));
         }
         // gamma and beta once the residual is out (their registers are not held
         // through the sum).
@@ -469,9 +536,10 @@ __global__ void __launch_bounds__(BLOCK) span_kernel(const Args a) {
 #pragma unroll
                 for (int e = 0; e < V; ++e) t[e] = (s[k][e] - off) * rstd;
                 E::widen_fma(t, gr[k], er[k], y);
-                put(a.out, k, E::narrow(y));
+                put(a.out, 0, k, E::narrow(y));
             }
         }
+        flush_seams();
     };
     int par = 0;
     for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x, par ^= 1) tile(t * RPB, par);
