@@ -256,15 +256,18 @@ def test_select_kernels():
     assert name(sel(4096, 0, mode=L.SKIP_BROADCAST)) == "rowtile_f32_g256_c4"
     assert name(sel(8192, 1)) == "rowtile_f16_g256_c4"
     assert name(sel(64, 0)) == "rowtile_f32_g16_c1"
-    # not a multiple of a 16-byte chunk with 16-byte aligned tensors: span row
-    # tiles (up to 2048 chunks touched); misaligned tensors or longer rows:
-    # element-wise row tiles; too long for every family: generic
-    assert name(sel(1001, 0)) == "span_f32_g64_c4"
-    assert name(sel(77, 1)) == "span_f16_g8_c2"
-    assert name(sel(3, 1)) == "span_f16_g8_c2"
+    # not a multiple of a 16-byte chunk with 16-byte aligned tensors and an
+    # exact skip: span row tiles for BiasSoftmax rows touching 8 to 2048
+    # chunks and BiasAdd rows touching 64 to 2048; the normalizations,
+    # misaligned tensors, broadcast forms and other lengths: element-wise row
+    # tiles; too long for every family: generic
+    assert name(sel(1001, 0)) == "rowelem_f32_g128_c8"
+    assert name(sel(77, 1)) == "rowelem_f16_g32_c4"
+    assert name(sel(3, 1)) == "rowelem_f16_g4_c1"
     assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g64_c4"
-    assert name(sel(2039, 1)) == "span_f16_g64_c4"           # 256 chunks touched
-    assert name(sel(2041, 1)) == "rowelem_f16_g256_c8"       # layer norm beyond one wavefront
+    assert name(sel(49, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g8_c2"      # 8 chunks touched
+    assert name(sel(47, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f16_g16_c4"  # 7
+    assert name(sel(2039, 1)) == "rowelem_f16_g256_c8"
     assert name(sel(16366, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g512_c4"    # 2047 chunks touched
     assert name(sel(16378, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f16_g1024_c16"
     assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowelem_f16_g256_c8"
@@ -312,6 +315,8 @@ def test_select_kernels():
     assert name(sel(768, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g192_c1_b192"
     assert name(sel(4096, 1, op=L.OP_BIAS_ADD)) == "biasadd_rowtile_f16_g256_c2"
     assert name(sel(1001, 1, op=L.OP_BIAS_ADD)) == "biasadd_span_f16_g64_c2"
+    assert name(sel(497, 1, op=L.OP_BIAS_ADD)) == "biasadd_span_f16_g32_c2"      # 64 chunks touched
+    assert name(sel(495, 1, op=L.OP_BIAS_ADD)).startswith("biasadd_rowelem_f16")  # 63
     assert name(sel(1001, 1, al=0, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
     # long rows: LDS-staged up to 163584 bytes of binary32 sums, then held
     # in registers up to 65536 values, then generic
@@ -335,7 +340,8 @@ def test_select_kernels():
     assert name(sel(8, 0, op=L.OP_BIAS_SOFTMAX, mode=L.SKIP_BROADCAST)) == "softmax_rowtile_f32_g4_c1"
     assert name(sel(4096, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowtile_f16_g128_c4"
     assert name(sel(20000, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_ldsrow_f32"
-    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f32_g8_c2"
+    assert name(sel(7, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f32_g4_c2"
+    assert name(sel(25, 0, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f32_g8_c2"
     assert name(sel(7, 0, al=0, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f32_g4_c2"
     assert name(sel(64, 1, op=L.OP_BIAS_SOFTMAX, v=L.VARIANT_LDSROW)) == "softmax_ldsrow_f16"
     assert sel(64, 0, mode=L.SKIP_BROADCAST_INNER) == -L.ERR_MODE
@@ -367,7 +373,7 @@ def test_every_geometry_is_an_automatic_choice():
              for g in range(lib.skipln_tune_element_geometries())}
     assert elems <= used_elem, f"element geometries no automatic choice takes: {elems - used_elem}"
     used_span = {L.kernel_name(SEL(op, h, dt)).split("span_")[1].split("_", 1)[1]
-                 for op in (L.OP_LAYER_NORM, L.OP_BIAS_SOFTMAX) for dt in (0, 1) for h in range(1, 16385, 3)
+                 for op in (L.OP_BIAS_ADD, L.OP_BIAS_SOFTMAX) for dt in (0, 1) for h in range(1, 16385, 3)
                  if "span_" in L.kernel_name(SEL(op, h, dt))}
     spans = {L.kernel_name(SEL(L.OP_LAYER_NORM, 1, 0, v=L.VARIANT_SPAN_GEOMETRY + g)).split("span_f32_")[1]
              for g in range(lib.skipln_tune_span_geometries())}

@@ -77,7 +77,7 @@ AUTO_LENGTHS = [1, 2, 3, 5, 7, 9, 13, 31, 33, 63, 77, 127, 197, 255, 257, 511, 7
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
 @pytest.mark.parametrize("hidden", AUTO_LENGTHS)
-@pytest.mark.parametrize("op", ["layer_norm", "bias_softmax"])
+@pytest.mark.parametrize("op", ["layer_norm", "bias_add", "bias_softmax"])
 def test_span_automatic_choice(dt, hidden, op):
     """Rows that are not whole chunks take the span tiles automatically where
     they measured faster (element-wise tiles elsewhere) and match the
@@ -88,15 +88,19 @@ def test_span_automatic_choice(dt, hidden, op):
         pytest.skip("whole chunks: the chunk row tiles")
     name = T.select_kernel(hidden, code, op=U.OPS[op])
     touched = (hidden * sz + 15) // 16 + 1
-    # exact skip or bias: span tiles up to 2048 chunks touched, layer norm
-    # within one wavefront (256 chunks)
-    span = touched <= (2048 if op == "bias_softmax" else 256)
+    # exact skip or bias: BiasSoftmax rows touching 8 to 2048 chunks, BiasAdd
+    # rows touching 64 to 2048; never the normalizations
+    lo = {"bias_softmax": 8, "bias_add": 64}.get(op)
+    span = lo is not None and lo <= touched <= 2048
     assert ("span_" in name) == span, name
-    bname = T.select_kernel(hidden, code, op=U.OPS[op], skip_mode=L.SKIP_BROADCAST)
-    assert "span_" not in bname, bname
+    if op != "bias_add":
+        bname = T.select_kernel(hidden, code, op=U.OPS[op], skip_mode=L.SKIP_BROADCAST)
+        assert "span_" not in bname, bname
     rows = 40 if hidden < 4096 else 8
     if op == "bias_softmax":
         w = W.small_case(rows, hidden, dt, op=op, seed=hidden)
+    elif op == "bias_add":
+        w = W.small_case(rows, hidden, dt, bias=True, op=op, seed=hidden)
     else:
         w = W.small_case(rows, hidden, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=hidden)
     U.note(f"span auto {op} {dt} H={hidden} -> {name}")

@@ -218,9 +218,7 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         return g >= 0 ? base + kElemFirst + g : -SKIPLN_ERR_UNSUPPORTED;
     }
     if (variant == kVariantSpan) {
-        int g = -1;  // the smallest geometry that holds the row
-        for (int i = 0; vec_ok && g < 0 && i < span_count(); ++i)
-            if (span_holds(i, hidden, dtype)) g = i;
+        const int g = vec_ok ? span_fit(op, hidden, dtype) : -1;
         return g >= 0 ? base + kSpanFirst + g : -SKIPLN_ERR_UNSUPPORTED;
     }
     if (variant >= kVariantSpanGeometry && variant < kVariantSpanGeometry + span_count()) {

@@ -168,11 +168,14 @@ bool regnorm_holds(int op, int64_t hidden, int dtype);
 hipError_t launch_regnorm(const Args& a, int op, int dtype, hipStream_t stream);
 // Span row tiles (rows of any length, every tensor 16-byte aligned): the
 // number of geometries, geometry g's group, chunks per lane and block,
-// whether it holds a row of `hidden` values, the automatic choice (or -1),
-// and the launch (one row per group, one tile of rows per block).
+// whether it holds a row of `hidden` values, the geometry a forced span
+// launch takes for the operation (the first in its order that holds the row,
+// or -1), the automatic choice (or -1: another family), and the launch (one
+// row per group, one tile of rows per block).
 int span_count();
 bool span_geometry(int geometry, int* g, int* ch, int* block);
 bool span_holds(int geometry, int64_t hidden, int dtype);
+int span_fit(int op, int64_t hidden, int dtype);
 int span_pick(int op, int64_t hidden, int dtype, bool broadcast);
 hipError_t launch_span(const Args& a, int op, int dtype, int geometry, hipStream_t stream);
 hipError_t launch_copy(void* dst, const void* src, int64_t chunks, hipStream_t stream);

@@ -591,29 +591,39 @@ bool span_holds(int geometry, int64_t hidden, int dtype) {
     return span_chunks(hidden, dtype == 0 ? 4 : 2) <= cap;
 }
 
-int span_pick(int op, int64_t hidden, int dtype, bool broadcast) {
-    int g = -1;
+int span_fit(int /*op*/, int64_t hidden, int dtype) {
     for (int i = 0; i < kNumSpanGeoms; ++i)
-        if (span_holds(i, hidden, dtype)) {
-            g = i;
-            break;
-        }
+        if (span_holds(i, hidden, dtype)) return i;
+    return -1;
+}
+
+int span_pick(int op, int64_t hidden, int dtype, bool broadcast) {
+    const int g = span_fit(op, hidden, dtype);
     if (g < 0) return -1;
-    // Measured on MI355X (graph replay, span against element-wise tiles):
-    // with an exact skip or bias the span tiles were faster -- softmax over
-    // 1500 / 2047 / 4095 float16 keys 206 / 176 / 190 against 300 / 197 /
-    // 211 us, 4095 float32 keys 277 against 288; BiasAdd of 1001 float16
-    // values 146 against 167; layer norm of 1001 values 229 / 261 against
-    // 236 / 267 (float32 / float16) -- except layer norm rows spanning
-    // several wavefronts (32768 rows of 4095 float16 values: 397 against
-    // 308 us).  With a broadcast skip or bias, whose rows must be shifted into
-    // place chunk by chunk, they lost more often than they won (softmax, 77 /
-    // 121 / 2047 / 4095 float16 keys with bias rows shared by many rows: 90 /
-    // 112 / 197 / 209 against 82 / 100 / 173 / 191 us; 197 / 1500 keys: 83 /
-    // 248 against 100 / 278), so broadcast forms keep the element-wise tiles.
+    // Measured on MI355X against the element-wise tiles (graph replay, exact
+    // skip or bias, 128 MiB per tensor; span / element us):
+    //  - BiasSoftmax: faster from 8 chunks touched on -- float16 keys 77 /
+    //    197 / 300 / 500 / 1001 / 1500 / 3001 / 4095: 93 / 80 / 84 / 74 / 68 /
+    //    67 / 69 / 86 against 145 / 126 / 157 / 110 / 86 / 111 / 125 / 103;
+    //    float32 keys 77 / 500 / 2047: 77 / 65 / 67 against 83 / 70 / 74 --
+    //    and slower on rows of a chunk or two (13 keys: 338 against 149).
+    //  - BiasAdd: faster from 64 chunks on -- float16 500 / 1001 / 3001
+    //    values: 71 / 74 / 80 against 87 / 84 / 92; float32 1001 / 2047: 79 /
+    //    76 against 83 / 85 -- mixed below (float16 121 / 255: 96 / 118
+    //    against 105 / 91; float32 77 / 121: 98 / 83 against 84 / 85).
+    //  - Layer norm and RMS: slower on short rows (float16 13 / 77 / 255
+    //    values: 543 / 222 / 212 against 183 / 184 / 133), within -15 % to
+    //    +50 % from 64 chunks on (500: 133 against 154, 2047: 207 against
+    //    136), so the normalizations keep the element-wise tiles.
+    // With a broadcast skip or bias, whose rows must be shifted into place
+    // chunk by chunk, the span tiles lost more often than they won (softmax
+    // over 77 / 121 / 2047 / 4095 float16 keys with bias rows shared by many
+    // rows: 90 / 112 / 197 / 209 against 82 / 100 / 173 / 191 us).
     if (broadcast) return -1;
-    if (op != kOpBiasSoftmax && kSpanGeoms[g].g > 64) return -1;
-    return g;
+    const int64_t touched = span_chunks(hidden, dtype == 0 ? 4 : 2);
+    if (op == kOpBiasSoftmax) return touched >= 8 ? g : -1;
+    if (op == kOpBiasAdd) return touched >= 64 ? g : -1;
+    return -1;
 }
 
 hipError_t launch_span(const Args& a, int op, int dtype, int geometry, hipStream_t st) {
