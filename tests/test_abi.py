@@ -264,7 +264,9 @@ def test_select_kernels():
     assert name(sel(1001, 0)) == "rowelem_f32_g128_c8"
     assert name(sel(77, 1)) == "rowelem_f16_g32_c4"
     assert name(sel(3, 1)) == "rowelem_f16_g4_c1"
-    assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g64_c4"
+    assert name(sel(1500, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g64_c3"     # 189 chunks touched
+    assert name(sel(2039, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g64_c4"     # 256
+    assert name(sel(2047, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g128_c3"    # 257
     assert name(sel(49, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_span_f16_g8_c2"      # 8 chunks touched
     assert name(sel(47, 1, op=L.OP_BIAS_SOFTMAX)) == "softmax_rowelem_f16_g16_c4"  # 7
     assert name(sel(2039, 1)) == "rowelem_f16_g256_c8"
@@ -283,11 +285,11 @@ def test_select_kernels():
     assert sel(1000, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0) == -L.ERR_UNSUPPORTED   # 4 elements
     assert name(sel(4, 0, v=L.VARIANT_ELEMENT_GEOMETRY + 0)) == "rowelem_f32_g4_c1"
     ns = lib.skipln_tune_span_geometries()
-    assert ns == 8
+    assert ns == 12
     assert sel(4, 0, v=L.VARIANT_SPAN_GEOMETRY + ns) == -L.ERR_VARIANT
     assert sel(4, 0, al=0, v=L.VARIANT_SPAN) == -L.ERR_UNSUPPORTED              # needs 16-byte aligned tensors
     assert sel(4001, 0, v=L.VARIANT_SPAN_GEOMETRY + 0) == -L.ERR_UNSUPPORTED    # too long for 8 x 2
-    assert name(sel(1024, 0, v=L.VARIANT_SPAN)) == "span_f32_g128_c4"           # any length when forced
+    assert name(sel(1024, 0, v=L.VARIANT_SPAN)) == "span_f32_g128_c3"           # any length when forced
     for g in range(ns):
         assert name(sel(5, 1, v=L.VARIANT_SPAN_GEOMETRY + g)).startswith("span_f16_g")
     ne = lib.skipln_tune_element_geometries()

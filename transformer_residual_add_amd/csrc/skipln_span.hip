@@ -38,6 +38,7 @@ struct SpanGeom {
 // choice takes the first that holds the row.
 constexpr SpanGeom kSpanGeoms[] = {
     {8, 2, 256}, {16, 2, 256}, {32, 2, 256}, {64, 2, 256}, {64, 4, 256}, {128, 4, 256}, {256, 4, 256}, {512, 4, 512},
+    {64, 3, 256}, {128, 3, 256}, {256, 3, 256}, {512, 3, 512},
 };
 constexpr int kNumSpanGeoms = sizeof(kSpanGeoms) / sizeof(kSpanGeoms[0]);
 static_assert(kSpanFirst + kNumSpanGeoms <= kRegRowIndex, "kernel index ranges are disjoint");
@@ -592,9 +593,13 @@ bool span_holds(int geometry, int64_t hidden, int dtype) {
 }
 
 int span_fit(int /*op*/, int64_t hidden, int dtype) {
+    // The geometry of least capacity (lanes x chunks) that holds the row.
+    int best = -1;
     for (int i = 0; i < kNumSpanGeoms; ++i)
-        if (span_holds(i, hidden, dtype)) return i;
-    return -1;
+        if (span_holds(i, hidden, dtype) &&
+            (best < 0 || kSpanGeoms[i].g * kSpanGeoms[i].ch < kSpanGeoms[best].g * kSpanGeoms[best].ch))
+            best = i;
+    return best;
 }
 
 int span_pick(int op, int64_t hidden, int dtype, bool broadcast) {
