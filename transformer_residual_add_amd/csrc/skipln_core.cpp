@@ -270,7 +270,7 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
             return base + kSplitRowIndex;
     }
     if (variant == kVariantAuto || variant == kVariantRowtile || variant == kVariantMultiwave) {
-        const int g = chunked ? rowtile_pick(op, hidden, dtype, broadcast, variant == kVariantMultiwave) : -1;
+        const int g = chunked ? rowtile_pick(op, hidden, dtype, broadcast, variant == kVariantMultiwave, rows) : -1;
         if (g >= 0) return base + kRowtileFirst + g;
         if (variant != kVariantAuto) return -SKIPLN_ERR_UNSUPPORTED;
         // Rows that are not whole chunks: span row tiles (16-byte aligned

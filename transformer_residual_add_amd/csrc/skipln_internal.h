@@ -116,9 +116,10 @@ constexpr int64_t kRowtileMaxAutoChunks = 2048;
 // Number of row-tile geometries and the one chosen for operation `op`,
 // `hidden` (elements) and the skip form, or -1 when none holds the row.
 // multiwave_only: the smallest geometry whose row group spans two or more
-// wavefronts.
+// wavefronts.  rows: the launch's row count (< 0: not known), which decides
+// where launches of the single-tile form take other geometries.
 int rowtile_count();
-int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only);
+int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only, int64_t rows = -1);
 // Whether geometry g holds a row of `hidden` elements (16-byte chunks).
 bool rowtile_holds(int geometry, int64_t hidden, int dtype);
 // The same for the element-wise row tiles (rows of any length, tensors

@@ -461,10 +461,19 @@ struct AutoEntry {
 // (16384 x 1024 float16: 22.9 against 23.3-23.6 us, interleaved runs).  At
 // 192 chunks the same change was 2.7 % faster on one box and 3.5 % slower on
 // another for BERT-base (1024 x 768 float32), so 192-lane groups stay.
+// Rows of 257-512 chunks run 128-lane groups of 4 chunks per lane, two rows
+// per block: 3-7 % faster than 256 x 2 tiles at 16384-32768 rows (layer
+// norm, float16 2560 / 3072 / 3584 / 4096 values at 32768 rows: 111.7 /
+// 132.5 / 156.2 / 172.7 against 116.9 / 138.3 / 163.4 / 180.2 us; float32
+// 1280 / 1536 / 2048: 109.2 / 133.0 / 172.4 against 117.4 / 141.0 / 182.4;
+// RMS float16 3072: 132.0 against 140.3).  Launches of the single-tile form
+// (rowtile_pick with the row count) keep 256 x 2 tiles, which that form runs
+// at 4 blocks per CU (65536 x 4096 float16: 343.0 against 345.9).
 constexpr AutoEntry kAutoNorm[] = {
-    {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 3}, {192, 15}, {256, 13}, {512, 16},
+    {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 3}, {192, 15}, {256, 13}, {512, 5},
     {768, 6}, {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
+constexpr int kGeom256x2 = 16;  // 256-lane groups of 2 chunks per lane
 // BiasAdd (no reduction) keeps the wider groups: one wavefront per row was
 // slower at 192 chunks (1024 x 768 float32: 3.74 against 3.54 us).
 constexpr AutoEntry kAutoExact[] = {
@@ -869,10 +878,13 @@ struct NameTable {
 
 int rowtile_count() { return kNumGeoms; }
 
-int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only) {
+int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only, int64_t rows) {
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     if (hidden <= 0 || hidden % v != 0) return -1;
     const int64_t hv = hidden / v;
+    if (!multiwave_only && !broadcast && (op == kOpLayerNorm || op == kOpSimplified) && hv > 256 && hv <= 512 &&
+        single_tile_launch(rows, hidden, 16 / v))
+        return kGeom256x2;
     if (!multiwave_only) {
         if (op == kOpBiasSoftmax) {
             for (const AutoEntry& e : kAutoSoftmax)
