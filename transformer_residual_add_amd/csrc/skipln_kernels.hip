@@ -468,10 +468,14 @@ struct AutoEntry {
 // 1280 / 1536 / 2048: 109.2 / 133.0 / 172.4 against 117.4 / 141.0 / 182.4;
 // RMS float16 3072: 132.0 against 140.3).  Launches of the single-tile form
 // (rowtile_pick with the row count) keep 256 x 2 tiles, which that form runs
-// at 4 blocks per CU (65536 x 4096 float16: 343.0 against 345.9).
+// at 4 blocks per CU (65536 x 4096 float16: 343.0 against 345.9).  Rows of
+// 513-768 chunks run 256 x 4 tiles rather than 256 x 3: layer norm, float32
+// 2560 / 3072 values 236.7 / 276.9 -> 226.6 / 264.8 us at 32768 rows (61.1 /
+// 71.3 -> 58.9 / 68.2 at 8192), float16 6144 values 277.4 -> 268.5, float16
+// 5120 within 1 % either way.
 constexpr AutoEntry kAutoNorm[] = {
     {4, 17}, {8, 18}, {16, 0}, {32, 1}, {64, 2}, {128, 3}, {192, 15}, {256, 13}, {512, 5},
-    {768, 6}, {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
+    {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 constexpr int kGeom256x2 = 16;  // 256-lane groups of 2 chunks per lane
 // BiasAdd (no reduction) keeps the wider groups: one wavefront per row was
@@ -878,6 +882,14 @@ struct NameTable {
 
 int rowtile_count() { return kNumGeoms; }
 
+// The first entry of an automatic-choice table that holds `hv` chunks.
+template <size_t N>
+int auto_pick(const AutoEntry (&table)[N], int64_t hv) {
+    for (const AutoEntry& e : table)
+        if (hv <= e.max_chunks) return e.geom;
+    return -1;
+}
+
 int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwave_only, int64_t rows) {
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     if (hidden <= 0 || hidden % v != 0) return -1;
@@ -886,14 +898,9 @@ int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwa
         single_tile_launch(rows, hidden, 16 / v))
         return kGeom256x2;
     if (!multiwave_only) {
-        if (op == kOpBiasSoftmax) {
-            for (const AutoEntry& e : kAutoSoftmax)
-                if (hv <= e.max_chunks) return e.geom;
-            return -1;
-        }
-        for (const AutoEntry& e : (broadcast ? kAutoBroadcast : op == kOpBiasAdd ? kAutoExact : kAutoNorm))
-            if (hv <= e.max_chunks) return e.geom;
-        return -1;
+        if (op == kOpBiasSoftmax) return auto_pick(kAutoSoftmax, hv);
+        if (broadcast) return auto_pick(kAutoBroadcast, hv);
+        return op == kOpBiasAdd ? auto_pick(kAutoExact, hv) : auto_pick(kAutoNorm, hv);
     }
     int best = -1;  // smallest capacity among groups of two or more wavefronts
     for (int i = 0; i < kNumGeoms; ++i) {
