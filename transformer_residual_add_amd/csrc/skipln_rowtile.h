@@ -648,6 +648,22 @@ hipError_t cap_lds(K kernel, int block, int cap, int static_bytes, std::atomic<i
 // automatic choice gives them only in large launches) hold one block per CU
 // in either form; the single form was faster (float16 20480: 446.6 -> 436.2
 // us; float32 12288: 403.8 -> 376.1).
+// Geometries whose single-tile form ran faster at every launch size
+// measured, not only in large launches: float16 layer norm rows of
+// 1537-2048 chunks (512 x 4; the walking form holds one block per CU).
+// Walking -> single-tile form at 1024 / 2048 / 4096 / 8192 rows: 14336
+// values 30.8 / 53.2 / 99.2 / 196.2 -> 26.3 / 44.1 / 80.7 / 155.9 us, 16384
+// values 32.3 / 56.7 / 109.5 / 207.3 -> 29.0 / 49.8 / 93.5 / 177.8; 12352
+// values at 1024 / 4096 rows 28.2 / 95.7 -> 23.7 / 72.7; at 256 rows the two
+// forms are equal.  RMS (fewer
+// registers) lost at 1024 rows (27.7 against 29.3) and float32 layer norm at
+// 32768 (3.6 %): both keep the large-launch rule.  Rows must be whole
+// 128-byte lines, as for large launches.
+template <typename E, int OP, int G, int CH>
+constexpr bool single_tile_always() {
+    return OP == kOpLayerNorm && E::kPerChunk == 8 && G == 512 && CH == 4;
+}
+
 template <typename E, int OP, int G, int CH>
 constexpr int single_tile_blocks() {
     if constexpr (OP != kOpLayerNorm && OP != kOpSimplified) return -1;
@@ -764,17 +780,21 @@ hipError_t launch_geom(const Args& a0, Tiling tiling, hipStream_t st) {
     }
     if constexpr (E::kPerChunk > 1) {
         if (mode != kTileSkipStationary && per <= 1) {
-            // The single-tile form when forced, or for a large launch where
-            // the table gives it blocks per CU (>= 0).
+            // The single-tile form when forced, or for a large launch (or a
+            // geometry that takes it at any size) where the table gives it
+            // blocks per CU (>= 0).
             bool single = false;
             int cap = kBlocksAuto;
             if (tiling.form == kFormOneTile) {
                 single = true;
                 cap = tiling.blocks_per_cu;
-            } else if (tiling.form == kFormAuto &&
-                       single_tile_launch(a.rows, a.hidden, static_cast<int>(16 / E::kPerChunk))) {
-                cap = single_tile_blocks<E, OP, g.g, g.ch>();
-                single = cap >= 0;
+            } else if (tiling.form == kFormAuto) {
+                const int eb = static_cast<int>(16 / E::kPerChunk);
+                const bool lines = a.hidden * eb % 128 == 0;
+                if (single_tile_launch(a.rows, a.hidden, eb) || (single_tile_always<E, OP, g.g, g.ch>() && lines)) {
+                    cap = single_tile_blocks<E, OP, g.g, g.ch>();
+                    single = cap >= 0;
+                }
             }
             if (single) {
                 size_t lds = 0;
