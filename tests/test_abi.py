@@ -573,8 +573,9 @@ def test_forward_config_argument_checks():
 
 
 def test_large_launches_take_1024_lane_row_tiles():
-    """Normalization rows of 2049-3072 chunks (float16: 2689-3072) of whole
-    128-byte lines leave the LDS-staged kernel for 1024-lane row tiles once
+    """Normalization rows of 2049-3072 chunks (float16: 2689-3072; float32 up
+    to 4096) of whole 128-byte lines leave the LDS-staged kernel for 1024-lane
+    row tiles once
     input, skip and output each span 512 MiB; broadcast skips, BiasSoftmax and
     other lengths do not."""
     sel = lambda h, dt, rows, op=L.OP_LAYER_NORM, mode=L.SKIP_EXACT: L.kernel_name(L.load_tune().skipln_tune_select(
@@ -588,8 +589,16 @@ def test_large_launches_take_1024_lane_row_tiles():
         assert sel(h, dt, n, mode=L.SKIP_BROADCAST).startswith("ldsrow_")
         assert sel(h, dt, n, L.OP_BIAS_SOFTMAX).startswith("softmax_")
     # too short, too long, or rows that end inside a 128-byte line
-    for h, dt in ((8192, L.F32), (12320, L.F32), (21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
+    for h, dt in ((8192, L.F32), (21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
         assert "g1024_c3" not in sel(h, dt, big(h, dt))
+    # float32 rows of 3073-4096 chunks: 1024 x 4 tiles; float16 rows of that
+    # length stay on the LDS-staged kernel
+    for h in (12416, 14336, 16384):
+        for op, prefix in ((L.OP_LAYER_NORM, ""), (L.OP_SIMPLIFIED, "rms_")):
+            assert sel(h, L.F32, big(h, L.F32), op) == f"{prefix}rowtile_f32_g1024_c4"
+            assert sel(h, L.F32, big(h, L.F32) - 1, op) == f"{prefix}ldsrow_f32"
+    assert sel(16416, L.F32, big(16416, L.F32)) == "ldsrow_f32"
+    assert sel(32768, L.F16, big(32768, L.F16)) == "ldsrow_f16"
     # float16 RMS from 2304 chunks
     assert sel(18432, L.F16, big(18432, L.F16), L.OP_SIMPLIFIED) == "rms_rowtile_f16_g1024_c3"
     assert sel(18368, L.F16, big(18368, L.F16), L.OP_SIMPLIFIED) == "rms_ldsrow_f16"

@@ -39,7 +39,8 @@ ORACLE_BLOCK = 4096  # rows per oracle call in the full-size comparison
 # The two largest configurations, the benchmark's full-size root-mean-square
 # and BiasAdd workloads, and 2 GiB layer norms that take the single-tile form.
 FULL_SIZE = list(W.ORDER[3:]) + ["rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "rows65536_h4096_f16",
-                                   "rows131072_h2048_f16", "rows16384_h16384_f16", "rows16384_h12288_f32"]
+                                   "rows131072_h2048_f16", "rows16384_h16384_f16", "rows16384_h12288_f32",
+                                   "rows16384_h14336_f32"]
 
 
 @pytest.mark.parametrize("name", FULL_SIZE)

@@ -252,11 +252,18 @@ int select(int op, int64_t hidden, int dtype, bool broadcast, bool vec_ok, bool 
         // the LDS kernel below 2689 chunks.  float16 RMS (58 VGPRs, two
         // blocks per CU where layer norm holds one) gains from 2304 chunks:
         // rows of 18432 / 20480 values 436.9 / 465.4 -> 422.0 / 437.9 us at
-        // 16384 rows.
+        // 16384 rows.  float32 rows of 3073-4096 chunks run 1024 x 4 tiles
+        // (32768 rows of 14336 / 16384 values: layer norm 1420.4 / 1927.1 ->
+        // 1360 / 1706 us, RMS of 16384 values 1794.0 -> 1604.9; 16384 rows:
+        // 692.8 / 961.8 -> 680.3 / 930.1, RMS 937.5 -> 906.0), though layer
+        // norm at the size threshold itself (8192 rows of 16384 values) ran
+        // 408.1 against 382.3; float16 rows of that length stay on the LDS
+        // kernel.
         const int64_t hv = hidden / v;
         const int64_t hv_min = dtype == SKIPLN_F32 ? 2049 : op == SKIPLN_OP_SIMPLIFIED ? 2304 : 2689;
+        const int64_t hv_max = dtype == SKIPLN_F32 ? 4096 : 3072;
         if (chunked && !broadcast && (op == SKIPLN_OP_LAYER_NORM || op == SKIPLN_OP_SIMPLIFIED) && hv >= hv_min &&
-            hv <= 3072 && single_tile_launch(rows, hidden, dtype == SKIPLN_F32 ? 4 : 2)) {
+            hv <= hv_max && single_tile_launch(rows, hidden, dtype == SKIPLN_F32 ? 4 : 2)) {
             const int g = rowtile_pick(op, hidden, dtype, false, false);
             if (g >= 0) return base + kRowtileFirst + g;
         }

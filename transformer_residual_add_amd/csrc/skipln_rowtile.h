@@ -647,7 +647,11 @@ hipError_t cap_lds(K kernel, int block, int cap, int static_bytes, std::atomic<i
 // 1024-lane tiles of 3 chunks per lane (rows of up to 3072 chunks, which the
 // automatic choice gives them only in large launches) hold one block per CU
 // in either form; the single form was faster (float16 20480: 446.6 -> 436.2
-// us; float32 12288: 403.8 -> 376.1).
+// us; float32 12288: 403.8 -> 376.1).  float32 rows of 3073-4096 chunks take
+// 1024 x 4 tiles in large launches, one block per CU (against the LDS-staged
+// kernel at 32768 rows: layer norm 14336 / 16384 values 1420.4 / 1927.1 ->
+// 1360 / 1706 us, RMS 16384 values 1794.0 -> 1604.9; with no limit RMS ran
+// 1668.8).
 // Geometries whose single-tile form ran faster at every launch size
 // measured, not only in large launches: float16 layer norm rows of
 // 1537-2048 chunks (512 x 4; the walking form holds one block per CU).
@@ -673,6 +677,7 @@ constexpr int single_tile_blocks() {
     if constexpr (G == 256 && CH == 2) return 4;
     if constexpr (G == 512 && CH == 4) return half ? 0 : -1;
     if constexpr (G == 1024 && CH == 3) return 0;
+    if constexpr (G == 1024 && CH == 4) return half ? -1 : 1;
     return -1;
 }
 

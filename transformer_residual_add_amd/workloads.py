@@ -292,6 +292,10 @@ EXTRA: Dict[str, Workload] = {
         Workload(name="rows16384_h12288_f32", shape=(16384, 12288), dtype="f32", skip_shape=(16384, 12288),
                  input_dist=normal(0, 1), skip_dist=normal(0, 1), bias_dist=normal(0, 0.1), residual=True, eps=1e-5,
                  seed=1044),
+        # ... and of 3584 chunks (1024 x 4 tiles, one block per CU).
+        Workload(name="rows16384_h14336_f32", shape=(16384, 14336), dtype="f32", skip_shape=(16384, 14336),
+                 input_dist=normal(0, 1), skip_dist=normal(0, 1), bias_dist=normal(0, 0.1), residual=True, eps=1e-5,
+                 seed=1045),
         # Rows beyond one workgroup's LDS (65536 values): the register-resident
         # rows against the generic kernel's chunk form (part of each row
         # parked in LDS) and the split-row kernels; 512 rows, so that every CU
