@@ -605,6 +605,27 @@ def test_large_launches_take_1024_lane_row_tiles():
     assert sel(18432, L.F16, big(18432, L.F16)) == "ldsrow_f16"
 
 
+def test_row_count_dependent_choices():
+    """The normalizations' row tiles that depend on the launch's rows: one
+    wavefront per row for 161-256 chunks from 16384 rows (below the
+    single-tile size), 128 x 4 tiles for 257-512 chunks except in single-tile
+    launches (256 x 2)."""
+    sel = lambda h, dt, rows, op=L.OP_LAYER_NORM, mode=L.SKIP_EXACT: L.kernel_name(L.load_tune().skipln_tune_select(
+        op, rows, h, dt, mode, 1, L.VARIANT_AUTO, 0, 256))
+    assert sel(2048, L.F16, 16384) == "rowtile_f16_g64_c4"
+    assert sel(2048, L.F16, 16383) == "rowtile_f16_g256_c1"
+    assert sel(1288, L.F16, 32768) == "rowtile_f16_g64_c4"                 # 161 chunks
+    assert sel(1280, L.F16, 32768) == "rowtile_f16_g192_c1_b192"           # 160
+    assert sel(768, L.F32, 131072, L.OP_SIMPLIFIED) == "rms_rowtile_f32_g64_c4"
+    assert sel(768, L.F32, 1024) == "rowtile_f32_g192_c1_b192"            # BERT-base
+    assert sel(2048, L.F16, 131072) == "rowtile_f16_g256_c1"               # single-tile launch
+    assert sel(2048, L.F16, 32768, mode=L.SKIP_BROADCAST) == "rowtile_f16_g256_c1"
+    assert sel(2048, L.F16, 32768, L.OP_BIAS_ADD) == "biasadd_rowtile_f16_g256_c1"
+    assert sel(4096, L.F16, 32768) == "rowtile_f16_g128_c4"
+    assert sel(4096, L.F16, 65536) == "rowtile_f16_g256_c2"                # single-tile launch
+    assert sel(4096, L.F16, 32768, mode=L.SKIP_BROADCAST) == "rowtile_f16_g256_c2"
+
+
 def test_forward_form_argument_checks():
     """skipln_tune_forward_form rejects these before any HIP call."""
     frm = lambda geom=0, form=1, cap=0, store=L.STORE_AUTO: L.load_tune().skipln_tune_forward_form(

@@ -478,6 +478,16 @@ constexpr AutoEntry kAutoNorm[] = {
     {1024, 7}, {1536, 8}, {2048, 9}, {3072, 10}, {4096, 11},
 };
 constexpr int kGeom256x2 = 16;  // 256-lane groups of 2 chunks per lane
+// Rows of 161-256 chunks in launches of 16384 rows or more (below the
+// single-tile size) run one wavefront per row, 4 chunks per lane, instead of
+// 192- or 256-lane groups: layer norm float16 1536 / 1792 / 2048 values at
+// 32768 rows 70.0 / 84.0 / 94.3 -> 66.9 / 79.1 / 88.9 us, at 131072 rows
+// 1536 / 1792: 278.0 / 339.2 -> 262.0 / 302.1; float32 768 at 131072 rows
+// 276.5 -> 265.7; RMS float16 1792 at 131072 rows 329.2 -> 304.1.  At 8192
+// rows the wider groups were 1-4 % faster, at 160 chunks (float16 1280) the
+// two equal, and large launches keep their single-tile tiles (float32 1024
+// at 131072 rows: 339.6 against 355.0).
+constexpr int kGeom64x4 = 4;
 // BiasAdd (no reduction) keeps the wider groups: one wavefront per row was
 // slower at 192 chunks (1024 x 768 float32: 3.74 against 3.54 us).
 constexpr AutoEntry kAutoExact[] = {
@@ -894,9 +904,10 @@ int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwa
     const int v = dtype == 0 ? Elem<float>::kPerChunk : Elem<_Float16>::kPerChunk;
     if (hidden <= 0 || hidden % v != 0) return -1;
     const int64_t hv = hidden / v;
-    if (!multiwave_only && !broadcast && (op == kOpLayerNorm || op == kOpSimplified) && hv > 256 && hv <= 512 &&
-        single_tile_launch(rows, hidden, 16 / v))
-        return kGeom256x2;
+    const bool norm = !multiwave_only && !broadcast && (op == kOpLayerNorm || op == kOpSimplified);
+    const bool large = single_tile_launch(rows, hidden, 16 / v);
+    if (norm && hv > 256 && hv <= 512 && large) return kGeom256x2;
+    if (norm && hv > 160 && hv <= 256 && rows >= 16384 && !large) return kGeom64x4;
     if (!multiwave_only) {
         if (op == kOpBiasSoftmax) return auto_pick(kAutoSoftmax, hv);
         if (broadcast) return auto_pick(kAutoBroadcast, hv);
