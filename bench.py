@@ -105,6 +105,9 @@ def parse_args(argv=None):
     p.add_argument("--summarize-config-counters", nargs=2, metavar=("DIR", "PLAN_JSON"), default=None,
                    help="no GPU work: per-configuration HBM bytes and L2 hits/misses from rocprofv3 --pmc runs "
                         "of a --counter-pass (DIR/<COUNTER>/run_counter_collection.csv), as a markdown table")
+    p.add_argument("--hidden-sizes", action="store_true",
+                   help="layer norm and RMS over model hidden sizes 768..8192 at 4096 and 32768 rows, both types "
+                        "(automatic choice, synthetic inputs with bias, beta and residual)")
     p.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"), default=None,
                    help="no GPU work: per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench.py run "
                         "against the HIP-event launch times that run printed (its JSON line), as a markdown table")
@@ -175,8 +178,11 @@ def time_workload(w, steps: int, warmup: int, launch: str, variant: int):
     kernel = T.select_kernel(w.hidden, code, True, variant, mode, op, workspace=ws_bytes > 0, rows=w.rows)
     alg = w.algorithmic_bytes()
     # Per-step bytes actually touched (the broadcast skip counted once) decide
-    # how many buffer copies keep the working set above the cache.
-    n_sets = max(1, min(96, -(-4 * CACHE_BYTES // alg)))
+    # how many buffer copies keep the working set above the cache: sixteen
+    # times its size.  With four times (1 GiB) the 16384 x 1024 float16 layer
+    # norm ran 23.6 us against 24.9 / 25.1 / 25.1 at 2 / 4 / 8 GiB: the
+    # last-level cache kept part of the inputs from one launch to the next.
+    n_sets = max(1, min(512, -(-16 * CACHE_BYTES // alg)))
     log(f"{w.name}: generating inputs (rows={w.rows} H={w.hidden} {w.dtype}), {n_sets} buffer set(s)")
     t0 = time.perf_counter()
     inputs = W.make_inputs(w)
@@ -431,7 +437,7 @@ def time_configs(w, configs, steps: int, warmup: int, reps: int, counter_pass: b
     alg = w.algorithmic_bytes()
     if T.workspace_bytes(op, w.rows, w.hidden, code, mode, srows) > 0:
         raise SystemExit(f"{w.name}: the automatic launch takes the split-row kernels; nothing to compare")
-    n_sets = max(1, min(96, -(-4 * CACHE_BYTES // alg)))
+    n_sets = max(1, min(512, -(-16 * CACHE_BYTES // alg)))
     inputs = W.make_inputs(w)
     dev = DeviceSets(w, inputs, n_sets)
     del inputs
@@ -771,6 +777,33 @@ def summarize_trace(trace_csv: str, bench_json: str) -> int:
     return 0
 
 
+HIDDEN_SIZES = (768, 1024, 1536, 2048, 2560, 3072, 4096, 5120, 6144, 7168, 8192)
+HIDDEN_ROWS = (4096, 32768)
+
+
+def hidden_sizes(steps: int, warmup: int):
+    """The automatic choice over common model hidden sizes: layer norm and
+    RMS, float16 and float32, with bias, beta and the residual output, at
+    HIDDEN_ROWS rows each (synthetic N(0,1) inputs, seeded)."""
+    from transformer_residual_add_amd import workloads as W
+
+    out = []
+    for op in ("layer_norm", "simplified"):
+        for dt in ("f16", "f32"):
+            for h in HIDDEN_SIZES:
+                for rows in HIDDEN_ROWS:
+                    w = W.small_case(rows, h, dt, beta=True, bias=True, residual=True, eps=1e-5, seed=h + rows,
+                                     op=op)
+                    n = max(5, min(steps, int(2.0 / max(w.algorithmic_bytes() / 5e12, 1e-9))))
+                    r = time_workload(w, n, min(warmup, 10), "graph", 0)
+                    out.append({"op": op, "dtype": dt, "hidden": h, "rows": rows, "kernel": r["kernel"],
+                                "launch_us": round(r["launch_us"], 2),
+                                "frac_of_peak": r["roofline"]["frac"]})
+                    log(f"{op} {dt} H={h} rows={rows}: {r['kernel']} {r['launch_us']:.1f} us "
+                        f"{r['roofline']['frac']:.1%}")
+    return out
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.summarize_trace:
@@ -802,6 +835,9 @@ def main(argv=None) -> int:
         print(json.dumps({"stream": time_streams(args.stream_ceilings, args.steps, args.warmup)}), flush=True)
         return 0
 
+    if args.hidden_sizes:
+        print(json.dumps({"hidden_sizes": hidden_sizes(args.steps, args.warmup)}), flush=True)
+        return 0
     if args.launch_configs:
         w = W.get(args.launch_configs)
         configs = [parse_config(c) for c in args.config] or default_configs(w)
