@@ -322,7 +322,9 @@ def test_select_kernels():
     assert name(sel(1001, 1, al=0, op=L.OP_BIAS_ADD)) == "biasadd_rowelem_f16_g128_c8"
     # long rows: LDS-staged up to 163584 bytes of binary32 sums, then held
     # in registers up to 65536 values, then generic
-    assert name(sel(8192, 0)) == "rowtile_f32_g512_c4"
+    assert name(sel(8192, 0)) == "rowtile_f32_g1024_c3"     # float32 layer norm, 1537-2048 chunks of whole lines
+    assert name(sel(8184, 0)) == "rowtile_f32_g512_c4"      # rows ending inside a line
+    assert name(sel(8192, 0, op=L.OP_SIMPLIFIED)) == "rms_rowtile_f32_g512_c4"
     assert name(sel(8196, 0)) == "ldsrow_f32"
     assert name(sel(40896, 0)) == "ldsrow_f32"
     assert name(sel(40900, 0)) == "regrow_f32"
@@ -589,7 +591,7 @@ def test_large_launches_take_1024_lane_row_tiles():
         assert sel(h, dt, n, mode=L.SKIP_BROADCAST).startswith("ldsrow_")
         assert sel(h, dt, n, L.OP_BIAS_SOFTMAX).startswith("softmax_")
     # too short, too long, or rows that end inside a 128-byte line
-    for h, dt in ((8192, L.F32), (21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
+    for h, dt in ((21504, L.F16), (24640, L.F16), (8196, L.F32), (22600, L.F16)):
         assert "g1024_c3" not in sel(h, dt, big(h, dt))
     # float32 rows of 3073-4096 chunks: 1024 x 4 tiles; float16 rows of that
     # length stay on the LDS-staged kernel

@@ -488,6 +488,15 @@ constexpr int kGeom256x2 = 16;  // 256-lane groups of 2 chunks per lane
 // two equal, and large launches keep their single-tile tiles (float32 1024
 // at 131072 rows: 339.6 against 355.0).
 constexpr int kGeom64x4 = 4;
+// float32 layer norm rows of 1537-2048 chunks (whole 128-byte lines) run
+// 1024 x 3 tiles in the single-tile form rather than 512 x 4 walking (which
+// holds one block per CU), one process, walking -> single-tile at 4096 /
+// 8192 / 32768 rows: 6400 values 84.4 / 168.4 / 636.3 -> 79.2 / 151.2 /
+// 589.5 us, 7168 values 91.2 / 178.9 / 680.7 -> 86.2 / 163.7 / 641.4, 8192
+// values 101.5 / 201.8 / 765.0 -> 97.0 / 188.6 / 735.9 (another box had 8192
+// x 32768 at 807.3 against 815.8).  RMS (fewer registers) measured best on
+// 512 x 4 walking.
+constexpr int kGeom1024x3 = 10;
 // BiasAdd (no reduction) keeps the wider groups: one wavefront per row was
 // slower at 192 chunks (1024 x 768 float32: 3.74 against 3.54 us).
 constexpr AutoEntry kAutoExact[] = {
@@ -908,6 +917,7 @@ int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwa
     const bool large = single_tile_launch(rows, hidden, 16 / v);
     if (norm && hv > 256 && hv <= 512 && large) return kGeom256x2;
     if (norm && hv > 160 && hv <= 256 && rows >= 16384 && !large) return kGeom64x4;
+    if (norm && op == kOpLayerNorm && v == 4 && hv > 1536 && hv <= 2048 && hidden * 4 % 128 == 0) return kGeom1024x3;
     if (!multiwave_only) {
         if (op == kOpBiasSoftmax) return auto_pick(kAutoSoftmax, hv);
         if (broadcast) return auto_pick(kAutoBroadcast, hv);

@@ -661,11 +661,15 @@ hipError_t cap_lds(K kernel, int block, int cap, int static_bytes, std::atomic<i
 // values at 1024 / 4096 rows 28.2 / 95.7 -> 23.7 / 72.7; at 256 rows the two
 // forms are equal.  RMS (fewer
 // registers) lost at 1024 rows (27.7 against 29.3) and float32 layer norm at
-// 32768 (3.6 %): both keep the large-launch rule.  Rows must be whole
-// 128-byte lines, as for large launches.
+// 32768 (3.6 %): both keep the large-launch rule.  float32 layer norm rows
+// of 1537-2048 chunks take 1024 x 3 tiles in this form instead (the
+// automatic choice in skipln_kernels.hip), and so does every other launch of
+// that tile (its walking form spills).  Rows must be whole 128-byte lines,
+// as for large launches.
 template <typename E, int OP, int G, int CH>
 constexpr bool single_tile_always() {
-    return OP == kOpLayerNorm && E::kPerChunk == 8 && G == 512 && CH == 4;
+    return OP == kOpLayerNorm && ((E::kPerChunk == 8 && G == 512 && CH == 4) ||
+                                  (E::kPerChunk == 4 && G == 1024 && CH == 3));
 }
 
 template <typename E, int OP, int G, int CH>
