@@ -120,6 +120,30 @@ def test_launch_configs(dt, tiling, geom, mode):
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16"])
+@pytest.mark.parametrize("per", [0, 1, 3, 8])
+@pytest.mark.parametrize("hidden", [64, 1024, 4096])
+def test_bias_stationary_blocks(dt, per, hidden):
+    """Cyclic bias rows kept stationary: each block keeps its tile of bias
+    rows and walks `per` batches (0: the launcher's default), bias rows a
+    whole number of tiles, a ragged last batch chunk (5 batches)."""
+    w = case(5 * 64, hidden, dt, "outer", bias_rows=64, seed=hidden + per)
+    inputs = W.make_inputs(w)
+    dc = U.DeviceCase(w, inputs, residual=False)
+    U.note(f"softmax stationary {dt} H={hidden} per={per}")
+    dc.run_config(-1, per, 2)
+    U.compare(w, dc.host(dc.out), None, U.oracle_rows(w, inputs))
+
+
+def test_large_cyclic_bias_automatic():
+    """A per-head bias of 32 MiB (16384 rows of 1024 float16 keys) reused by 4
+    batches: the automatic launch keeps it stationary; every row against the
+    oracle."""
+    w = case(4 * 16384, 1024, "f16", "outer", bias_rows=16384, seed=5)
+    U.note("softmax large cyclic bias 65536 x 1024 f16, 16384 bias rows")
+    dc, _ = U.check_case(w)
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16"])
 def test_many_rows_packed(dt):
     """Many tiny rows (4- and 8-lane groups, many tiles per block)."""
     for hidden in (4, 8, 16, 32):
