@@ -38,7 +38,8 @@ CPU_BASELINE_SWEEP = ("bcast_64x512x4096_f32",)
 CPU_SAMPLE_ROWS = 2048
 SWEEP = ["bert_base_8x128x768_f32", "rows16384_h1024_f16", "bcast_64x512x4096_f32",
          "rms_rows65536_h8192_f16", "biasadd_64x512x4096_f16", "softmax_attn_16x16x512x512_f16_padmask",
-         "softmax_relpos_64x12x128x128_f32", "softmax_frames_8x8x1500x1500_f16_fullbias",
+         "softmax_relpos_64x12x128x128_f32", "softmax_headbias_8x16x2048x2048_f16",
+         "softmax_frames_8x8x1500x1500_f16_fullbias",
          "softmax_vocab_4096x128256_f16", "rows65536_h4096_f16",
          "rows16384_h16384_f16"]
 OPS = {"layer_norm": 0, "simplified": 1, "bias_add": 2, "bias_softmax": 3}  # SKIPLN_OP_*

@@ -367,6 +367,22 @@ EXTRA: Dict[str, Workload] = {
             seed=1022,
             op="bias_softmax",
         ),
+        # A per-head position bias over a long sequence (16 heads x 2048
+        # queries x 2048 keys, 128 MiB) shared by the 8 sequences of the batch
+        # (outer broadcast): larger than the caches, so each block keeps its
+        # bias rows across batches.
+        Workload(
+            name="softmax_headbias_8x16x2048x2048_f16",
+            shape=(8 * 16 * 2048, 2048),
+            dtype="f16",
+            skip_shape=(16 * 2048, 2048),
+            input_dist=normal(0, 2),
+            skip_dist=normal(0, 1),
+            gamma_dist=None,
+            beta_dist=None,
+            seed=1025,
+            op="bias_softmax",
+        ),
         # Attention over 1500 keys (an audio encoder's frames), with an
         # additive bias as large as the scores (one bias row per data row):
         # rows of 3000 bytes, not whole 16-byte chunks, so each row starts at
