@@ -674,6 +674,12 @@ constexpr bool single_tile_always() {
 
 template <typename E, int OP, int G, int CH>
 constexpr int single_tile_blocks() {
+    // float16 BiasSoftmax rows of 513-1024 chunks (512 x 2 tiles): large
+    // launches of 262144 rows of 8192 keys with a padding mask ran 1354 /
+    // 1431 us in the single-tile form against about 1500 / 1507 walking on two
+    // boxes.  float32 rows on 512 x 2 and 512 x 4 tiles gained 5-6 % on one box
+    // and lost 1-10 % on the other, and stay walking.
+    if constexpr (OP == kOpBiasSoftmax) return E::kPerChunk == 8 && G == 512 && CH == 2 ? 0 : -1;
     if constexpr (OP != kOpLayerNorm && OP != kOpSimplified) return -1;
     constexpr bool half = E::kPerChunk == 8;
     if constexpr (G == 64 && CH == 2) return half ? 4 : 3;
