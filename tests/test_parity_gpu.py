@@ -1021,3 +1021,14 @@ def test_random_shapes(seed):
         dc.run()
         ref = U.oracle_rows(w, inputs)
         U.compare(w, dc.host(dc.out), dc.host(dc.res) if w.residual else None, ref)
+
+
+@pytest.mark.parametrize("op", ["layer_norm", "simplified"])
+def test_large_broadcast_skip_automatic(op):
+    """A 16 MiB skip (2048 rows of 4096 float16 values) broadcast over 5
+    batches: the automatic launch keeps the skip rows stationary and walks up
+    to 8 batches per block (here all 5); every row against the oracle."""
+    w = W.small_case(5 * 2048, 4096, "f16", skip_rows=2048, beta=True, bias=True, residual=True, eps=1e-5,
+                     seed=77, op=op)
+    U.note(f"large broadcast skip {op} (5, 2048, 4096) f16")
+    U.check_case(w)

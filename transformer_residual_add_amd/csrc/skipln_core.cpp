@@ -87,11 +87,19 @@ bool generic_outruns_split(int op, int64_t rows, int cus) {
 // 2078.8 us streamed, 95.5 / 360.0 / 1747.3 stationary over 3 batches,
 // 1631.3 over 8 at 8192 keys (365.8 at 2048); float32 4096 keys 2103.2 ->
 // 1630.2.  An 8 MiB bias streamed 1.5 % faster (91.3 against 92.7).
+// Normalizations with a skip of 16 MiB or more walk 8 batches per block
+// instead of 3, re-reading the skip less often: layer norm float16 (32, 2048,
+// 8192) / (64, 1024, 8192) / (32, 4096, 4096) 403.4 / 402.9 / 380.7 ->
+// 366.7 / 365.4 / 359.9 us, float32 (16, 4096, 4096) 375.6 -> 366.7, RMS
+// float16 (32, 2048, 8192) 370.7 -> 366.3; with the 8 MiB skip of (64, 512,
+// 4096) float32 the two were within 1 % (182.2 / 183.6).
 Tiling auto_tiling(int op, int skip_mode, int64_t skip_bytes) {
     const bool softmax = op == SKIPLN_OP_BIAS_SOFTMAX;
-    const bool cyclic = skip_mode == SKIPLN_SKIP_BROADCAST && (!softmax || skip_bytes >= (int64_t{16} << 20));
+    const bool big = skip_bytes >= (int64_t{16} << 20);
+    const bool cyclic = skip_mode == SKIPLN_SKIP_BROADCAST && (!softmax || big);
+    const bool walk_all = softmax ? skip_bytes >= (int64_t{256} << 20) : big;
     Tiling t;
-    t.tiles_per_block = cyclic ? (softmax && skip_bytes >= (int64_t{256} << 20) ? 8 : 0) : 1;
+    t.tiles_per_block = cyclic ? (walk_all ? 8 : 0) : 1;
     t.mode = cyclic ? kTileSkipStationary : kTileStrided;
     return t;
 }
