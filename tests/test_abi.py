@@ -621,6 +621,7 @@ def test_row_count_dependent_choices():
     assert sel(768, L.F32, 131072, L.OP_SIMPLIFIED) == "rms_rowtile_f32_g64_c4"
     assert sel(768, L.F32, 1024) == "rowtile_f32_g192_c1_b192"            # BERT-base
     assert sel(2048, L.F16, 131072) == "rowtile_f16_g256_c1"               # single-tile launch
+    assert sel(1536, L.F16, 262144) == "rowtile_f16_g64_c4"                # ... but not at 161-192 chunks
     assert sel(2048, L.F16, 32768, mode=L.SKIP_BROADCAST) == "rowtile_f16_g64_c4"
     assert sel(2048, L.F16, 32768, L.OP_BIAS_ADD) == "biasadd_rowtile_f16_g256_c1"
     assert sel(4096, L.F16, 32768) == "rowtile_f16_g128_c4"

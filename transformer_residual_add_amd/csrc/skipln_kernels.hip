@@ -485,8 +485,11 @@ constexpr int kGeom256x2 = 16;  // 256-lane groups of 2 chunks per lane
 // 1536 / 1792: 278.0 / 339.2 -> 262.0 / 302.1; float32 768 at 131072 rows
 // 276.5 -> 265.7; RMS float16 1792 at 131072 rows 329.2 -> 304.1.  At 8192
 // rows the wider groups were 1-4 % faster, at 160 chunks (float16 1280) the
-// two equal, and large launches keep their single-tile tiles (float32 1024
-// at 131072 rows: 339.6 against 355.0).
+// two equal.  Large launches of 161-192 chunks take it too (262144 rows:
+// layer norm float16 1536 / 1408 values 565.4 / 518.1 -> 531.6 / 495.2 us,
+// float32 768 563.7 -> 534.0, RMS float16 1536 565.1 -> 523.1); those of
+// 193-256 keep their single-tile 256 x 1 tiles (float32 1024 at 131072
+// rows: 339.6 against 355.0).
 constexpr int kGeom64x4 = 4;
 // float32 layer norm rows of 1537-2048 chunks (whole 128-byte lines) run
 // 1024 x 3 tiles in the single-tile form rather than 512 x 4 walking (which
@@ -922,7 +925,7 @@ int rowtile_pick(int op, int64_t hidden, int dtype, bool broadcast, bool multiwa
     const bool norm = !multiwave_only && !broadcast && (op == kOpLayerNorm || op == kOpSimplified);
     const bool large = single_tile_launch(rows, hidden, 16 / v);
     if (norm && hv > 256 && hv <= 512 && large) return kGeom256x2;
-    if (norm && hv > 160 && hv <= 256 && rows >= 16384 && !large) return kGeom64x4;
+    if (norm && hv > 160 && hv <= 256 && rows >= 16384 && (hv <= 192 || !large)) return kGeom64x4;
     if (norm && op == kOpLayerNorm && v == 4 && hv > 1536 && hv <= 2048 && hidden * 4 % 128 == 0) return kGeom1024x3;
     if (!multiwave_only) {
         if (op == kOpBiasSoftmax) return auto_pick(kAutoSoftmax, hv);
